@@ -1,0 +1,262 @@
+// C ABI of the Block-GTQ packed-cache decode path: argument checks, sizes, launches.
+// Declared and documented in include/bgtq.h.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "bgtq_internal.h"
+
+using namespace bgtq;
+
+namespace {
+
+thread_local std::string g_last_error;
+std::mutex g_init_mutex;
+bool g_device_ready[64] = {};
+
+bgtq_status fail(bgtq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bgtq_status fail(bgtq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bgtq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BGTQ_OK;
+  return fail(BGTQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bgtq_status ensure_init() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(BGTQ_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_init_mutex);
+  if (g_device_ready[dev]) return BGTQ_OK;
+  e = upload_tables(host_tables());
+  if (e != hipSuccess) return hip_status(e, "upload codebook tables");
+  g_device_ready[dev] = true;
+  return BGTQ_OK;
+}
+
+bool head_dim_ok(int d) { return d >= 2 && d <= BGTQ_MAX_HEAD_DIM && d % 2 == 0; }
+
+bgtq_status check_cache(const bgtq_cache* c, bool need_layout) {
+  if (!c) return fail(BGTQ_ERR_INVALID_ARG, "cache is NULL");
+  if (c->batch < 1 || c->n_kv_heads < 1) return fail(BGTQ_ERR_INVALID_ARG, "batch and n_kv_heads must be >= 1");
+  if (!head_dim_ok(c->head_dim)) return fail(BGTQ_ERR_INVALID_ARG, "head_dim %d must be even, 2..256", c->head_dim);
+  if (c->v_bits < 1 || c->v_bits > BGTQ_MAX_BITS) return fail(BGTQ_ERR_INVALID_ARG, "v_bits must be 1..8");
+  if (c->k_width_sum < 0 || c->k_width_sum > BGTQ_MAX_BITS * (c->head_dim / 2))
+    return fail(BGTQ_ERR_BUDGET, "k_width_sum %d outside [0, 8 * head_dim/2]", c->k_width_sum);
+  if (c->capacity < kTile || c->capacity % kTile)
+    return fail(BGTQ_ERR_INVALID_ARG, "capacity must be a positive multiple of 64");
+  if (c->capacity > (int64_t(1) << 31) - 64) return fail(BGTQ_ERR_INVALID_ARG, "capacity too large");
+  if (c->pairing != BGTQ_PAIR_HALF && c->pairing != BGTQ_PAIR_INTERLEAVED)
+    return fail(BGTQ_ERR_INVALID_ARG, "bad pairing");
+  if (!c->k_codes && c->k_width_sum > 0) return fail(BGTQ_ERR_INVALID_ARG, "k_codes is NULL");
+  if (!c->k_norms || !c->v_codes || !c->v_norms || !c->lengths)
+    return fail(BGTQ_ERR_INVALID_ARG, "cache arrays must not be NULL");
+  if (need_layout && !c->layouts) return fail(BGTQ_ERR_INVALID_ARG, "layouts is NULL");
+  return BGTQ_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* bgtq_status_string(bgtq_status s) {
+  switch (s) {
+    case BGTQ_OK: return "ok";
+    case BGTQ_ERR_INVALID_ARG: return "invalid argument";
+    case BGTQ_ERR_BUDGET: return "infeasible bit budget";
+    case BGTQ_ERR_CAPACITY: return "cache capacity exceeded";
+    case BGTQ_ERR_WORKSPACE: return "workspace too small";
+    case BGTQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BGTQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* bgtq_last_error(void) { return g_last_error.c_str(); }
+
+bgtq_status bgtq_init(void) { return ensure_init(); }
+
+bgtq_status bgtq_codebook(int bits, float* thresholds, float* centroids, double* distortion) {
+  if (bits < 0 || bits > BGTQ_MAX_BITS) return fail(BGTQ_ERR_INVALID_ARG, "bits must be 0..8");
+  const Tables& t = host_tables();
+  if (distortion) *distortion = t.dist[bits];
+  if (bits == 0) return BGTQ_OK;
+  if (thresholds) std::memcpy(thresholds, t.thr[bits - 1], sizeof(float) * ((1u << bits) - 1));
+  if (centroids) std::memcpy(centroids, t.cen[bits - 1], sizeof(float) * (1u << bits));
+  return BGTQ_OK;
+}
+
+size_t bgtq_cache_bytes(int batch, int n_kv_heads, int head_dim, int k_width_sum, int v_bits, int64_t capacity,
+                        size_t* out4) {
+  if (batch < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || v_bits < 1 || v_bits > BGTQ_MAX_BITS ||
+      k_width_sum < 0 || k_width_sum > BGTQ_MAX_BITS * (head_dim / 2) || capacity < kTile || capacity % kTile)
+    return 0;
+  const size_t heads = size_t(batch) * n_kv_heads, tiles = size_t(capacity / kTile);
+  const size_t kc = heads * tiles * record_chunks(k_width_sum) * kTile * 16;
+  const size_t kn = heads * tiles * kMaxGroups * kTile * 2;
+  const size_t vc = heads * tiles * head_dim * 8 * v_bits;
+  const size_t vn = heads * tiles * kTile * 2;
+  if (out4) { out4[0] = kc; out4[1] = kn; out4[2] = vc; out4[3] = vn; }
+  return kc + kn + vc + vn;
+}
+
+size_t bgtq_energy_workspace_bytes(int n_heads, int64_t n_tokens, int head_dim) {
+  if (n_heads < 1 || n_tokens < 1 || !head_dim_ok(head_dim)) return 0;
+  const int64_t chunks = (n_tokens + kEnergyChunk - 1) / kEnergyChunk;
+  return size_t(n_heads) * size_t(chunks) * size_t(head_dim / 2) * sizeof(double);
+}
+
+bgtq_status bgtq_block_energy(const void* keys, bgtq_dtype dtype, int n_heads, int64_t n_tokens, int head_dim,
+                              int64_t stride_head, int64_t stride_token, bgtq_pairing pairing, double* energy_out,
+                              void* workspace, size_t workspace_bytes, bgtq_stream stream) {
+  if (!keys || !energy_out) return fail(BGTQ_ERR_INVALID_ARG, "keys and energy_out must not be NULL");
+  if (dtype != BGTQ_F32 && dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad dtype");
+  if (n_heads < 1 || n_tokens < 1) return fail(BGTQ_ERR_INVALID_ARG, "n_heads and n_tokens must be >= 1");
+  if (!head_dim_ok(head_dim)) return fail(BGTQ_ERR_INVALID_ARG, "head_dim %d must be even, 2..256", head_dim);
+  if (pairing != BGTQ_PAIR_HALF && pairing != BGTQ_PAIR_INTERLEAVED) return fail(BGTQ_ERR_INVALID_ARG, "bad pairing");
+  if (stride_token < head_dim || (n_heads > 1 && stride_head < 1))
+    return fail(BGTQ_ERR_INVALID_ARG, "strides must not overlap a key row");
+  const size_t need = bgtq_energy_workspace_bytes(n_heads, n_tokens, head_dim);
+  if (!workspace || workspace_bytes < need)
+    return fail(BGTQ_ERR_WORKSPACE, "energy workspace needs %zu bytes", need);
+  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
+  return hip_status(launch_energy(keys, dtype, n_heads, n_tokens, head_dim, stride_head, stride_token, pairing,
+                                  energy_out, static_cast<double*>(workspace), static_cast<hipStream_t>(stream)),
+                    "block energy launch");
+}
+
+bgtq_status bgtq_allocate_bits(const double* energy, int n_heads, int head_dim, int k_width_sum, int b_min,
+                               int b_max, bgtq_pairing pairing, uint8_t* widths_out, void* layouts_out,
+                               bgtq_stream stream) {
+  if (!energy || !widths_out || !layouts_out) return fail(BGTQ_ERR_INVALID_ARG, "NULL pointer");
+  if (n_heads < 1) return fail(BGTQ_ERR_INVALID_ARG, "n_heads must be >= 1");
+  if (!head_dim_ok(head_dim)) return fail(BGTQ_ERR_INVALID_ARG, "head_dim %d must be even, 2..256", head_dim);
+  if (pairing != BGTQ_PAIR_HALF && pairing != BGTQ_PAIR_INTERLEAVED) return fail(BGTQ_ERR_INVALID_ARG, "bad pairing");
+  const int n = head_dim / 2;
+  if (b_min < 0 || b_max < b_min || b_max > BGTQ_MAX_BITS)
+    return fail(BGTQ_ERR_BUDGET, "need 0 <= b_min <= b_max <= 8 (got %d, %d)", b_min, b_max);
+  if (k_width_sum < n * b_min || k_width_sum > n * b_max)
+    return fail(BGTQ_ERR_BUDGET, "k_width_sum %d outside [%d, %d]", k_width_sum, n * b_min, n * b_max);
+  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
+  return hip_status(launch_allocate(energy, n_heads, n, k_width_sum - n * b_min, b_min, b_max, pairing, widths_out,
+                                    static_cast<HeadLayout*>(layouts_out), static_cast<hipStream_t>(stream)),
+                    "allocate launch");
+}
+
+bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cache, int seq_begin, int n_seqs,
+                                 const void* keys, const void* values, bgtq_dtype dtype, int64_t n_new,
+                                 int64_t stride_seq, int64_t stride_head, int64_t stride_token, bgtq_stream stream) {
+  if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
+  if (!qz || !qz->rot_bank || !qz->rot_v) return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
+  if (qz->head_dim != cache->head_dim) return fail(BGTQ_ERR_INVALID_ARG, "quantizer head_dim != cache head_dim");
+  if (!keys || !values) return fail(BGTQ_ERR_INVALID_ARG, "keys and values must not be NULL");
+  if (dtype != BGTQ_F32 && dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad dtype");
+  if (n_seqs < 1 || seq_begin < 0 || seq_begin + n_seqs > cache->batch)
+    return fail(BGTQ_ERR_INVALID_ARG, "sequence range [%d, %d) outside batch %d", seq_begin, seq_begin + n_seqs,
+                cache->batch);
+  if (n_new < 1) return fail(BGTQ_ERR_INVALID_ARG, "n_new must be >= 1");
+  if (n_new > cache->capacity) return fail(BGTQ_ERR_CAPACITY, "n_new %lld exceeds capacity %lld",
+                                           (long long)n_new, (long long)cache->capacity);
+  if (stride_token < cache->head_dim || stride_head < 1 || stride_seq < 1)
+    return fail(BGTQ_ERR_INVALID_ARG, "strides must be positive and not overlap a row");
+  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
+  AppendArgs a{};
+  a.rot_bank = qz->rot_bank;
+  a.rot_v = qz->rot_v;
+  a.keys = keys;
+  a.values = values;
+  a.stride_seq = stride_seq;
+  a.stride_head = stride_head;
+  a.stride_token = stride_token;
+  a.k_codes = cache->k_codes;
+  a.k_norms = cache->k_norms;
+  a.v_codes = cache->v_codes;
+  a.v_norms = cache->v_norms;
+  a.lengths = cache->lengths;
+  a.layouts = static_cast<const HeadLayout*>(cache->layouts);
+  a.status = cache->status;
+  a.capacity = cache->capacity;
+  a.n_new = n_new;
+  a.seq_begin = seq_begin;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.d = cache->head_dim;
+  a.v_bits = cache->v_bits;
+  a.chunks = record_chunks(cache->k_width_sum);
+  return hip_status(launch_append(a, dtype, n_seqs, static_cast<hipStream_t>(stream)), "quantize-append launch");
+}
+
+size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t capacity) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || capacity < kTile) return 0;
+  const int splits = decode_splits(batch, n_kv_heads, capacity);
+  const size_t qrot = align256(size_t(batch) * n_kv_heads * head_dim * kQPad * 4);
+  const size_t part = align256(size_t(batch) * n_q_heads * splits * (head_dim + 2) * 4);
+  return qrot + part;
+}
+
+bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
+                                  bgtq_dtype q_dtype, const int64_t* q_pos, double rope_theta, float softmax_scale,
+                                  float* out, float* logits_out, void* workspace, size_t workspace_bytes,
+                                  bgtq_stream stream) {
+  if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
+  if (!qz || !qz->rot_bank || !qz->rot_v) return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
+  if (qz->head_dim != cache->head_dim) return fail(BGTQ_ERR_INVALID_ARG, "quantizer head_dim != cache head_dim");
+  if (!q || !out) return fail(BGTQ_ERR_INVALID_ARG, "q and out must not be NULL");
+  if (q_dtype != BGTQ_F32 && q_dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad q dtype");
+  if (n_q_heads < cache->n_kv_heads || n_q_heads % cache->n_kv_heads)
+    return fail(BGTQ_ERR_INVALID_ARG, "n_q_heads %d must be a multiple of n_kv_heads %d", n_q_heads,
+                cache->n_kv_heads);
+  const int group = n_q_heads / cache->n_kv_heads;
+  if (group > BGTQ_MAX_GROUP) return fail(BGTQ_ERR_UNSUPPORTED, "group size %d > %d", group, BGTQ_MAX_GROUP);
+  const int d = cache->head_dim;
+  if (d != 64 && d != 128 && d != 256) return fail(BGTQ_ERR_UNSUPPORTED, "decode is built for head_dim 64/128/256");
+  if (!(softmax_scale > 0.0f)) return fail(BGTQ_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  const size_t need = bgtq_decode_workspace_bytes(cache->batch, n_q_heads, cache->n_kv_heads, d, cache->capacity);
+  if (!workspace || workspace_bytes < need)
+    return fail(BGTQ_ERR_WORKSPACE, "decode workspace needs %zu bytes", need);
+  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
+  DecodeArgs a{};
+  a.rot_bank = qz->rot_bank;
+  a.rot_v = qz->rot_v;
+  a.q = q;
+  a.q_pos = q_pos;
+  a.k_codes = cache->k_codes;
+  a.k_norms = cache->k_norms;
+  a.v_codes = cache->v_codes;
+  a.v_norms = cache->v_norms;
+  a.lengths = cache->lengths;
+  a.layouts = static_cast<const HeadLayout*>(cache->layouts);
+  a.out = out;
+  a.logits = logits_out;
+  a.n_split = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity);
+  a.qrot = static_cast<float*>(workspace);
+  a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256(size_t(cache->batch) * cache->n_kv_heads * d * kQPad * 4));
+  a.rope_theta = rope_theta;
+  a.scale = softmax_scale;
+  a.capacity = cache->capacity;
+  a.batch = cache->batch;
+  a.n_q = n_q_heads;
+  a.n_kv = cache->n_kv_heads;
+  a.group = group;
+  a.d = d;
+  a.v_bits = cache->v_bits;
+  a.chunks = record_chunks(cache->k_width_sum);
+  a.pairing = cache->pairing;
+  return hip_status(launch_decode(a, q_dtype, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+"""Prefill and decode steps composed from the four library calls.
+
+Prefill of one sequence (per layer): block energy of its keys, greedy widths
+under the K budget, then quantize-and-append of the whole prompt.  A decode
+step: append the new token's key and value, then attend (the query's own
+token is the newest cached one).  Every step runs in the HIP library.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import bgtq
+
+
+def prefill(quantizer, cache: bgtq.PackedCache, keys: torch.Tensor, values: torch.Tensor, seq: int,
+            b_min: int = 0, b_max: int = 8) -> None:
+    """keys, values [n_kv_heads, T, head_dim] of sequence `seq` (post-RoPE keys)."""
+    energy = bgtq.bgtq_block_energy(keys, cache.pairing)
+    bgtq.bgtq_allocate_bits(energy, cache.k_width_sum, b_min, b_max, cache.pairing,
+                            widths_out=cache.widths[seq], layouts_out=cache.layouts[seq])
+    bgtq.bgtq_quantize_append(quantizer, cache, keys.unsqueeze(0), values.unsqueeze(0), seq_begin=seq)
+
+
+def decode_step(quantizer, cache: bgtq.PackedCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                q: torch.Tensor, rope_theta: float, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """k_new, v_new [batch, n_kv_heads, 1, head_dim]; q [batch, n_q_heads, head_dim] (pre-RoPE)."""
+    bgtq.bgtq_quantize_append(quantizer, cache, k_new, v_new, seq_begin=0)
+    return bgtq.bgtq_decode_attention(quantizer, cache, q, rope_theta, out=out, workspace=workspace)

@@ -1,0 +1,217 @@
+/*
+ * bgtq.h -- C ABI of the Block-GTQ packed-cache decode path for AMD MI355X (gfx950).
+ *
+ * Method: "RoPE-Aware Bit Allocation for KV-Cache Quantization" (Liang, Zhang,
+ * Jia; arXiv 2606.24033), abstract.  Per layer and KV head the method scores
+ * the energy of every 2-D RoPE frequency block, hands out integer bit widths
+ * greedily by marginal gain under a matched K bit budget, quantizes keys with
+ * TurboQuant-MSE at those widths and values at a uniform width, and serves
+ * decode attention from the packed cache.  The four calls below are those
+ * steps.  Where the abstract leaves a detail open, the reading is stated at
+ * the call.
+ *
+ * Conventions for every call
+ *   - All tensors are device memory owned by the caller; the library never
+ *     allocates, frees or keeps device memory, and keeps no per-call state.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream) and the call returns without waiting.
+ *   - Arguments are validated on the host before anything is enqueued; a bad
+ *     argument returns an error status and enqueues nothing.  A failed launch
+ *     returns BGTQ_ERR_HIP.  bgtq_last_error() gives a message for the last
+ *     failure on the calling thread.  No call aborts or throws.
+ *   - Strides are in elements.  fp16 data is IEEE binary16 stored as uint16.
+ *   - Call bgtq_init() once per device before capturing calls in a HIP graph;
+ *     otherwise the first call on a device initialises it (a synchronous copy
+ *     of the codebook tables to device constant memory).
+ */
+#ifndef BGTQ_H
+#define BGTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BGTQ_OK = 0,
+  BGTQ_ERR_INVALID_ARG = 1,   /* null pointer, bad size, stride or enum */
+  BGTQ_ERR_BUDGET = 2,        /* k_width_sum outside [n*b_min, n*b_max], or b_max > 8 */
+  BGTQ_ERR_CAPACITY = 3,      /* capacity too small for the request */
+  BGTQ_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
+  BGTQ_ERR_UNSUPPORTED = 5,   /* valid but not built: head_dim, GQA group size */
+  BGTQ_ERR_HIP = 6            /* the HIP runtime reported an error */
+} bgtq_status;
+
+typedef enum { BGTQ_F32 = 0, BGTQ_BF16 = 1 } bgtq_dtype;
+
+/* Which two coordinates form RoPE block j (the pages only say "two-dimensional
+ * frequency blocks"): HALF pairs (j, j + d/2) as Llama/Qwen checkpoints do,
+ * INTERLEAVED pairs (2j, 2j + 1). */
+typedef enum { BGTQ_PAIR_HALF = 0, BGTQ_PAIR_INTERLEAVED = 1 } bgtq_pairing;
+
+typedef void* bgtq_stream;
+
+/* Limits of this build. */
+#define BGTQ_MAX_HEAD_DIM 256
+#define BGTQ_MAX_BITS 8
+#define BGTQ_MAX_GROUP 16        /* query heads per KV head */
+#define BGTQ_TILE 64             /* token slots per cache tile */
+#define BGTQ_LAYOUT_BYTES 2048   /* size of one per-head layout descriptor */
+
+/* Random rotations the quantizer draws (TQ-MSE rotates before scalar coding).
+ * Device memory, caller-owned, read-only, shared by all layers and heads.
+ *   rot_bank: Haar matrices for the key width groups, m = 2, 4, ..., head_dim,
+ *             each m x m row-major (y = R x), concatenated in that order
+ *             (sum over even m of m*m floats).
+ *   rot_v:    head_dim x head_dim row-major rotation for values. */
+typedef struct {
+  const float* rot_bank;
+  const float* rot_v;
+  int head_dim;
+} bgtq_quantizer;
+
+/* Packed K/V cache of one layer for a batch of sequences.  All pointers are
+ * device memory the caller allocates (sizes from bgtq_cache_bytes) and owns.
+ * Region of sequence s, KV head h = [s * n_kv_heads + h] of each array.
+ * With tiles = capacity / 64 and chunks = ceil(2 * k_width_sum / 128):
+ *   k_codes  uint8  [batch][n_kv_heads][tiles][chunks][64][16]
+ *            slot j of a tile holds the token's K record: its codes in storage
+ *            order, LSB first, code p at record bits [offset_p, offset_p+w_p).
+ *   k_norms  fp16   [batch][n_kv_heads][tiles][8][64]  width-group norms.
+ *   v_codes  uint8  [batch][n_kv_heads][tiles][head_dim][8*v_bits]
+ *            rotated coordinate r of a tile is a 64*v_bits-bit segment; slot j
+ *            holds its code at bits [j*v_bits, (j+1)*v_bits).
+ *   v_norms  fp16   [batch][n_kv_heads][tiles][64].
+ *   lengths  int32  [batch]  tokens cached per sequence; advanced by
+ *            bgtq_quantize_append.  The caller sets it (normally 0) at start.
+ *   widths   uint8  [batch][n_kv_heads][head_dim/2], layouts
+ *            [batch][n_kv_heads][BGTQ_LAYOUT_BYTES]: written by
+ *            bgtq_allocate_bits at prefill and read by the other calls.
+ *   status   int32  [1], nullable: a kernel sets bit 0 when an append would
+ *            pass capacity (that append is then skipped for that sequence).
+ * Unused slots may hold anything; only slots below lengths[s] are read. */
+typedef struct {
+  int batch;
+  int n_kv_heads;
+  int head_dim;
+  int k_width_sum;      /* B = sum of block widths = (K bits per coordinate) * head_dim/2 */
+  int v_bits;           /* 1..8 */
+  int64_t capacity;     /* token slots per sequence, multiple of 64 */
+  bgtq_pairing pairing;
+  uint8_t* k_codes;
+  uint16_t* k_norms;
+  uint8_t* v_codes;
+  uint16_t* v_norms;
+  int32_t* lengths;
+  uint8_t* widths;
+  void* layouts;
+  int32_t* status;
+} bgtq_cache;
+
+/* Label-free energy score of every RoPE block (abstract: "for each layer and
+ * KV head ... a label-free energy score for each RoPE block").
+ * Reading: E_j = (1/T) * sum_t (k[t,a_j]^2 + k[t,b_j]^2) over the given keys,
+ * in fp64, summed in ascending t inside chunks of 256 tokens and then over the
+ * chunks in ascending order (a fixed order, so the result is reproducible).
+ *   keys        [n_heads] x [n_tokens] x [head_dim] of `dtype` with strides
+ *               (stride_head, stride_token, 1); post-RoPE keys are fine, RoPE
+ *               does not change block norms.
+ *   energy_out  fp64 [n_heads][head_dim/2].
+ *   workspace   >= bgtq_energy_workspace_bytes(n_heads, n_tokens, head_dim).
+ * Errors: INVALID_ARG (null, n_tokens < 1, odd or oversized head_dim),
+ * WORKSPACE, HIP. */
+bgtq_status bgtq_block_energy(const void* keys, bgtq_dtype dtype, int n_heads, int64_t n_tokens,
+                              int head_dim, int64_t stride_head, int64_t stride_token,
+                              bgtq_pairing pairing, double* energy_out, void* workspace,
+                              size_t workspace_bytes, bgtq_stream stream);
+size_t bgtq_energy_workspace_bytes(int n_heads, int64_t n_tokens, int head_dim);
+
+/* Greedy integer bit widths by marginal gain (abstract: "greedily allocates
+ * integer bit widths by marginal gain"; "high-energy RoPE blocks ... should
+ * receive more bits"; budgets matched to uniform TQ-MSE).
+ * Reading: all blocks start at b_min; k_width_sum - n*b_min times, one bit goes
+ * to the block with the largest gain E_j * (D(b_j) - D(b_j + 1)) among blocks
+ * below b_max, ties to the lowest j, where D(b) = fl32(MSE of the b-bit
+ * Lloyd-Max quantizer of N(0,1)) and D(0) = 1; gains are fp64.
+ *   energy       fp64 [n_heads][head_dim/2] (device), e.g. from bgtq_block_energy.
+ *   widths_out   uint8 [n_heads][head_dim/2].
+ *   layouts_out  [n_heads][BGTQ_LAYOUT_BYTES]: width groups (descending width,
+ *                blocks ascending), storage order and bit offsets.
+ * Errors: INVALID_ARG, BUDGET (k_width_sum infeasible or 0 > b_min > b_max > 8),
+ * HIP. */
+bgtq_status bgtq_allocate_bits(const double* energy, int n_heads, int head_dim, int k_width_sum,
+                               int b_min, int b_max, bgtq_pairing pairing, uint8_t* widths_out,
+                               void* layouts_out, bgtq_stream stream);
+
+/* TQ-MSE quantize-and-pack of new tokens (abstract: Block-GTQ "built on
+ * TurboQuant-MSE"; "packed-cache serving path").
+ * Reading (width-group TQ-MSE): blocks of equal width w >= 1 form one vector of
+ * m = 2*|group| coordinates coded at w bits: fp32 norm n (sequential sum of
+ * squares, sqrt), y = R_m x (sequential, no fused multiply-add), z = (y/n)*fl32(sqrt(m)),
+ * code = #{k : z > T_w[k]} with the fp32 Lloyd-Max thresholds of N(0,1);
+ * norm stored fp16 (nearest-even, saturated).  Values: one group of m =
+ * head_dim with rot_v at v_bits.  Codes, norms and packed bytes are
+ * reproducible bit for bit.
+ * Appends n_new tokens to each sequence s in [seq_begin, seq_begin + n_seqs):
+ * token i of s goes to slot lengths[s] + i, then lengths[s] += n_new.
+ *   keys, values  [n_seqs][n_kv_heads][n_new][head_dim] of `dtype` with strides
+ *                 (stride_seq, stride_head, stride_token, 1); keys post-RoPE.
+ * The sequence's widths/layouts must already be written by bgtq_allocate_bits.
+ * Errors: INVALID_ARG, CAPACITY (n_new > capacity; an overflow that depends on
+ * the device lengths is reported through cache->status instead), HIP. */
+bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cache, int seq_begin,
+                                 int n_seqs, const void* keys, const void* values, bgtq_dtype dtype,
+                                 int64_t n_new, int64_t stride_seq, int64_t stride_head,
+                                 int64_t stride_token, bgtq_stream stream);
+
+/* Decode attention straight from the packed cache (abstract: RoPE query-key
+ * logits; "packed-cache serving path" that attends over packed K3V3 at 128K).
+ * For every sequence s and query head h (KV head h / (n_q_heads/n_kv_heads)):
+ * q' = RoPE(q[s][h], pos) with angles pos*rope_theta^(-2j/d) formed in fp64;
+ * logits l_t = softmax_scale * q' . k_hat_t over the cached slots t <
+ * lengths[s]; out = sum_t softmax(l)_t * v_hat_t, with k_hat, v_hat the TQ-MSE
+ * reconstructions (width-0 blocks are zero).  The packed codes are decoded in
+ * registers; the query is rotated into each width group's frame instead of
+ * un-rotating every key, and the value rotation is undone once per head.
+ *   q           [batch][n_q_heads][head_dim] of q_dtype, pre-RoPE (contiguous).
+ *   q_pos       int64 [batch] (device) query positions, or NULL for
+ *               lengths[s] - 1 (the newest cached token).
+ *   rope_theta  RoPE base; <= 0 means q is already rotated.
+ *   out         fp32 [batch][n_q_heads][head_dim].
+ *   logits_out  nullable fp32 [batch][n_q_heads][capacity]; slots >= lengths[s]
+ *               are left untouched.
+ *   workspace   >= bgtq_decode_workspace_bytes(...); must be zero-filled before
+ *               its first use; every call leaves it ready for the next.
+ * A sequence with lengths[s] == 0 gets out = 0.
+ * Errors: INVALID_ARG, UNSUPPORTED (group size > 16, head_dim not 64/128/256),
+ * WORKSPACE, HIP. */
+bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads,
+                                  const void* q, bgtq_dtype q_dtype, const int64_t* q_pos,
+                                  double rope_theta, float softmax_scale, float* out,
+                                  float* logits_out, void* workspace, size_t workspace_bytes,
+                                  bgtq_stream stream);
+size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                   int64_t capacity);
+
+/* Bytes of each cache array for the given geometry (k_codes, k_norms, v_codes,
+ * v_norms, in that order, written to out4); returns the total, 0 if invalid. */
+size_t bgtq_cache_bytes(int batch, int n_kv_heads, int head_dim, int k_width_sum, int v_bits,
+                        int64_t capacity, size_t* out4);
+
+/* The frozen fp32 Lloyd-Max tables and fl32(D(b)) the kernels use, copied to host
+ * memory: thresholds[2^bits - 1], centroids[2^bits], *distortion (bits 0..8;
+ * bits 0 has no tables).  Host-only, enqueues nothing. */
+bgtq_status bgtq_codebook(int bits, float* thresholds, float* centroids, double* distortion);
+
+/* Copy the frozen tables to the current device's constant memory (synchronous). */
+bgtq_status bgtq_init(void);
+
+const char* bgtq_status_string(bgtq_status s);
+const char* bgtq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BGTQ_H */

@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every declared call, and validates on the host (CPU only)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from decode_attention_rope_amd import bgtq
+from oracle import codebook, pack
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation before any HIP call
+
+
+def test_exports_every_declared_symbol():
+    names = bgtq.header_functions()
+    assert {"bgtq_block_energy", "bgtq_allocate_bits", "bgtq_quantize_append", "bgtq_decode_attention"} <= set(names)
+    lib = bgtq.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(bgtq._SIGNATURES), "binding and header disagree"
+
+
+@pytest.mark.parametrize("bits", range(0, 9))
+def test_library_tables_equal_oracle_tables(bits):
+    """The library's own Lloyd-Max solve (C++) agrees bit for bit with the oracle's (numpy)."""
+    thr, cen, dist = bgtq.codebook(bits)
+    assert dist == codebook.distortion32()[bits]
+    if bits:
+        np.testing.assert_array_equal(thr, codebook.thresholds32(bits))
+        np.testing.assert_array_equal(cen, codebook.centroids32(bits))
+
+
+@pytest.mark.parametrize("d,ksum,vb,cap", [(64, 96, 3, 256), (128, 192, 3, 131136), (128, 128, 2, 64),
+                                           (256, 1024, 8, 128), (128, 0, 1, 64)])
+def test_cache_sizes_match_layout(d, ksum, vb, cap):
+    total, parts = bgtq.cache_bytes(2, 3, d, ksum, vb, cap)
+    chunks = -(-2 * ksum // 128)
+    ref = pack.region_sizes(d, chunks, vb, cap)
+    per = [ref["k_codes"], ref["k_norms"] * 2, ref["v_codes"], ref["v_norms"] * 2]
+    assert list(parts) == [6 * x for x in per] and total == sum(parts)
+
+
+def test_invalid_geometry_sizes_are_zero():
+    lib = bgtq.lib()
+    assert lib.bgtq_cache_bytes(1, 1, 63, 96, 3, 256, None) == 0
+    assert lib.bgtq_cache_bytes(1, 1, 64, 96, 3, 100, None) == 0
+    assert lib.bgtq_cache_bytes(1, 1, 64, 96, 9, 256, None) == 0
+    assert lib.bgtq_cache_bytes(1, 1, 64, 257, 3, 256, None) == 0
+    assert lib.bgtq_decode_workspace_bytes(1, 16, 2, 128, 131072) > 0
+
+
+def test_energy_validation():
+    lib = bgtq.lib()
+    ws = 1 << 20
+    assert lib.bgtq_block_energy(None, 0, 1, 10, 64, 640, 64, 0, FAKE, FAKE, ws, None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_block_energy(FAKE, 0, 1, 10, 63, 630, 63, 0, FAKE, FAKE, ws, None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_block_energy(FAKE, 0, 1, 0, 64, 640, 64, 0, FAKE, FAKE, ws, None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_block_energy(FAKE, 7, 1, 10, 64, 640, 64, 0, FAKE, FAKE, ws, None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_block_energy(FAKE, 0, 1, 10, 64, 640, 32, 0, FAKE, FAKE, ws, None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_block_energy(FAKE, 0, 1, 10, 64, 640, 64, 0, FAKE, FAKE, 8, None) == bgtq.ERR_WORKSPACE
+    assert lib.bgtq_block_energy(FAKE, 0, 1, 10, 64, 640, 64, 0, FAKE, None, ws, None) == bgtq.ERR_WORKSPACE
+    assert b"workspace" in lib.bgtq_last_error()
+
+
+def test_allocate_validation():
+    lib = bgtq.lib()
+    assert lib.bgtq_allocate_bits(None, 1, 64, 96, 0, 8, 0, FAKE, FAKE, None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_allocate_bits(FAKE, 1, 64, 257, 0, 8, 0, FAKE, FAKE, None) == bgtq.ERR_BUDGET
+    assert lib.bgtq_allocate_bits(FAKE, 1, 64, 31, 1, 8, 0, FAKE, FAKE, None) == bgtq.ERR_BUDGET
+    assert lib.bgtq_allocate_bits(FAKE, 1, 64, 96, 0, 9, 0, FAKE, FAKE, None) == bgtq.ERR_BUDGET
+    assert lib.bgtq_allocate_bits(FAKE, 1, 64, 96, 4, 3, 0, FAKE, FAKE, None) == bgtq.ERR_BUDGET
+    assert lib.bgtq_allocate_bits(FAKE, 0, 64, 96, 0, 8, 0, FAKE, FAKE, None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_allocate_bits(FAKE, 1, 64, 96, 0, 8, 5, FAKE, FAKE, None) == bgtq.ERR_INVALID_ARG
+
+
+def _desc(**over):
+    base = dict(batch=1, n_kv_heads=2, head_dim=128, k_width_sum=192, v_bits=3, capacity=256, pairing=0,
+                k_codes=FAKE, k_norms=FAKE, v_codes=FAKE, v_norms=FAKE, lengths=FAKE, widths=FAKE,
+                layouts=FAKE, status=None)
+    base.update(over)
+    return bgtq.CacheDesc(*[base[f] for f, _ in bgtq.CacheDesc._fields_])
+
+
+def _quantizer(d=128):
+    return bgtq.Quantizer(FAKE, FAKE, d)
+
+
+def test_append_validation():
+    lib = bgtq.lib()
+
+    def call(desc, qz=None, n_new=1, seq_begin=0, n_seqs=1, st=(1, 1, 128), dtype=0, keys=FAKE):
+        qz = qz or _quantizer()
+        return lib.bgtq_quantize_append(ctypes.byref(qz), ctypes.byref(desc), seq_begin, n_seqs, keys, FAKE,
+                                        dtype, n_new, *(st[0] * 1000, st[1] * 300, st[2]), None)
+
+    assert call(_desc(capacity=100)) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(v_bits=0)) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(k_width_sum=1025)) == bgtq.ERR_BUDGET
+    assert call(_desc(lengths=None)) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(layouts=None)) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), qz=_quantizer(64)) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), n_new=0) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), n_new=257) == bgtq.ERR_CAPACITY
+    assert call(_desc(), seq_begin=1) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), st=(1, 1, 64)) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), dtype=3) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), keys=None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_quantize_append(None, ctypes.byref(_desc()), 0, 1, FAKE, FAKE, 0, 1, 1, 1, 128,
+                                    None) == bgtq.ERR_INVALID_ARG
+
+
+def test_decode_validation():
+    lib = bgtq.lib()
+    need = lib.bgtq_decode_workspace_bytes(1, 16, 2, 128, 256)
+
+    def call(desc, n_q=16, ws=need, qz=None, scale=0.088, d=None):
+        qz = qz or _quantizer()
+        return lib.bgtq_decode_attention(ctypes.byref(qz), ctypes.byref(desc), n_q, FAKE, 0, None, 1e6, scale,
+                                         FAKE, None, FAKE, ws, None)
+
+    assert call(_desc(), n_q=15) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), n_q=1) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), n_q=34) == bgtq.ERR_UNSUPPORTED
+    assert call(_desc(head_dim=96), qz=_quantizer(96)) == bgtq.ERR_UNSUPPORTED
+    assert call(_desc(), ws=need - 1) == bgtq.ERR_WORKSPACE
+    assert call(_desc(), scale=0.0) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
+
+
+def test_status_strings():
+    lib = bgtq.lib()
+    for s in range(7):
+        assert lib.bgtq_status_string(s)
+    assert lib.bgtq_status_string(99) == b"unknown status"

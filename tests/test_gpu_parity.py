@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle (needs an MI355X).
+
+Bit-exact: energies, widths, layout descriptors, codes, norms and packed bytes.
+Within 2e-3 normwise max relative error per (sequence, query head): logits and outputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_rope_amd import bgtq, pipeline, synth
+from oracle import allocate, codebook, energy, layout, rope
+from _ref import TOL, assert_region_equal, decode_reference, head_reference, rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device(DEV)
+
+
+def _t(x, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def rot128():
+    _cuda()
+    bank, rv = synth.rotation_bank(128), synth.rotation_v(128)
+    return bank, rv, bgtq.make_quantizer(_t(bank), _t(rv), 128)
+
+
+@pytest.fixture(scope="module")
+def rot64():
+    _cuda()
+    bank, rv = synth.rotation_bank(64), synth.rotation_v(64)
+    return bank, rv, bgtq.make_quantizer(_t(bank), _t(rv), 64)
+
+
+# ---------------------------------------------------------------- energy
+
+@pytest.mark.parametrize("t_len,dtype,pairing", [(1, "f32", 0), (255, "f32", 1), (256, "bf16", 0),
+                                                 (257, "f32", 0), (5000, "bf16", 1), (70000, "f32", 0)])
+def test_block_energy_bit_exact(t_len, dtype, pairing):
+    _cuda()
+    _say(f"energy T={t_len} {dtype} pairing={pairing}")
+    rng = np.random.default_rng(t_len)
+    k = (rng.standard_normal((3, t_len, 128)) * np.exp(rng.uniform(-3, 2, size=(3, 1, 128)))).astype(np.float32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    kt = _t(k, tdt)
+    k_exact = kt.float().cpu().numpy()
+    # a strided view: heads interleaved with padding
+    big = torch.zeros((3, t_len, 160), dtype=tdt, device=DEV)
+    big[:, :, :128] = kt
+    got = bgtq.bgtq_block_energy(big[:, :, :128], pairing).cpu().numpy()
+    want = np.stack([energy.block_energy(k_exact[h], pairing) for h in range(3)])
+    np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------- allocation
+
+def _layout_fields(raw: np.ndarray):
+    i32 = raw[:144].view(np.int32)
+    return {"n_groups": i32[0], "d_eff": i32[1], "code_bits": i32[2], "chunks": i32[3],
+            "g_width": i32[4:12], "g_first": i32[12:20], "g_m": i32[20:28], "g_bitoff": i32[28:36],
+            "perm": raw[144:400], "group": raw[400:656], "offset": raw[656:1168].view(np.uint16)}
+
+
+@pytest.mark.parametrize("n,seed", [(32, 0), (64, 1), (64, 2), (128, 3)])
+def test_allocate_bit_exact(n, seed):
+    _cuda()
+    _say(f"allocate n={n} seed={seed}")
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(12):
+        kind = i % 4
+        e = [rng.exponential(size=n), np.exp(rng.uniform(-9, 1, size=n)),
+             rng.integers(0, 3, size=n).astype(float), np.full(n, 0.5)][kind]
+        b_min = int(rng.integers(0, 3))
+        b_max = int(rng.integers(max(b_min, 1), 9))
+        budget = int(rng.integers(n * b_min, n * b_max + 1))
+        cases.append((e, budget, b_min, b_max, int(rng.integers(2))))
+    for e, budget, b_min, b_max, pairing in cases:
+        w, lay = bgtq.bgtq_allocate_bits(_t(e[None], torch.float64), budget, b_min, b_max, pairing)
+        want = allocate.greedy(e, budget, b_min, b_max)
+        np.testing.assert_array_equal(w.cpu().numpy()[0], want)
+        ref = layout.build(want, pairing)
+        f = _layout_fields(lay.cpu().numpy()[0])
+        assert f["n_groups"] == len(ref.groups) and f["d_eff"] == ref.d_eff
+        assert f["code_bits"] == ref.code_bits and f["chunks"] == ref.chunks
+        for g, grp in enumerate(ref.groups):
+            assert (f["g_width"][g], f["g_first"][g], f["g_m"][g], f["g_bitoff"][g]) == \
+                (grp.width, grp.first, grp.m, grp.bit_offset)
+        np.testing.assert_array_equal(f["perm"][:ref.d_eff], ref.perm)
+        np.testing.assert_array_equal(f["offset"][:ref.d_eff], ref.offset)
+
+
+# ---------------------------------------------------------------- quantize + pack
+
+@pytest.mark.parametrize("d,k_bits,v_bits,appends", [
+    (128, 3, 3, [100, 1, 37, 64, 5]),
+    (128, 2, 2, [300]),
+    (64, 3, 1, [1, 1, 70, 33]),
+    (128, 8, 8, [65]),
+    (128, 0, 3, [40]),
+    (256, 3, 2, [129]),
+])
+def test_quantize_append_bytes_bit_exact(d, k_bits, v_bits, appends):
+    dev = _cuda()
+    _say(f"append d={d} K{k_bits}V{v_bits} appends={appends}")
+    t_len = sum(appends)
+    cap = -(-t_len // 64) * 64 + 64
+    wl = synth.Workload("append_case", 90, d=d, h_q=4, h_kv=2, theta=1e4, layers=1, seq_lens=(t_len,),
+                        k_bits=k_bits, v_bits=v_bits, key_dtype="f32", profile="decay", outlier_blocks=2)
+    bank, rv = synth.rotation_bank(d, seed=5), synth.rotation_v(d, seed=5)
+    qz = bgtq.make_quantizer(_t(bank), _t(rv), d)
+    k = np.stack([synth.keys(wl, 0, 0, h, 0, t_len) for h in range(2)])
+    v = np.stack([synth.values(wl, 0, 0, h, 0, t_len) for h in range(2)])
+    cache = bgtq.PackedCache(1, 2, d, wl.budget, v_bits, cap, device=dev)
+    e = bgtq.bgtq_block_energy(_t(k))
+    bgtq.bgtq_allocate_bits(e, wl.budget, widths_out=cache.widths[0], layouts_out=cache.layouts[0])
+    start = 0
+    for n in appends:
+        bgtq.bgtq_quantize_append(qz, cache, _t(k[:, start:start + n])[None], _t(v[:, start:start + n])[None])
+        start += n
+    torch.cuda.synchronize()
+    assert int(cache.lengths[0]) == t_len and int(cache.status[0]) == 0
+    for h in range(2):
+        ref = head_reference(k[h], v[h], wl.budget, v_bits, bank, rv, cap)
+        np.testing.assert_array_equal(cache.widths[0, h].cpu().numpy(), ref["widths"])
+        assert_region_equal(cache.region(0, h), ref["region"], t_len, ref["layout"], v_bits, d)
+
+
+def test_capacity_overflow_sets_status(rot64):
+    dev = _cuda()
+    bank, rv, qz = rot64
+    cache = bgtq.PackedCache(2, 1, 64, 96, 3, 128, device=dev)
+    k = torch.randn((2, 1, 100, 64), device=dev)
+    e = bgtq.bgtq_block_energy(k[0])
+    for s in range(2):
+        bgtq.bgtq_allocate_bits(e, 96, widths_out=cache.widths[s], layouts_out=cache.layouts[s])
+    bgtq.bgtq_quantize_append(qz, cache, k, k)
+    before = cache.k_codes.clone()
+    bgtq.bgtq_quantize_append(qz, cache, k[:, :, :50].contiguous(), k[:, :, :50].contiguous())
+    torch.cuda.synchronize()
+    assert cache.lengths.tolist() == [100, 100]
+    assert int(cache.status[0]) == 1
+    assert torch.equal(before, cache.k_codes)
+
+
+# ---------------------------------------------------------------- decode
+
+def _decode_vs_oracle(wl, t_lens, qz, bank, rv, dtype=torch.float32, append_then_attend=False, pairing=0,
+                      theta=None, check_logits=True):
+    dev = _cuda()
+    d, h_kv, g = wl.d, wl.h_kv, wl.group
+    theta = wl.theta if theta is None else theta
+    batch = len(t_lens)
+    cap = -(-(max(t_lens) + 1) // 64) * 64
+    cache = bgtq.PackedCache(batch, h_kv, d, wl.budget, wl.v_bits, cap, pairing=pairing, device=dev)
+    refs, kv = [], []
+    for s, t_len in enumerate(t_lens):
+        n_pre = t_len - 1 if append_then_attend else t_len
+        k = np.stack([synth.keys(wl, s, 0, h, 0, t_len) for h in range(h_kv)])
+        v = np.stack([synth.values(wl, s, 0, h, 0, t_len) for h in range(h_kv)])
+        kv.append((k, v))
+        if n_pre > 0:
+            pipeline.prefill(qz, cache, _t(k[:, :n_pre], dtype), _t(v[:, :n_pre], dtype), s)
+    if append_then_attend:
+        for s, (k, v) in enumerate(kv):
+            bgtq.bgtq_quantize_append(qz, cache, _t(k[:, -1:], dtype)[None], _t(v[:, -1:], dtype)[None], seq_begin=s)
+    q = np.stack([synth.queries(wl, s, 0) for s in range(batch)])
+    pos = None if append_then_attend else torch.tensor(t_lens, dtype=torch.int64, device=dev)
+    out, logits = bgtq.bgtq_decode_attention(qz, cache, _t(q), theta, q_pos=pos, logits=True)
+    torch.cuda.synchronize()
+    out, logits = out.cpu().numpy(), logits.cpu().numpy()
+    worst = 0.0
+    for s, t_len in enumerate(t_lens):
+        k, v = kv[s]
+        kx = torch.from_numpy(k).to(dtype).float().numpy()
+        vx = torch.from_numpy(v).to(dtype).float().numpy()
+        n_pre = t_len - 1 if append_then_attend else t_len
+        qpos = t_len - 1 if append_then_attend else t_len
+        for h in range(h_kv):
+            ref = head_reference(kx[h, :n_pre], vx[h, :n_pre], wl.budget, wl.v_bits, bank, rv, cap, pairing)
+            if append_then_attend:
+                # the appended token is quantized with the prefill allocation
+                from oracle import quantize as oq
+                kc, kn = oq.quantize_keys(kx[h, n_pre:], ref["layout"], bank)
+                vc, vn = oq.quantize_values(vx[h, n_pre:], rv, wl.v_bits)
+                ref["k_hat"] = np.concatenate([ref["k_hat"], oq.dequantize_keys(kc, kn, ref["layout"], bank)])
+                ref["v_hat"] = np.concatenate([ref["v_hat"], oq.dequantize_values(vc, vn, rv, wl.v_bits)])
+            o_ref, l_ref = decode_reference(q[s, h * g:(h + 1) * g], qpos, theta, ref, pairing=pairing)
+            e_out = rel_err(out[s, h * g:(h + 1) * g], o_ref)
+            assert np.all(e_out <= TOL), f"seq {s} head {h}: output error {e_out}"
+            if check_logits:
+                e_log = rel_err(logits[s, h * g:(h + 1) * g, :t_len], l_ref)
+                assert np.all(e_log <= TOL), f"seq {s} head {h}: logit error {e_log}"
+                worst = max(worst, float(e_log.max()))
+            worst = max(worst, float(e_out.max()))
+    _say(f"  worst rel err {worst:.2e}")
+    return cache
+
+
+def test_decode_tiny(rot64):
+    _say("decode tiny")
+    bank, rv, qz = rot64
+    _decode_vs_oracle(synth.TINY, [256], qz, bank, rv)
+
+
+@pytest.mark.parametrize("t_lens", [[1], [63], [64], [65], [1000, 3, 129, 4096]])
+def test_decode_ragged_lengths(t_lens, rot128):
+    _say(f"decode ragged {t_lens}")
+    bank, rv, qz = rot128
+    wl = synth.Workload("ragged", 91, d=128, h_q=14, h_kv=2, theta=1e6, layers=1, seq_lens=tuple(t_lens),
+                        k_bits=3, v_bits=2, key_dtype="f32", profile="decay", outlier_blocks=2)
+    _decode_vs_oracle(wl, t_lens, qz, bank, rv)
+
+
+def test_decode_interleaved_pairing_and_no_rope(rot64):
+    _say("decode interleaved / no rope")
+    bank, rv, qz = rot64
+    wl = synth.Workload("inter", 92, d=64, h_q=2, h_kv=1, theta=1e4, layers=1, seq_lens=(300,),
+                        k_bits=2, v_bits=3, key_dtype="f32", profile="decay", outlier_blocks=2)
+    _decode_vs_oracle(wl, [300], qz, bank, rv, pairing=1)
+    _decode_vs_oracle(wl, [300], qz, bank, rv, theta=0.0)
+
+
+def test_decode_append_then_attend(rot128):
+    _say("decode append-then-attend")
+    bank, rv, qz = rot128
+    wl = synth.Workload("ata", 93, d=128, h_q=16, h_kv=2, theta=1e6, layers=1, seq_lens=(777,),
+                        k_bits=3, v_bits=3, key_dtype="f32", profile="decay_jitter", outlier_blocks=2)
+    _decode_vs_oracle(wl, [777], qz, bank, rv, append_then_attend=True)
+
+
+def test_decode_llama8b_layer_32k_bf16(rot128):
+    """Llama-3.1-8B-shaped layer: 32 q / 8 kv heads, 32K bf16 keys with heavy-tailed outliers, K2V2."""
+    _say("decode llama8b 32K bf16")
+    bank, rv, qz = rot128
+    wl = synth.LLAMA8B_LAYER
+    _decode_vs_oracle(wl, list(wl.seq_lens), qz, bank, rv, dtype=torch.bfloat16)
+
+
+def test_decode_empty_sequence_and_zero_budget(rot64):
+    dev = _cuda()
+    _say("decode empty sequence / zero K budget")
+    bank, rv, qz = rot64
+    cache = bgtq.PackedCache(2, 1, 64, 0, 3, 128, device=dev)
+    rng = np.random.default_rng(0)
+    k = rng.standard_normal((1, 50, 64)).astype(np.float32)
+    v = rng.standard_normal((1, 50, 64)).astype(np.float32)
+    pipeline.prefill(qz, cache, _t(k), _t(v), 0)        # sequence 1 stays empty
+    q = _t(rng.standard_normal((2, 1, 64)))
+    out = bgtq.bgtq_decode_attention(qz, cache, q, 1e4, q_pos=torch.tensor([50, 0], device=dev))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert not out[1].any()
+    ref = head_reference(k[0], v[0], 0, 3, bank, rv, 128)
+    assert not ref["k_hat"].any()                         # every block dropped: logits all zero
+    np.testing.assert_allclose(out[0, 0], ref["v_hat"].mean(0), rtol=0, atol=TOL * np.abs(ref["v_hat"].mean(0)).max())
+
+
+def test_decode_is_deterministic(rot128):
+    _say("decode determinism")
+    bank, rv, qz = rot128
+    wl = synth.Workload("det", 94, d=128, h_q=8, h_kv=1, theta=1e6, layers=1, seq_lens=(5000,),
+                        k_bits=3, v_bits=3, key_dtype="f32", profile="decay", outlier_blocks=2)
+    cache = _decode_vs_oracle(wl, [5000], qz, bank, rv, check_logits=False)
+    q = _t(synth.queries(wl, 0, 0)[None])
+    a = bgtq.bgtq_decode_attention(qz, cache, q, wl.theta)
+    b = bgtq.bgtq_decode_attention(qz, cache, q, wl.theta)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_qwen3b_layer_128k_full_size(rot128):
+    """One layer of the Qwen2.5-3B-shaped 128K decode at full size (16 q / 2 kv heads, K3V3), in the
+    launch configuration the benchmark times: prefill 131072 tokens, append one, attend over 131073."""
+    _say("decode qwen3b 128K full size")
+    bank, rv, qz = rot128
+    wl = synth.QWEN3B_128K
+    _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=True)
