@@ -26,7 +26,7 @@ F32, BF16 = 0, 1
 PAIR_HALF, PAIR_INTERLEAVED = 0, 1
 TILE = 64
 MAX_GROUPS = 8
-LAYOUT_BYTES = 2048
+LAYOUT_BYTES = 4096
 
 _c = ctypes
 _vp, _i32, _i64, _sz, _f32, _f64 = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_size_t, _c.c_float, _c.c_double

@@ -1,8 +1,10 @@
 // C ABI of the Block-GTQ packed-cache decode path: argument checks, sizes, launches.
 // Declared and documented in include/bgtq.h.
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -201,10 +203,10 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
 
 size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t capacity) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || capacity < kTile) return 0;
-  const int splits = decode_splits(batch, n_kv_heads, capacity);
-  const size_t qrot = align256(size_t(batch) * n_kv_heads * head_dim * kQPad * 4);
+  const int splits = decode_splits(batch, n_kv_heads, capacity, true);
   const size_t part = align256(size_t(batch) * n_q_heads * splits * (head_dim + 2) * 4);
-  return qrot + part;
+  return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + align256(decode_qmma_bytes(batch, n_kv_heads)) +
+         part;
 }
 
 bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
@@ -241,11 +243,17 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.layouts = static_cast<const HeadLayout*>(cache->layouts);
   a.out = out;
   a.logits = logits_out;
-  a.n_split = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity);
-  a.qrot = static_cast<float*>(workspace);
-  a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       align256(size_t(cache->batch) * cache->n_kv_heads * d * kQPad * 4));
+  const char* which = std::getenv("BGTQ_DECODE_KERNEL");
+  a.use_mfma = group <= 8 && !(which && std::strcmp(which, "valu") == 0);
+  a.n_split = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma);
+  char* ws = static_cast<char*>(workspace);
+  const size_t qrot_b = align256(decode_qrot_bytes(cache->batch, cache->n_kv_heads, d));
+  const size_t qmma_b = align256(decode_qmma_bytes(cache->batch, cache->n_kv_heads));
+  a.qrot = reinterpret_cast<float*>(ws);
+  a.qmma = reinterpret_cast<uint16_t*>(ws + qrot_b);
+  a.partial = reinterpret_cast<float*>(ws + qrot_b + qmma_b);
   a.rope_theta = rope_theta;
+  for (int j = 0; j < d / 2; ++j) a.inv_freq[j] = rope_theta > 0.0 ? std::pow(rope_theta, -2.0 * j / d) : 0.0;
   a.scale = softmax_scale;
   a.capacity = cache->capacity;
   a.batch = cache->batch;

@@ -15,6 +15,9 @@ constexpr int kMaxGroups = 8;        // widths 1..8 -> at most 8 width groups
 constexpr int kTile = 64;            // token slots per cache tile
 constexpr int kEnergyChunk = 256;    // tokens per fixed-order energy partial sum
 constexpr int kQPad = 16;            // query-head padding of the rotated-query workspace
+constexpr int kMaxKSteps = BGTQ_MAX_HEAD_DIM / 32 + 10;  // 32-position MFMA k-steps per head
+constexpr int kSegLen = 8;
+constexpr int kMaxRecordDwords = 2 * BGTQ_MAX_BITS * BGTQ_MAX_HEAD_DIM / 2 / 32;   // 64           // storage positions per MFMA k-segment (one lane's share of a k-step)
 
 // Per-(sequence, KV head) description of the width groups and the K record, written by
 // the allocation kernel.  Storage position p holds original coordinate perm[p], belongs
@@ -31,14 +34,36 @@ struct alignas(16) HeadLayout {
   uint8_t perm[BGTQ_MAX_HEAD_DIM];
   uint8_t group[BGTQ_MAX_HEAD_DIM];
   uint16_t offset[BGTQ_MAX_HEAD_DIM];
-  uint8_t reserved[BGTQ_LAYOUT_BYTES - 16 - 4 * 4 * kMaxGroups - 4 * BGTQ_MAX_HEAD_DIM];
+  // Matrix-core view of the K record.  Every width group is cut into segments of at most 8
+  // storage positions, taken in storage order; k-step s holds segments 4 s + j (lane group j)
+  // from at most two groups: group kgroups[s] & 0xff feeds output columns 0-7 and group
+  // kgroups[s] >> 8 columns 8-15, so every group's partial logit can be scaled by its own
+  // fp32 norm.  seg = bit offset | width << 16 | group << 20 | count << 24 | half << 28;
+  // an unused slot decodes bit 0 with width 1 and meets zero query entries.
+  int32_t n_ksteps;
+  int32_t reserved0[3];
+  uint32_t seg[4 * kMaxKSteps];
+  uint32_t kgroups[kMaxKSteps];
+  uint16_t kpos[BGTQ_MAX_HEAD_DIM];   // storage position -> k index (32 s + 8 j + e)
+  // record dword w holds bits of storage positions dw_first[w] .. dw_end[w] - 1
+  uint16_t dw_first[kMaxRecordDwords];
+  uint16_t dw_end[kMaxRecordDwords];
+  uint8_t reserved[BGTQ_LAYOUT_BYTES - 16 - 4 * 4 * kMaxGroups - 4 * BGTQ_MAX_HEAD_DIM - 16 -
+                   20 * kMaxKSteps - 2 * BGTQ_MAX_HEAD_DIM - 4 * kMaxRecordDwords];
 };
 static_assert(sizeof(HeadLayout) == BGTQ_LAYOUT_BYTES, "layout descriptor size");
 
 // Frozen quantizer tables (fp32 as the kernels read them; fp64 distortions).
+constexpr int kPairWords = 1364;    // fp16 pair tables of widths 1..5: sum over w of 4^w entries
+constexpr int kSingleHalves = 448;  // fp16 level tables of widths 6..8
+
 struct Tables {
   float thr[kMaxBits][255];   // thr[b-1][k], k < 2^b - 1, ascending
   float cen[kMaxBits][256];   // cen[b-1][k], k < 2^b, ascending
+  // decoder tables: fp16 (nearest-even) of cen.  pair[(4^w - 4)/3 + (c0 | c1 << w)] holds the
+  // levels of codes c0 (low half) and c1 (high half) of width w <= 5; single[] widths 6..8.
+  uint32_t pair[kPairWords];
+  uint16_t single[kSingleHalves];
   double dgain[kMaxBits];     // dist[b] - dist[b+1], b = 0..7
   double dist[kMaxBits + 1];  // fl32(D(b)), dist[0] = 1
 };
@@ -51,7 +76,9 @@ inline size_t rot_bank_offset(int m) {  // floats before the m x m matrix (m eve
   for (int k = 2; k < m; k += 2) o += size_t(k) * k;
   return o;
 }
-int decode_splits(int batch, int n_kv_heads, int64_t capacity);
+int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma);
+size_t decode_qrot_bytes(int batch, int n_kv_heads, int d);
+size_t decode_qmma_bytes(int batch, int n_kv_heads);
 
 // ---------------------------------------------------------------- launchers (kernels.hip)
 hipError_t upload_tables(const Tables& t);
@@ -99,12 +126,15 @@ struct DecodeArgs {
   const HeadLayout* layouts;
   float* out;
   float* logits;
-  float* qrot;        // [batch][n_kv][d][kQPad]
+  float* qrot;        // [batch][n_kv][d][kQPad] fp32 (vector-ALU kernel)
+  uint16_t* qmma;     // [batch][n_kv][kMaxKSteps][2][64][8] fp16 hi/lo matrix-core B operands
   float* partial;     // [batch][n_q][n_split][d + 2]
   double rope_theta;
+  double inv_freq[BGTQ_MAX_HEAD_DIM / 2];   // rope_theta^(-2j/d), fp64, computed on the host
   float scale;
   int64_t capacity;
   int batch, n_q, n_kv, group, d, v_bits, chunks, n_split, pairing;
+  int use_mfma;
 };
 hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s);
 

@@ -19,6 +19,8 @@ typedef const HeadLayout __attribute__((address_space(4))) cLayout;
 __constant__ float c_thr[kMaxBits][255];
 __constant__ float c_cen[kMaxBits][256];
 __constant__ double c_dgain[kMaxBits];
+__constant__ uint32_t c_pair[kPairWords];
+__constant__ uint16_t c_single[kSingleHalves];
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -165,6 +167,39 @@ __global__ __launch_bounds__(64) void k_allocate(const double* __restrict__ ener
       }
     }
     lay.n_groups = g; lay.d_eff = pos; lay.code_bits = bit; lay.chunks = (bit + 127) / 128;
+    // matrix-core view: segments of at most 8 positions in storage order; a k-step takes up to
+    // 4 consecutive segments from at most two groups (the two halves of the output columns)
+    int ks = -1, slot = 4, ga = -1, gb = -1;
+    for (int gg = 0; gg < g; ++gg) {
+      const int w = lay.g_width[gg];
+      for (int s0 = 0; s0 < lay.g_m[gg]; s0 += kSegLen) {
+        if (slot == 4 || (gg != ga && gg != gb && gb >= 0)) {
+          if (ks >= 0) lay.kgroups[ks] = uint32_t(ga) | uint32_t(gb >= 0 ? gb : ga) << 8;
+          ++ks; slot = 0; ga = gg; gb = -1;
+        } else if (gg != ga && gb < 0) {
+          gb = gg;
+        }
+        const int cnt = lay.g_m[gg] - s0 < kSegLen ? lay.g_m[gg] - s0 : kSegLen;
+        const uint32_t half = gg == ga ? 0u : 1u;
+        lay.seg[4 * ks + slot] = uint32_t(lay.g_bitoff[gg] + s0 * w) | uint32_t(w) << 16 | uint32_t(gg) << 20 |
+                                 uint32_t(cnt) << 24 | half << 28;
+        for (int e = 0; e < cnt; ++e)
+          lay.kpos[lay.g_first[gg] + s0 + e] = uint16_t(32 * ks + kSegLen * slot + e);
+        ++slot;
+      }
+    }
+    if (ks >= 0) lay.kgroups[ks] = uint32_t(ga) | uint32_t(gb >= 0 ? gb : ga) << 8;
+    lay.n_ksteps = ks + 1;
+    // storage positions with bits in record dword w (offsets ascend with the position)
+    for (int w = 0, p0 = 0, p1 = 0; w < 4 * lay.chunks; ++w) {
+      while (p0 < pos && int(lay.offset[p0]) + lay.g_width[lay.group[p0]] <= 32 * w) ++p0;
+      if (p1 < p0) p1 = p0;
+      while (p1 < pos && int(lay.offset[p1]) < 32 * w + 32) ++p1;
+      lay.dw_first[w] = uint16_t(p0);
+      lay.dw_end[w] = uint16_t(p1);
+    }
+    for (int i = 0; i < 4 * lay.n_ksteps; ++i)
+      if (lay.seg[i] == 0u) lay.seg[i] = 1u << 16;   // unused slot: width 1 at bit 0
   }
   __syncthreads();
   uint32_t* dst = reinterpret_cast<uint32_t*>(layouts + h);
@@ -181,10 +216,24 @@ __global__ __launch_bounds__(64) void k_allocate(const double* __restrict__ ener
 // atomics are needed.  Slots that are not being appended keep their bits.
 constexpr int kHalf = 32;
 
+// Sequential fp32 dot product sum_k R[k] * x[k] (ascending k, no fused multiply-add), R read as
+// float2 (m is even and every row starts 8-byte aligned) so that many loads are in flight.
+__device__ __forceinline__ float seq_dot(const float* __restrict__ R, const float* x, int m) {
+  const float2* R2 = reinterpret_cast<const float2*>(R);
+  float acc = 0.0f;
+#pragma unroll 8
+  for (int k2 = 0; k2 < m / 2; ++k2) {
+    const float2 r = R2[k2];
+    acc = acc + r.x * x[2 * k2];
+    acc = acc + r.y * x[2 * k2 + 1];
+  }
+  return acc;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   extern __shared__ float sm[];
-  const int d = a.d, n = d / 2;
+  const int d = a.d;
   const int si = blockIdx.z, s = a.seq_begin + si, hk = blockIdx.y;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int64_t len = a.lengths[s];
@@ -196,89 +245,77 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   const int64_t lo = len > ht * kHalf ? len : ht * kHalf;
   const int64_t hi = (len + a.n_new) < (ht + 1) * kHalf ? (len + a.n_new) : (ht + 1) * kHalf;
   if (lo >= hi) return;
+  const int r0 = int(lo - ht * kHalf), nrows = int(hi - lo);   // active rows r0 .. r0 + nrows - 1
   const int64_t tile = ht / 2;
   const int half = int(ht & 1);
   const int XS = d + 1;
-  float* xs = sm;                                   // [32][d+1]
-  float* thr = xs + kHalf * XS;                     // [8][255]
+  float* xg = sm;                                   // [32][d+1] keys in storage order
+  float* xs = sm;                                   // same buffer, later: values in original order
+  float* thr = xg + kHalf * XS;                     // [8][255]
   float* knrm = thr + kMaxBits * 255;               // [32][8]
   float* vnrm = knrm + kHalf * kMaxGroups;          // [32]
-  uint8_t* kcode = reinterpret_cast<uint8_t*>(vnrm + kHalf);   // [32][256]
-  uint8_t* vcode = kcode + kHalf * BGTQ_MAX_HEAD_DIM;            // [32][256]
-  int* pb = reinterpret_cast<int*>(vcode + kHalf * BGTQ_MAX_HEAD_DIM);  // [64] first position per dword
-  int* pe = pb + 64;                                                    // [64] end position per dword
+  uint8_t* kcode = reinterpret_cast<uint8_t*>(vnrm + kHalf);             // [32][256]
+  uint8_t* vcode = kcode + kHalf * BGTQ_MAX_HEAD_DIM;                      // [32][256]
+  HeadLayout* Ls = reinterpret_cast<HeadLayout*>(vcode + kHalf * BGTQ_MAX_HEAD_DIM);   // LDS copy
 
-  const HeadLayout& L = a.layouts[int64_t(s) * a.n_kv_heads + hk];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.layouts + int64_t(s) * a.n_kv_heads + hk);
+    uint4* dst = reinterpret_cast<uint4*>(Ls);
+    for (int i = tid; i < int(sizeof(HeadLayout) / 16); i += nt) dst[i] = src[i];
+  }
+  const HeadLayout& L = *Ls;
+  __syncthreads();
   const int ng = L.n_groups, d_eff = L.d_eff, n_dw = 4 * a.chunks;
   const size_t reg = size_t(s) * a.n_kv_heads + hk;
   const int64_t tiles = a.capacity / kTile;
-  (void)n;
+  // few rows (decode): spread one row's outputs over the threads; many rows: lanes run over rows
+  const bool by_pos = nrows <= 4;
 
   for (int i = tid; i < kMaxBits * 255; i += nt) thr[i] = c_thr[i / 255][i % 255];
-  for (int w = tid; w < n_dw; w += nt) {
-    int p = 0;
-    while (p < d_eff && int(L.offset[p]) + L.g_width[L.group[p]] <= 32 * w) ++p;
-    int q = p;
-    while (q < d_eff && int(L.offset[q]) < 32 * w + 32) ++q;
-    pb[w] = p; pe[w] = q;
-  }
   const T* kin = static_cast<const T*>(a.keys) + si * a.stride_seq + hk * a.stride_head;
   const T* vin = static_cast<const T*>(a.values) + si * a.stride_seq + hk * a.stride_head;
-  for (int idx = tid; idx < kHalf * d; idx += nt) {
-    const int r = idx / d, c = idx % d;
-    const int64_t slot = ht * kHalf + r;
-    xs[r * XS + c] = (slot >= lo && slot < hi) ? load_f(kin, (slot - len) * a.stride_token + c) : 0.0f;
+  for (int idx = tid; idx < nrows * d_eff; idx += nt) {
+    const int r = r0 + idx / d_eff, p = idx % d_eff;
+    xg[r * XS + p] = load_f(kin, (ht * kHalf + r - len) * a.stride_token + L.perm[p]);
   }
   __syncthreads();
-  // key group norms
-  for (int it = tid; it < kHalf * ng; it += nt) {
-    const int r = it % kHalf, g = it / kHalf;
-    const int first = L.g_first[g], m = L.g_m[g];
+  // key group norms: sequential fp32 sum of squares in storage order
+  for (int it = tid; it < nrows * ng; it += nt) {
+    const int r = r0 + it % nrows, g = it / nrows;
+    const float* x = xg + r * XS + L.g_first[g];
     float ss = 0.0f;
-    for (int k = 0; k < m; ++k) {
-      const float v = xs[r * XS + L.perm[first + k]];
-      ss = ss + v * v;
-    }
+    for (int k = 0; k < L.g_m[g]; ++k) ss = ss + x[k] * x[k];
     knrm[r * kMaxGroups + g] = sqrtf(ss);
   }
   __syncthreads();
   // key codes, storage order
-  for (int it = tid; it < kHalf * d_eff; it += nt) {
-    const int r = it % kHalf, p = it / kHalf;
+  for (int it = tid; it < nrows * d_eff; it += nt) {
+    const int r = r0 + (by_pos ? it / d_eff : it % nrows);
+    const int p = by_pos ? it % d_eff : it / nrows;
     const int g = L.group[p], w = L.g_width[g], m = L.g_m[g], first = L.g_first[g];
-    const float* R = a.rot_bank + bank_offset(m) + size_t(p - first) * m;
-    float acc = 0.0f;
-    for (int k = 0; k < m; ++k) acc = acc + R[k] * xs[r * XS + L.perm[first + k]];
+    const float acc = seq_dot(a.rot_bank + bank_offset(m) + size_t(p - first) * m, xg + r * XS + first, m);
     const float nv = knrm[r * kMaxGroups + g];
     int code = 0;
-    if (nv != 0.0f) {
-      const float z = (acc / nv) * sqrtf(float(m));
-      code = code_of(thr + (w - 1) * 255, w, z);
-    }
+    if (nv != 0.0f) code = code_of(thr + (w - 1) * 255, w, (acc / nv) * sqrtf(float(m)));
     kcode[r * BGTQ_MAX_HEAD_DIM + p] = uint8_t(code);
   }
   __syncthreads();
-  for (int idx = tid; idx < kHalf * d; idx += nt) {
-    const int r = idx / d, c = idx % d;
-    const int64_t slot = ht * kHalf + r;
-    xs[r * XS + c] = (slot >= lo && slot < hi) ? load_f(vin, (slot - len) * a.stride_token + c) : 0.0f;
+  for (int idx = tid; idx < nrows * d; idx += nt) {
+    const int r = r0 + idx / d, c = idx % d;
+    xs[r * XS + c] = load_f(vin, (ht * kHalf + r - len) * a.stride_token + c);
   }
   __syncthreads();
-  for (int r = tid; r < kHalf; r += nt) {
+  for (int r = r0 + tid; r < r0 + nrows; r += nt) {
     float ss = 0.0f;
-    for (int k = 0; k < d; ++k) {
-      const float v = xs[r * XS + k];
-      ss = ss + v * v;
-    }
+    for (int k = 0; k < d; ++k) ss = ss + xs[r * XS + k] * xs[r * XS + k];
     vnrm[r] = sqrtf(ss);
   }
   __syncthreads();
   const float sd = sqrtf(float(d));
-  for (int it = tid; it < kHalf * d; it += nt) {
-    const int r = it % kHalf, i = it / kHalf;
-    const float* R = a.rot_v + size_t(i) * d;
-    float acc = 0.0f;
-    for (int k = 0; k < d; ++k) acc = acc + R[k] * xs[r * XS + k];
+  for (int it = tid; it < nrows * d; it += nt) {
+    const int r = r0 + (by_pos ? it / d : it % nrows);
+    const int i = by_pos ? it % d : it / nrows;
+    const float acc = seq_dot(a.rot_v + size_t(i) * d, xs + r * XS, d);
     const float nv = vnrm[r];
     int code = 0;
     if (nv != 0.0f) code = code_of(thr + (a.v_bits - 1) * 255, a.v_bits, (acc / nv) * sd);
@@ -287,12 +324,11 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   __syncthreads();
   // pack key records (one thread per (slot, record dword))
   uint32_t* kc = reinterpret_cast<uint32_t*>(a.k_codes) + reg * tiles * a.chunks * kTile * 4;
-  for (int it = tid; it < kHalf * n_dw; it += nt) {
-    const int r = it % kHalf, w = it / kHalf;
+  for (int it = tid; it < nrows * n_dw; it += nt) {
+    const int r = r0 + it % nrows, w = it / nrows;
     const int64_t slot = ht * kHalf + r;
-    if (slot < lo || slot >= hi) continue;
     uint32_t v = 0;
-    for (int p = pb[w]; p < pe[w]; ++p) {
+    for (int p = L.dw_first[w]; p < L.dw_end[w]; ++p) {
       const uint32_t c = kcode[r * BGTQ_MAX_HEAD_DIM + p];
       const int o = int(L.offset[p]) - 32 * w;
       v |= o >= 0 ? (c << o) : (c >> (-o));
@@ -306,9 +342,12 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   for (int it = tid; it < d * bv; it += nt) {
     const int i = it / bv, w = half * bv + it % bv;
     uint32_t* addr = vc + (size_t(tile) * d + i) * 2 * bv + w;
-    uint32_t v = *addr;
     const int bit0 = 32 * w;
-    for (int j = bit0 / bv; j * bv < bit0 + 32; ++j) {
+    const int j_lo = bit0 / bv, j_hi = (bit0 + 31) / bv;
+    // only dwords that hold bits of an appended slot are rewritten
+    if (tile * kTile + j_hi < lo || tile * kTile + j_lo >= hi) continue;
+    uint32_t v = *addr;
+    for (int j = j_lo; j <= j_hi; ++j) {
       const int64_t slot = tile * kTile + j;
       if (slot < lo || slot >= hi) continue;
       const uint32_t c = vcode[int(slot - ht * kHalf) * BGTQ_MAX_HEAD_DIM + i];
@@ -321,15 +360,13 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   // norms
   uint16_t* kn = a.k_norms + reg * tiles * kMaxGroups * kTile;
   uint16_t* vn = a.v_norms + reg * tiles * kTile;
-  for (int it = tid; it < kHalf * ng; it += nt) {
-    const int r = it % kHalf, g = it / kHalf;
+  for (int it = tid; it < nrows * ng; it += nt) {
+    const int r = r0 + it % nrows, g = it / nrows;
     const int64_t slot = ht * kHalf + r;
-    if (slot < lo || slot >= hi) continue;
     kn[(tile * kMaxGroups + g) * kTile + slot % kTile] = f32_to_f16_bits(fminf(knrm[r * kMaxGroups + g], 65504.0f));
   }
-  for (int r = tid; r < kHalf; r += nt) {
+  for (int r = r0 + tid; r < r0 + nrows; r += nt) {
     const int64_t slot = ht * kHalf + r;
-    if (slot < lo || slot >= hi) continue;
     vn[tile * kTile + slot % kTile] = f32_to_f16_bits(fminf(vnrm[r], 65504.0f));
   }
 }
@@ -350,10 +387,13 @@ __global__ void k_advance(int32_t* __restrict__ lengths, int seq_begin, int n_se
 // every group's frame and the keys are never un-rotated.
 
 // Prologue: q' = RoPE(q, pos) (fp64 angles), then q'' per storage position, scaled by
-// softmax_scale * log2(e) / sqrt(m) so that logits come out in base-2 units.
+// softmax_scale * log2(e) / sqrt(m) so that logits come out in base-2 units.  Written in two
+// forms: fp32 [position][head] for the vector-ALU kernel and fp16 matrix-core B operands
+// [k-step][lane][8] for the MFMA kernel (k index 32 s + 8 j + e lives in lane 16 j + head).
 template <typename T>
 __global__ __launch_bounds__(128) void k_decode_prep(DecodeArgs a) {
   __shared__ float qs[BGTQ_MAX_HEAD_DIM];
+  __shared__ float qk[32 * kMaxKSteps];
   const int h = blockIdx.x, s = blockIdx.y;
   const int hk = h / a.group, hl = h % a.group;
   const int d = a.d, n = d / 2;
@@ -363,7 +403,7 @@ __global__ __launch_bounds__(128) void k_decode_prep(DecodeArgs a) {
     const int ca = a.pairing ? 2 * j : j, cb = a.pairing ? 2 * j + 1 : j + n;
     const float x0 = load_f(q, ca), x1 = load_f(q, cb);
     if (a.rope_theta > 0.0) {
-      const double ang = fmod(double(pos) * pow(a.rope_theta, -2.0 * j / d), kTwoPi);
+      const double ang = fmod(double(pos) * a.inv_freq[j], kTwoPi);
       double sn, cs;
       sincos(ang, &sn, &cs);
       qs[ca] = float(double(x0) * cs - double(x1) * sn);
@@ -373,6 +413,7 @@ __global__ __launch_bounds__(128) void k_decode_prep(DecodeArgs a) {
       qs[cb] = x1;
     }
   }
+  for (int i = threadIdx.x; i < 32 * kMaxKSteps; i += blockDim.x) qk[i] = 0.0f;
   __syncthreads();
   const HeadLayout& L = a.layouts[int64_t(s) * a.n_kv + hk];
   float* dst = a.qrot + (int64_t(s) * a.n_kv + hk) * d * kQPad;
@@ -384,8 +425,38 @@ __global__ __launch_bounds__(128) void k_decode_prep(DecodeArgs a) {
       float acc = 0.0f;
       for (int k = 0; k < m; ++k) acc = fmaf(R[k], qs[L.perm[first + k]], acc);
       v = acc * (a.scale * kLog2e / sqrtf(float(m)));
+      qk[L.kpos[p]] = v;
     }
     dst[p * kQPad + hl] = v;
+  }
+  __syncthreads();
+  // matrix-core B operands: lane 16 j + c of k-step ks holds k indices 32 ks + 8 j + e; column
+  // c < 8 carries head c for the k-step's first group, column c + 8 head c for its second
+  // group; each value is split into an fp16 high part and an fp16 remainder.
+  if (!a.use_mfma) return;   // the matrix-core kernel is used only for group sizes <= 8
+  uint16_t* qm = a.qmma + (int64_t(s) * a.n_kv + hk) * kMaxKSteps * 2 * 64 * 8;
+  const int nk = L.n_ksteps * 32;
+  for (int i = threadIdx.x; i < nk; i += blockDim.x) {
+    const int ks = i / 32, jj = (i / 8) % 4, e = i % 8;
+    const uint32_t half = (L.seg[4 * ks + jj] >> 28) & 1u;
+    const float v = qk[i];
+    const uint16_t vh = f32_to_f16_bits(v);
+    const uint16_t vl = f32_to_f16_bits(v - f16_bits_to_f32(vh));
+    const int lane_on = jj * 16 + hl + 8 * int(half), lane_off = jj * 16 + hl + 8 * int(1u - half);
+    qm[((ks * 2 + 0) * 64 + lane_on) * 8 + e] = vh;
+    qm[((ks * 2 + 1) * 64 + lane_on) * 8 + e] = vl;
+    qm[((ks * 2 + 0) * 64 + lane_off) * 8 + e] = 0;
+    qm[((ks * 2 + 1) * 64 + lane_off) * 8 + e] = 0;
+  }
+  if (hl == 0) {  // columns of absent query heads stay zero
+    const int pad = 8 - a.group;
+    for (int i = threadIdx.x; i < nk * 2 * pad; i += blockDim.x) {
+      const int c = a.group + i % pad, rest = i / pad;
+      const int k = rest % nk, part = rest / nk;     // part: 0..1 = column half
+      const int ks = k / 32, jj = (k / 8) % 4, e = k % 8;
+      qm[((ks * 2 + 0) * 64 + jj * 16 + c + 8 * part) * 8 + e] = 0;
+      qm[((ks * 2 + 1) * 64 + jj * 16 + c + 8 * part) * 8 + e] = 0;
+    }
   }
 }
 
@@ -420,9 +491,9 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 
   for (int i = tid; i < 510; i += blockDim.x) {
     const int w = 31 - __clz(i + 2);
-    cbk[i] = c_cen[w - 1][i + 2 - (1 << w)];
+    cbk[i] = f16_bits_to_f32(f32_to_f16_bits(c_cen[w - 1][i + 2 - (1 << w)]));   // fp16 levels
   }
-  for (int i = tid; i < (1 << bv); i += blockDim.x) cbv[i] = c_cen[bv - 1][i];
+  for (int i = tid; i < (1 << bv); i += blockDim.x) cbv[i] = f16_bits_to_f32(f32_to_f16_bits(c_cen[bv - 1][i]));
   __syncthreads();
 
   cLayout* L = (cLayout*)(a.layouts + int64_t(s) * a.n_kv + hk);
@@ -570,27 +641,285 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   }
 }
 
-// Merge the splits of one query head and undo the value rotation:
-// out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t].
+// ---------------------------------------------------------------- matrix-core split-K pass
+// Same partial results as k_decode_split, with both contractions on MFMA (v_mfma_f32_16x16x32_f16).
+//   Keys: S^T[token][head] = K_hat[token][k] * Q''[k][head].  A rows are 16 tokens, the k axis
+//   is the head's width groups cut into 8-position segments (lane group j = lane / 16 decodes
+//   segment 4 s + j of k-step s from the token's K record staged in LDS), B is the resident
+//   rotated query (16 columns; columns >= G are zero).  A holds C[code] * n_group in fp16.
+//   Rows of M-tile mt of sub-tile st are tokens 32 st + 8 (m / 4) + 4 mt + m % 4, so each lane
+//   ends with 8 consecutive tokens of one head -- exactly the B operand layout of P V.
+//   Values: acc^T[coord][head] += V_hat^T[coord][token] * P'^T[token][head], P' = p * n_v; A
+//   rows are coordinates, each lane decodes 8 consecutive tokens of one coordinate from the
+//   tile's coordinate-major value segment (staged in LDS).
+//   Codes become fp16 through pair tables (two codes of width w <= 5 index one packed half2).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSegWords = 4 * kMaxKSteps + kMaxKSteps + 2;       // staged seg[] and kgroups[], 16-byte rounded
+constexpr int kTableWords = kPairWords + kSingleHalves / 2 + ((kSegWords + 3) & ~3);
+
+__device__ __forceinline__ int pair_base(int w) { return ((1 << (2 * w)) - 4) / 3; }
+
+// Per-wave LDS words of the matrix-core kernel (K records, norms, value segments; reused for
+// the final merge), rounded to 16 bytes.
+__host__ __device__ inline int mfma_region_words(int D, int RS, int VS) {
+  const int stage = 64 * RS + 64 * kMaxGroups + D * VS;
+  const int merge = 16 * (D + 2);
+  return ((stage > merge ? stage : merge) + 3) & ~3;
+}
+__device__ __forceinline__ int single_base(int w) { return w == 6 ? 0 : (w == 7 ? 64 : 192); }
+
+// Eight consecutive codes of width w starting at bit `sh` of the 96-bit window (d2:d1:d0),
+// decoded to fp16 reconstruction levels (low half = first code).
+__device__ __forceinline__ u32x4 decode8(uint32_t d0, uint32_t d1, uint32_t d2, int sh, int w,
+                                         const uint32_t* ptab, const uint16_t* stab) {
+  const uint32_t lo = __builtin_amdgcn_alignbit(d1, d0, sh);
+  const uint32_t hi = __builtin_amdgcn_alignbit(d2, d1, sh);
+  const uint64_t x = (uint64_t(hi) << 32) | lo;
+  u32x4 r;
+  if (w <= 5) {
+    const uint32_t* t = ptab + pair_base(w);
+    const uint32_t mask = (1u << (2 * w)) - 1u;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) r[e2] = t[uint32_t(x >> (2 * e2 * w)) & mask];
+  } else {
+    const uint16_t* t = stab + single_base(w);
+    const uint32_t mask = (1u << w) - 1u;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const uint32_t c0 = uint32_t(x >> (2 * e2 * w)) & mask;
+      const uint32_t c1 = uint32_t(x >> ((2 * e2 + 1) * w)) & mask;
+      r[e2] = uint32_t(t[c0]) | (uint32_t(t[c1]) << 16);
+    }
+  }
+  return r;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a) {
-  __shared__ float red[256];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_mfma(DecodeArgs a) {
+  constexpr int MT = D / 16;
+  extern __shared__ uint32_t smem[];
+  const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int len = a.lengths[s];
+  const int tiles = (len + kTile - 1) / kTile;
+  const int per = (tiles + a.n_split - 1) / a.n_split;
+  const int t0 = split * per;
+  const int t1 = t0 + per < tiles ? t0 + per : tiles;
+  const int bv = a.v_bits, chunks = a.chunks;
+  const int RS = 4 * chunks + 3, VS = 2 * bv + 3;
+  const int region_words = mfma_region_words(D, RS, VS);
+
+  uint32_t* ptab = smem;
+  uint16_t* stab = reinterpret_cast<uint16_t*>(smem + kPairWords);
+  uint32_t* krec = smem + kTableWords + wave * region_words;   // [64][RS]
+  float* knorm = reinterpret_cast<float*>(krec + 64 * RS);       // [8][64] fp32 group norms
+  uint32_t* vseg = krec + 64 * RS + 64 * kMaxGroups;            // [D][VS]
+
+  uint32_t* lseg = smem + kPairWords + kSingleHalves / 2;        // [4 * kMaxKSteps] then kgroups
+  uint32_t* lkg = lseg + 4 * kMaxKSteps;
+  const HeadLayout* L = a.layouts + int64_t(s) * a.n_kv + hk;
+  for (int i = tid; i < kPairWords; i += blockDim.x) ptab[i] = c_pair[i];
+  for (int i = tid; i < kSingleHalves; i += blockDim.x) stab[i] = c_single[i];
+  for (int i = tid; i < 4 * kMaxKSteps; i += blockDim.x) lseg[i] = L->seg[i];
+  for (int i = tid; i < kMaxKSteps; i += blockDim.x) lkg[i] = L->kgroups[i];
+  __syncthreads();
+
+  const int ng = L->n_groups, nks = L->n_ksteps;
+  const uint4* qm = reinterpret_cast<const uint4*>(a.qmma + (int64_t(s) * a.n_kv + hk) * kMaxKSteps * 2 * 64 * 8);
+  const size_t reg = size_t(s) * a.n_kv + hk;
+  const int64_t cap_tiles = a.capacity / kTile;
+  const uint4* kc = reinterpret_cast<const uint4*>(a.k_codes) + reg * cap_tiles * chunks * kTile;
+  const uint16_t* kn = a.k_norms + reg * cap_tiles * kMaxGroups * kTile;
+  const uint32_t* vc = reinterpret_cast<const uint32_t*>(a.v_codes) + reg * cap_tiles * D * 2 * bv;
+  const uint16_t* vn = a.v_norms + reg * cap_tiles * kTile;
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const bool real_col = n < 8 && n < a.group;   // output column n carries query head n
+
+  for (int tile = t0 + wave; tile < t1; tile += nwaves) {
+    const int valid = len - tile * kTile < kTile ? len - tile * kTile : kTile;
+    // ---- stage the tile: K records and group norms (lane = slot), value segments
+    for (int c = 0; c < chunks; ++c) {
+      const uint4 v = kc[(size_t(tile) * chunks + c) * kTile + lane];
+      uint32_t* row = krec + lane * RS + 4 * c;
+      row[0] = v.x; row[1] = v.y; row[2] = v.z; row[3] = v.w;
+    }
+    krec[lane * RS + 4 * chunks] = 0u;
+    krec[lane * RS + 4 * chunks + 1] = 0u;
+    krec[lane * RS + 4 * chunks + 2] = 0u;
+    for (int g = 0; g < ng; ++g)
+      knorm[g * 64 + lane] = f16_bits_to_f32(kn[(size_t(tile) * kMaxGroups + g) * kTile + lane]);
+    const uint32_t* vt = vc + size_t(tile) * D * 2 * bv;
+    for (int idx = lane; idx < D * 2 * bv; idx += 64) {
+      const int r = idx / (2 * bv);
+      vseg[r * VS + (idx - r * 2 * bv)] = vt[idx];
+    }
+    for (int r = lane; r < D; r += 64) {
+      vseg[r * VS + 2 * bv] = 0u;
+      vseg[r * VS + 2 * bv + 1] = 0u;
+      vseg[r * VS + 2 * bv + 2] = 0u;
+    }
+    wave_sync();
+
+    // ---- logits: per k-step two MFMAs (query high part, remainder) per 16-token M-tile; the
+    // k-step's group partials are scaled by fp32 norms.  M-tile M = 2 st + mt has row m as
+    // token 32 st + 8 (m / 4) + 4 mt + m % 4; output rows 4 j + r are tokens 32 st + 8 j + 4 mt + r.
+    f32x4 S[4];
+#pragma unroll
+    for (int M = 0; M < 4; ++M) S[M] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 qh_next = nks > 0 ? qm[lane] : uint4{0u, 0u, 0u, 0u};
+    uint4 ql_next = nks > 0 ? qm[64 + lane] : uint4{0u, 0u, 0u, 0u};
+#pragma unroll 1
+    for (int ks = 0; ks < nks; ++ks) {
+      const f16x8 qh = __builtin_bit_cast(f16x8, qh_next);
+      const f16x8 ql = __builtin_bit_cast(f16x8, ql_next);
+      if (ks + 1 < nks) {   // prefetch the next k-step's query operands
+        qh_next = qm[((ks + 1) * 2 + 0) * 64 + lane];
+        ql_next = qm[((ks + 1) * 2 + 1) * 64 + lane];
+      }
+      const uint32_t desc = lseg[4 * ks + j];
+      const uint32_t kg = lkg[ks];
+      const int ngrp = n < 8 ? int(kg & 0xff) : int((kg >> 8) & 0xff);
+      const int w = (desc >> 16) & 15, o = desc & 0xffff;
+#pragma unroll
+      for (int M = 0; M < 4; ++M) {
+        const int tok = 32 * (M >> 1) + 8 * (n >> 2) + 4 * (M & 1) + (n & 3);
+        const uint32_t* row = krec + tok * RS + (o >> 5);
+        const f16x8 A = __builtin_bit_cast(f16x8, decode8(row[0], row[1], row[2], o & 31, w, ptab, stab));
+        f32x4 T = {0.f, 0.f, 0.f, 0.f};
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh, T, 0, 0, 0);
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql, T, 0, 0, 0);
+        const float4 nv = *reinterpret_cast<const float4*>(knorm + ngrp * 64 + 32 * (M >> 1) + 8 * j + 4 * (M & 1));
+        S[M][0] = fmaf(T[0], nv.x, S[M][0]);
+        S[M][1] = fmaf(T[1], nv.y, S[M][1]);
+        S[M][2] = fmaf(T[2], nv.z, S[M][2]);
+        S[M][3] = fmaf(T[3], nv.w, S[M][3]);
+      }
+    }
+    // head c's logit = column c + column c + 8 (lanes n and n ^ 8 of the same row)
+#pragma unroll
+    for (int M = 0; M < 4; ++M) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = S[M][r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[M][r] = v[r];
+    }
+
+    // ---- per 32-token sub-tile: online softmax (base 2), then P V on the matrix cores
+#pragma unroll 1
+    for (int st = 0; st < 2; ++st) {
+      if (32 * st >= valid) break;
+      float sv[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = st == 0 ? S[e >> 2][e & 3] : S[2 + (e >> 2)][e & 3];
+        sv[e] = (32 * st + 8 * j + e < valid) ? x : -INFINITY;
+        tmax = fmaxf(tmax, sv[e]);
+      }
+      if (a.logits && real_col) {
+        float* lg = a.logits + (int64_t(s) * a.n_q + hk * a.group + n) * a.capacity + int64_t(tile) * kTile +
+                    32 * st + 8 * j;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (32 * st + 8 * j + e < valid) lg[e] = sv[e] * kLn2;
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mn = fmaxf(m_run, tmax);
+      const float alpha = exp2f(m_run - mn);
+      m_run = mn;
+      const uint4 nvraw = *reinterpret_cast<const uint4*>(vn + size_t(tile) * kTile + 32 * st + 8 * j);
+      const f16x8 nvv = __builtin_bit_cast(f16x8, nvraw);
+      float psum = 0.0f;
+      f16x8 bp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp2f(sv[e] - mn);
+        psum += p;
+        bp[e] = (_Float16)((real_col && 32 * st + 8 * j + e < valid) ? p * float(nvv[e]) : 0.0f);
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) acc[mi] *= alpha;
+      const int start = (32 * st + 8 * j) * bv;
+      const int wofs = start >> 5, sh = start & 31;
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        const uint32_t* row = vseg + (16 * mi + n) * VS + wofs;
+        const u32x4 raw = decode8(row[0], row[1], row[2], sh, bv, ptab, stab);
+        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw), bp, acc[mi], 0, 0, 0);
+      }
+    }
+    wave_sync();
+  }
+
+  // ---- merge the wavefronts of this workgroup: lane (n, j) holds head n, coords 16 mi + 4 j + r
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();
+  float* comb = reinterpret_cast<float*>(smem + kTableWords) + wave * region_words;   // [16][D + 2]
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) comb[n * (D + 2) + 16 * mi + 4 * j + r] = acc[mi][r];
+  if (j == 0) {
+    comb[n * (D + 2) + D] = m_run;
+    comb[n * (D + 2) + D + 1] = l_run;
+  }
+  __syncthreads();
+  const float* comb0 = reinterpret_cast<const float*>(smem + kTableWords);
+  for (int item = tid; item < a.group * (D + 2); item += blockDim.x) {
+    const int hh = item / (D + 2), c = item % (D + 2);
+    float mmax = -INFINITY;
+    for (int w = 0; w < nwaves; ++w) mmax = fmaxf(mmax, comb0[w * region_words + hh * (D + 2) + D]);
+    float v = 0.0f;
+    if (c == D) {
+      v = mmax;
+    } else if (mmax != -INFINITY) {
+      for (int w = 0; w < nwaves; ++w) {
+        const float mw = comb0[w * region_words + hh * (D + 2) + D];
+        if (mw != -INFINITY) v += comb0[w * region_words + hh * (D + 2) + c] * exp2f(mw - mmax);
+      }
+    }
+    a.partial[((int64_t(s) * a.n_q + hk * a.group + hh) * a.n_split + split) * (D + 2) + c] = v;
+  }
+}
+
+// Merge the splits of one query head and undo the value rotation:
+// out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t].  1024 threads: NSUB
+// threads share a coordinate, each over every NSUB-th split, so many loads are in flight.
+template <int D>
+__global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
+  constexpr int NT = 1024, NSUB = NT / D;
+  __shared__ float red[NT];
   __shared__ float accs[D];
   __shared__ float wts[1024];
   const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const float* part = a.partial + (int64_t(s) * a.n_q + h) * a.n_split * (D + 2);
   float mloc = -INFINITY;
-  for (int i = tid; i < a.n_split; i += blockDim.x) mloc = fmaxf(mloc, part[i * (D + 2) + D]);
+  for (int i = tid; i < a.n_split; i += NT) mloc = fmaxf(mloc, part[i * (D + 2) + D]);
   red[tid] = mloc;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
+  for (int o = NT / 2; o > 0; o >>= 1) {
     if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
     __syncthreads();
   }
   const float mmax = red[0];
   __syncthreads();
   float lloc = 0.0f;
-  for (int i = tid; i < a.n_split; i += blockDim.x) {
+  for (int i = tid; i < a.n_split; i += NT) {
     const float mi = part[i * (D + 2) + D];
     const float w = (mi == -INFINITY) ? 0.0f : exp2f(mi - mmax);
     wts[i] = w;
@@ -598,23 +927,39 @@ __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a) {
   }
   red[tid] = lloc;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
+  for (int o = NT / 2; o > 0; o >>= 1) {
     if (tid < o) red[tid] += red[tid + o];
     __syncthreads();
   }
   const float ltot = red[0];
-  for (int r = tid; r < D; r += blockDim.x) {
+  __syncthreads();
+  const int c = tid % D, q = tid / D;
+  {
     float v = 0.0f;
-    for (int i = 0; i < a.n_split; ++i) v = fmaf(wts[i], part[i * (D + 2) + r], v);
-    accs[r] = v;
+#pragma unroll 8
+    for (int i = q; i < a.n_split; i += NSUB) v = fmaf(wts[i], part[i * (D + 2) + c], v);
+    red[tid] = v;
   }
   __syncthreads();
-  const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
-  float* o = a.out + (int64_t(s) * a.n_q + h) * D;
-  for (int j = tid; j < D; j += blockDim.x) {
+  if (tid < D) {
     float v = 0.0f;
-    for (int r = 0; r < D; ++r) v = fmaf(a.rot_v[r * D + j], accs[r], v);
-    o[j] = v * inv;
+    for (int qq = 0; qq < NSUB; ++qq) v += red[qq * D + tid];
+    accs[tid] = v;
+  }
+  __syncthreads();
+  {
+    constexpr int RPER = D / NSUB;
+    float v = 0.0f;
+#pragma unroll 8
+    for (int r = q * RPER; r < (q + 1) * RPER; ++r) v = fmaf(a.rot_v[r * D + c], accs[r], v);
+    red[tid] = v;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float v = 0.0f;
+    for (int qq = 0; qq < NSUB; ++qq) v += red[qq * D + tid];
+    const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
+    a.out[(int64_t(s) * a.n_q + h) * D + tid] = v * inv;
   }
 }
 
@@ -624,22 +969,31 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st)
     hipLaunchKernelGGL(k_decode_prep<uint16_t>, dim3(a.n_q, a.batch), dim3(128), 0, st, a);
   else
     hipLaunchKernelGGL(k_decode_prep<float>, dim3(a.n_q, a.batch), dim3(128), 0, st, a);
-  const int maxg = a.group <= 1 ? 1 : a.group <= 2 ? 2 : a.group <= 4 ? 4 : a.group <= 8 ? 8 : 16;
-  const int RS = 4 * a.chunks + 1, VS = 2 * a.v_bits + 1;
-  const int kbuf_words = 64 * RS > D * VS ? 64 * RS : D * VS;
-  const int wave_words = kbuf_words + 64 * kMaxGroups + 64 * maxg;
-  int nwaves = 4;
-  while (nwaves > 1 && (768 + nwaves * wave_words) * 4 > 64 * 1024) --nwaves;
-  const size_t lds = size_t(768 + nwaves * wave_words) * 4;
-  const dim3 grid(a.n_split, a.n_kv, a.batch), block(64 * nwaves);
-  switch (maxg) {
-    case 1: hipLaunchKernelGGL((k_decode_split<D, 1>), grid, block, lds, st, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_split<D, 2>), grid, block, lds, st, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_split<D, 4>), grid, block, lds, st, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_split<D, 8>), grid, block, lds, st, a); break;
-    default: hipLaunchKernelGGL((k_decode_split<D, 16>), grid, block, lds, st, a); break;
+  const dim3 grid(a.n_split, a.n_kv, a.batch);
+  if (a.use_mfma) {
+    const int region_words = mfma_region_words(D, 4 * a.chunks + 3, 2 * a.v_bits + 3);
+    int nwaves = 4;
+    while (nwaves > 1 && (kTableWords + nwaves * region_words) * 4 > 64 * 1024) --nwaves;
+    const size_t lds = size_t(kTableWords + nwaves * region_words) * 4;
+    hipLaunchKernelGGL(k_decode_mfma<D>, grid, dim3(64 * nwaves), lds, st, a);
+  } else {
+    const int maxg = a.group <= 1 ? 1 : a.group <= 2 ? 2 : a.group <= 4 ? 4 : a.group <= 8 ? 8 : 16;
+    const int RS = 4 * a.chunks + 1, VS = 2 * a.v_bits + 1;
+    const int kbuf_words = 64 * RS > D * VS ? 64 * RS : D * VS;
+    const int wave_words = kbuf_words + 64 * kMaxGroups + 64 * maxg;
+    int nwaves = 4;
+    while (nwaves > 1 && (768 + nwaves * wave_words) * 4 > 64 * 1024) --nwaves;
+    const size_t lds = size_t(768 + nwaves * wave_words) * 4;
+    const dim3 block(64 * nwaves);
+    switch (maxg) {
+      case 1: hipLaunchKernelGGL((k_decode_split<D, 1>), grid, block, lds, st, a); break;
+      case 2: hipLaunchKernelGGL((k_decode_split<D, 2>), grid, block, lds, st, a); break;
+      case 4: hipLaunchKernelGGL((k_decode_split<D, 4>), grid, block, lds, st, a); break;
+      case 8: hipLaunchKernelGGL((k_decode_split<D, 8>), grid, block, lds, st, a); break;
+      default: hipLaunchKernelGGL((k_decode_split<D, 16>), grid, block, lds, st, a); break;
+    }
   }
-  hipLaunchKernelGGL(k_decode_combine<D>, dim3(a.n_q, a.batch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_decode_combine<D>, dim3(a.n_q, a.batch), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
@@ -651,6 +1005,8 @@ hipError_t upload_tables(const Tables& t) {
   hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(c_thr), t.thr, sizeof(t.thr));
   if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_cen), t.cen, sizeof(t.cen));
   if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_dgain), t.dgain, sizeof(t.dgain));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_pair), t.pair, sizeof(t.pair));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_single), t.single, sizeof(t.single));
   return e;
 }
 
@@ -682,7 +1038,7 @@ hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStre
   const int halves = int((a.n_new + kHalf - 1) / kHalf) + 1;
   const dim3 grid(halves, a.n_kv_heads, n_seqs);
   const size_t lds = size_t(kHalf) * (a.d + 1) * 4 + kMaxBits * 255 * 4 + kHalf * kMaxGroups * 4 + kHalf * 4 +
-                     2 * kHalf * BGTQ_MAX_HEAD_DIM + 2 * 64 * 4;
+                     2 * kHalf * BGTQ_MAX_HEAD_DIM + sizeof(HeadLayout);
   if (dt == BGTQ_BF16)
     hipLaunchKernelGGL(k_append<uint16_t>, grid, dim3(256), lds, s, a);
   else
@@ -701,15 +1057,24 @@ hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s) {
   }
 }
 
-int decode_splits(int batch, int n_kv_heads, int64_t capacity) {
+int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma) {
   const int64_t tiles = capacity / kTile;
   const int64_t units = int64_t(batch) * n_kv_heads;
   int64_t want = (1024 + units - 1) / units;         // about 1024 workgroups in flight
-  const int64_t by_work = (tiles + 7) / 8;            // at least 8 tiles per split
+  const int64_t per_split = mfma ? 8 : 8;             // tiles per split at least
+  const int64_t by_work = (tiles + per_split - 1) / per_split;
   if (want > by_work) want = by_work;
   if (want < 1) want = 1;
   if (want > 1024) want = 1024;
   return int(want);
+}
+
+size_t decode_qrot_bytes(int batch, int n_kv_heads, int d) {
+  return size_t(batch) * n_kv_heads * d * kQPad * 4;
+}
+
+size_t decode_qmma_bytes(int batch, int n_kv_heads) {
+  return size_t(batch) * n_kv_heads * kMaxKSteps * 2 * 64 * 8 * 2;
 }
 
 }  // namespace bgtq

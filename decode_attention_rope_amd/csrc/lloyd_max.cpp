@@ -16,6 +16,7 @@
 // quantiles.  All arithmetic is fp64; the tables are then rounded to fp32.
 
 #include <cmath>
+#include <cstring>
 #include <vector>
 
 #include "bgtq_internal.h"
@@ -130,6 +131,19 @@ Tables build_tables() {
     (void)N;
   }
   for (int b = 0; b < kMaxBits; ++b) t.dgain[b] = t.dist[b] - t.dist[b + 1];
+  // fp16 decoder tables (round to nearest even from the fp32 levels)
+  auto h16 = [](float x) { const _Float16 h = (_Float16)x; uint16_t u; std::memcpy(&u, &h, 2); return u; };
+  for (int w = 1; w <= 5; ++w) {
+    const int base = ((1 << (2 * w)) - 4) / 3;
+    for (int idx = 0; idx < (1 << (2 * w)); ++idx) {
+      const int c0 = idx & ((1 << w) - 1), c1 = idx >> w;
+      t.pair[base + idx] = uint32_t(h16(t.cen[w - 1][c0])) | uint32_t(h16(t.cen[w - 1][c1])) << 16;
+    }
+  }
+  for (int w = 6; w <= 8; ++w) {
+    const int base = w == 6 ? 0 : (w == 7 ? 64 : 192);
+    for (int c = 0; c < (1 << w); ++c) t.single[base + c] = h16(t.cen[w - 1][c]);
+  }
   return t;
 }
 

@@ -58,7 +58,7 @@ typedef void* bgtq_stream;
 #define BGTQ_MAX_BITS 8
 #define BGTQ_MAX_GROUP 16        /* query heads per KV head */
 #define BGTQ_TILE 64             /* token slots per cache tile */
-#define BGTQ_LAYOUT_BYTES 2048   /* size of one per-head layout descriptor */
+#define BGTQ_LAYOUT_BYTES 4096   /* size of one per-head layout descriptor */
 
 /* Random rotations the quantizer draws (TQ-MSE rotates before scalar coding).
  * Device memory, caller-owned, read-only, shared by all layers and heads.

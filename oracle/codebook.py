@@ -16,8 +16,11 @@ The Lloyd-Max conditions for N = 2^b cells with thresholds t_1 < ... < t_{N-1}
 
 They are solved here by Newton's method on the thresholds, started from the
 Panter-Dite companding guess t_k = sqrt(3) * Phi^{-1}(k/N).  The tables are
-then made exactly antisymmetric and rounded to fp32, which is the precision in
-which the quantizer compares and the decoder reads them.  D(b) is the MSE of
+then made exactly antisymmetric and rounded to fp32: the quantizer compares
+against the fp32 decision levels.  Reconstruction uses the fp32 levels rounded
+once more to fp16 (nearest-even), the precision in which the packed cache is
+decoded (reading: the pages fix no precision for the codebook; fp16 levels
+differ from the fp32 ones by at most 2^-11 relative).  D(b) is the MSE of
 the b-bit quantizer of N(0, 1); D(0) = 1 (a coordinate coded with zero bits is
 reconstructed as 0).  The allocator uses fl32(D(b)).
 """
@@ -113,6 +116,11 @@ def thresholds32(bits: int) -> np.ndarray:
 def centroids32(bits: int) -> np.ndarray:
     """fp32 reconstruction levels C_b[0..2^b-1] (ascending) for N(0, 1)."""
     return solve(bits)[1].astype(np.float32)
+
+
+def levels16(bits: int) -> np.ndarray:
+    """Reconstruction levels: the fp32 centroids rounded to fp16 (nearest-even), as fp64 values."""
+    return centroids32(bits).astype(np.float16).astype(np.float64)
 
 
 def distortion32() -> np.ndarray:

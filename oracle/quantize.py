@@ -8,7 +8,8 @@ Reading of TQ-MSE for one vector x in R^m at b bits (from the TurboQuant paper,
 outside the pages): store the norm n = |x|; rotate with a fixed random
 orthogonal m x m matrix Pi; scale so that the coordinates are close to
 N(0, 1): z = (Pi x / n) * sqrt(m); code every coordinate with the b-bit
-Lloyd-Max quantizer of N(0, 1).  Reconstruction is n * Pi^T (C_b[code] / sqrt(m)).
+Lloyd-Max quantizer of N(0, 1).  Reconstruction is n * Pi^T (C_b[code] / sqrt(m)),
+with C_b the fp16-rounded reconstruction levels and n the stored fp16 norm.
 No residual (QJL) stage, no renormalisation.
 
 Bit-exact arithmetic (so that a GPU kernel can reproduce every code and norm):
@@ -91,7 +92,7 @@ def dequantize_keys(codes, norms, lay: Layout, bank) -> np.ndarray:
     t_len = codes.shape[0]
     out = np.zeros((t_len, lay.d), dtype=np.float64)
     for g, grp in enumerate(lay.groups):
-        cen = codebook.centroids32(grp.width).astype(np.float64)
+        cen = codebook.levels16(grp.width)
         rot = bank_matrix(bank, grp.m).astype(np.float64)
         yhat = cen[codes[:, grp.first:grp.first + grp.m]] / np.sqrt(grp.m)
         xg = (yhat @ rot) * norms[:, g].astype(np.float64)[:, None]   # rows: Pi^T yhat
@@ -101,6 +102,6 @@ def dequantize_keys(codes, norms, lay: Layout, bank) -> np.ndarray:
 
 def dequantize_values(codes, norms, rot_v, bits: int) -> np.ndarray:
     d = rot_v.shape[0]
-    cen = codebook.centroids32(bits).astype(np.float64)
+    cen = codebook.levels16(bits)
     yhat = cen[np.asarray(codes)] / np.sqrt(d)
     return (yhat @ np.asarray(rot_v, dtype=np.float64)) * np.asarray(norms, dtype=np.float64)[:, None]

@@ -200,11 +200,11 @@ def _decode_vs_oracle(wl, t_lens, qz, bank, rv, dtype=torch.float32, append_then
                 ref["v_hat"] = np.concatenate([ref["v_hat"], oq.dequantize_values(vc, vn, rv, wl.v_bits)])
             o_ref, l_ref = decode_reference(q[s, h * g:(h + 1) * g], qpos, theta, ref, pairing=pairing)
             e_out = rel_err(out[s, h * g:(h + 1) * g], o_ref)
-            assert np.all(e_out <= TOL), f"seq {s} head {h}: output error {e_out}"
             if check_logits:
                 e_log = rel_err(logits[s, h * g:(h + 1) * g, :t_len], l_ref)
-                assert np.all(e_log <= TOL), f"seq {s} head {h}: logit error {e_log}"
+                assert np.all(e_log <= TOL), f"seq {s} head {h}: logit error {e_log} (output error {e_out})"
                 worst = max(worst, float(e_log.max()))
+            assert np.all(e_out <= TOL), f"seq {s} head {h}: output error {e_out}"
             worst = max(worst, float(e_out.max()))
     _say(f"  worst rel err {worst:.2e}")
     return cache
