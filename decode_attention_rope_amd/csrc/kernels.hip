@@ -216,16 +216,24 @@ __global__ __launch_bounds__(64) void k_allocate(const double* __restrict__ ener
 // atomics are needed.  Slots that are not being appended keep their bits.
 constexpr int kHalf = 32;
 
-// Sequential fp32 dot product sum_k R[k] * x[k] (ascending k, no fused multiply-add), R read as
-// float2 (m is even and every row starts 8-byte aligned) so that many loads are in flight.
+// Sequential fp32 dot product sum_k R[k] * x[k] (ascending k, no fused multiply-add).  R is
+// read as float2 (m is even and every row starts 8-byte aligned), 64 values per batch with
+// all of a batch's loads issued before the first add, so one memory latency covers 64 terms.
 __device__ __forceinline__ float seq_dot(const float* __restrict__ R, const float* x, int m) {
   const float2* R2 = reinterpret_cast<const float2*>(R);
   float acc = 0.0f;
-#pragma unroll 8
-  for (int k2 = 0; k2 < m / 2; ++k2) {
-    const float2 r = R2[k2];
-    acc = acc + r.x * x[2 * k2];
-    acc = acc + r.y * x[2 * k2 + 1];
+  for (int k0 = 0; k0 < m; k0 += 64) {
+    float2 r[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (k0 + 2 * i < m) r[i] = R2[k0 / 2 + i];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (k0 + 2 * i < m) {
+        acc = acc + r[i].x * x[k0 + 2 * i];
+        acc = acc + r[i].y * x[k0 + 2 * i + 1];
+      }
+    }
   }
   return acc;
 }
@@ -421,9 +429,21 @@ __global__ __launch_bounds__(128) void k_decode_prep(DecodeArgs a) {
     float v = 0.0f;
     if (p < L.d_eff) {
       const int g = L.group[p], m = L.g_m[g], first = L.g_first[g];
-      const float* R = a.rot_bank + bank_offset(m) + size_t(p - first) * m;
+      const float2* R2 = reinterpret_cast<const float2*>(a.rot_bank + bank_offset(m) + size_t(p - first) * m);
       float acc = 0.0f;
-      for (int k = 0; k < m; ++k) acc = fmaf(R[k], qs[L.perm[first + k]], acc);
+      for (int k0 = 0; k0 < m; k0 += 64) {
+        float2 r[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (k0 + 2 * i < m) r[i] = R2[k0 / 2 + i];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (k0 + 2 * i < m) {
+            acc = fmaf(r[i].x, qs[L.perm[first + k0 + 2 * i]], acc);
+            acc = fmaf(r[i].y, qs[L.perm[first + k0 + 2 * i + 1]], acc);
+          }
+        }
+      }
       v = acc * (a.scale * kLog2e / sqrtf(float(m)));
       qk[L.kpos[p]] = v;
     }
@@ -746,26 +766,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   for (int tile = t0 + wave; tile < t1; tile += nwaves) {
     const int valid = len - tile * kTile < kTile ? len - tile * kTile : kTile;
-    // ---- stage the tile: K records and group norms (lane = slot), value segments
-    for (int c = 0; c < chunks; ++c) {
-      const uint4 v = kc[(size_t(tile) * chunks + c) * kTile + lane];
-      uint32_t* row = krec + lane * RS + 4 * c;
-      row[0] = v.x; row[1] = v.y; row[2] = v.z; row[3] = v.w;
-    }
-    krec[lane * RS + 4 * chunks] = 0u;
-    krec[lane * RS + 4 * chunks + 1] = 0u;
-    krec[lane * RS + 4 * chunks + 2] = 0u;
-    for (int g = 0; g < ng; ++g)
-      knorm[g * 64 + lane] = f16_bits_to_f32(kn[(size_t(tile) * kMaxGroups + g) * kTile + lane]);
-    const uint32_t* vt = vc + size_t(tile) * D * 2 * bv;
-    for (int idx = lane; idx < D * 2 * bv; idx += 64) {
-      const int r = idx / (2 * bv);
-      vseg[r * VS + (idx - r * 2 * bv)] = vt[idx];
-    }
-    for (int r = lane; r < D; r += 64) {
-      vseg[r * VS + 2 * bv] = 0u;
-      vseg[r * VS + 2 * bv + 1] = 0u;
-      vseg[r * VS + 2 * bv + 2] = 0u;
+    // ---- stage the tile: K records and group norms (lane = slot), value segments (lane =
+    // coordinate row).  All loads of the tile are issued before the first LDS write.
+    {
+      constexpr int MAXCH = D / 16;                 // record chunks at 8 bits per coordinate
+      constexpr int MAXVW = 8;                      // 8-byte words per value segment (8 bits)
+      constexpr int RPL = D / 64;                   // value rows per lane
+      uint4 kr[MAXCH];
+      uint16_t knv[kMaxGroups];
+      uint2 vr[RPL][MAXVW];
+#pragma unroll
+      for (int c = 0; c < MAXCH; ++c)
+        if (c < chunks) kr[c] = kc[(size_t(tile) * chunks + c) * kTile + lane];
+#pragma unroll
+      for (int g = 0; g < kMaxGroups; ++g)
+        if (g < ng) knv[g] = kn[(size_t(tile) * kMaxGroups + g) * kTile + lane];
+      const uint2* vt2 = reinterpret_cast<const uint2*>(vc + size_t(tile) * D * 2 * bv);
+#pragma unroll
+      for (int i = 0; i < RPL; ++i)
+#pragma unroll
+        for (int wv = 0; wv < MAXVW; ++wv)
+          if (wv < bv) vr[i][wv] = vt2[(lane + 64 * i) * bv + wv];
+#pragma unroll
+      for (int c = 0; c < MAXCH; ++c) {
+        if (c < chunks) {
+          uint32_t* row = krec + lane * RS + 4 * c;
+          row[0] = kr[c].x; row[1] = kr[c].y; row[2] = kr[c].z; row[3] = kr[c].w;
+        }
+      }
+      krec[lane * RS + 4 * chunks] = 0u;
+      krec[lane * RS + 4 * chunks + 1] = 0u;
+      krec[lane * RS + 4 * chunks + 2] = 0u;
+#pragma unroll
+      for (int g = 0; g < kMaxGroups; ++g)
+        if (g < ng) knorm[g * 64 + lane] = f16_bits_to_f32(knv[g]);
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        uint32_t* row = vseg + (lane + 64 * i) * VS;
+#pragma unroll
+        for (int wv = 0; wv < MAXVW; ++wv) {
+          if (wv < bv) { row[2 * wv] = vr[i][wv].x; row[2 * wv + 1] = vr[i][wv].y; }
+        }
+        row[2 * bv] = 0u;
+        row[2 * bv + 1] = 0u;
+        row[2 * bv + 2] = 0u;
+      }
     }
     wave_sync();
 
@@ -789,11 +834,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const uint32_t kg = lkg[ks];
       const int ngrp = n < 8 ? int(kg & 0xff) : int((kg >> 8) & 0xff);
       const int w = (desc >> 16) & 15, o = desc & 0xffff;
+      const int sh = o & 31;
+      const uint32_t* krow0 = krec + (o >> 5);
+      // the lane's window of its four tokens' records
+      uint32_t d0[4], d1[4];
 #pragma unroll
       for (int M = 0; M < 4; ++M) {
-        const int tok = 32 * (M >> 1) + 8 * (n >> 2) + 4 * (M & 1) + (n & 3);
-        const uint32_t* row = krec + tok * RS + (o >> 5);
-        const f16x8 A = __builtin_bit_cast(f16x8, decode8(row[0], row[1], row[2], o & 31, w, ptab, stab));
+        const uint32_t* row = krow0 + (32 * (M >> 1) + 8 * (n >> 2) + 4 * (M & 1) + (n & 3)) * RS;
+        d0[M] = row[0];
+        d1[M] = row[1];
+      }
+      u32x4 raw[4];
+      if (w <= 4) {   // 8 codes fit one 32-bit window: one bit-field extract per pair
+        const uint32_t* t = ptab + pair_base(w);
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+          const uint32_t x = __builtin_amdgcn_alignbit(d1[M], d0[M], sh);
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) raw[M][e2] = t[__builtin_amdgcn_ubfe(x, 2 * e2 * w, 2 * w)];
+        }
+      } else {
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+          const uint32_t* row = krow0 + (32 * (M >> 1) + 8 * (n >> 2) + 4 * (M & 1) + (n & 3)) * RS;
+          raw[M] = decode8(d0[M], d1[M], row[2], sh, w, ptab, stab);
+        }
+      }
+#pragma unroll
+      for (int M = 0; M < 4; ++M) {
+        const f16x8 A = __builtin_bit_cast(f16x8, raw[M]);
         f32x4 T = {0.f, 0.f, 0.f, 0.f};
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh, T, 0, 0, 0);
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql, T, 0, 0, 0);
@@ -851,15 +920,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         bp[e] = (_Float16)((real_col && 32 * st + 8 * j + e < valid) ? p * float(nvv[e]) : 0.0f);
       }
       l_run = l_run * alpha + psum;
+      if (__any(alpha != 1.0f)) {   // the running maxima moved: rescale the accumulators
 #pragma unroll
-      for (int mi = 0; mi < MT; ++mi) acc[mi] *= alpha;
+        for (int mi = 0; mi < MT; ++mi) acc[mi] *= alpha;
+      }
       const int start = (32 * st + 8 * j) * bv;
       const int wofs = start >> 5, sh = start & 31;
+      const uint32_t* vrow0 = vseg + n * VS + wofs;
+      if (bv <= 4) {   // uniform: 8 codes per 32-bit window, pair fields at fixed offsets
+        const uint32_t* t = ptab + pair_base(bv);
+        uint32_t x[MT];
 #pragma unroll
-      for (int mi = 0; mi < MT; ++mi) {
-        const uint32_t* row = vseg + (16 * mi + n) * VS + wofs;
-        const u32x4 raw = decode8(row[0], row[1], row[2], sh, bv, ptab, stab);
-        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw), bp, acc[mi], 0, 0, 0);
+        for (int mi = 0; mi < MT; ++mi) {
+          const uint32_t* row = vrow0 + 16 * mi * VS;
+          x[mi] = __builtin_amdgcn_alignbit(row[1], row[0], sh);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+          u32x4 raw;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) raw[e2] = t[__builtin_amdgcn_ubfe(x[mi], 2 * e2 * bv, 2 * bv)];
+          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw), bp, acc[mi], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+          const uint32_t* row = vrow0 + 16 * mi * VS;
+          const u32x4 raw = decode8(row[0], row[1], row[2], sh, bv, ptab, stab);
+          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw), bp, acc[mi], 0, 0, 0);
+        }
       }
     }
     wave_sync();
