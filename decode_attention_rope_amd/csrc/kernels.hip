@@ -2,7 +2,7 @@
 //
 // Method: "RoPE-Aware Bit Allocation for KV-Cache Quantization" (arXiv 2606.24033), abstract.
 // Each kernel states the reading of the abstract it implements.  Kernels that must agree
-// bit for bit with the reference arithmetic (energy, allocation, quantize-and-pack) are
+// bit for bit with the specified arithmetic (energy, allocation, quantize-and-pack) are
 // compiled without floating-point contraction (-ffp-contract=off) and use only correctly
 // rounded fp32/fp64 operations in a fixed order; decode attention uses explicit fmaf.
 

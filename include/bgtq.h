@@ -46,14 +46,14 @@ typedef enum {
 
 typedef enum { BGTQ_F32 = 0, BGTQ_BF16 = 1 } bgtq_dtype;
 
-/* Which two coordinates form RoPE block j (the pages only say "two-dimensional
- * frequency blocks"): HALF pairs (j, j + d/2) as Llama/Qwen checkpoints do,
+/* Which two coordinates form RoPE block j (the abstract speaks of 2-D
+ * frequency blocks but fixes no coordinate layout): HALF pairs (j, j + d/2) as Llama/Qwen checkpoints do,
  * INTERLEAVED pairs (2j, 2j + 1). */
 typedef enum { BGTQ_PAIR_HALF = 0, BGTQ_PAIR_INTERLEAVED = 1 } bgtq_pairing;
 
 typedef void* bgtq_stream;
 
-/* Limits of this build. */
+/* Library limits. */
 #define BGTQ_MAX_HEAD_DIM 256
 #define BGTQ_MAX_BITS 8
 #define BGTQ_MAX_GROUP 16        /* query heads per KV head */
@@ -110,8 +110,8 @@ typedef struct {
   int32_t* status;
 } bgtq_cache;
 
-/* Label-free energy score of every RoPE block (abstract: "for each layer and
- * KV head ... a label-free energy score for each RoPE block").
+/* Energy score of every RoPE block, computed from keys alone (abstract: one
+ * score per block, per layer and KV head, with no labels needed).
  * Reading: E_j = (1/T) * sum_t (k[t,a_j]^2 + k[t,b_j]^2) over the given keys,
  * in fp64, summed in ascending t inside chunks of 256 tokens and then over the
  * chunks in ascending order (a fixed order, so the result is reproducible).
@@ -128,9 +128,10 @@ bgtq_status bgtq_block_energy(const void* keys, bgtq_dtype dtype, int n_heads, i
                               size_t workspace_bytes, bgtq_stream stream);
 size_t bgtq_energy_workspace_bytes(int n_heads, int64_t n_tokens, int head_dim);
 
-/* Greedy integer bit widths by marginal gain (abstract: "greedily allocates
- * integer bit widths by marginal gain"; "high-energy RoPE blocks ... should
- * receive more bits"; budgets matched to uniform TQ-MSE).
+/* Greedy integer bit widths by marginal gain (abstract: integer widths are
+ * handed out one bit at a time to the block that gains most, so blocks with
+ * more energy end up with more bits; the K budget equals that of uniform
+ * TQ-MSE).
  * Reading: all blocks start at b_min; k_width_sum - n*b_min times, one bit goes
  * to the block with the largest gain E_j * (D(b_j) - D(b_j + 1)) among blocks
  * below b_max, ties to the lowest j, where D(b) = fl32(MSE of the b-bit
@@ -145,8 +146,9 @@ bgtq_status bgtq_allocate_bits(const double* energy, int n_heads, int head_dim, 
                                int b_min, int b_max, bgtq_pairing pairing, uint8_t* widths_out,
                                void* layouts_out, bgtq_stream stream);
 
-/* TQ-MSE quantize-and-pack of new tokens (abstract: Block-GTQ "built on
- * TurboQuant-MSE"; "packed-cache serving path").
+/* TQ-MSE quantize-and-pack of new tokens (abstract: the method uses
+ * TurboQuant-MSE as its base quantizer, and its serving path keeps the cache
+ * packed).
  * Reading (width-group TQ-MSE): blocks of equal width w >= 1 form one vector of
  * m = 2*|group| coordinates coded at w bits: fp32 norm n (sequential sum of
  * squares, sqrt), y = R_m x (sequential, no fused multiply-add), z = (y/n)*fl32(sqrt(m)),
@@ -167,7 +169,7 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
                                  int64_t stride_token, bgtq_stream stream);
 
 /* Decode attention straight from the packed cache (abstract: RoPE query-key
- * logits; "packed-cache serving path" that attends over packed K3V3 at 128K).
+ * logits; the serving path attends over a packed K3V3 cache at 128K context).
  * For every sequence s and query head h (KV head h / (n_q_heads/n_kv_heads)):
  * q' = RoPE(q[s][h], pos) with angles pos*rope_theta^(-2j/d) formed in fp64;
  * logits l_t = softmax_scale * q' . k_hat_t over the cached slots t <

@@ -1,8 +1,9 @@
-"""Label-free per-block energy score (oracle).
+"""Per-block energy score that needs no labels (oracle).
 
-RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: for each layer
-and KV head Block-GTQ computes a label-free energy score for every RoPE block;
-high-energy blocks are the ones most sensitive to quantization error.
+RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: the allocator
+scores every RoPE frequency block separately per layer and per KV head, using
+no labels, and blocks with more energy are the ones that matter most for the
+logit error.
 
 Reading (no formula on the pages): the score of block j is the mean over the
 sequence's cached keys of the squared norm of the block's two coordinates,

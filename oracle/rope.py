@@ -1,8 +1,8 @@
 """Rotary position embedding in fp64 (oracle).
 
-RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: under RoPE a
-key's contribution to a later attention logit is a position-dependent sum over
-two-dimensional frequency blocks.  Block j rotates its two coordinates by the
+RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: with RoPE, the
+logit a cached key contributes to splits into one term per 2-D frequency block,
+and each term depends on the query-key position gap.  Block j rotates its two coordinates by the
 angle pos * theta_j with theta_j = base^(-2j/d).
 
 Readings (the pages give no layout): block j pairs coordinates (j, j + d/2)
