@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--workload", default="qwen3b_36L_128k_K3V3")
     p.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="after timing, run one plain device copy of this many MiB (scale for PMC byte counters)")
     return p.parse_args()
 
 
@@ -188,6 +190,14 @@ def main():
     ctx = lengths[0]
     bytes_per_launch = float(np.mean([sum(b) for b in layer_bytes])) * ctx
     achieved = bytes_per_launch / (us_per_launch * 1e-6) / 1e9
+
+    if args.copy_mb > 0:   # a plain copy kernel of known size, for counter calibration
+        src = torch.ones(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     result = {
         "metric": "decode-attn tok/s + achieved HBM GB/s (% peak), packed K3V3 cache, 128K ctx",

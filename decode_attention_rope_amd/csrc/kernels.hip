@@ -662,327 +662,410 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- matrix-core split-K pass
-// Same partial results as k_decode_split, with both contractions on MFMA (v_mfma_f32_16x16x32_f16).
-//   Keys: S^T[token][head] = K_hat[token][k] * Q''[k][head].  A rows are 16 tokens, the k axis
-//   is the head's width groups cut into 8-position segments (lane group j = lane / 16 decodes
-//   segment 4 s + j of k-step s from the token's K record staged in LDS), B is the resident
-//   rotated query (16 columns; columns >= G are zero).  A holds C[code] * n_group in fp16.
-//   Rows of M-tile mt of sub-tile st are tokens 32 st + 8 (m / 4) + 4 mt + m % 4, so each lane
-//   ends with 8 consecutive tokens of one head -- exactly the B operand layout of P V.
-//   Values: acc^T[coord][head] += V_hat^T[coord][token] * P'^T[token][head], P' = p * n_v; A
-//   rows are coordinates, each lane decodes 8 consecutive tokens of one coordinate from the
-//   tile's coordinate-major value segment (staged in LDS).
-//   Codes become fp16 through pair tables (two codes of width w <= 5 index one packed half2).
+// Same partial results as k_decode_split, with both contractions on MFMA
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation).  The four wavefronts of a workgroup work on
+// one 64-token tile at a time:
+//   keys    wave w owns tokens 16 w .. 16 w + 15 (the 16 rows of its A operand); its lane
+//           (n, j) decodes 8 codes of token 16 w + n for k-step s from segment 4 s + j of the
+//           token's K record; B is the rotated query (columns 0-7: the G heads restricted to
+//           the k-step's first width group, columns 8-15: its second group), split into an
+//           fp16 high part and an fp16 remainder (two MFMAs); each column half's partial
+//           logit is scaled by its group's fp32 norm, and column c + column c + 8 is head c.
+//   softmax the tile maximum per head is shared through LDS; p * n_v goes to LDS as the fp16
+//           B operand of P V (lane group j of sub-tile st holds tokens 32 st + 8 j .. + 7).
+//   values  wave w owns rotated coordinates D/4 w .. D/4 (w + 1) - 1; A rows are coordinates,
+//           each lane decodes 8 consecutive tokens of one coordinate.
+// Codes become fp16 levels through pair tables (two codes of width w <= 5 index one packed
+// half2) or single tables (widths 6..8) staged in LDS.  Every wave stages only the bytes it
+// reads (its tokens' K records and norms, its coordinates' value segments) with direct
+// global-to-LDS loads, three tiles deep, so staging needs no workgroup barrier.
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSegWords = 4 * kMaxKSteps + kMaxKSteps + 2;       // staged seg[] and kgroups[], 16-byte rounded
-constexpr int kTableWords = kPairWords + kSingleHalves / 2 + ((kSegWords + 3) & ~3);
+constexpr int kQRegSteps = 8;        // k-steps whose query operands stay in registers
 
 __device__ __forceinline__ int pair_base(int w) { return ((1 << (2 * w)) - 4) / 3; }
-
-// Per-wave LDS words of the matrix-core kernel (K records, norms, value segments; reused for
-// the final merge), rounded to 16 bytes.
-__host__ __device__ inline int mfma_region_words(int D, int RS, int VS) {
-  const int stage = 64 * RS + 64 * kMaxGroups + D * VS;
-  const int merge = 16 * (D + 2);
-  return ((stage > merge ? stage : merge) + 3) & ~3;
-}
 __device__ __forceinline__ int single_base(int w) { return w == 6 ? 0 : (w == 7 ? 64 : 192); }
 
-// Eight consecutive codes of width w starting at bit `sh` of the 96-bit window (d2:d1:d0),
-// decoded to fp16 reconstruction levels (low half = first code).
-__device__ __forceinline__ u32x4 decode8(uint32_t d0, uint32_t d1, uint32_t d2, int sh, int w,
-                                         const uint32_t* ptab, const uint16_t* stab) {
-  const uint32_t lo = __builtin_amdgcn_alignbit(d1, d0, sh);
-  const uint32_t hi = __builtin_amdgcn_alignbit(d2, d1, sh);
-  const uint64_t x = (uint64_t(hi) << 32) | lo;
+// Per-wave staging of one tile (bytes): K records of the wave's 16 tokens [token][chunk][16 B],
+// group norms and value norms [g][16] fp16 (value norms at g = n_groups), value segments of
+// the wave's D/4 coordinates [coord][8 b_v B].
+struct TcStage {
+  int n_off, v_off, bytes;
+};
+__host__ __device__ inline TcStage tc_stage(int D, int chunks, int bv) {
+  TcStage g;
+  g.n_off = 256 * chunks;
+  g.v_off = g.n_off + 16 * (2 * kMaxGroups + 2);
+  g.bytes = (g.v_off + 2 * D * bv + 255) & ~255;
+  return g;
+}
+// Workgroup LDS (bytes): tables, k-step descriptors, P operands, softmax exchange, ring.
+constexpr int kTcTab = 4 * kPairWords + 2 * kSingleHalves;           // 6352
+constexpr int kTcDesc = kTcTab;                                       // uint4 [kMaxKSteps][4]
+constexpr int kTcNorm = kTcDesc + 16 * 4 * kMaxKSteps;                // uint32 [kMaxKSteps]
+constexpr int kTcP = (kTcNorm + 4 * kMaxKSteps + 15) & ~15;           // [2][64][16 B]
+constexpr int kTcMx = kTcP + 2048;                                    // float [8][16] maxima, [4][8] sums
+constexpr int kTcRing = (kTcMx + 4 * (128 + 32) + 255) & ~255;
+__host__ __device__ inline int tc_lds_bytes(int D, int chunks, int bv) {
+  return kTcRing + 4 * tc_stage(D, chunks, bv).bytes;
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const uint32_t*>(base + off);
+}
+
+// Eight consecutive codes of width w starting at bit sh of the window d2:d1:d0, as fp16
+// levels (low half = first code).  tb = byte offset of the width's table in LDS.
+__device__ __forceinline__ u32x4 decode8(uint32_t d0, uint32_t d1, uint32_t d2, int sh, int w, const uint8_t* lds,
+                                         uint32_t tb) {
   u32x4 r;
-  if (w <= 5) {
-    const uint32_t* t = ptab + pair_base(w);
-    const uint32_t mask = (1u << (2 * w)) - 1u;
+  if (w <= 4) {      // 8 codes fit one 32-bit window
+    const uint32_t x = __builtin_amdgcn_alignbit(d1, d0, sh);
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) r[e2] = t[uint32_t(x >> (2 * e2 * w)) & mask];
+    for (int e2 = 0; e2 < 4; ++e2) r[e2] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, 2 * e2 * w, 2 * w));
   } else {
-    const uint16_t* t = stab + single_base(w);
-    const uint32_t mask = (1u << w) - 1u;
+    const uint32_t lo = __builtin_amdgcn_alignbit(d1, d0, sh);
+    const uint32_t hi = __builtin_amdgcn_alignbit(d2, d1, sh);
+    const uint64_t x = (uint64_t(hi) << 32) | lo;
+    if (w == 5) {
+      const uint32_t mask = 0x3ffu;
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const uint32_t c0 = uint32_t(x >> (2 * e2 * w)) & mask;
-      const uint32_t c1 = uint32_t(x >> ((2 * e2 + 1) * w)) & mask;
-      r[e2] = uint32_t(t[c0]) | (uint32_t(t[c1]) << 16);
+      for (int e2 = 0; e2 < 4; ++e2) r[e2] = lds_u32(lds, tb + 4 * (uint32_t(x >> (10 * e2)) & mask));
+    } else {
+      const uint32_t mask = (1u << w) - 1u;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t c0 = uint32_t(x >> (2 * e2 * w)) & mask;
+        const uint32_t c1 = uint32_t(x >> ((2 * e2 + 1) * w)) & mask;
+        const uint32_t h0 = *reinterpret_cast<const uint16_t*>(lds + tb + 2 * c0);
+        const uint32_t h1 = *reinterpret_cast<const uint16_t*>(lds + tb + 2 * c1);
+        r[e2] = h0 | (h1 << 16);
+      }
     }
   }
   return r;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_mfma(DecodeArgs a) {
-  constexpr int MT = D / 16;
-  extern __shared__ uint32_t smem[];
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
+// outstanding global loads, so staging loads for later tiles stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Byte offset, in the per-wave K staging [chunk][16 slots][16 B], of record dword wd.
+__device__ __forceinline__ uint32_t kdw_off(uint32_t wd) { return (wd >> 2) * 256u + (wd & 3u) * 4u; }
+
+template <int D, bool NARROW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_decode_mfma(DecodeArgs a) {
+  constexpr int CPW = D / 4;                          // value coordinates per wave
+  constexpr int MTV = CPW / 16;                       // value M-tiles per wave
+  constexpr int MAXNK = NARROW ? 1 : (D + 63) / 64;                  // K staging loads per lane
+  constexpr int MAXNV = NARROW ? (D / 2 + 63) / 64 : (D + 63) / 64;  // value staging loads per lane
+  extern __shared__ __align__(16) uint8_t lds[];
   const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
   const int len = a.lengths[s];
   const int tiles = (len + kTile - 1) / kTile;
   const int per = (tiles + a.n_split - 1) / a.n_split;
   const int t0 = split * per;
   const int t1 = t0 + per < tiles ? t0 + per : tiles;
+  const int count = t1 > t0 ? t1 - t0 : 0;
   const int bv = a.v_bits, chunks = a.chunks;
-  const int RS = 4 * chunks + 3, VS = 2 * bv + 3;
-  const int region_words = mfma_region_words(D, RS, VS);
-
-  uint32_t* ptab = smem;
-  uint16_t* stab = reinterpret_cast<uint16_t*>(smem + kPairWords);
-  uint32_t* krec = smem + kTableWords + wave * region_words;   // [64][RS]
-  float* knorm = reinterpret_cast<float*>(krec + 64 * RS);       // [8][64] fp32 group norms
-  uint32_t* vseg = krec + 64 * RS + 64 * kMaxGroups;            // [D][VS]
-
-  uint32_t* lseg = smem + kPairWords + kSingleHalves / 2;        // [4 * kMaxKSteps] then kgroups
-  uint32_t* lkg = lseg + 4 * kMaxKSteps;
+  const TcStage geo = tc_stage(D, chunks, bv);
   const HeadLayout* L = a.layouts + int64_t(s) * a.n_kv + hk;
-  for (int i = tid; i < kPairWords; i += blockDim.x) ptab[i] = c_pair[i];
-  for (int i = tid; i < kSingleHalves; i += blockDim.x) stab[i] = c_single[i];
-  for (int i = tid; i < 4 * kMaxKSteps; i += blockDim.x) lseg[i] = L->seg[i];
-  for (int i = tid; i < kMaxKSteps; i += blockDim.x) lkg[i] = L->kgroups[i];
-  __syncthreads();
-
   const int ng = L->n_groups, nks = L->n_ksteps;
-  const uint4* qm = reinterpret_cast<const uint4*>(a.qmma + (int64_t(s) * a.n_kv + hk) * kMaxKSteps * 2 * 64 * 8);
+
+  // ---- workgroup set-up: level tables, k-step descriptors, zero P columns 8-15
+  {
+    uint32_t* ptab = reinterpret_cast<uint32_t*>(lds);
+    for (int i = tid; i < kPairWords; i += 256) ptab[i] = c_pair[i];
+    uint16_t* stab = reinterpret_cast<uint16_t*>(lds + 4 * kPairWords);
+    for (int i = tid; i < kSingleHalves; i += 256) stab[i] = c_single[i];
+    // per segment: x = byte offset of the window's first record dword, y = control of the
+    // 4-bit-or-narrower decode (shift | 2w << 8 | table << 16; wider segments get a harmless
+    // width-1 control), z = control of the general decode (shift | w << 8 | table << 16).
+    // Segments past the last k-step, up to the register-resident ones, decode bit 0 at width 1.
+    uint4* kd = reinterpret_cast<uint4*>(lds + kTcDesc);
+    const int nseg = 4 * (nks > kQRegSteps ? nks : kQRegSteps);
+    for (int i = tid; i < nseg; i += 256) {
+      const uint32_t seg = i < 4 * nks ? L->seg[i] : (1u << 16);
+      const uint32_t o = seg & 0xffffu, w = (seg >> 16) & 15u;
+      const uint32_t tb = w <= 5 ? 4u * uint32_t(pair_base(int(w))) : 4u * kPairWords + 2u * uint32_t(single_base(int(w)));
+      const uint32_t fast = w <= 4 ? ((o & 31u) | ((2u * w) << 8) | (tb << 16)) : (2u << 8);
+      kd[i] = uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tb << 16), 0u};
+    }
+    uint32_t* kn = reinterpret_cast<uint32_t*>(lds + kTcNorm);
+    for (int i = tid; i < kMaxKSteps; i += 256) {
+      const uint32_t kg = i < nks ? L->kgroups[i] : 0u;
+      kn[i] = (32u * (kg & 0xffu)) | ((32u * ((kg >> 8) & 0xffu)) << 16);
+    }
+    uint32_t* pw = reinterpret_cast<uint32_t*>(lds + kTcP);
+    for (int i = tid; i < 512; i += 256) {
+      const int ln = (i >> 2) & 63;      // lane of the 16-byte B operand
+      if ((ln & 15) >= 8) pw[i] = 0u;
+    }
+  }
+
+  // ---- staging of one tile's share of this wave, through registers: K records of the wave's
+  // 16 tokens record-major ([token][chunk][16 B], unit u = token * chunks + chunk), group and
+  // value norms [g][16] fp16 (value norms at g = n_groups), value segments of the wave's
+  // D/4 coordinates.  Loads for the next tile are in flight while this tile is computed.
   const size_t reg = size_t(s) * a.n_kv + hk;
   const int64_t cap_tiles = a.capacity / kTile;
-  const uint4* kc = reinterpret_cast<const uint4*>(a.k_codes) + reg * cap_tiles * chunks * kTile;
-  const uint16_t* kn = a.k_norms + reg * cap_tiles * kMaxGroups * kTile;
-  const uint32_t* vc = reinterpret_cast<const uint32_t*>(a.v_codes) + reg * cap_tiles * D * 2 * bv;
-  const uint16_t* vn = a.v_norms + reg * cap_tiles * kTile;
-
-  f32x4 acc[MT];
+  const uint8_t* kc = a.k_codes + reg * cap_tiles * chunks * kTile * 16;
+  const uint16_t* knp = a.k_norms + reg * cap_tiles * kMaxGroups * kTile;
+  const uint8_t* vc = a.v_codes + reg * cap_tiles * D * 8 * bv;
+  const uint16_t* vnp = a.v_norms + reg * cap_tiles * kTile;
+  // Every lane loads and stores (no divergent memory operations): lanes past the last
+  // 16-byte unit repeat the last unit, writing the same bytes to the same place.  A head
+  // whose K budget is zero has no K records (chunks == 0): nothing is staged for K.
+  const bool has_k = chunks > 0;
+  uint32_t ksrc[MAXNK], kdst[MAXNK], vdst[MAXNV];
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  const bool real_col = n < 8 && n < a.group;   // output column n carries query head n
+  for (int i = 0; i < MAXNK; ++i) {
+    const int u = has_k ? min(64 * i + lane, 16 * chunks - 1) : 0;
+    const int t = has_k ? u / chunks : 0, c = u - t * (has_k ? chunks : 1);
+    ksrc[i] = uint32_t((c * kTile + 16 * wave + t) * 16);
+    kdst[i] = uint32_t(16 * u);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXNV; ++i) vdst[i] = uint32_t(16 * min(64 * i + lane, D * bv / 8 - 1));
+  const int nu = min(lane, 2 * ng + 1);                      // norm unit of this lane
+  const bool nu_k = nu < 2 * ng;                             // group norm (else value norm)
+  const size_t nsrc = nu_k ? (size_t(nu >> 1) * kTile + 16 * wave + 8 * (nu & 1))
+                           : (size_t(16 * wave + 8 * (nu & 1)));
+  uint4 pk[MAXNK], pn, pv[MAXNV];
+  auto load_tile = [&](int it) {
+    const int tile = t0 + it;
+    const uint8_t* kt = kc + size_t(tile) * chunks * kTile * 16;
+    if (has_k) {
+#pragma unroll
+      for (int i = 0; i < MAXNK; ++i) pk[i] = *reinterpret_cast<const uint4*>(kt + ksrc[i]);
+    }
+    const uint16_t* nb = nu_k ? knp + size_t(tile) * kMaxGroups * kTile : vnp + size_t(tile) * kTile;
+    pn = *reinterpret_cast<const uint4*>(nb + nsrc);
+    const uint8_t* vt = vc + (size_t(tile) * D + CPW * wave) * 8 * bv;
+#pragma unroll
+    for (int i = 0; i < MAXNV; ++i) pv[i] = *reinterpret_cast<const uint4*>(vt + vdst[i]);
+  };
+  uint8_t* const buf = lds + kTcRing + wave * geo.bytes;
+  auto store_tile = [&]() {
+    if (has_k) {
+#pragma unroll
+      for (int i = 0; i < MAXNK; ++i) *reinterpret_cast<uint4*>(buf + kdst[i]) = pk[i];
+    }
+    *reinterpret_cast<uint4*>(buf + geo.n_off + 16 * nu) = pn;
+#pragma unroll
+    for (int i = 0; i < MAXNV; ++i) *reinterpret_cast<uint4*>(buf + geo.v_off + vdst[i]) = pv[i];
+  };
+  if (count > 0) load_tile(0);
 
-  for (int tile = t0 + wave; tile < t1; tile += nwaves) {
+  // ---- rotated query operands of the first k-steps in registers (zero past the last one)
+  const uint4* qm = reinterpret_cast<const uint4*>(a.qmma + reg * kMaxKSteps * 2 * 64 * 8);
+  f16x8 qh[kQRegSteps], ql[kQRegSteps];
+#pragma unroll
+  for (int ks = 0; ks < kQRegSteps; ++ks) {
+    const uint4 z = uint4{0u, 0u, 0u, 0u};
+    qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qm[(ks * 2 + 0) * 64 + lane] : z);
+    ql[ks] = __builtin_bit_cast(f16x8, ks < nks ? qm[(ks * 2 + 1) * 64 + lane] : z);
+  }
+  __syncthreads();
+
+  const uint4* kd = reinterpret_cast<const uint4*>(lds + kTcDesc);
+  const uint32_t* knsel = reinterpret_cast<const uint32_t*>(lds + kTcNorm);
+  const int nsh = n < 8 ? 0 : 16;
+  const uint32_t krec = uint32_t(16 * chunks * n);
+  const uint32_t knb = uint32_t(geo.n_off + 8 * j);
+  uint32_t wide = 0u;   // k-steps with a segment wider than 4 bits
+  for (int ks = 0; ks < nks; ++ks) {
+    const uint32_t wmax = max(max((kd[4 * ks].z >> 8) & 15u, (kd[4 * ks + 1].z >> 8) & 15u),
+                              max((kd[4 * ks + 2].z >> 8) & 15u, (kd[4 * ks + 3].z >> 8) & 15u));
+    if (wmax > 4u) wide |= 1u << ks;
+  }
+  // value windows: coordinate row 16 mi + n of the wave's block, tokens 32 st + 8 j ..
+  const uint32_t vrow = uint32_t(geo.v_off + n * 8 * bv);
+  const uint32_t vw0 = uint32_t(4 * ((8 * j * bv) >> 5)), vsh0 = uint32_t((8 * j * bv) & 31);
+  const uint32_t vw1 = uint32_t(4 * (((32 + 8 * j) * bv) >> 5)), vsh1 = uint32_t(((32 + 8 * j) * bv) & 31);
+  const uint32_t vtb = bv <= 5 ? 4u * uint32_t(pair_base(bv)) : 4u * kPairWords + 2u * uint32_t(single_base(bv));
+
+  f32x4 acc[MTV];
+#pragma unroll
+  for (int mi = 0; mi < MTV; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.0f;
+  const bool real_col = n < a.group;
+  float* mx = reinterpret_cast<float*>(lds + kTcMx);   // [8 heads][4 waves][4 lane groups]
+
+  // every load issued so far (query operands, set-up reads) is complete here, so the only
+  // loads in flight inside the loop are the next tile's
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int it = 0; it < count; ++it) {
+    const int tile = t0 + it;
     const int valid = len - tile * kTile < kTile ? len - tile * kTile : kTile;
-    // ---- stage the tile: K records and group norms (lane = slot), value segments (lane =
-    // coordinate row).  All loads of the tile are issued before the first LDS write.
+    store_tile();                             // this wave's staging is read only by this wave
+    asm volatile("" ::: "memory");            // issue the next tile's loads after these stores
+    if (it + 1 < count) load_tile(it + 1);
+
+    // ---- logits of tokens 16 wave + n (A rows).  Pass A issues a chunk's window reads and
+    // level lookups (k-steps narrower than 5 bits), pass B runs the matrix cores on them;
+    // wide k-steps are decoded separately afterwards.
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    auto mfma_kstep = [&](const u32x4& raw, const f16x8& bh, const f16x8& bl, const f16x4& nv) {
+      const f16x8 A = __builtin_bit_cast(f16x8, raw);
+      f32x4 T = {0.f, 0.f, 0.f, 0.f};
+      T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, T, 0, 0, 0);
+      T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, T, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[r] = fmaf(T[r], float(nv[r]), S[r]);
+    };
+    constexpr int KC = 4;
+#pragma unroll
+    for (int kc = 0; kc < kQRegSteps; kc += KC) {
+      if (kc < nks) {
+        u32x4 raw[KC];
+        f16x4 nrm[KC];
+        uint32_t wd0[KC], wd1[KC], ctl[KC];
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+          const uint2 d = *reinterpret_cast<const uint2*>(kd + 4 * (kc + q) + j);
+          ctl[q] = d.y;
+          wd0[q] = lds_u32(buf, krec + d.x);
+          wd1[q] = lds_u32(buf, krec + d.x + 4);
+          nrm[q] = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[kc + q] >> nsh) & 0xffffu));
+        }
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+          const uint32_t x = __builtin_amdgcn_alignbit(wd1[q], wd0[q], ctl[q]);   // shift = ctl & 31
+          const uint32_t w2 = ctl[q] >> 8;                                          // low 5 bits: 2w
+          const uint32_t o4 = w2 << 1, o6 = w2 + o4, tb = ctl[q] >> 16;
+          raw[q][0] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, 0u, w2));
+          raw[q][1] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, w2, w2));
+          raw[q][2] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, o4, w2));
+          raw[q][3] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, o6, w2));
+        }
+#pragma unroll
+        for (int q = 0; q < KC; ++q)
+          if (kc + q < nks && !(wide & (1u << (kc + q)))) mfma_kstep(raw[q], qh[kc + q], ql[kc + q], nrm[q]);
+      }
+    }
+    // wide k-steps (codes of 5..8 bits in some segment): general decode
+#pragma unroll
+    for (int ks = 0; ks < kQRegSteps; ++ks) {
+      if (wide & (1u << ks)) {
+        const uint4 d = kd[4 * ks + j];
+        const int w = int((d.z >> 8) & 15u);
+        const uint32_t ka = krec + d.x;
+        const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
+        const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
+        mfma_kstep(decode8(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16), qh[ks], ql[ks], nv);
+      }
+    }
+    for (int ks = kQRegSteps; ks < nks; ++ks) {   // k-steps beyond the register-resident ones
+      const uint4 d = kd[4 * ks + j];
+      const int w = int((d.z >> 8) & 15u);
+      const uint32_t ka = krec + d.x;
+      const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
+      const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
+      mfma_kstep(decode8(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16),
+                 __builtin_bit_cast(f16x8, qm[(ks * 2 + 0) * 64 + lane]),
+                 __builtin_bit_cast(f16x8, qm[(ks * 2 + 1) * 64 + lane]), nv);
+    }
+
+    // ---- online softmax (base 2); head c = column c + column c + 8 (rotate the 16-lane row
+    // by 8 with DPP); the tile maximum per head goes through LDS
+    float v[4];
+    float lm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sr = S[r];
+      const float other = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sr), 0x128, 0xf, 0xf, false));
+      v[r] = sr + other;
+      if (16 * wave + 4 * j + r >= valid) v[r] = -INFINITY;
+      lm = fmaxf(lm, v[r]);
+    }
+    if (a.logits && real_col) {
+      float* lg = a.logits + (int64_t(s) * a.n_q + hk * a.group + n) * a.capacity + int64_t(tile) * kTile +
+                  16 * wave + 4 * j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * wave + 4 * j + r < valid) lg[r] = v[r] * kLn2;
+    }
+    if (n < 8) mx[16 * n + 4 * wave + j] = lm;
+    lds_barrier();
+    float tmax;
     {
-      constexpr int MAXCH = D / 16;                 // record chunks at 8 bits per coordinate
-      constexpr int MAXVW = 8;                      // 8-byte words per value segment (8 bits)
-      constexpr int RPL = D / 64;                   // value rows per lane
-      uint4 kr[MAXCH];
-      uint16_t knv[kMaxGroups];
-      uint2 vr[RPL][MAXVW];
-#pragma unroll
-      for (int c = 0; c < MAXCH; ++c)
-        if (c < chunks) kr[c] = kc[(size_t(tile) * chunks + c) * kTile + lane];
-#pragma unroll
-      for (int g = 0; g < kMaxGroups; ++g)
-        if (g < ng) knv[g] = kn[(size_t(tile) * kMaxGroups + g) * kTile + lane];
-      const uint2* vt2 = reinterpret_cast<const uint2*>(vc + size_t(tile) * D * 2 * bv);
-#pragma unroll
-      for (int i = 0; i < RPL; ++i)
-#pragma unroll
-        for (int wv = 0; wv < MAXVW; ++wv)
-          if (wv < bv) vr[i][wv] = vt2[(lane + 64 * i) * bv + wv];
-#pragma unroll
-      for (int c = 0; c < MAXCH; ++c) {
-        if (c < chunks) {
-          uint32_t* row = krec + lane * RS + 4 * c;
-          row[0] = kr[c].x; row[1] = kr[c].y; row[2] = kr[c].z; row[3] = kr[c].w;
-        }
-      }
-      krec[lane * RS + 4 * chunks] = 0u;
-      krec[lane * RS + 4 * chunks + 1] = 0u;
-      krec[lane * RS + 4 * chunks + 2] = 0u;
-#pragma unroll
-      for (int g = 0; g < kMaxGroups; ++g)
-        if (g < ng) knorm[g * 64 + lane] = f16_bits_to_f32(knv[g]);
-#pragma unroll
-      for (int i = 0; i < RPL; ++i) {
-        uint32_t* row = vseg + (lane + 64 * i) * VS;
-#pragma unroll
-        for (int wv = 0; wv < MAXVW; ++wv) {
-          if (wv < bv) { row[2 * wv] = vr[i][wv].x; row[2 * wv + 1] = vr[i][wv].y; }
-        }
-        row[2 * bv] = 0u;
-        row[2 * bv + 1] = 0u;
-        row[2 * bv + 2] = 0u;
-      }
+      const float4* mr = reinterpret_cast<const float4*>(mx + 16 * (n & 7));
+      const float4 m0 = mr[0], m1 = mr[1], m2 = mr[2], m3 = mr[3];
+      tmax = fmaxf(fmaxf(fmaxf(fmaxf(m0.x, m0.y), fmaxf(m0.z, m0.w)), fmaxf(fmaxf(m1.x, m1.y), fmaxf(m1.z, m1.w))),
+                   fmaxf(fmaxf(fmaxf(m2.x, m2.y), fmaxf(m2.z, m2.w)), fmaxf(fmaxf(m3.x, m3.y), fmaxf(m3.z, m3.w))));
     }
-    wave_sync();
+    const float m_new = fmaxf(m_run, tmax);          // finite: every tile has a valid token
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const f16x4 vn = *reinterpret_cast<const f16x4*>(buf + geo.n_off + 32 * ng + 8 * j);
+    f16x4 bp;
+    float psum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(v[r] - m_new);
+      psum += p;
+      bp[r] = (_Float16)(p * float(vn[r]));
+    }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+    if (n < 8) {
+      const int st = wave >> 1, jj = 2 * (wave & 1) + (j >> 1);
+      *reinterpret_cast<f16x4*>(lds + kTcP + (st * 64 + jj * 16 + n) * 16 + 8 * (j & 1)) = bp;
+    }
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int mi = 0; mi < MTV; ++mi) acc[mi] *= alpha;
+    }
+    lds_barrier();
 
-    // ---- logits: per k-step two MFMAs (query high part, remainder) per 16-token M-tile; the
-    // k-step's group partials are scaled by fp32 norms.  M-tile M = 2 st + mt has row m as
-    // token 32 st + 8 (m / 4) + 4 mt + m % 4; output rows 4 j + r are tokens 32 st + 8 j + 4 mt + r.
-    f32x4 S[4];
+    // ---- P V for the wave's coordinates
 #pragma unroll
-    for (int M = 0; M < 4; ++M) S[M] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 qh_next = nks > 0 ? qm[lane] : uint4{0u, 0u, 0u, 0u};
-    uint4 ql_next = nks > 0 ? qm[64 + lane] : uint4{0u, 0u, 0u, 0u};
-#pragma unroll 1
-    for (int ks = 0; ks < nks; ++ks) {
-      const f16x8 qh = __builtin_bit_cast(f16x8, qh_next);
-      const f16x8 ql = __builtin_bit_cast(f16x8, ql_next);
-      if (ks + 1 < nks) {   // prefetch the next k-step's query operands
-        qh_next = qm[((ks + 1) * 2 + 0) * 64 + lane];
-        ql_next = qm[((ks + 1) * 2 + 1) * 64 + lane];
-      }
-      const uint32_t desc = lseg[4 * ks + j];
-      const uint32_t kg = lkg[ks];
-      const int ngrp = n < 8 ? int(kg & 0xff) : int((kg >> 8) & 0xff);
-      const int w = (desc >> 16) & 15, o = desc & 0xffff;
-      const int sh = o & 31;
-      const uint32_t* krow0 = krec + (o >> 5);
-      // the lane's window of its four tokens' records
-      uint32_t d0[4], d1[4];
-#pragma unroll
-      for (int M = 0; M < 4; ++M) {
-        const uint32_t* row = krow0 + (32 * (M >> 1) + 8 * (n >> 2) + 4 * (M & 1) + (n & 3)) * RS;
-        d0[M] = row[0];
-        d1[M] = row[1];
-      }
-      u32x4 raw[4];
-      if (w <= 4) {   // 8 codes fit one 32-bit window: one bit-field extract per pair
-        const uint32_t* t = ptab + pair_base(w);
-#pragma unroll
-        for (int M = 0; M < 4; ++M) {
-          const uint32_t x = __builtin_amdgcn_alignbit(d1[M], d0[M], sh);
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) raw[M][e2] = t[__builtin_amdgcn_ubfe(x, 2 * e2 * w, 2 * w)];
-        }
-      } else {
-#pragma unroll
-        for (int M = 0; M < 4; ++M) {
-          const uint32_t* row = krow0 + (32 * (M >> 1) + 8 * (n >> 2) + 4 * (M & 1) + (n & 3)) * RS;
-          raw[M] = decode8(d0[M], d1[M], row[2], sh, w, ptab, stab);
-        }
-      }
-#pragma unroll
-      for (int M = 0; M < 4; ++M) {
-        const f16x8 A = __builtin_bit_cast(f16x8, raw[M]);
-        f32x4 T = {0.f, 0.f, 0.f, 0.f};
-        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh, T, 0, 0, 0);
-        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql, T, 0, 0, 0);
-        const float4 nv = *reinterpret_cast<const float4*>(knorm + ngrp * 64 + 32 * (M >> 1) + 8 * j + 4 * (M & 1));
-        S[M][0] = fmaf(T[0], nv.x, S[M][0]);
-        S[M][1] = fmaf(T[1], nv.y, S[M][1]);
-        S[M][2] = fmaf(T[2], nv.z, S[M][2]);
-        S[M][3] = fmaf(T[3], nv.w, S[M][3]);
-      }
-    }
-    // head c's logit = column c + column c + 8 (lanes n and n ^ 8 of the same row)
-#pragma unroll
-    for (int M = 0; M < 4; ++M) {
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = S[M][r];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[M][r] = v[r];
-    }
-
-    // ---- per 32-token sub-tile: online softmax (base 2), then P V on the matrix cores
-#pragma unroll 1
     for (int st = 0; st < 2; ++st) {
-      if (32 * st >= valid) break;
-      float sv[8];
-      float tmax = -INFINITY;
+      if (32 * st < valid) {
+        const f16x8 bpv = *reinterpret_cast<const f16x8*>(lds + kTcP + (st * 64 + lane) * 16);
+        const uint32_t vw = st == 0 ? vw0 : vw1, vsh = st == 0 ? vsh0 : vsh1;
+        uint32_t d0[MTV], d1[MTV], d2[MTV];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = st == 0 ? S[e >> 2][e & 3] : S[2 + (e >> 2)][e & 3];
-        sv[e] = (32 * st + 8 * j + e < valid) ? x : -INFINITY;
-        tmax = fmaxf(tmax, sv[e]);
-      }
-      if (a.logits && real_col) {
-        float* lg = a.logits + (int64_t(s) * a.n_q + hk * a.group + n) * a.capacity + int64_t(tile) * kTile +
-                    32 * st + 8 * j;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (32 * st + 8 * j + e < valid) lg[e] = sv[e] * kLn2;
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - mn);
-      m_run = mn;
-      const uint4 nvraw = *reinterpret_cast<const uint4*>(vn + size_t(tile) * kTile + 32 * st + 8 * j);
-      const f16x8 nvv = __builtin_bit_cast(f16x8, nvraw);
-      float psum = 0.0f;
-      f16x8 bp;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(sv[e] - mn);
-        psum += p;
-        bp[e] = (_Float16)((real_col && 32 * st + 8 * j + e < valid) ? p * float(nvv[e]) : 0.0f);
-      }
-      l_run = l_run * alpha + psum;
-      if (__any(alpha != 1.0f)) {   // the running maxima moved: rescale the accumulators
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) acc[mi] *= alpha;
-      }
-      const int start = (32 * st + 8 * j) * bv;
-      const int wofs = start >> 5, sh = start & 31;
-      const uint32_t* vrow0 = vseg + n * VS + wofs;
-      if (bv <= 4) {   // uniform: 8 codes per 32-bit window, pair fields at fixed offsets
-        const uint32_t* t = ptab + pair_base(bv);
-        uint32_t x[MT];
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-          const uint32_t* row = vrow0 + 16 * mi * VS;
-          x[mi] = __builtin_amdgcn_alignbit(row[1], row[0], sh);
+        for (int mi = 0; mi < MTV; ++mi) {
+          const uint32_t ra = vrow + uint32_t(16 * mi * 8 * bv) + vw;
+          d0[mi] = lds_u32(buf, ra);
+          d1[mi] = lds_u32(buf, ra + 4);
+          d2[mi] = bv > 4 ? lds_u32(buf, ra + 8) : 0u;
         }
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-          u32x4 raw;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) raw[e2] = t[__builtin_amdgcn_ubfe(x[mi], 2 * e2 * bv, 2 * bv)];
-          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw), bp, acc[mi], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-          const uint32_t* row = vrow0 + 16 * mi * VS;
-          const u32x4 raw = decode8(row[0], row[1], row[2], sh, bv, ptab, stab);
-          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw), bp, acc[mi], 0, 0, 0);
+        for (int mi = 0; mi < MTV; ++mi) {
+          const u32x4 raw = decode8(d0[mi], d1[mi], d2[mi], int(vsh), bv, lds, vtb);
+          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw), bpv, acc[mi], 0, 0, 0);
         }
       }
     }
-    wave_sync();
+    // the P operands and maxima of this tile are overwritten only after the next tile's first
+    // barrier, which every wave reaches after finishing this tile
   }
 
-  // ---- merge the wavefronts of this workgroup: lane (n, j) holds head n, coords 16 mi + 4 j + r
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  // ---- partial result of this split: lane (n, j) holds head n, coordinates
+  // D/4 wave + 16 mi + 4 j + r; the row sum is spread over lanes and waves
+  float l = l_part;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float* lsm = mx + 128;
+  if (j == 0 && n < 8) lsm[8 * wave + n] = l;
   __syncthreads();
-  float* comb = reinterpret_cast<float*>(smem + kTableWords) + wave * region_words;   // [16][D + 2]
+  if (real_col) {
+    float* dst = a.partial + ((int64_t(s) * a.n_q + hk * a.group + n) * a.n_split + split) * (D + 2);
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
+    for (int mi = 0; mi < MTV; ++mi)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) comb[n * (D + 2) + 16 * mi + 4 * j + r] = acc[mi][r];
-  if (j == 0) {
-    comb[n * (D + 2) + D] = m_run;
-    comb[n * (D + 2) + D + 1] = l_run;
-  }
-  __syncthreads();
-  const float* comb0 = reinterpret_cast<const float*>(smem + kTableWords);
-  for (int item = tid; item < a.group * (D + 2); item += blockDim.x) {
-    const int hh = item / (D + 2), c = item % (D + 2);
-    float mmax = -INFINITY;
-    for (int w = 0; w < nwaves; ++w) mmax = fmaxf(mmax, comb0[w * region_words + hh * (D + 2) + D]);
-    float v = 0.0f;
-    if (c == D) {
-      v = mmax;
-    } else if (mmax != -INFINITY) {
-      for (int w = 0; w < nwaves; ++w) {
-        const float mw = comb0[w * region_words + hh * (D + 2) + D];
-        if (mw != -INFINITY) v += comb0[w * region_words + hh * (D + 2) + c] * exp2f(mw - mmax);
-      }
+      for (int r = 0; r < 4; ++r) dst[CPW * wave + 16 * mi + 4 * j + r] = acc[mi][r];
+    if (wave == 0 && j == 0) {
+      dst[D] = m_run;
+      dst[D + 1] = lsm[n] + lsm[8 + n] + lsm[16 + n] + lsm[24 + n];
     }
-    a.partial[((int64_t(s) * a.n_q + hk * a.group + hh) * a.n_split + split) * (D + 2) + c] = v;
   }
 }
 
@@ -1060,11 +1143,18 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st)
     hipLaunchKernelGGL(k_decode_prep<float>, dim3(a.n_q, a.batch), dim3(128), 0, st, a);
   const dim3 grid(a.n_split, a.n_kv, a.batch);
   if (a.use_mfma) {
-    const int region_words = mfma_region_words(D, 4 * a.chunks + 3, 2 * a.v_bits + 3);
-    int nwaves = 4;
-    while (nwaves > 1 && (kTableWords + nwaves * region_words) * 4 > 64 * 1024) --nwaves;
-    const size_t lds = size_t(kTableWords + nwaves * region_words) * 4;
-    hipLaunchKernelGGL(k_decode_mfma<D>, grid, dim3(64 * nwaves), lds, st, a);
+    const int lds = tc_lds_bytes(D, a.chunks, a.v_bits);
+    const bool narrow = a.chunks <= 4 && a.v_bits <= 4;
+    const void* fn = narrow ? reinterpret_cast<const void*>(&k_decode_mfma<D, true>)
+                            : reinterpret_cast<const void*>(&k_decode_mfma<D, false>);
+    if (lds > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+    }
+    if (narrow)
+      hipLaunchKernelGGL((k_decode_mfma<D, true>), grid, dim3(256), size_t(lds), st, a);
+    else
+      hipLaunchKernelGGL((k_decode_mfma<D, false>), grid, dim3(256), size_t(lds), st, a);
   } else {
     const int maxg = a.group <= 1 ? 1 : a.group <= 2 ? 2 : a.group <= 4 ? 4 : a.group <= 8 ? 8 : 16;
     const int RS = 4 * a.chunks + 1, VS = 2 * a.v_bits + 1;
@@ -1150,7 +1240,7 @@ int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma) {
   const int64_t tiles = capacity / kTile;
   const int64_t units = int64_t(batch) * n_kv_heads;
   int64_t want = (1024 + units - 1) / units;         // about 1024 workgroups in flight
-  const int64_t per_split = mfma ? 8 : 8;             // tiles per split at least
+  const int64_t per_split = mfma ? 6 : 8;             // tiles per split at least
   const int64_t by_work = (tiles + per_split - 1) / per_split;
   if (want > by_work) want = by_work;
   if (want < 1) want = 1;
