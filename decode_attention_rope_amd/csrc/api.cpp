@@ -204,7 +204,8 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
 size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t capacity) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || capacity < kTile) return 0;
   const int splits = decode_splits(batch, n_kv_heads, capacity, true);
-  const size_t part = align256(size_t(batch) * n_q_heads * splits * (head_dim + 2) * 4);
+  const size_t part = align256(size_t(batch) * n_q_heads * splits * head_dim * 4) +
+                      align256(size_t(batch) * n_q_heads * splits * 8);
   return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + align256(decode_qmma_bytes(batch, n_kv_heads)) +
          part;
 }
@@ -252,6 +253,8 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.qrot = reinterpret_cast<float*>(ws);
   a.qmma = reinterpret_cast<uint16_t*>(ws + qrot_b);
   a.partial = reinterpret_cast<float*>(ws + qrot_b + qmma_b);
+  a.part_ml = reinterpret_cast<float2*>(ws + qrot_b + qmma_b +
+                                        align256(size_t(cache->batch) * n_q_heads * a.n_split * d * 4));
   a.rope_theta = rope_theta;
   for (int j = 0; j < d / 2; ++j) a.inv_freq[j] = rope_theta > 0.0 ? std::pow(rope_theta, -2.0 * j / d) : 0.0;
   a.scale = softmax_scale;

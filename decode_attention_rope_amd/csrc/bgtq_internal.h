@@ -128,7 +128,8 @@ struct DecodeArgs {
   float* logits;
   float* qrot;        // [batch][n_kv][d][kQPad] fp32 (vector-ALU kernel)
   uint16_t* qmma;     // [batch][n_kv][kMaxKSteps][2][64][8] fp16 hi/lo matrix-core B operands
-  float* partial;     // [batch][n_q][n_split][d + 2]
+  float* partial;     // [batch][n_q][n_split][d] split accumulators
+  float2* part_ml;    // [batch][n_q][n_split] split (running max, row sum)
   double rope_theta;
   double inv_freq[BGTQ_MAX_HEAD_DIM / 2];   // rope_theta^(-2j/d), fp64, computed on the host
   float scale;

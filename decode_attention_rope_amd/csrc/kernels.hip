@@ -394,89 +394,98 @@ __global__ void k_advance(int32_t* __restrict__ lengths, int seq_begin, int n_se
 // q''_i C[code_i] with q'' = R_m q'_G / sqrt(m): the query is rotated once per head into
 // every group's frame and the keys are never un-rotated.
 
-// Prologue: q' = RoPE(q, pos) (fp64 angles), then q'' per storage position, scaled by
-// softmax_scale * log2(e) / sqrt(m) so that logits come out in base-2 units.  Written in two
-// forms: fp32 [position][head] for the vector-ALU kernel and fp16 matrix-core B operands
-// [k-step][lane][8] for the MFMA kernel (k index 32 s + 8 j + e lives in lane 16 j + head).
+// Prologue: q' = RoPE(q, pos) for the G query heads of one (sequence, KV head) with fp64
+// angles, then q'' for storage positions p of the head's layout,
+//   q''[h][p] = (softmax_scale * log2(e) / sqrt(m)) * sum_k R_m[p - first][k] q'[h][perm[first + k]],
+// m and first those of p's width group, so that logits come out in base-2 units.  Workgroup
+// z of the (sequence, KV head) writes the matrix-core B operands of k-steps z, z + kPrepZ, ..:
+// lane 16 j + c of k-step s holds k indices 32 s + 8 j + e, column c < 8 is head c for the
+// k-step's first width group, column c + 8 head c for its second, as an fp16 high part and
+// an fp16 remainder.  For the vector-ALU kernel it writes fp32 q'' [position][kQPad] of
+// positions z, z + kPrepZ, ...
+constexpr int kPrepZ = 8;
 template <typename T>
-__global__ __launch_bounds__(128) void k_decode_prep(DecodeArgs a) {
-  __shared__ float qs[BGTQ_MAX_HEAD_DIM];
-  __shared__ float qk[32 * kMaxKSteps];
-  const int h = blockIdx.x, s = blockIdx.y;
-  const int hk = h / a.group, hl = h % a.group;
-  const int d = a.d, n = d / 2;
-  const int64_t pos = a.q_pos ? a.q_pos[s] : int64_t(a.lengths[s]) - 1;
-  const T* q = static_cast<const T*>(a.q) + (int64_t(s) * a.n_q + h) * d;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    const int ca = a.pairing ? 2 * j : j, cb = a.pairing ? 2 * j + 1 : j + n;
-    const float x0 = load_f(q, ca), x1 = load_f(q, cb);
-    if (a.rope_theta > 0.0) {
-      const double ang = fmod(double(pos) * a.inv_freq[j], kTwoPi);
-      double sn, cs;
-      sincos(ang, &sn, &cs);
-      qs[ca] = float(double(x0) * cs - double(x1) * sn);
-      qs[cb] = float(double(x0) * sn + double(x1) * cs);
-    } else {
-      qs[ca] = x0;
-      qs[cb] = x1;
-    }
+__global__ __launch_bounds__(256) void k_decode_prep(DecodeArgs a) {
+  __shared__ HeadLayout L;
+  __shared__ float qs[BGTQ_MAX_GROUP * BGTQ_MAX_HEAD_DIM];          // q' by coordinate
+  __shared__ float qp[BGTQ_MAX_GROUP * (BGTQ_MAX_HEAD_DIM + 1)];    // q' by storage position
+  __shared__ float qv[32 * BGTQ_MAX_GROUP];                         // q'' of one k-step [t][h]
+  __shared__ int16_t pos_of_k[32 * kMaxKSteps];
+  const int hk = blockIdx.x, s = blockIdx.y, z = blockIdx.z, tid = threadIdx.x;
+  const int G = a.group, d = a.d, n = d / 2, QS = d + 1;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.layouts + int64_t(s) * a.n_kv + hk);
+    uint4* dst = reinterpret_cast<uint4*>(&L);
+    for (int i = tid; i < int(sizeof(HeadLayout) / 16); i += 256) dst[i] = src[i];
   }
-  for (int i = threadIdx.x; i < 32 * kMaxKSteps; i += blockDim.x) qk[i] = 0.0f;
+  const int64_t pos = a.q_pos ? a.q_pos[s] : int64_t(a.lengths[s]) - 1;
+  const T* q = static_cast<const T*>(a.q) + (int64_t(s) * a.n_q + int64_t(hk) * G) * d;
+  for (int idx = tid; idx < G * n; idx += 256) {
+    const int h = idx / n, j = idx - h * n;
+    const int ca = a.pairing ? 2 * j : j, cb = a.pairing ? 2 * j + 1 : j + n;
+    const double x0 = load_f(q + int64_t(h) * d, ca), x1 = load_f(q + int64_t(h) * d, cb);
+    double sv = 0.0, cv = 1.0;
+    if (a.rope_theta > 0.0) sincos(fmod(double(pos) * a.inv_freq[j], kTwoPi), &sv, &cv);
+    qs[h * d + ca] = float(x0 * cv - x1 * sv);
+    qs[h * d + cb] = float(x0 * sv + x1 * cv);
+  }
+  for (int k = tid; k < 32 * kMaxKSteps; k += 256) pos_of_k[k] = -1;
   __syncthreads();
-  const HeadLayout& L = a.layouts[int64_t(s) * a.n_kv + hk];
-  float* dst = a.qrot + (int64_t(s) * a.n_kv + hk) * d * kQPad;
-  for (int p = threadIdx.x; p < d; p += blockDim.x) {
-    float v = 0.0f;
-    if (p < L.d_eff) {
-      const int g = L.group[p], m = L.g_m[g], first = L.g_first[g];
-      const float2* R2 = reinterpret_cast<const float2*>(a.rot_bank + bank_offset(m) + size_t(p - first) * m);
-      float acc = 0.0f;
-      for (int k0 = 0; k0 < m; k0 += 64) {
-        float2 r[32];
+  const int d_eff = L.d_eff, nks = L.n_ksteps;
+  for (int idx = tid; idx < G * d_eff; idx += 256) {
+    const int h = idx / d_eff, p = idx - h * d_eff;
+    qp[h * QS + p] = qs[h * d + L.perm[p]];
+  }
+  for (int p = tid; p < d_eff; p += 256) pos_of_k[L.kpos[p]] = int16_t(p);
+  __syncthreads();
+  const float kscale = a.scale * kLog2e;
+  // q'' of position p and head h: the group's rotation row times q' (fp32 fused multiply-adds)
+  auto qpp = [&](int p, int h) {
+    const int g = L.group[p], m = L.g_m[g], first = L.g_first[g];
+    const float2* R2 = reinterpret_cast<const float2*>(a.rot_bank + bank_offset(m) + size_t(p - first) * m);
+    const float* x = qp + h * QS + first;
+    float acc = 0.0f;
+#pragma unroll 16
+    for (int k = 0; k < m; k += 2) {
+      const float2 r = R2[k >> 1];
+      acc = fmaf(r.x, x[k], acc);
+      acc = fmaf(r.y, x[k + 1], acc);
+    }
+    return acc * (kscale / sqrtf(float(m)));
+  };
+  if (!a.use_mfma) {   // vector-ALU kernel: fp32 [position][kQPad], zero past d_eff and G
+    float* dst = a.qrot + (int64_t(s) * a.n_kv + hk) * d * kQPad;
+    for (int idx = tid; idx < ((d - z + kPrepZ - 1) / kPrepZ) * kQPad; idx += 256) {
+      const int p = z + kPrepZ * (idx / kQPad), h = idx % kQPad;
+      dst[p * kQPad + h] = (p < d_eff && h < G) ? qpp(p, h) : 0.0f;
+    }
+    return;
+  }
+  uint4* qm = reinterpret_cast<uint4*>(a.qmma + (int64_t(s) * a.n_kv + hk) * kMaxKSteps * 2 * 64 * 8);
+  for (int ks = z; ks < nks; ks += kPrepZ) {
+    {  // q'' of the k-step's positions, thread (t, h)
+      const int t = tid >> 3, h = tid & 7;
+      const int p = pos_of_k[32 * ks + t];
+      qv[tid] = (p >= 0 && h < G) ? qpp(p, h) : 0.0f;
+    }
+    __syncthreads();
+    if (tid < 128) {
+      const int part = tid >> 6, lane = tid & 63;
+      const int c = lane & 15, jj = lane >> 4, head = c & 7;
+      const uint32_t half = (L.seg[4 * ks + jj] >> 28) & 1u;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (int(half) == (c >> 3) && head < G) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (k0 + 2 * i < m) r[i] = R2[k0 / 2 + i];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          if (k0 + 2 * i < m) {
-            acc = fmaf(r[i].x, qs[L.perm[first + k0 + 2 * i]], acc);
-            acc = fmaf(r[i].y, qs[L.perm[first + k0 + 2 * i + 1]], acc);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const float v = qv[8 * (8 * jj + e) + head];
+          const uint16_t hi = f32_to_f16_bits(v);
+          const uint16_t bits = part == 0 ? hi : f32_to_f16_bits(v - f16_bits_to_f32(hi));
+          w[e >> 1] |= uint32_t(bits) << (16 * (e & 1));
         }
       }
-      v = acc * (a.scale * kLog2e / sqrtf(float(m)));
-      qk[L.kpos[p]] = v;
+      qm[(ks * 2 + part) * 64 + lane] = uint4{w[0], w[1], w[2], w[3]};
     }
-    dst[p * kQPad + hl] = v;
-  }
-  __syncthreads();
-  // matrix-core B operands: lane 16 j + c of k-step ks holds k indices 32 ks + 8 j + e; column
-  // c < 8 carries head c for the k-step's first group, column c + 8 head c for its second
-  // group; each value is split into an fp16 high part and an fp16 remainder.
-  if (!a.use_mfma) return;   // the matrix-core kernel is used only for group sizes <= 8
-  uint16_t* qm = a.qmma + (int64_t(s) * a.n_kv + hk) * kMaxKSteps * 2 * 64 * 8;
-  const int nk = L.n_ksteps * 32;
-  for (int i = threadIdx.x; i < nk; i += blockDim.x) {
-    const int ks = i / 32, jj = (i / 8) % 4, e = i % 8;
-    const uint32_t half = (L.seg[4 * ks + jj] >> 28) & 1u;
-    const float v = qk[i];
-    const uint16_t vh = f32_to_f16_bits(v);
-    const uint16_t vl = f32_to_f16_bits(v - f16_bits_to_f32(vh));
-    const int lane_on = jj * 16 + hl + 8 * int(half), lane_off = jj * 16 + hl + 8 * int(1u - half);
-    qm[((ks * 2 + 0) * 64 + lane_on) * 8 + e] = vh;
-    qm[((ks * 2 + 1) * 64 + lane_on) * 8 + e] = vl;
-    qm[((ks * 2 + 0) * 64 + lane_off) * 8 + e] = 0;
-    qm[((ks * 2 + 1) * 64 + lane_off) * 8 + e] = 0;
-  }
-  if (hl == 0) {  // columns of absent query heads stay zero
-    const int pad = 8 - a.group;
-    for (int i = threadIdx.x; i < nk * 2 * pad; i += blockDim.x) {
-      const int c = a.group + i % pad, rest = i / pad;
-      const int k = rest % nk, part = rest / nk;     // part: 0..1 = column half
-      const int ks = k / 32, jj = (k / 8) % 4, e = k % 8;
-      qm[((ks * 2 + 0) * 64 + jj * 16 + c + 8 * part) * 8 + e] = 0;
-      qm[((ks * 2 + 1) * 64 + jj * 16 + c + 8 * part) * 8 + e] = 0;
-    }
+    __syncthreads();
   }
 }
 
@@ -643,7 +652,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
     __syncthreads();
     float mmax = -INFINITY;
     for (int w = 0; w < nwaves; ++w) mmax = fmaxf(mmax, comb[w * (D + 2) + D]);
-    float* dst = a.partial + ((int64_t(s) * a.n_q + hk * a.group + h) * a.n_split + split) * (D + 2);
+    const int64_t row = (int64_t(s) * a.n_q + hk * a.group + h) * a.n_split + split;
+    float* dst = a.partial + row * D;
     for (int c = tid; c < D + 2; c += blockDim.x) {
       float v = 0.0f;
       if (c == D) {
@@ -655,7 +665,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
           if (mw != -INFINITY) v += comb[w * (D + 2) + src] * exp2f(mw - mmax);
         }
       }
-      dst[c] = v;
+      if (c < D) dst[c] = v;
+      else reinterpret_cast<float*>(a.part_ml + row)[c - D] = v;
     }
     __syncthreads();
   }
@@ -1057,90 +1068,103 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   if (j == 0 && n < 8) lsm[8 * wave + n] = l;
   __syncthreads();
   if (real_col) {
-    float* dst = a.partial + ((int64_t(s) * a.n_q + hk * a.group + n) * a.n_split + split) * (D + 2);
+    const int64_t row = (int64_t(s) * a.n_q + hk * a.group + n) * a.n_split + split;
+    float* dst = a.partial + row * D;
 #pragma unroll
     for (int mi = 0; mi < MTV; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[CPW * wave + 16 * mi + 4 * j + r] = acc[mi][r];
-    if (wave == 0 && j == 0) {
-      dst[D] = m_run;
-      dst[D + 1] = lsm[n] + lsm[8 + n] + lsm[16 + n] + lsm[24 + n];
-    }
+      *reinterpret_cast<float4*>(dst + CPW * wave + 16 * mi + 4 * j) = float4{acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]};
+    if (wave == 0 && j == 0) a.part_ml[row] = float2{m_run, lsm[n] + lsm[8 + n] + lsm[16 + n] + lsm[24 + n]};
   }
 }
 
 // Merge the splits of one query head and undo the value rotation:
-// out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t].  1024 threads: NSUB
-// threads share a coordinate, each over every NSUB-th split, so many loads are in flight.
+// out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t], from the per-split
+// (m, l) pairs and accumulators; split i is weighted by exp2(m_i - max m).  Every split's
+// accumulator loads are issued before the maximum is known, so they overlap.
 template <int D>
 __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
-  constexpr int NT = 1024, NSUB = NT / D;
-  __shared__ float red[NT];
+  constexpr int NT = 1024, C4 = D / 4, NG = NT / C4, RS = NT / D, NB = 12;
+  __shared__ float red[2][NT / 64];
+  __shared__ float4 part4[NT];
   __shared__ float accs[D];
-  __shared__ float wts[1024];
-  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
-  const float* part = a.partial + (int64_t(s) * a.n_q + h) * a.n_split * (D + 2);
+  __shared__ float outp[NT];
+  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = a.n_split;
+  const size_t base = (size_t(s) * a.n_q + h) * ns;
+  const float2* ml = a.part_ml + base;
+  const float4* acc4 = reinterpret_cast<const float4*>(a.partial + base * D);
+  const int c4 = tid % C4, g = tid / C4;
+  float4 x[NB];
+  float2 mlv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {            // first NB splits of this thread's class
+    const int i = g + NG * b;
+    if (i < ns) { x[b] = acc4[size_t(i) * C4 + c4]; mlv[b] = ml[i]; }
+  }
   float mloc = -INFINITY;
-  for (int i = tid; i < a.n_split; i += NT) mloc = fmaxf(mloc, part[i * (D + 2) + D]);
-  red[tid] = mloc;
+  for (int i = tid; i < ns; i += NT) mloc = fmaxf(mloc, ml[i].x);
+  mloc = wave_max(mloc);
+  if (lane == 0) red[0][wave] = mloc;
   __syncthreads();
-  for (int o = NT / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float mmax = red[0];
-  __syncthreads();
+  float mmax = red[0][0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) mmax = fmaxf(mmax, red[0][w]);
   float lloc = 0.0f;
-  for (int i = tid; i < a.n_split; i += NT) {
-    const float mi = part[i * (D + 2) + D];
-    const float w = (mi == -INFINITY) ? 0.0f : exp2f(mi - mmax);
-    wts[i] = w;
-    lloc += w * part[i * (D + 2) + D + 1];
+  for (int i = tid; i < ns; i += NT) {
+    const float2 v = ml[i];
+    lloc += (v.x == -INFINITY) ? 0.0f : exp2f(v.x - mmax) * v.y;
   }
-  red[tid] = lloc;
+  lloc = wave_sum(lloc);
+  if (lane == 0) red[1][wave] = lloc;
+  float4 v = {0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const float4& xx, const float2& mm) {
+    const float w = (mm.x == -INFINITY) ? 0.0f : exp2f(mm.x - mmax);
+    v.x = fmaf(w, xx.x, v.x);
+    v.y = fmaf(w, xx.y, v.y);
+    v.z = fmaf(w, xx.z, v.z);
+    v.w = fmaf(w, xx.w, v.w);
+  };
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (g + NG * b < ns) add(x[b], mlv[b]);
+  for (int i = g + NG * NB; i < ns; i += NG) add(acc4[size_t(i) * C4 + c4], ml[i]);
+  part4[tid] = v;
   __syncthreads();
-  for (int o = NT / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
+  float ltot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) ltot += red[1][w];
+  if (tid < C4) {
+    float4 t = part4[tid];
+    for (int gg = 1; gg < NG; ++gg) {
+      const float4 y = part4[gg * C4 + tid];
+      t.x += y.x; t.y += y.y; t.z += y.z; t.w += y.w;
+    }
+    accs[4 * tid] = t.x; accs[4 * tid + 1] = t.y; accs[4 * tid + 2] = t.z; accs[4 * tid + 3] = t.w;
   }
-  const float ltot = red[0];
   __syncthreads();
-  const int c = tid % D, q = tid / D;
   {
-    float v = 0.0f;
+    const int r = tid % D, qq = tid / D;
+    float o = 0.0f;
 #pragma unroll 8
-    for (int i = q; i < a.n_split; i += NSUB) v = fmaf(wts[i], part[i * (D + 2) + c], v);
-    red[tid] = v;
+    for (int c = qq * (D / RS); c < (qq + 1) * (D / RS); ++c) o = fmaf(a.rot_v[c * D + r], accs[c], o);
+    outp[tid] = o;
   }
   __syncthreads();
   if (tid < D) {
-    float v = 0.0f;
-    for (int qq = 0; qq < NSUB; ++qq) v += red[qq * D + tid];
-    accs[tid] = v;
-  }
-  __syncthreads();
-  {
-    constexpr int RPER = D / NSUB;
-    float v = 0.0f;
-#pragma unroll 8
-    for (int r = q * RPER; r < (q + 1) * RPER; ++r) v = fmaf(a.rot_v[r * D + c], accs[r], v);
-    red[tid] = v;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float v = 0.0f;
-    for (int qq = 0; qq < NSUB; ++qq) v += red[qq * D + tid];
+    float o = 0.0f;
+#pragma unroll
+    for (int qq = 0; qq < RS; ++qq) o += outp[qq * D + tid];
     const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
-    a.out[(int64_t(s) * a.n_q + h) * D + tid] = v * inv;
+    a.out[(int64_t(s) * a.n_q + h) * D + tid] = o * inv;
   }
 }
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st) {
   if (q_dt == BGTQ_BF16)
-    hipLaunchKernelGGL(k_decode_prep<uint16_t>, dim3(a.n_q, a.batch), dim3(128), 0, st, a);
+    hipLaunchKernelGGL(k_decode_prep<uint16_t>, dim3(a.n_kv, a.batch, kPrepZ), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_decode_prep<float>, dim3(a.n_q, a.batch), dim3(128), 0, st, a);
+    hipLaunchKernelGGL(k_decode_prep<float>, dim3(a.n_kv, a.batch, kPrepZ), dim3(256), 0, st, a);
   const dim3 grid(a.n_split, a.n_kv, a.batch);
   if (a.use_mfma) {
     const int lds = tc_lds_bytes(D, a.chunks, a.v_bits);
