@@ -39,7 +39,7 @@ class BgtqError(RuntimeError):
 
 
 class Quantizer(_c.Structure):
-    _fields_ = [("rot_bank", _vp), ("rot_v", _vp), ("head_dim", _i32)]
+    _fields_ = [("rot_bank", _vp), ("rot_v", _vp), ("rot_bank_t", _vp), ("rot_v_t", _vp), ("head_dim", _i32)]
 
 
 class CacheDesc(_c.Structure):
@@ -52,6 +52,8 @@ class CacheDesc(_c.Structure):
 _SIGNATURES = {
     "bgtq_block_energy": (_i32, [_vp, _i32, _i32, _i64, _i32, _i64, _i64, _i32, _vp, _vp, _sz, _vp]),
     "bgtq_energy_workspace_bytes": (_sz, [_i32, _i64, _i32]),
+    "bgtq_rotation_bank_floats": (_sz, [_i32]),
+    "bgtq_transpose_rotations": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp]),
     "bgtq_allocate_bits": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "bgtq_quantize_append": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _vp]),
     "bgtq_decode_attention": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _f64, _f32, _vp, _vp, _vp, _sz, _vp]),
@@ -139,9 +141,18 @@ def init() -> None:
 # ------------------------------------------------------------------ device objects
 
 def make_quantizer(rot_bank: torch.Tensor, rot_v: torch.Tensor, head_dim: int):
-    """Keeps the rotation tensors alive together with the C descriptor."""
-    q = Quantizer(rot_bank.data_ptr(), rot_v.data_ptr(), head_dim)
-    q._keep = (rot_bank, rot_v)
+    """C descriptor of the rotations; the library writes their transposed copies (kept alive with it)."""
+    n = int(lib().bgtq_rotation_bank_floats(head_dim))
+    if n == 0 or rot_bank.numel() != n or rot_v.numel() != head_dim * head_dim:
+        raise ValueError("rotation bank / value rotation do not match head_dim")
+    if rot_bank.dtype != torch.float32 or rot_v.dtype != torch.float32:
+        raise ValueError("rotations must be float32")
+    rot_bank, rot_v = rot_bank.contiguous(), rot_v.contiguous()
+    bank_t, rv_t = torch.empty_like(rot_bank), torch.empty_like(rot_v)
+    _check(lib().bgtq_transpose_rotations(rot_bank.data_ptr(), rot_v.data_ptr(), head_dim, bank_t.data_ptr(),
+                                          rv_t.data_ptr(), _stream()))
+    q = Quantizer(rot_bank.data_ptr(), rot_v.data_ptr(), bank_t.data_ptr(), rv_t.data_ptr(), head_dim)
+    q._keep = (rot_bank, rot_v, bank_t, rv_t)
     return q
 
 

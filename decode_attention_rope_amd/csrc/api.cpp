@@ -102,6 +102,20 @@ bgtq_status bgtq_codebook(int bits, float* thresholds, float* centroids, double*
   return BGTQ_OK;
 }
 
+size_t bgtq_rotation_bank_floats(int head_dim) {
+  if (head_dim < 2 || head_dim > BGTQ_MAX_HEAD_DIM || head_dim % 2) return 0;
+  return rot_bank_offset(head_dim + 2);
+}
+
+bgtq_status bgtq_transpose_rotations(const float* rot_bank, const float* rot_v, int head_dim, float* rot_bank_t,
+                                     float* rot_v_t, bgtq_stream stream) {
+  if (!rot_bank || !rot_v || !rot_bank_t || !rot_v_t) return fail(BGTQ_ERR_INVALID_ARG, "NULL rotation pointer");
+  if (bgtq_rotation_bank_floats(head_dim) == 0) return fail(BGTQ_ERR_INVALID_ARG, "bad head_dim %d", head_dim);
+  return hip_status(launch_transpose_rotations(rot_bank, rot_v, head_dim, rot_bank_t, rot_v_t,
+                                               static_cast<hipStream_t>(stream)),
+                    "rotation transpose launch");
+}
+
 size_t bgtq_cache_bytes(int batch, int n_kv_heads, int head_dim, int k_width_sum, int v_bits, int64_t capacity,
                         size_t* out4) {
   if (batch < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || v_bits < 1 || v_bits > BGTQ_MAX_BITS ||
@@ -163,7 +177,8 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
                                  const void* keys, const void* values, bgtq_dtype dtype, int64_t n_new,
                                  int64_t stride_seq, int64_t stride_head, int64_t stride_token, bgtq_stream stream) {
   if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
-  if (!qz || !qz->rot_bank || !qz->rot_v) return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
+  if (!qz || !qz->rot_bank || !qz->rot_v || !qz->rot_bank_t || !qz->rot_v_t)
+    return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
   if (qz->head_dim != cache->head_dim) return fail(BGTQ_ERR_INVALID_ARG, "quantizer head_dim != cache head_dim");
   if (!keys || !values) return fail(BGTQ_ERR_INVALID_ARG, "keys and values must not be NULL");
   if (dtype != BGTQ_F32 && dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad dtype");
@@ -179,6 +194,8 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
   AppendArgs a{};
   a.rot_bank = qz->rot_bank;
   a.rot_v = qz->rot_v;
+  a.rot_bank_t = qz->rot_bank_t;
+  a.rot_v_t = qz->rot_v_t;
   a.keys = keys;
   a.values = values;
   a.stride_seq = stride_seq;
@@ -215,7 +232,8 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
                                   float* out, float* logits_out, void* workspace, size_t workspace_bytes,
                                   bgtq_stream stream) {
   if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
-  if (!qz || !qz->rot_bank || !qz->rot_v) return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
+  if (!qz || !qz->rot_bank || !qz->rot_v || !qz->rot_bank_t || !qz->rot_v_t)
+    return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
   if (qz->head_dim != cache->head_dim) return fail(BGTQ_ERR_INVALID_ARG, "quantizer head_dim != cache head_dim");
   if (!q || !out) return fail(BGTQ_ERR_INVALID_ARG, "q and out must not be NULL");
   if (q_dtype != BGTQ_F32 && q_dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad q dtype");
@@ -234,6 +252,7 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
   DecodeArgs a{};
   a.rot_bank = qz->rot_bank;
   a.rot_v = qz->rot_v;
+  a.rot_bank_t = qz->rot_bank_t;
   a.q = q;
   a.q_pos = q_pos;
   a.k_codes = cache->k_codes;

@@ -93,6 +93,8 @@ hipError_t launch_allocate(const double* energy, int n_heads, int n_blocks, int 
 struct AppendArgs {
   const float* rot_bank;
   const float* rot_v;
+  const float* rot_bank_t;
+  const float* rot_v_t;
   const void* keys;
   const void* values;
   int64_t stride_seq, stride_head, stride_token;
@@ -116,6 +118,7 @@ hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStre
 struct DecodeArgs {
   const float* rot_bank;
   const float* rot_v;
+  const float* rot_bank_t;
   const void* q;
   const int64_t* q_pos;
   const uint8_t* k_codes;
@@ -138,5 +141,8 @@ struct DecodeArgs {
   int use_mfma;
 };
 hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s);
+
+hipError_t launch_transpose_rotations(const float* rot_bank, const float* rot_v, int d, float* rot_bank_t,
+                                      float* rot_v_t, hipStream_t s);
 
 }  // namespace bgtq

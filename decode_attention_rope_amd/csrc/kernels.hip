@@ -379,6 +379,163 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   }
 }
 
+// Decode-time append of one token to each sequence (n_new == 1), same arithmetic as
+// k_append.  One workgroup per sequence; its KV heads run two at a time on 512 threads each
+// (threads 0..d-1 rotate the value, d..d+d_eff-1 the key positions, the next ones form the
+// norms), every input of a head is loaded before any arithmetic, and the sequence length
+// is advanced by the same workgroup once all of its heads are written.
+//
+// Sequential fp32 dot product of row `row` of an m x m matrix stored transposed (element
+// (row, k) at Rt[k * m + row]) with x, k ascending, no fused multiply-add; lanes on
+// consecutive rows read consecutive floats.  The loop runs to mu >= m (the same bound for
+// the whole wavefront, a multiple of 16 past it is read from x): terms with k >= m are exact
+// zeros and leave the sum unchanged.  x is 8-byte aligned.
+__device__ __forceinline__ float dot_rows_t(const float* __restrict__ Rt, int m, int mu, int row, const float* x) {
+  float acc = 0.0f;
+  for (int k0 = 0; k0 < mu; k0 += 16) {
+    float r[16], xv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = k0 + i < m ? k0 + i : m - 1;
+      r[i] = Rt[size_t(k) * m + row];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float2 v = *reinterpret_cast<const float2*>(x + k0 + i);
+      xv[i] = v.x; xv[i + 1] = v.y;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool in = k0 + i < m;
+      acc = acc + (in ? r[i] : 0.0f) * (in ? xv[i] : 0.0f);
+    }
+  }
+  return acc;
+}
+
+// Sequential fp32 sum of squares of x[0..m) (m even, x 8-byte aligned).
+__device__ __forceinline__ float seq_sumsq(const float* x, int m) {
+  float ss = 0.0f;
+  int k = 0;
+  for (; k + 8 <= m; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float2 t = *reinterpret_cast<const float2*>(x + k + i);
+      v[i] = t.x; v[i + 1] = t.y;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = ss + v[i] * v[i];
+  }
+  for (; k < m; ++k) ss = ss + x[k] * x[k];
+  return ss;
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
+  constexpr int HP = 2;
+  constexpr int DM = BGTQ_MAX_HEAD_DIM;
+  __shared__ HeadLayout Ls[HP];
+  __shared__ __align__(16) float ko[HP][DM];       // key, original coordinate order
+  __shared__ __align__(16) float xk[HP][2 * DM + 16];   // key, storage order, zero past d_eff
+  __shared__ __align__(16) float xv[HP][DM];       // value
+  __shared__ float nrm[HP][kMaxGroups + 1];        // group norms, value norm last
+  __shared__ uint8_t cd[HP][2 * DM];               // key codes (storage order), value codes at DM
+  const int si = blockIdx.x, s = a.seq_begin + si;
+  const int tid = threadIdx.x, hp = tid >> 9, t = tid & 511;
+  const int d = a.d, bv = a.v_bits;
+  const int64_t len = a.lengths[s];
+  if (len + 1 > a.capacity) {
+    if (tid == 0 && a.status) atomicOr(a.status, 1);
+    return;
+  }
+  const int64_t tiles = a.capacity / kTile;
+  const int64_t tile = len / kTile;
+  const int slot = int(len - tile * kTile);
+  const uint32_t vmask = (1u << bv) - 1u;
+  const int vbit = slot * bv, vw = vbit >> 5, vsh = vbit & 31;
+  const bool vsplit = vsh + bv > 32;
+  for (int h0 = 0; h0 < a.n_kv_heads; h0 += HP) {
+    const int hk = h0 + hp;
+    const bool act = hk < a.n_kv_heads;
+    const size_t reg = size_t(s) * a.n_kv_heads + (act ? hk : 0);
+    HeadLayout& L = Ls[hp];
+    const T* kin = static_cast<const T*>(a.keys) + si * a.stride_seq + int64_t(act ? hk : 0) * a.stride_head;
+    const T* vin = static_cast<const T*>(a.values) + si * a.stride_seq + int64_t(act ? hk : 0) * a.stride_head;
+    uint32_t* vseg = reinterpret_cast<uint32_t*>(a.v_codes) + (reg * tiles + tile) * d * 2 * bv;
+    uint32_t old0 = 0u, old1 = 0u;
+    if (act) {
+      if (t < 256) reinterpret_cast<uint4*>(&L)[t] = reinterpret_cast<const uint4*>(a.layouts + reg)[t];
+      if (t < d) {
+        ko[hp][t] = load_f(kin, t);
+        xv[hp][t] = load_f(vin, t);
+        old0 = vseg[t * 2 * bv + vw];
+        if (vsplit) old1 = vseg[t * 2 * bv + vw + 1];
+      }
+    }
+    __syncthreads();
+    const int ng = act ? L.n_groups : 0, d_eff = act ? L.d_eff : 0;
+    int mmax = 0;
+    for (int g = 0; g < ng; ++g) mmax = L.g_m[g] > mmax ? L.g_m[g] : mmax;
+    for (int i = t; i < 2 * DM + 16; i += 512) xk[hp][i] = i < d_eff ? ko[hp][L.perm[i]] : 0.0f;
+    __syncthreads();
+    // norms run beside the rotations when the head has threads to spare (always for d <= 128)
+    const bool norms_beside = d + d_eff + ng + 1 <= 512;
+    float acc = 0.0f;
+    if (act && t < d) {                                  // value rotation, row t
+      acc = dot_rows_t(a.rot_v_t, d, d, t, xv[hp]);
+    } else if (t >= d && t < d + d_eff) {                // key position p, row p - first of its group
+      const int p = t - d, g = L.group[p], m = L.g_m[g], first = L.g_first[g];
+      acc = dot_rows_t(a.rot_bank_t + bank_offset(m), m, mmax, p - first, xk[hp] + first);
+    } else if (norms_beside && t >= d + d_eff && t < d + d_eff + ng) {   // group norm
+      const int g = t - d - d_eff;
+      nrm[hp][g] = sqrtf(seq_sumsq(xk[hp] + L.g_first[g], L.g_m[g]));
+    } else if (act && norms_beside && t == d + d_eff + ng) {             // value norm
+      nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
+    }
+    if (!norms_beside) {
+      if (t < ng) nrm[hp][t] = sqrtf(seq_sumsq(xk[hp] + L.g_first[t], L.g_m[t]));
+      else if (act && t == ng) nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
+    }
+    __syncthreads();
+    if (act && t < d) {
+      const float nv = nrm[hp][kMaxGroups];
+      cd[hp][DM + t] = uint8_t(nv != 0.0f ? code_of(c_thr[bv - 1], bv, (acc / nv) * sqrtf(float(d))) : 0);
+    } else if (t >= d && t < d + d_eff) {
+      const int p = t - d, g = L.group[p], w = L.g_width[g], m = L.g_m[g];
+      const float nv = nrm[hp][g];
+      cd[hp][p] = uint8_t(nv != 0.0f ? code_of(c_thr[w - 1], w, (acc / nv) * sqrtf(float(m))) : 0);
+    }
+    __syncthreads();
+    if (act) {
+      // key record dwords of the slot
+      uint32_t* kc = reinterpret_cast<uint32_t*>(a.k_codes) + (reg * tiles + tile) * a.chunks * kTile * 4;
+      if (t < 4 * a.chunks) {
+        const int w = t;
+        uint32_t v = 0u;
+        for (int p = L.dw_first[w]; p < L.dw_end[w]; ++p) {
+          const uint32_t c = cd[hp][p];
+          const int o = int(L.offset[p]) - 32 * w;
+          v |= o >= 0 ? (c << o) : (c >> (-o));
+        }
+        kc[((w >> 2) * kTile + slot) * 4 + (w & 3)] = v;
+      }
+      // value segment bits of the slot (the dwords were read before any arithmetic)
+      if (t < d) {
+        const uint32_t code = cd[hp][DM + t];
+        vseg[t * 2 * bv + vw] = (old0 & ~(vmask << vsh)) | (code << vsh);
+        if (vsplit) vseg[t * 2 * bv + vw + 1] = (old1 & ~(vmask >> (32 - vsh))) | (code >> (32 - vsh));
+      }
+      uint16_t* kn = a.k_norms + (reg * tiles + tile) * kMaxGroups * kTile;
+      if (t >= 256 && t < 256 + ng) kn[(t - 256) * kTile + slot] = f32_to_f16_bits(fminf(nrm[hp][t - 256], 65504.0f));
+      if (t == 256 + kMaxGroups)
+        a.v_norms[(reg * tiles + tile) * kTile + slot] = f32_to_f16_bits(fminf(nrm[hp][kMaxGroups], 65504.0f));
+    }
+    __syncthreads();
+  }
+  if (tid == 0) a.lengths[s] = int32_t(len + 1);
+}
+
 __global__ void k_advance(int32_t* __restrict__ lengths, int seq_begin, int n_seqs, int64_t n_new,
                           int64_t capacity) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1238,6 +1395,13 @@ hipError_t launch_allocate(const double* energy, int n_heads, int n_blocks, int 
 }
 
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s) {
+  if (a.n_new == 1) {   // decode step: one token per sequence, length advanced in the same kernel
+    if (dt == BGTQ_BF16)
+      hipLaunchKernelGGL(k_append_one<uint16_t>, dim3(n_seqs), dim3(1024), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_append_one<float>, dim3(n_seqs), dim3(1024), 0, s, a);
+    return hipGetLastError();
+  }
   const int halves = int((a.n_new + kHalf - 1) / kHalf) + 1;
   const dim3 grid(halves, a.n_kv_heads, n_seqs);
   const size_t lds = size_t(kHalf) * (a.d + 1) * 4 + kMaxBits * 255 * 4 + kHalf * kMaxGroups * 4 + kHalf * 4 +
@@ -1248,6 +1412,27 @@ hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStre
     hipLaunchKernelGGL(k_append<float>, grid, dim3(256), lds, s, a);
   hipLaunchKernelGGL(k_advance, dim3((n_seqs + 63) / 64), dim3(64), 0, s, a.lengths, a.seq_begin, n_seqs, a.n_new,
                      a.capacity);
+  return hipGetLastError();
+}
+
+// Transposed copies of the rotation bank (block m = 2 blockIdx.y + 2) and of the value rotation
+// (blockIdx.y = d / 2).
+__global__ __launch_bounds__(256) void k_transpose_rotations(const float* __restrict__ bank, const float* __restrict__ rv,
+                                                             int d, float* __restrict__ bank_t, float* __restrict__ rv_t) {
+  const bool value = int(blockIdx.y) == d / 2;
+  const int m = value ? d : 2 * int(blockIdx.y) + 2;
+  const float* src = value ? rv : bank + bank_offset(m);
+  float* dst = value ? rv_t : bank_t + bank_offset(m);
+  for (int e = int(blockIdx.x) * 256 + int(threadIdx.x); e < m * m; e += int(gridDim.x) * 256) {
+    const int row = e / m, col = e - row * m;
+    dst[col * m + row] = src[e];
+  }
+}
+
+hipError_t launch_transpose_rotations(const float* rot_bank, const float* rot_v, int d, float* rot_bank_t,
+                                      float* rot_v_t, hipStream_t s) {
+  hipLaunchKernelGGL(k_transpose_rotations, dim3((d * d + 255) / 256, d / 2 + 1), dim3(256), 0, s, rot_bank, rot_v,
+                     d, rot_bank_t, rot_v_t);
   return hipGetLastError();
 }
 

@@ -62,15 +62,32 @@ typedef void* bgtq_stream;
 
 /* Random rotations the quantizer draws (TQ-MSE rotates before scalar coding).
  * Device memory, caller-owned, read-only, shared by all layers and heads.
- *   rot_bank: Haar matrices for the key width groups, m = 2, 4, ..., head_dim,
- *             each m x m row-major (y = R x), concatenated in that order
- *             (sum over even m of m*m floats).
- *   rot_v:    head_dim x head_dim row-major rotation for values. */
+ *   rot_bank:   Haar matrices for the key width groups, m = 2, 4, ..., head_dim,
+ *               each m x m row-major (y = R x), concatenated in that order
+ *               (bgtq_rotation_bank_floats(head_dim) floats).
+ *   rot_v:      head_dim x head_dim row-major rotation for values.
+ *   rot_bank_t, rot_v_t: the same matrices transposed (each block column-major),
+ *               written by bgtq_transpose_rotations; kernels that form one
+ *               output row per lane read these so that a wavefront's loads are
+ *               contiguous. */
 typedef struct {
   const float* rot_bank;
   const float* rot_v;
+  const float* rot_bank_t;
+  const float* rot_v_t;
   int head_dim;
 } bgtq_quantizer;
+
+/* Floats in a rotation bank for head_dim (sum of m*m over even m <= head_dim), 0 if
+ * head_dim is not a supported even size. */
+size_t bgtq_rotation_bank_floats(int head_dim);
+
+/* Writes the transposed copies a bgtq_quantizer carries: every m x m block of
+ * rot_bank transposed into rot_bank_t (same offsets), rot_v into rot_v_t.
+ * All device pointers, caller-owned; rot_bank_t and rot_v_t must not overlap the
+ * inputs.  Enqueued on `stream`.  Errors: INVALID_ARG, HIP. */
+bgtq_status bgtq_transpose_rotations(const float* rot_bank, const float* rot_v, int head_dim,
+                                     float* rot_bank_t, float* rot_v_t, bgtq_stream stream);
 
 /* Packed K/V cache of one layer for a batch of sequences.  All pointers are
  * device memory the caller allocates (sizes from bgtq_cache_bytes) and owns.

@@ -82,7 +82,7 @@ def _desc(**over):
 
 
 def _quantizer(d=128):
-    return bgtq.Quantizer(FAKE, FAKE, d)
+    return bgtq.Quantizer(FAKE, FAKE, FAKE, FAKE, d)
 
 
 def test_append_validation():
@@ -107,6 +107,22 @@ def test_append_validation():
     assert call(_desc(), keys=None) == bgtq.ERR_INVALID_ARG
     assert lib.bgtq_quantize_append(None, ctypes.byref(_desc()), 0, 1, FAKE, FAKE, 0, 1, 1, 1, 128,
                                     None) == bgtq.ERR_INVALID_ARG
+
+
+def test_rotation_helpers_validation():
+    lib = bgtq.lib()
+    assert lib.bgtq_rotation_bank_floats(128) == sum(m * m for m in range(2, 129, 2))
+    assert lib.bgtq_rotation_bank_floats(64) == sum(m * m for m in range(2, 65, 2))
+    assert lib.bgtq_rotation_bank_floats(63) == 0 and lib.bgtq_rotation_bank_floats(258) == 0
+    assert lib.bgtq_transpose_rotations(None, FAKE, 128, FAKE, FAKE, None) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_transpose_rotations(FAKE, FAKE, 127, FAKE, FAKE, None) == bgtq.ERR_INVALID_ARG
+
+
+def test_quantizer_without_transposed_rotations_is_rejected():
+    lib = bgtq.lib()
+    qz = bgtq.Quantizer(FAKE, FAKE, None, FAKE, 128)
+    assert lib.bgtq_quantize_append(ctypes.byref(qz), ctypes.byref(_desc()), 0, 1, FAKE, FAKE, 0, 1, 1000, 300,
+                                    128, None) == bgtq.ERR_INVALID_ARG
 
 
 def test_decode_validation():

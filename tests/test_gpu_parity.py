@@ -156,6 +156,47 @@ def test_capacity_overflow_sets_status(rot64):
     assert torch.equal(before, cache.k_codes)
 
 
+@pytest.mark.parametrize("d,k_bits,v_bits,h_kv,prefill,steps,dtype,seq_begin", [
+    (128, 3, 3, 2, [60, 0, 130], 70, "f32", 0),     # three sequences, tile crossings
+    (64, 2, 5, 6, [10, 63], 40, "bf16", 0),         # more heads than one pass, straddling value codes
+    (64, 3, 3, 3, [7, 20], 30, "f32", 1),           # only the second sequence grows
+    (256, 3, 7, 1, [5], 70, "f32", 0),
+    (128, 0, 3, 2, [3], 66, "f32", 0),              # zero key budget
+])
+def test_append_one_token_per_step_bit_exact(d, k_bits, v_bits, h_kv, prefill, steps, dtype, seq_begin):
+    """Decode-style appends (one token per sequence per call) against the oracle, byte for byte."""
+    dev = _cuda()
+    _say(f"append-one d={d} K{k_bits}V{v_bits} h_kv={h_kv} prefill={prefill} steps={steps} {dtype} sb={seq_begin}")
+    n_seq = len(prefill)
+    grow = list(range(seq_begin, n_seq))
+    t_lens = [p + (steps if s in grow else 0) for s, p in enumerate(prefill)]
+    cap = -(-max(t_lens) // 64) * 64 + 64
+    wl = synth.Workload("append_one", 91, d=d, h_q=h_kv, h_kv=h_kv, theta=1e4, layers=1, seq_lens=tuple(t_lens),
+                        k_bits=k_bits, v_bits=v_bits, key_dtype=dtype, profile="decay", outlier_blocks=2)
+    bank, rv = synth.rotation_bank(d, seed=7), synth.rotation_v(d, seed=7)
+    qz = bgtq.make_quantizer(_t(bank), _t(rv), d)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ks = [np.stack([synth.keys(wl, s, 0, h, 0, t_lens[s]) for h in range(h_kv)]) for s in range(n_seq)]
+    vs = [np.stack([synth.values(wl, s, 0, h, 0, t_lens[s]) for h in range(h_kv)]) for s in range(n_seq)]
+    cache = bgtq.PackedCache(n_seq, h_kv, d, wl.budget, v_bits, cap, device=dev)
+    for s in range(n_seq):
+        bgtq.bgtq_allocate_bits(bgtq.bgtq_block_energy(_t(ks[s])), wl.budget, widths_out=cache.widths[s],
+                                layouts_out=cache.layouts[s])
+        if prefill[s]:
+            bgtq.bgtq_quantize_append(qz, cache, _t(ks[s][:, :prefill[s]])[None].to(tdt),
+                                      _t(vs[s][:, :prefill[s]])[None].to(tdt), seq_begin=s)
+    for step in range(steps):
+        kn = torch.stack([_t(ks[s][:, prefill[s] + step:prefill[s] + step + 1]) for s in grow]).to(tdt)
+        vn = torch.stack([_t(vs[s][:, prefill[s] + step:prefill[s] + step + 1]) for s in grow]).to(tdt)
+        bgtq.bgtq_quantize_append(qz, cache, kn.contiguous(), vn.contiguous(), seq_begin=seq_begin)
+    torch.cuda.synchronize()
+    assert cache.lengths.tolist() == t_lens and int(cache.status[0]) == 0
+    for s in range(n_seq):
+        for h in range(h_kv):
+            ref = head_reference(ks[s][h], vs[s][h], wl.budget, v_bits, bank, rv, cap)
+            assert_region_equal(cache.region(s, h), ref["region"], t_lens[s], ref["layout"], v_bits, d)
+
+
 # ---------------------------------------------------------------- decode
 
 def _decode_vs_oracle(wl, t_lens, qz, bank, rv, dtype=torch.float32, append_then_attend=False, pairing=0,
