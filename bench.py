@@ -53,6 +53,24 @@ def bytes_per_token_head(widths_row, v_bits, d) -> int:
     return k_code_bits // 8 + 2 * groups + v_bits * d // 8 + 2
 
 
+def measured_traffic(workload: str):
+    """HBM bytes of one decode call from the committed rocprofv3 byte counters (profiles/), or None
+    when they were taken on another workload or on a kernel source that has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    src = os.path.join(ROOT, "decode_attention_rope_amd", "csrc", "kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    return float(rec["traffic_bytes_per_call"])
+
+
 def cpu_baseline(wl, layer_sample: int = 1):
     """The oracle, as it stands, on `layer_sample` of the workload's layers (one decode step each)."""
     import numpy as np
@@ -216,8 +234,9 @@ def main():
                    "head_dim": wl.d, "context": ctx, "batch": 1, "budget": f"K{wl.k_bits}V{wl.v_bits}",
                    "capacity": cap},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode attention (one bgtq_decode_attention call per layer)",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
+                     "kernel": "decode attention: one bgtq_decode_attention call per layer "
+                               "(k_decode_prep + k_decode_mfma + k_decode_combine)",
                      "us_per_launch": us_per_launch, "alg_bytes_per_launch": bytes_per_launch},
         "prefill_ms_per_layer": pre_ms / wl.layers,
         "packed_cache_bytes_per_layer": caches[0].nbytes,
