@@ -382,33 +382,62 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 // Decode-time append of one token to each sequence (n_new == 1), same arithmetic as
 // k_append.  One workgroup per sequence; its KV heads run two at a time on 512 threads each
 // (threads 0..d-1 rotate the value, d..d+d_eff-1 the key positions, the next ones form the
-// norms), every input of a head is loaded before any arithmetic, and the sequence length
-// is advanced by the same workgroup once all of its heads are written.
+// norms).  Every input is requested before any arithmetic: the layout, key and value of each
+// head, the quantizer thresholds (copied to LDS) and, for head_dim <= 128, the value rotation
+// (copied to LDS with rows padded to d + 1 floats, so lanes on consecutive rows hit distinct
+// banks).  The sequence length is advanced by the same workgroup once all heads are written.
 //
 // Sequential fp32 dot product of row `row` of an m x m matrix stored transposed (element
 // (row, k) at Rt[k * m + row]) with x, k ascending, no fused multiply-add; lanes on
 // consecutive rows read consecutive floats.  The loop runs to mu >= m (the same bound for
-// the whole wavefront, a multiple of 16 past it is read from x): terms with k >= m are exact
-// zeros and leave the sum unchanged.  x is 8-byte aligned.
+// the whole wavefront, rounded up to 16, read from x): terms with k >= m are exact zeros and
+// leave the sum unchanged.  Up to 32 terms are requested before the first add.  x is 8-byte
+// aligned.
 __device__ __forceinline__ float dot_rows_t(const float* __restrict__ Rt, int m, int mu, int row, const float* x) {
   float acc = 0.0f;
-  for (int k0 = 0; k0 < mu; k0 += 16) {
+  for (int k0 = 0; k0 < mu; k0 += 32) {
+    float r[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int k = k0 + i < m ? k0 + i : m - 1;
+      if (i < 16 || k0 + i < mu) r[i] = Rt[size_t(k) * m + row];
+    }
+#pragma unroll
+    for (int b = 0; b < 32; b += 16) {
+      if (b == 0 || k0 + b < mu) {
+        float xv[16];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float2 v = *reinterpret_cast<const float2*>(x + k0 + b + i);
+          xv[i] = v.x; xv[i + 1] = v.y;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool in = k0 + b + i < m;
+          acc = acc + (in ? r[b + i] : 0.0f) * (in ? xv[i] : 0.0f);
+        }
+      }
+    }
+  }
+  return acc;
+}
+
+// Sequential fp32 dot product of row `row` of an LDS matrix with row stride ld and x (both in
+// LDS), k ascending over [0, m), m a multiple of 16.
+__device__ __forceinline__ float dot_rows_lds(const float* R, int ld, int m, int row, const float* x) {
+  float acc = 0.0f;
+  const float* rr = R + row * ld;
+  for (int k0 = 0; k0 < m; k0 += 16) {
     float r[16], xv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = k0 + i < m ? k0 + i : m - 1;
-      r[i] = Rt[size_t(k) * m + row];
-    }
+    for (int i = 0; i < 16; ++i) r[i] = rr[k0 + i];
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const float2 v = *reinterpret_cast<const float2*>(x + k0 + i);
       xv[i] = v.x; xv[i + 1] = v.y;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool in = k0 + i < m;
-      acc = acc + (in ? r[i] : 0.0f) * (in ? xv[i] : 0.0f);
-    }
+    for (int i = 0; i < 16; ++i) acc = acc + r[i] * xv[i];
   }
   return acc;
 }
@@ -431,10 +460,19 @@ __device__ __forceinline__ float seq_sumsq(const float* x, int m) {
   return ss;
 }
 
-template <typename T>
+// Dynamic LDS of k_append_one: thresholds, then (STAGE_V) the padded value rotation.
+constexpr int kAppendThrFloats = kMaxBits * 255;
+__host__ __device__ inline size_t append_one_lds_bytes(int d, bool stage_v) {
+  return size_t(kAppendThrFloats) * 4 + (stage_v ? size_t(d) * (d + 1) * 4 : 0);
+}
+
+template <typename T, bool STAGE_V>
 __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
   constexpr int HP = 2;
   constexpr int DM = BGTQ_MAX_HEAD_DIM;
+  extern __shared__ __align__(16) float dyn[];
+  float* thr = dyn;                                // [8][255]
+  float* rv = dyn + kAppendThrFloats;              // [d][d + 1] (STAGE_V)
   __shared__ HeadLayout Ls[HP];
   __shared__ __align__(16) float ko[HP][DM];       // key, original coordinate order
   __shared__ __align__(16) float xk[HP][2 * DM + 16];   // key, storage order, zero past d_eff
@@ -444,6 +482,17 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
   const int si = blockIdx.x, s = a.seq_begin + si;
   const int tid = threadIdx.x, hp = tid >> 9, t = tid & 511;
   const int d = a.d, bv = a.v_bits;
+  // ---- inputs that do not depend on the sequence length
+  for (int i = tid; i < kAppendThrFloats; i += 1024) thr[i] = (&c_thr[0][0])[i];
+  if (STAGE_V) {
+    const float4* src = reinterpret_cast<const float4*>(a.rot_v);
+    for (int i = tid; i < d * d / 4; i += 1024) {
+      const float4 v = src[i];
+      const int row = (4 * i) / d, col = 4 * i - row * d;
+      float* dst = rv + row * (d + 1) + col;
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    }
+  }
   const int64_t len = a.lengths[s];
   if (len + 1 > a.capacity) {
     if (tid == 0 && a.status) atomicOr(a.status, 1);
@@ -477,13 +526,14 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
     const int ng = act ? L.n_groups : 0, d_eff = act ? L.d_eff : 0;
     int mmax = 0;
     for (int g = 0; g < ng; ++g) mmax = L.g_m[g] > mmax ? L.g_m[g] : mmax;
+    mmax = (mmax + 15) & ~15;
     for (int i = t; i < 2 * DM + 16; i += 512) xk[hp][i] = i < d_eff ? ko[hp][L.perm[i]] : 0.0f;
     __syncthreads();
     // norms run beside the rotations when the head has threads to spare (always for d <= 128)
     const bool norms_beside = d + d_eff + ng + 1 <= 512;
     float acc = 0.0f;
     if (act && t < d) {                                  // value rotation, row t
-      acc = dot_rows_t(a.rot_v_t, d, d, t, xv[hp]);
+      acc = STAGE_V ? dot_rows_lds(rv, d + 1, d, t, xv[hp]) : dot_rows_t(a.rot_v_t, d, d, t, xv[hp]);
     } else if (t >= d && t < d + d_eff) {                // key position p, row p - first of its group
       const int p = t - d, g = L.group[p], m = L.g_m[g], first = L.g_first[g];
       acc = dot_rows_t(a.rot_bank_t + bank_offset(m), m, mmax, p - first, xk[hp] + first);
@@ -500,11 +550,11 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
     __syncthreads();
     if (act && t < d) {
       const float nv = nrm[hp][kMaxGroups];
-      cd[hp][DM + t] = uint8_t(nv != 0.0f ? code_of(c_thr[bv - 1], bv, (acc / nv) * sqrtf(float(d))) : 0);
+      cd[hp][DM + t] = uint8_t(nv != 0.0f ? code_of(thr + (bv - 1) * 255, bv, (acc / nv) * sqrtf(float(d))) : 0);
     } else if (t >= d && t < d + d_eff) {
       const int p = t - d, g = L.group[p], w = L.g_width[g], m = L.g_m[g];
       const float nv = nrm[hp][g];
-      cd[hp][p] = uint8_t(nv != 0.0f ? code_of(c_thr[w - 1], w, (acc / nv) * sqrtf(float(m))) : 0);
+      cd[hp][p] = uint8_t(nv != 0.0f ? code_of(thr + (w - 1) * 255, w, (acc / nv) * sqrtf(float(m))) : 0);
     }
     __syncthreads();
     if (act) {
@@ -1396,10 +1446,22 @@ hipError_t launch_allocate(const double* energy, int n_heads, int n_blocks, int 
 
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s) {
   if (a.n_new == 1) {   // decode step: one token per sequence, length advanced in the same kernel
-    if (dt == BGTQ_BF16)
-      hipLaunchKernelGGL(k_append_one<uint16_t>, dim3(n_seqs), dim3(1024), 0, s, a);
-    else
-      hipLaunchKernelGGL(k_append_one<float>, dim3(n_seqs), dim3(1024), 0, s, a);
+    const bool stage_v = a.d <= 128;
+    const size_t lds = append_one_lds_bytes(a.d, stage_v);
+    const void* fn = dt == BGTQ_BF16
+        ? (stage_v ? reinterpret_cast<const void*>(&k_append_one<uint16_t, true>)
+                   : reinterpret_cast<const void*>(&k_append_one<uint16_t, false>))
+        : (stage_v ? reinterpret_cast<const void*>(&k_append_one<float, true>)
+                   : reinterpret_cast<const void*>(&k_append_one<float, false>));
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    if (dt == BGTQ_BF16) {
+      if (stage_v) hipLaunchKernelGGL((k_append_one<uint16_t, true>), dim3(n_seqs), dim3(1024), lds, s, a);
+      else hipLaunchKernelGGL((k_append_one<uint16_t, false>), dim3(n_seqs), dim3(1024), lds, s, a);
+    } else {
+      if (stage_v) hipLaunchKernelGGL((k_append_one<float, true>), dim3(n_seqs), dim3(1024), lds, s, a);
+      else hipLaunchKernelGGL((k_append_one<float, false>), dim3(n_seqs), dim3(1024), lds, s, a);
+    }
     return hipGetLastError();
   }
   const int halves = int((a.n_new + kHalf - 1) / kHalf) + 1;
