@@ -223,8 +223,7 @@ size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
   const int splits = decode_splits(batch, n_kv_heads, capacity, true);
   const size_t part = align256(size_t(batch) * n_q_heads * splits * head_dim * 4) +
                       align256(size_t(batch) * n_q_heads * splits * 8);
-  return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + align256(decode_qmma_bytes(batch, n_kv_heads)) +
-         part;
+  return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + part;
 }
 
 bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
@@ -268,12 +267,9 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.n_split = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma);
   char* ws = static_cast<char*>(workspace);
   const size_t qrot_b = align256(decode_qrot_bytes(cache->batch, cache->n_kv_heads, d));
-  const size_t qmma_b = align256(decode_qmma_bytes(cache->batch, cache->n_kv_heads));
   a.qrot = reinterpret_cast<float*>(ws);
-  a.qmma = reinterpret_cast<uint16_t*>(ws + qrot_b);
-  a.partial = reinterpret_cast<float*>(ws + qrot_b + qmma_b);
-  a.part_ml = reinterpret_cast<float2*>(ws + qrot_b + qmma_b +
-                                        align256(size_t(cache->batch) * n_q_heads * a.n_split * d * 4));
+  a.partial = reinterpret_cast<float*>(ws + qrot_b);
+  a.part_ml = reinterpret_cast<float2*>(ws + qrot_b + align256(size_t(cache->batch) * n_q_heads * a.n_split * d * 4));
   a.rope_theta = rope_theta;
   for (int j = 0; j < d / 2; ++j) a.inv_freq[j] = rope_theta > 0.0 ? std::pow(rope_theta, -2.0 * j / d) : 0.0;
   a.scale = softmax_scale;

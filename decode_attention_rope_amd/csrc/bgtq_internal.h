@@ -78,7 +78,6 @@ inline size_t rot_bank_offset(int m) {  // floats before the m x m matrix (m eve
 }
 int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma);
 size_t decode_qrot_bytes(int batch, int n_kv_heads, int d);
-size_t decode_qmma_bytes(int batch, int n_kv_heads);
 
 // ---------------------------------------------------------------- launchers (kernels.hip)
 hipError_t upload_tables(const Tables& t);
@@ -130,7 +129,6 @@ struct DecodeArgs {
   float* out;
   float* logits;
   float* qrot;        // [batch][n_kv][d][kQPad] fp32 (vector-ALU kernel)
-  uint16_t* qmma;     // [batch][n_kv][kMaxKSteps][2][64][8] fp16 hi/lo matrix-core B operands
   float* partial;     // [batch][n_q][n_split][d] split accumulators
   float2* part_ml;    // [batch][n_q][n_split] split (running max, row sum)
   double rope_theta;

@@ -601,23 +601,18 @@ __global__ void k_advance(int32_t* __restrict__ lengths, int seq_begin, int n_se
 // q''_i C[code_i] with q'' = R_m q'_G / sqrt(m): the query is rotated once per head into
 // every group's frame and the keys are never un-rotated.
 
-// Prologue: q' = RoPE(q, pos) for the G query heads of one (sequence, KV head) with fp64
-// angles, then q'' for storage positions p of the head's layout,
+// Query prologue of the vector-ALU kernel: q' = RoPE(q, pos) for the G query heads of one
+// (sequence, KV head) with fp64 angles, then q'' for storage positions p of the head's layout,
 //   q''[h][p] = (softmax_scale * log2(e) / sqrt(m)) * sum_k R_m[p - first][k] q'[h][perm[first + k]],
 // m and first those of p's width group, so that logits come out in base-2 units.  Workgroup
-// z of the (sequence, KV head) writes the matrix-core B operands of k-steps z, z + kPrepZ, ..:
-// lane 16 j + c of k-step s holds k indices 32 s + 8 j + e, column c < 8 is head c for the
-// k-step's first width group, column c + 8 head c for its second, as an fp16 high part and
-// an fp16 remainder.  For the vector-ALU kernel it writes fp32 q'' [position][kQPad] of
-// positions z, z + kPrepZ, ...
+// z of the (sequence, KV head) writes fp32 q'' [position][kQPad] of positions z, z + kPrepZ, ..
+// (the matrix-core kernel computes the same quantity in its own prologue).
 constexpr int kPrepZ = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void k_decode_prep(DecodeArgs a) {
   __shared__ HeadLayout L;
   __shared__ float qs[BGTQ_MAX_GROUP * BGTQ_MAX_HEAD_DIM];          // q' by coordinate
   __shared__ float qp[BGTQ_MAX_GROUP * (BGTQ_MAX_HEAD_DIM + 1)];    // q' by storage position
-  __shared__ float qv[32 * BGTQ_MAX_GROUP];                         // q'' of one k-step [t][h]
-  __shared__ int16_t pos_of_k[32 * kMaxKSteps];
   const int hk = blockIdx.x, s = blockIdx.y, z = blockIdx.z, tid = threadIdx.x;
   const int G = a.group, d = a.d, n = d / 2, QS = d + 1;
   {
@@ -636,14 +631,12 @@ __global__ __launch_bounds__(256) void k_decode_prep(DecodeArgs a) {
     qs[h * d + ca] = float(x0 * cv - x1 * sv);
     qs[h * d + cb] = float(x0 * sv + x1 * cv);
   }
-  for (int k = tid; k < 32 * kMaxKSteps; k += 256) pos_of_k[k] = -1;
   __syncthreads();
-  const int d_eff = L.d_eff, nks = L.n_ksteps;
+  const int d_eff = L.d_eff;
   for (int idx = tid; idx < G * d_eff; idx += 256) {
     const int h = idx / d_eff, p = idx - h * d_eff;
     qp[h * QS + p] = qs[h * d + L.perm[p]];
   }
-  for (int p = tid; p < d_eff; p += 256) pos_of_k[L.kpos[p]] = int16_t(p);
   __syncthreads();
   const float kscale = a.scale * kLog2e;
   // q'' of position p and head h: the group's rotation row times q' (fp32 fused multiply-adds)
@@ -660,39 +653,12 @@ __global__ __launch_bounds__(256) void k_decode_prep(DecodeArgs a) {
     }
     return acc * (kscale / sqrtf(float(m)));
   };
-  if (!a.use_mfma) {   // vector-ALU kernel: fp32 [position][kQPad], zero past d_eff and G
+  {   // fp32 [position][kQPad], zero past d_eff and G
     float* dst = a.qrot + (int64_t(s) * a.n_kv + hk) * d * kQPad;
     for (int idx = tid; idx < ((d - z + kPrepZ - 1) / kPrepZ) * kQPad; idx += 256) {
       const int p = z + kPrepZ * (idx / kQPad), h = idx % kQPad;
       dst[p * kQPad + h] = (p < d_eff && h < G) ? qpp(p, h) : 0.0f;
     }
-    return;
-  }
-  uint4* qm = reinterpret_cast<uint4*>(a.qmma + (int64_t(s) * a.n_kv + hk) * kMaxKSteps * 2 * 64 * 8);
-  for (int ks = z; ks < nks; ks += kPrepZ) {
-    {  // q'' of the k-step's positions, thread (t, h)
-      const int t = tid >> 3, h = tid & 7;
-      const int p = pos_of_k[32 * ks + t];
-      qv[tid] = (p >= 0 && h < G) ? qpp(p, h) : 0.0f;
-    }
-    __syncthreads();
-    if (tid < 128) {
-      const int part = tid >> 6, lane = tid & 63;
-      const int c = lane & 15, jj = lane >> 4, head = c & 7;
-      const uint32_t half = (L.seg[4 * ks + jj] >> 28) & 1u;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-      if (int(half) == (c >> 3) && head < G) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = qv[8 * (8 * jj + e) + head];
-          const uint16_t hi = f32_to_f16_bits(v);
-          const uint16_t bits = part == 0 ? hi : f32_to_f16_bits(v - f16_bits_to_f32(hi));
-          w[e >> 1] |= uint32_t(bits) << (16 * (e & 1));
-        }
-      }
-      qm[(ks * 2 + part) * 64 + lane] = uint4{w[0], w[1], w[2], w[3]};
-    }
-    __syncthreads();
   }
 }
 
@@ -927,8 +893,16 @@ constexpr int kTcNorm = kTcDesc + 16 * 4 * kMaxKSteps;                // uint32 
 constexpr int kTcP = (kTcNorm + 4 * kMaxKSteps + 15) & ~15;           // [2][64][16 B]
 constexpr int kTcMx = kTcP + 2048;                                    // float [8][16] maxima, [4][8] sums
 constexpr int kTcRing = (kTcMx + 4 * (128 + 32) + 255) & ~255;
+// The query prologue's copy of the layout descriptor and q' [coordinate][8 heads] alias the
+// ring (first written inside the tile loop); the rotated-query B operands
+// [k-step][hi, lo][64 lanes][16 B] follow the ring.
+__host__ __device__ constexpr int tc_ksteps(int D) { return D / 32 + 10; }
+__host__ __device__ inline int tc_qb_off(int D, int chunks, int bv) {
+  const int ring = 4 * tc_stage(D, chunks, bv).bytes, pro = BGTQ_LAYOUT_BYTES + 32 * D;
+  return (kTcRing + (ring > pro ? ring : pro) + 255) & ~255;
+}
 __host__ __device__ inline int tc_lds_bytes(int D, int chunks, int bv) {
-  return kTcRing + 4 * tc_stage(D, chunks, bv).bytes;
+  return tc_qb_off(D, chunks, bv) + 2048 * tc_ksteps(D);
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
@@ -974,7 +948,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // Byte offset, in the per-wave K staging [chunk][16 slots][16 B], of record dword wd.
 __device__ __forceinline__ uint32_t kdw_off(uint32_t wd) { return (wd >> 2) * 256u + (wd & 3u) * 4u; }
 
-template <int D, bool NARROW>
+template <int D, bool NARROW, typename QT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_decode_mfma(DecodeArgs a) {
   constexpr int CPW = D / 4;                          // value coordinates per wave
   constexpr int MTV = CPW / 16;                       // value M-tiles per wave
@@ -994,37 +968,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const TcStage geo = tc_stage(D, chunks, bv);
   const HeadLayout* L = a.layouts + int64_t(s) * a.n_kv + hk;
   const int ng = L->n_groups, nks = L->n_ksteps;
-
-  // ---- workgroup set-up: level tables, k-step descriptors, zero P columns 8-15
-  {
-    uint32_t* ptab = reinterpret_cast<uint32_t*>(lds);
-    for (int i = tid; i < kPairWords; i += 256) ptab[i] = c_pair[i];
-    uint16_t* stab = reinterpret_cast<uint16_t*>(lds + 4 * kPairWords);
-    for (int i = tid; i < kSingleHalves; i += 256) stab[i] = c_single[i];
-    // per segment: x = byte offset of the window's first record dword, y = control of the
-    // 4-bit-or-narrower decode (shift | 2w << 8 | table << 16; wider segments get a harmless
-    // width-1 control), z = control of the general decode (shift | w << 8 | table << 16).
-    // Segments past the last k-step, up to the register-resident ones, decode bit 0 at width 1.
-    uint4* kd = reinterpret_cast<uint4*>(lds + kTcDesc);
-    const int nseg = 4 * (nks > kQRegSteps ? nks : kQRegSteps);
-    for (int i = tid; i < nseg; i += 256) {
-      const uint32_t seg = i < 4 * nks ? L->seg[i] : (1u << 16);
-      const uint32_t o = seg & 0xffffu, w = (seg >> 16) & 15u;
-      const uint32_t tb = w <= 5 ? 4u * uint32_t(pair_base(int(w))) : 4u * kPairWords + 2u * uint32_t(single_base(int(w)));
-      const uint32_t fast = w <= 4 ? ((o & 31u) | ((2u * w) << 8) | (tb << 16)) : (2u << 8);
-      kd[i] = uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tb << 16), 0u};
-    }
-    uint32_t* kn = reinterpret_cast<uint32_t*>(lds + kTcNorm);
-    for (int i = tid; i < kMaxKSteps; i += 256) {
-      const uint32_t kg = i < nks ? L->kgroups[i] : 0u;
-      kn[i] = (32u * (kg & 0xffu)) | ((32u * ((kg >> 8) & 0xffu)) << 16);
-    }
-    uint32_t* pw = reinterpret_cast<uint32_t*>(lds + kTcP);
-    for (int i = tid; i < 512; i += 256) {
-      const int ln = (i >> 2) & 63;      // lane of the 16-byte B operand
-      if ((ln & 15) >= 8) pw[i] = 0u;
-    }
-  }
 
   // ---- staging of one tile's share of this wave, through registers: K records of the wave's
   // 16 tokens record-major ([token][chunk][16 B], unit u = token * chunks + chunk), group and
@@ -1078,18 +1021,180 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
     for (int i = 0; i < MAXNV; ++i) *reinterpret_cast<uint4*>(buf + geo.v_off + vdst[i]) = pv[i];
   };
-  if (count > 0) load_tile(0);
+  // ---- workgroup set-up and query prologue.  The rotated query of this (sequence, KV head) is
+  // computed here: q' = RoPE(q, pos) (angle formed and reduced modulo 2 pi in fp64),
+  // q''[h][p] = (softmax_scale * log2(e) / sqrt(m)) * sum_k R_m[p - first][k] q'[h][perm[first + k]]
+  // (m and first of storage position p's width group), split into an fp16 high part and an
+  // fp16 remainder and scattered into the B operand layout: lane 16 j + c of k-step s holds
+  // k indices 32 s + 8 j + e, column c < 8 is head c for the k-step's first width group,
+  // c + 8 head c for its second; every other entry (other column half, heads >= G, unused k
+  // indices) is 0.  Global reads come in two rounds: everything that does not depend on the
+  // layout descriptor (descriptor, level tables, query, first tile), then the rotation rows.
+  constexpr int NP = D / 2;
+  constexpr int QI = 8 * NP / 256 > 0 ? 8 * NP / 256 : 1;   // (head, pair) items per thread
+  constexpr int RR = D / 4 < 32 ? D / 4 : 32;     // rotation-row float2 per batch (half a row of m <= 128)
+  constexpr int PW = (kPairWords + 255) / 256, SW = (kSingleHalves + 255) / 256;
+  static_assert(BGTQ_LAYOUT_BYTES == 256 * 16, "one 16-byte piece of the layout per thread");
+  static_assert(256 % NP == 0 || NP % 256 == 0, "pair index of a thread's items");
+  const int G = a.group;
+  uint8_t* const pro = lds + kTcRing;             // aliases the ring, first written in the loop
+  HeadLayout* const Ls = reinterpret_cast<HeadLayout*>(pro);
+  float* const qc = reinterpret_cast<float*>(pro + BGTQ_LAYOUT_BYTES);           // q' [coordinate][8 heads]
+  uint4* const qb = reinterpret_cast<uint4*>(lds + tc_qb_off(D, chunks, bv));    // [k-step][hi, lo][lane]
+  {
+    const uint4 lw = reinterpret_cast<const uint4*>(L)[tid];
+    uint32_t pt[PW];
+    uint16_t st[SW];
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      if (tid + 256 * i < kPairWords) pt[i] = c_pair[tid + 256 * i];
+#pragma unroll
+    for (int i = 0; i < SW; ++i)
+      if (tid + 256 * i < kSingleHalves) st[i] = c_single[tid + 256 * i];
+    // items (head h, pair jx): idx = tid + 256 it, jx = idx % NP, h = idx / NP
+    const QT* qg = static_cast<const QT*>(a.q) + (int64_t(s) * a.n_q + int64_t(hk) * G) * D;
+    float x0[QI], x1[QI];
+#pragma unroll
+    for (int it = 0; it < QI; ++it) {
+      const int idx = tid + 256 * it, jx = idx % NP, h = idx / NP;
+      x0[it] = 0.0f;
+      x1[it] = 0.0f;
+      if (h < G) {
+        x0[it] = load_f(qg + h * D, a.pairing ? 2 * jx : jx);
+        x1[it] = load_f(qg + h * D, a.pairing ? 2 * jx + 1 : jx + NP);
+      }
+    }
+    const double fr = a.rope_theta > 0.0 ? a.inv_freq[tid % NP] : 0.0;
+    if (count > 0) load_tile(0);
+    reinterpret_cast<uint4*>(Ls)[tid] = lw;
+    uint32_t* ptab = reinterpret_cast<uint32_t*>(lds);
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      if (tid + 256 * i < kPairWords) ptab[tid + 256 * i] = pt[i];
+    uint16_t* stab = reinterpret_cast<uint16_t*>(lds + 4 * kPairWords);
+#pragma unroll
+    for (int i = 0; i < SW; ++i)
+      if (tid + 256 * i < kSingleHalves) stab[tid + 256 * i] = st[i];
+    uint32_t* pw = reinterpret_cast<uint32_t*>(lds + kTcP);
+    for (int i = tid; i < 512; i += 256) {
+      const int ln = (i >> 2) & 63;      // lane of the 16-byte B operand
+      if ((ln & 15) >= 8) pw[i] = 0u;
+    }
+    for (int i = tid; i < 2 * 64 * nks; i += 256) qb[i] = uint4{0u, 0u, 0u, 0u};
+    const int64_t pos = a.q_pos ? a.q_pos[s] : int64_t(len) - 1;
+    float cv = 1.0f, sv = 0.0f;
+    if (a.rope_theta > 0.0) {
+      const double ang = double(pos) * fr;
+      sincosf(float(ang - kTwoPi * floor(ang * (1.0 / kTwoPi))), &sv, &cv);
+    }
+#pragma unroll
+    for (int it = 0; it < QI; ++it) {
+      const int idx = tid + 256 * it, jx = idx % NP, h = idx / NP;
+      if (h < 8) {
+        const double a0 = x0[it], a1 = x1[it];   // zero for heads >= G
+        qc[8 * (a.pairing ? 2 * jx : jx) + h] = float(a0 * cv - a1 * sv);
+        qc[8 * (a.pairing ? 2 * jx + 1 : jx + NP) + h] = float(a0 * sv + a1 * cv);
+      }
+    }
+  }
+  lds_barrier();
+  // per segment: x = byte offset of the window's first record dword, y = control of the
+  // 4-bit-or-narrower decode (shift | 2w << 8 | table << 16; wider segments get a harmless
+  // width-1 control), z = control of the general decode (shift | w << 8 | table << 16).
+  // Segments past the last k-step, up to the register-resident ones, decode bit 0 at width 1.
+  {
+    uint4* kd = reinterpret_cast<uint4*>(lds + kTcDesc);
+    const int nseg = 4 * (nks > kQRegSteps ? nks : kQRegSteps);
+    for (int i = tid; i < nseg; i += 256) {
+      const uint32_t seg = i < 4 * nks ? Ls->seg[i] : (1u << 16);
+      const uint32_t o = seg & 0xffffu, w = (seg >> 16) & 15u;
+      const uint32_t tb = w <= 5 ? 4u * uint32_t(pair_base(int(w))) : 4u * kPairWords + 2u * uint32_t(single_base(int(w)));
+      const uint32_t fast = w <= 4 ? ((o & 31u) | ((2u * w) << 8) | (tb << 16)) : (2u << 8);
+      kd[i] = uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tb << 16), 0u};
+    }
+    uint32_t* kn = reinterpret_cast<uint32_t*>(lds + kTcNorm);
+    for (int i = tid; i < kMaxKSteps; i += 256) {
+      const uint32_t kg = i < nks ? Ls->kgroups[i] : 0u;
+      kn[i] = (32u * (kg & 0xffu)) | ((32u * ((kg >> 8) & 0xffu)) << 16);
+    }
+  }
+  // q'' of storage position p = p0 + tid / 2 (every 128 positions): the thread pair splits
+  // the rotation row in two halves and covers all 8 heads, then each thread scatters 4 heads
+  {
+    const int d_eff = Ls->d_eff, kh = tid & 1;
+    const float kscale = a.scale * kLog2e;
+    uint16_t* q16 = reinterpret_cast<uint16_t*>(qb);
+    float2 rr[RR];
+    for (int p0 = 0; p0 < d_eff; p0 += 128) {
+      const int p = p0 + (tid >> 1);
+      int m = 2, first = 0;
+      const float2* R2 = nullptr;
+      if (p < d_eff) {
+        const int g = Ls->group[p];
+        m = Ls->g_m[g];
+        first = Ls->g_first[g];
+        R2 = reinterpret_cast<const float2*>(a.rot_bank + bank_offset(m) + size_t(p - first) * m) + kh * (m / 4);
+      }
+      const int nh = p < d_eff ? (kh == 0 ? m / 4 : m / 2 - m / 4) : 0;   // float2 of this half
+      const uint8_t* pm = Ls->perm + first + 2 * kh * (m / 4);           // its coordinates
+      float acc[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
+      for (int b0 = 0; b0 < nh; b0 += RR) {         // one batch unless m > 4 RR
+#pragma unroll
+        for (int i = 0; i < RR; ++i)
+          if (b0 + i < nh) rr[i] = R2[b0 + i];
+#pragma unroll
+        for (int i = 0; i < RR; ++i) {
+          if (b0 + i < nh) {
+            const float4* xa = reinterpret_cast<const float4*>(qc + 8 * pm[2 * (b0 + i)]);
+            const float4* xb = reinterpret_cast<const float4*>(qc + 8 * pm[2 * (b0 + i) + 1]);
+            const float4 a0 = xa[0], a1 = xa[1], c0 = xb[0], c1 = xb[1];
+            const float r0 = rr[i].x, r1 = rr[i].y;
+            acc[0] = fmaf(r0, a0.x, acc[0]); acc[1] = fmaf(r0, a0.y, acc[1]);
+            acc[2] = fmaf(r0, a0.z, acc[2]); acc[3] = fmaf(r0, a0.w, acc[3]);
+            acc[4] = fmaf(r0, a1.x, acc[4]); acc[5] = fmaf(r0, a1.y, acc[5]);
+            acc[6] = fmaf(r0, a1.z, acc[6]); acc[7] = fmaf(r0, a1.w, acc[7]);
+            acc[0] = fmaf(r1, c0.x, acc[0]); acc[1] = fmaf(r1, c0.y, acc[1]);
+            acc[2] = fmaf(r1, c0.z, acc[2]); acc[3] = fmaf(r1, c0.w, acc[3]);
+            acc[4] = fmaf(r1, c1.x, acc[4]); acc[5] = fmaf(r1, c1.y, acc[5]);
+            acc[6] = fmaf(r1, c1.z, acc[6]); acc[7] = fmaf(r1, c1.w, acc[7]);
+          }
+        }
+      }
+      // the pair's two halves, lower coordinates first; this thread keeps heads 4 kh .. 4 kh + 3
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float mine = acc[4 * kh + e], give = acc[4 * (1 - kh) + e];
+        const float other = __shfl_xor(give, 1);
+        v[e] = (kh == 0 ? mine + other : other + mine) * (kscale / sqrtf(float(m)));
+      }
+      if (p < d_eff) {
+        const int kx = Ls->kpos[p], ks = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7;
+        const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks + jj] >> 28) & 1u);
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          const int h = 4 * kh + hh;
+          if (h < G) {
+            const uint16_t hi = f32_to_f16_bits(v[hh]);
+            q16[((ks * 2 + 0) * 64 + lb + h) * 8 + e] = hi;
+            q16[((ks * 2 + 1) * 64 + lb + h) * 8 + e] = f32_to_f16_bits(v[hh] - f16_bits_to_f32(hi));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();   // also orders the prologue's reads of the ring before the first staging store
 
-  // ---- rotated query operands of the first k-steps in registers (zero past the last one)
-  const uint4* qm = reinterpret_cast<const uint4*>(a.qmma + reg * kMaxKSteps * 2 * 64 * 8);
+  // ---- query operands of the first k-steps in registers (zero past the last one)
   f16x8 qh[kQRegSteps], ql[kQRegSteps];
 #pragma unroll
   for (int ks = 0; ks < kQRegSteps; ++ks) {
     const uint4 z = uint4{0u, 0u, 0u, 0u};
-    qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qm[(ks * 2 + 0) * 64 + lane] : z);
-    ql[ks] = __builtin_bit_cast(f16x8, ks < nks ? qm[(ks * 2 + 1) * 64 + lane] : z);
+    qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qb[(ks * 2 + 0) * 64 + lane] : z);
+    ql[ks] = __builtin_bit_cast(f16x8, ks < nks ? qb[(ks * 2 + 1) * 64 + lane] : z);
   }
-  __syncthreads();
 
   const uint4* kd = reinterpret_cast<const uint4*>(lds + kTcDesc);
   const uint32_t* knsel = reinterpret_cast<const uint32_t*>(lds + kTcNorm);
@@ -1186,8 +1291,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
       const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
       mfma_kstep(decode8(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16),
-                 __builtin_bit_cast(f16x8, qm[(ks * 2 + 0) * 64 + lane]),
-                 __builtin_bit_cast(f16x8, qm[(ks * 2 + 1) * 64 + lane]), nv);
+                 __builtin_bit_cast(f16x8, qb[(ks * 2 + 0) * 64 + lane]),
+                 __builtin_bit_cast(f16x8, qb[(ks * 2 + 1) * 64 + lane]), nv);
     }
 
     // ---- online softmax (base 2); head c = column c + column c + 8 (rotate the 16-lane row
@@ -1368,25 +1473,23 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st) {
-  if (q_dt == BGTQ_BF16)
-    hipLaunchKernelGGL(k_decode_prep<uint16_t>, dim3(a.n_kv, a.batch, kPrepZ), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_decode_prep<float>, dim3(a.n_kv, a.batch, kPrepZ), dim3(256), 0, st, a);
   const dim3 grid(a.n_split, a.n_kv, a.batch);
   if (a.use_mfma) {
     const int lds = tc_lds_bytes(D, a.chunks, a.v_bits);
-    const bool narrow = a.chunks <= 4 && a.v_bits <= 4;
-    const void* fn = narrow ? reinterpret_cast<const void*>(&k_decode_mfma<D, true>)
-                            : reinterpret_cast<const void*>(&k_decode_mfma<D, false>);
+    const bool narrow = a.chunks <= 4 && a.v_bits <= 4, bf16 = q_dt == BGTQ_BF16;
+    void (*fn)(DecodeArgs) = narrow ? (bf16 ? k_decode_mfma<D, true, uint16_t> : k_decode_mfma<D, true, float>)
+                                    : (bf16 ? k_decode_mfma<D, false, uint16_t> : k_decode_mfma<D, false, float>);
     if (lds > 64 * 1024) {
-      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
     }
-    if (narrow)
-      hipLaunchKernelGGL((k_decode_mfma<D, true>), grid, dim3(256), size_t(lds), st, a);
-    else
-      hipLaunchKernelGGL((k_decode_mfma<D, false>), grid, dim3(256), size_t(lds), st, a);
+    hipLaunchKernelGGL(fn, grid, dim3(256), size_t(lds), st, a);
   } else {
+    if (q_dt == BGTQ_BF16)
+      hipLaunchKernelGGL(k_decode_prep<uint16_t>, dim3(a.n_kv, a.batch, kPrepZ), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_decode_prep<float>, dim3(a.n_kv, a.batch, kPrepZ), dim3(256), 0, st, a);
     const int maxg = a.group <= 1 ? 1 : a.group <= 2 ? 2 : a.group <= 4 ? 4 : a.group <= 8 ? 8 : 16;
     const int RS = 4 * a.chunks + 1, VS = 2 * a.v_bits + 1;
     const int kbuf_words = 64 * RS > D * VS ? 64 * RS : D * VS;
@@ -1521,10 +1624,6 @@ int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma) {
 
 size_t decode_qrot_bytes(int batch, int n_kv_heads, int d) {
   return size_t(batch) * n_kv_heads * d * kQPad * 4;
-}
-
-size_t decode_qmma_bytes(int batch, int n_kv_heads) {
-  return size_t(batch) * n_kv_heads * kMaxKSteps * 2 * 64 * 8 * 2;
 }
 
 }  // namespace bgtq

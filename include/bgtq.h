@@ -188,7 +188,8 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
 /* Decode attention straight from the packed cache (abstract: RoPE query-key
  * logits; the serving path attends over a packed K3V3 cache at 128K context).
  * For every sequence s and query head h (KV head h / (n_q_heads/n_kv_heads)):
- * q' = RoPE(q[s][h], pos) with angles pos*rope_theta^(-2j/d) formed in fp64;
+ * q' = RoPE(q[s][h], pos) with angles pos*rope_theta^(-2j/d) formed and reduced
+ * modulo 2*pi in fp64;
  * logits l_t = softmax_scale * q' . k_hat_t over the cached slots t <
  * lengths[s]; out = sum_t softmax(l)_t * v_hat_t, with k_hat, v_hat the TQ-MSE
  * reconstructions (width-0 blocks are zero).  The packed codes are decoded in
