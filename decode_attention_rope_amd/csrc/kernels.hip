@@ -10,6 +10,8 @@
 
 #include "bgtq_internal.h"
 
+#include <type_traits>
+
 namespace bgtq {
 namespace {
 
@@ -1098,6 +1100,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
   }
   lds_barrier();
+  // This kernel takes the layout's k-steps in a different order: the narrow ones (every
+  // segment at most 4 bits wide) first, in layout order, then the wide ones.  wmask marks
+  // the layout's wide k-steps; kperm maps a layout k-step to its place here.
+  uint32_t wmask;
+  {
+    bool wd = false;
+    if (lane < nks) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) wd = wd || ((Ls->seg[4 * lane + sl] >> 16) & 15u) > 4u;
+    }
+    wmask = uint32_t(__ballot(wd));
+  }
+  const int nn = nks - __popc(wmask);               // narrow k-steps
+  auto kperm = [&](int ks) {
+    const int below = __popc(wmask & ((1u << ks) - 1u));
+    return ((wmask >> ks) & 1u) ? nn + below : ks - below;
+  };
   // per segment: x = byte offset of the window's first record dword, y = control of the
   // 4-bit-or-narrower decode (shift | 2w << 8 | table << 16; wider segments get a harmless
   // width-1 control), z = control of the general decode (shift | w << 8 | table << 16).
@@ -1110,12 +1129,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       const uint32_t o = seg & 0xffffu, w = (seg >> 16) & 15u;
       const uint32_t tb = w <= 5 ? 4u * uint32_t(pair_base(int(w))) : 4u * kPairWords + 2u * uint32_t(single_base(int(w)));
       const uint32_t fast = w <= 4 ? ((o & 31u) | ((2u * w) << 8) | (tb << 16)) : (2u << 8);
-      kd[i] = uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tb << 16), 0u};
+      kd[i < 4 * nks ? 4 * kperm(i >> 2) + (i & 3) : i] = uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tb << 16), 0u};
     }
     uint32_t* kn = reinterpret_cast<uint32_t*>(lds + kTcNorm);
     for (int i = tid; i < kMaxKSteps; i += 256) {
       const uint32_t kg = i < nks ? Ls->kgroups[i] : 0u;
-      kn[i] = (32u * (kg & 0xffu)) | ((32u * ((kg >> 8) & 0xffu)) << 16);
+      kn[i < nks ? kperm(i) : i] = (32u * (kg & 0xffu)) | ((32u * ((kg >> 8) & 0xffu)) << 16);
     }
   }
   // q'' of storage position p = p0 + tid / 2 (every 128 positions): the thread pair splits
@@ -1171,8 +1190,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         v[e] = (kh == 0 ? mine + other : other + mine) * (kscale / sqrtf(float(m)));
       }
       if (p < d_eff) {
-        const int kx = Ls->kpos[p], ks = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7;
-        const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks + jj] >> 28) & 1u);
+        const int kx = Ls->kpos[p], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm(ks0);
+        const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks0 + jj] >> 28) & 1u);
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
           const int h = 4 * kh + hh;
@@ -1201,12 +1220,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int nsh = n < 8 ? 0 : 16;
   const uint32_t krec = uint32_t(16 * chunks * n);
   const uint32_t knb = uint32_t(geo.n_off + 8 * j);
-  uint32_t wide = 0u;   // k-steps with a segment wider than 4 bits
-  for (int ks = 0; ks < nks; ++ks) {
-    const uint32_t wmax = max(max((kd[4 * ks].z >> 8) & 15u, (kd[4 * ks + 1].z >> 8) & 15u),
-                              max((kd[4 * ks + 2].z >> 8) & 15u, (kd[4 * ks + 3].z >> 8) & 15u));
-    if (wmax > 4u) wide |= 1u << ks;
-  }
+  const uint32_t wide = ((1u << nks) - 1u) & ~((1u << nn) - 1u);   // k-steps nn .. nks - 1
   // value windows: coordinate row 16 mi + n of the wave's block, tokens 32 st + 8 j ..
   const uint32_t vrow = uint32_t(geo.v_off + n * 8 * bv);
   const uint32_t vw0 = uint32_t(4 * ((8 * j * bv) >> 5)), vsh0 = uint32_t((8 * j * bv) & 31);
@@ -1242,10 +1256,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[r] = fmaf(T[r], float(nv[r]), S[r]);
     };
-    constexpr int KC = 4;
-#pragma unroll
-    for (int kc = 0; kc < kQRegSteps; kc += KC) {
-      if (kc < nks) {
+    // narrow k-steps in chunks of 4, 2 and 2 (a chunk past the last narrow k-step is skipped;
+    // inside the last one, slots past it are decoded but not multiplied)
+    auto narrow_chunk = [&](auto kc_c, auto kn_c) {
+      constexpr int kc = decltype(kc_c)::value, KC = decltype(kn_c)::value;
+      {
         u32x4 raw[KC];
         f16x4 nrm[KC];
         uint32_t wd0[KC], wd1[KC], ctl[KC];
@@ -1269,9 +1284,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         }
 #pragma unroll
         for (int q = 0; q < KC; ++q)
-          if (kc + q < nks && !(wide & (1u << (kc + q)))) mfma_kstep(raw[q], qh[kc + q], ql[kc + q], nrm[q]);
+          if (kc + q < nn) mfma_kstep(raw[q], qh[kc + q], ql[kc + q], nrm[q]);
       }
-    }
+    };
+    static_assert(kQRegSteps == 8, "chunks 4 + 2 + 2");
+    if (0 < nn) narrow_chunk(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+    if (4 < nn) narrow_chunk(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
+    if (6 < nn) narrow_chunk(std::integral_constant<int, 6>{}, std::integral_constant<int, 2>{});
     // wide k-steps (codes of 5..8 bits in some segment): general decode
 #pragma unroll
     for (int ks = 0; ks < kQRegSteps; ++ks) {
