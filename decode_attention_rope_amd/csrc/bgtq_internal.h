@@ -55,13 +55,13 @@ static_assert(sizeof(HeadLayout) == BGTQ_LAYOUT_BYTES, "layout descriptor size")
 
 // Frozen quantizer tables (fp32 as the kernels read them; fp64 distortions).
 constexpr int kPairWords = 1364;    // fp16 pair tables of widths 1..5: sum over w of 4^w entries
-constexpr int kSingleHalves = 448;  // fp16 level tables of widths 6..8
+constexpr int kSingleHalves = 510;  // fp16 level tables of widths 1..8 (width w at 2^w - 2)
 
 struct Tables {
   float thr[kMaxBits][255];   // thr[b-1][k], k < 2^b - 1, ascending
   float cen[kMaxBits][256];   // cen[b-1][k], k < 2^b, ascending
   // decoder tables: fp16 (nearest-even) of cen.  pair[(4^w - 4)/3 + (c0 | c1 << w)] holds the
-  // levels of codes c0 (low half) and c1 (high half) of width w <= 5; single[] widths 6..8.
+  // levels of codes c0 (low half) and c1 (high half) of width w <= 5; single[] widths 1..8.
   uint32_t pair[kPairWords];
   uint16_t single[kSingleHalves];
   double dgain[kMaxBits];     // dist[b] - dist[b+1], b = 0..7

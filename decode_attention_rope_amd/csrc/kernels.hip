@@ -873,7 +873,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kQRegSteps = 8;        // k-steps whose query operands stay in registers
 
 __device__ __forceinline__ int pair_base(int w) { return ((1 << (2 * w)) - 4) / 3; }
-__device__ __forceinline__ int single_base(int w) { return w == 6 ? 0 : (w == 7 ? 64 : 192); }
+__device__ __forceinline__ int single_base(int w) { return (1 << w) - 2; }
 
 // Per-wave staging of one tile (bytes): K records of the wave's 16 tokens [token][chunk][16 B],
 // group norms and value norms [g][16] fp16 (value norms at g = n_groups), value segments of
@@ -889,7 +889,7 @@ __host__ __device__ inline TcStage tc_stage(int D, int chunks, int bv) {
   return g;
 }
 // Workgroup LDS (bytes): tables, k-step descriptors, P operands, softmax exchange, ring.
-constexpr int kTcTab = 4 * kPairWords + 2 * kSingleHalves;           // 6352
+constexpr int kTcTab = (4 * kPairWords + 2 * kSingleHalves + 15) & ~15;   // 6480
 constexpr int kTcDesc = kTcTab;                                       // uint4 [kMaxKSteps][4]
 constexpr int kTcNorm = kTcDesc + 16 * 4 * kMaxKSteps;                // uint32 [kMaxKSteps]
 constexpr int kTcP = (kTcNorm + 4 * kMaxKSteps + 15) & ~15;           // [2][64][16 B]
@@ -943,6 +943,26 @@ __device__ __forceinline__ u32x4 decode8(uint32_t d0, uint32_t d1, uint32_t d2, 
   return r;
 }
 
+// Eight consecutive codes of any width w (1..8) starting at bit sh of the window d2:d1:d0, as
+// fp16 levels from the width's single-level table at byte offset tb (low half = first code).
+// One instruction sequence for every width, so lanes whose segments differ in width run it
+// together instead of one width class after another.
+__device__ __forceinline__ u32x4 decode8_any(uint32_t d0, uint32_t d1, uint32_t d2, int sh, int w,
+                                             const uint8_t* lds, uint32_t tb) {
+  const uint64_t x = (uint64_t(__builtin_amdgcn_alignbit(d2, d1, sh)) << 32) | __builtin_amdgcn_alignbit(d1, d0, sh);
+  const uint32_t mask = (1u << w) - 1u;
+  u32x4 r;
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    const uint32_t c0 = uint32_t(x >> (2 * e2 * w)) & mask;
+    const uint32_t c1 = uint32_t(x >> ((2 * e2 + 1) * w)) & mask;
+    const uint32_t h0 = *reinterpret_cast<const uint16_t*>(lds + tb + 2 * c0);
+    const uint32_t h1 = *reinterpret_cast<const uint16_t*>(lds + tb + 2 * c1);
+    r[e2] = h0 | (h1 << 16);
+  }
+  return r;
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
 // outstanding global loads, so staging loads for later tiles stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -962,10 +982,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int n = lane & 15, j = lane >> 4;
   const int len = a.lengths[s];
   const int tiles = (len + kTile - 1) / kTile;
-  const int per = (tiles + a.n_split - 1) / a.n_split;
-  const int t0 = split * per;
-  const int t1 = t0 + per < tiles ? t0 + per : tiles;
-  const int count = t1 > t0 ? t1 - t0 : 0;
+  // split i takes tiles [i T / n, (i + 1) T / n): counts differ by at most one
+  const int t0 = int(int64_t(split) * tiles / a.n_split);
+  const int t1 = int(int64_t(split + 1) * tiles / a.n_split);
+  const int count = t1 - t0;
   const int bv = a.v_bits, chunks = a.chunks;
   const TcStage geo = tc_stage(D, chunks, bv);
   const HeadLayout* L = a.layouts + int64_t(s) * a.n_kv + hk;
@@ -1118,8 +1138,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     return ((wmask >> ks) & 1u) ? nn + below : ks - below;
   };
   // per segment: x = byte offset of the window's first record dword, y = control of the
-  // 4-bit-or-narrower decode (shift | 2w << 8 | table << 16; wider segments get a harmless
-  // width-1 control), z = control of the general decode (shift | w << 8 | table << 16).
+  // 4-bit-or-narrower decode (shift | 2w << 8 | pair table << 16; wider segments get a
+  // harmless width-1 control), z = control of the any-width decode (shift | w << 8 | single
+  // table << 16).
   // Segments past the last k-step, up to the register-resident ones, decode bit 0 at width 1.
   {
     uint4* kd = reinterpret_cast<uint4*>(lds + kTcDesc);
@@ -1127,9 +1148,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     for (int i = tid; i < nseg; i += 256) {
       const uint32_t seg = i < 4 * nks ? Ls->seg[i] : (1u << 16);
       const uint32_t o = seg & 0xffffu, w = (seg >> 16) & 15u;
-      const uint32_t tb = w <= 5 ? 4u * uint32_t(pair_base(int(w))) : 4u * kPairWords + 2u * uint32_t(single_base(int(w)));
-      const uint32_t fast = w <= 4 ? ((o & 31u) | ((2u * w) << 8) | (tb << 16)) : (2u << 8);
-      kd[i < 4 * nks ? 4 * kperm(i >> 2) + (i & 3) : i] = uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tb << 16), 0u};
+      const uint32_t tbp = 4u * uint32_t(pair_base(int(w)));
+      const uint32_t tbs = 4u * kPairWords + 2u * uint32_t(single_base(int(w)));
+      const uint32_t fast = w <= 4 ? ((o & 31u) | ((2u * w) << 8) | (tbp << 16)) : (2u << 8);
+      kd[i < 4 * nks ? 4 * kperm(i >> 2) + (i & 3) : i] = uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tbs << 16), 0u};
     }
     uint32_t* kn = reinterpret_cast<uint32_t*>(lds + kTcNorm);
     for (int i = tid; i < kMaxKSteps; i += 256) {
@@ -1300,7 +1322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const uint32_t ka = krec + d.x;
         const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
         const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
-        mfma_kstep(decode8(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16), qh[ks], ql[ks], nv);
+        mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16), qh[ks], ql[ks], nv);
       }
     }
     for (int ks = kQRegSteps; ks < nks; ++ks) {   // k-steps beyond the register-resident ones
@@ -1309,7 +1331,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       const uint32_t ka = krec + d.x;
       const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
       const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
-      mfma_kstep(decode8(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16),
+      mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16),
                  __builtin_bit_cast(f16x8, qb[(ks * 2 + 0) * 64 + lane]),
                  __builtin_bit_cast(f16x8, qb[(ks * 2 + 1) * 64 + lane]), nv);
     }
@@ -1632,8 +1654,11 @@ hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s) {
 int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma) {
   const int64_t tiles = capacity / kTile;
   const int64_t units = int64_t(batch) * n_kv_heads;
-  int64_t want = (1024 + units - 1) / units;         // about 1024 workgroups in flight
-  const int64_t per_split = mfma ? 6 : 8;             // tiles per split at least
+  // matrix-core kernel: three resident workgroups on each of the 256 compute units, tile
+  // ranges balanced to within one tile; vector-ALU kernel: about 1024 workgroups
+  const int64_t target = mfma ? 768 : 1024;
+  int64_t want = (target + units - 1) / units;
+  const int64_t per_split = mfma ? 4 : 8;             // tiles per split at least
   const int64_t by_work = (tiles + per_split - 1) / per_split;
   if (want > by_work) want = by_work;
   if (want < 1) want = 1;

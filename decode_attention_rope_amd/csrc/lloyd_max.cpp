@@ -140,8 +140,8 @@ Tables build_tables() {
       t.pair[base + idx] = uint32_t(h16(t.cen[w - 1][c0])) | uint32_t(h16(t.cen[w - 1][c1])) << 16;
     }
   }
-  for (int w = 6; w <= 8; ++w) {
-    const int base = w == 6 ? 0 : (w == 7 ? 64 : 192);
+  for (int w = 1; w <= 8; ++w) {
+    const int base = (1 << w) - 2;
     for (int c = 0; c < (1 << w); ++c) t.single[base + c] = h16(t.cen[w - 1][c]);
   }
   return t;
