@@ -853,18 +853,19 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 // one 64-token tile at a time:
 //   keys    wave w owns tokens 16 w .. 16 w + 15 (the 16 rows of its A operand); its lane
 //           (n, j) decodes 8 codes of token 16 w + n for k-step s from segment 4 s + j of the
-//           token's K record; B is the rotated query (columns 0-7: the G heads restricted to
-//           the k-step's first width group, columns 8-15: its second group), split into an
-//           fp16 high part and an fp16 remainder (two MFMAs); each column half's partial
-//           logit is scaled by its group's fp32 norm, and column c + column c + 8 is head c.
+//           token's K record; B is the rotated query (columns 0-7: the G heads restricted
+//           to the k-step's first width group, columns 8-15: its second group) as an fp16
+//           high part (registers) and an fp16 remainder (LDS), two MFMAs; each column
+//           half's partial logit is scaled by its group's fp32 norm, and column c + column
+//           c + 8 is head c.
 //   softmax the tile maximum per head is shared through LDS; p * n_v goes to LDS as the fp16
 //           B operand of P V (lane group j of sub-tile st holds tokens 32 st + 8 j .. + 7).
 //   values  wave w owns rotated coordinates D/4 w .. D/4 (w + 1) - 1; A rows are coordinates,
 //           each lane decodes 8 consecutive tokens of one coordinate.
-// Codes become fp16 levels through pair tables (two codes of width w <= 5 index one packed
-// half2) or single tables (widths 6..8) staged in LDS.  Every wave stages only the bytes it
-// reads (its tokens' K records and norms, its coordinates' value segments) with direct
-// global-to-LDS loads, three tiles deep, so staging needs no workgroup barrier.
+// Codes become fp16 levels through pair tables (two codes of width w <= 4 index one packed
+// half2) or, for k-steps with a wider segment, single-level tables of every width.  Every wave
+// stages only the bytes it reads (its tokens' K records and norms, its coordinates' value
+// segments); the next tile's loads go to registers while the current tile is computed.
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -895,16 +896,22 @@ constexpr int kTcNorm = kTcDesc + 16 * 4 * kMaxKSteps;                // uint32 
 constexpr int kTcP = (kTcNorm + 4 * kMaxKSteps + 15) & ~15;           // [2][64][16 B]
 constexpr int kTcMx = kTcP + 2048;                                    // float [8][16] maxima, [4][8] sums
 constexpr int kTcRing = (kTcMx + 4 * (128 + 32) + 255) & ~255;
-// The query prologue's copy of the layout descriptor and q' [coordinate][8 heads] alias the
-// ring (first written inside the tile loop); the rotated-query B operands
-// [k-step][hi, lo][64 lanes][16 B] follow the ring.
-__host__ __device__ constexpr int tc_ksteps(int D) { return D / 32 + 10; }
-__host__ __device__ inline int tc_qb_off(int D, int chunks, int bv) {
-  const int ring = 4 * tc_stage(D, chunks, bv).bytes, pro = BGTQ_LAYOUT_BYTES + 32 * D;
+// Largest k-step count of a layout: 5, 7 and 11 for head dims 64, 128 and 256 (exhaustive
+// over the segment counts that width groups of those dims can have), so only head dim 256
+// has k-steps past the register-resident ones.
+__host__ __device__ constexpr int tc_ksteps(int D) { return D / 32 + 3; }
+// The query prologue's copy of the layout descriptor, q' [coordinate][8 heads] and the high
+// parts of the register-resident k-steps' B operands [k-step][64 lanes][16 B] alias the ring
+// (first written inside the tile loop, after those operands are in registers).  After the
+// ring: the low parts of the register-resident k-steps, then both parts of later k-steps.
+__host__ __device__ constexpr int tc_qhi_off(int D) { return BGTQ_LAYOUT_BYTES + 32 * D; }   // from the ring
+__host__ __device__ inline int tc_qlo_off(int D, int chunks, int bv) {
+  const int ring = 4 * tc_stage(D, chunks, bv).bytes, pro = tc_qhi_off(D) + 1024 * kQRegSteps;
   return (kTcRing + (ring > pro ? ring : pro) + 255) & ~255;
 }
 __host__ __device__ inline int tc_lds_bytes(int D, int chunks, int bv) {
-  return tc_qb_off(D, chunks, bv) + 2048 * tc_ksteps(D);
+  const int later = tc_ksteps(D) > kQRegSteps ? tc_ksteps(D) - kQRegSteps : 0;
+  return tc_qlo_off(D, chunks, bv) + 1024 * kQRegSteps + 2048 * later;
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
@@ -971,7 +978,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 __device__ __forceinline__ uint32_t kdw_off(uint32_t wd) { return (wd >> 2) * 256u + (wd & 3u) * 4u; }
 
 template <int D, bool NARROW, typename QT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_decode_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_mfma(DecodeArgs a) {
   constexpr int CPW = D / 4;                          // value coordinates per wave
   constexpr int MTV = CPW / 16;                       // value M-tiles per wave
   constexpr int MAXNK = NARROW ? 1 : (D + 63) / 64;                  // K staging loads per lane
@@ -1054,7 +1061,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // layout descriptor (descriptor, level tables, query, first tile), then the rotation rows.
   constexpr int NP = D / 2;
   constexpr int QI = 8 * NP / 256 > 0 ? 8 * NP / 256 : 1;   // (head, pair) items per thread
-  constexpr int RR = D / 4 < 32 ? D / 4 : 32;     // rotation-row float2 per batch (half a row of m <= 128)
+  constexpr int RR = D / 4 < 16 ? D / 4 : 16;     // rotation-row float2 per batch (half a row of m <= 64)
   constexpr int PW = (kPairWords + 255) / 256, SW = (kSingleHalves + 255) / 256;
   static_assert(BGTQ_LAYOUT_BYTES == 256 * 16, "one 16-byte piece of the layout per thread");
   static_assert(256 % NP == 0 || NP % 256 == 0, "pair index of a thread's items");
@@ -1062,7 +1069,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   uint8_t* const pro = lds + kTcRing;             // aliases the ring, first written in the loop
   HeadLayout* const Ls = reinterpret_cast<HeadLayout*>(pro);
   float* const qc = reinterpret_cast<float*>(pro + BGTQ_LAYOUT_BYTES);           // q' [coordinate][8 heads]
-  uint4* const qb = reinterpret_cast<uint4*>(lds + tc_qb_off(D, chunks, bv));    // [k-step][hi, lo][lane]
+  uint4* const qhi = reinterpret_cast<uint4*>(pro + tc_qhi_off(D));                // [k-step < 8][lane]
+  uint4* const qlo = reinterpret_cast<uint4*>(lds + tc_qlo_off(D, chunks, bv));     // [k-step < 8][lane]
+  uint4* const qlate = qlo + 64 * kQRegSteps;                                       // [k-step - 8][hi, lo][lane]
   {
     const uint4 lw = reinterpret_cast<const uint4*>(L)[tid];
     uint32_t pt[PW];
@@ -1102,7 +1111,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       const int ln = (i >> 2) & 63;      // lane of the 16-byte B operand
       if ((ln & 15) >= 8) pw[i] = 0u;
     }
-    for (int i = tid; i < 2 * 64 * nks; i += 256) qb[i] = uint4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < 64 * nks; i += 256) {
+      const uint4 z = uint4{0u, 0u, 0u, 0u};
+      if (i < 64 * kQRegSteps) {
+        qhi[i] = z;
+        qlo[i] = z;
+      } else {
+        qlate[2 * (i - 64 * kQRegSteps) - (i & 63)] = z;            // [ks - 8][0][lane]
+        qlate[2 * (i - 64 * kQRegSteps) - (i & 63) + 64] = z;       // [ks - 8][1][lane]
+      }
+    }
     const int64_t pos = a.q_pos ? a.q_pos[s] : int64_t(len) - 1;
     float cv = 1.0f, sv = 0.0f;
     if (a.rope_theta > 0.0) {
@@ -1164,7 +1182,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   {
     const int d_eff = Ls->d_eff, kh = tid & 1;
     const float kscale = a.scale * kLog2e;
-    uint16_t* q16 = reinterpret_cast<uint16_t*>(qb);
     float2 rr[RR];
     for (int p0 = 0; p0 < d_eff; p0 += 128) {
       const int p = p0 + (tid >> 1);
@@ -1214,13 +1231,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       if (p < d_eff) {
         const int kx = Ls->kpos[p], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm(ks0);
         const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks0 + jj] >> 28) & 1u);
+        uint16_t* h16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qhi + 64 * ks : qlate + 128 * (ks - kQRegSteps));
+        uint16_t* l16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qlo + 64 * ks : qlate + 128 * (ks - kQRegSteps) + 64);
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
           const int h = 4 * kh + hh;
           if (h < G) {
             const uint16_t hi = f32_to_f16_bits(v[hh]);
-            q16[((ks * 2 + 0) * 64 + lb + h) * 8 + e] = hi;
-            q16[((ks * 2 + 1) * 64 + lb + h) * 8 + e] = f32_to_f16_bits(v[hh] - f16_bits_to_f32(hi));
+            h16[(lb + h) * 8 + e] = hi;
+            l16[(lb + h) * 8 + e] = f32_to_f16_bits(v[hh] - f16_bits_to_f32(hi));
           }
         }
       }
@@ -1229,12 +1248,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   __syncthreads();   // also orders the prologue's reads of the ring before the first staging store
 
   // ---- query operands of the first k-steps in registers (zero past the last one)
-  f16x8 qh[kQRegSteps], ql[kQRegSteps];
+  f16x8 qh[kQRegSteps];
 #pragma unroll
   for (int ks = 0; ks < kQRegSteps; ++ks) {
     const uint4 z = uint4{0u, 0u, 0u, 0u};
-    qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qb[(ks * 2 + 0) * 64 + lane] : z);
-    ql[ks] = __builtin_bit_cast(f16x8, ks < nks ? qb[(ks * 2 + 1) * 64 + lane] : z);
+    qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qhi[ks * 64 + lane] : z);
   }
 
   const uint4* kd = reinterpret_cast<const uint4*>(lds + kTcDesc);
@@ -1306,7 +1324,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         }
 #pragma unroll
         for (int q = 0; q < KC; ++q)
-          if (kc + q < nn) mfma_kstep(raw[q], qh[kc + q], ql[kc + q], nrm[q]);
+          if (kc + q < nn) mfma_kstep(raw[q], qh[kc + q], __builtin_bit_cast(f16x8, qlo[(kc + q) * 64 + lane]), nrm[q]);
       }
     };
     static_assert(kQRegSteps == 8, "chunks 4 + 2 + 2");
@@ -1322,7 +1340,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const uint32_t ka = krec + d.x;
         const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
         const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
-        mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16), qh[ks], ql[ks], nv);
+        mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16), qh[ks],
+                   __builtin_bit_cast(f16x8, qlo[ks * 64 + lane]), nv);
       }
     }
     for (int ks = kQRegSteps; ks < nks; ++ks) {   // k-steps beyond the register-resident ones
@@ -1332,8 +1351,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
       const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
       mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16),
-                 __builtin_bit_cast(f16x8, qb[(ks * 2 + 0) * 64 + lane]),
-                 __builtin_bit_cast(f16x8, qb[(ks * 2 + 1) * 64 + lane]), nv);
+                 __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + lane]),
+                 __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + 64 + lane]), nv);
     }
 
     // ---- online softmax (base 2); head c = column c + column c + 8 (rotate the 16-lane row
@@ -1436,7 +1455,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // accumulator loads are issued before the maximum is known, so they overlap.
 template <int D>
 __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
-  constexpr int NT = 1024, C4 = D / 4, NG = NT / C4, RS = NT / D, NB = 12;
+  constexpr int NT = 1024, C4 = D / 4, NG = NT / C4, RS = NT / D, NB = 16;
   __shared__ float red[2][NT / 64];
   __shared__ float4 part4[NT];
   __shared__ float accs[D];
@@ -1654,9 +1673,9 @@ hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s) {
 int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma) {
   const int64_t tiles = capacity / kTile;
   const int64_t units = int64_t(batch) * n_kv_heads;
-  // matrix-core kernel: three resident workgroups on each of the 256 compute units, tile
+  // matrix-core kernel: four resident workgroups on each of the 256 compute units, tile
   // ranges balanced to within one tile; vector-ALU kernel: about 1024 workgroups
-  const int64_t target = mfma ? 768 : 1024;
+  const int64_t target = 1024;
   int64_t want = (target + units - 1) / units;
   const int64_t per_split = mfma ? 4 : 8;             // tiles per split at least
   const int64_t by_work = (tiles + per_split - 1) / per_split;
