@@ -1432,20 +1432,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 
   // ---- partial result of this split: lane (n, j) holds head n, coordinates
-  // D/4 wave + 16 mi + 4 j + r; the row sum is spread over lanes and waves
+  // D/4 wave + 16 mi + 4 j + r; the row sum is spread over lanes and waves.  The lane indices
+  // are taken afresh here (opaque copies), so that no address of this epilogue is computed
+  // before the tile loop and kept live through it.
+  int le = lane;
+  asm volatile("" : "+v"(le));
+  const int ne = le & 15, je = le >> 4;
   float l = l_part;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   float* lsm = mx + 128;
-  if (j == 0 && n < 8) lsm[8 * wave + n] = l;
+  if (je == 0 && ne < 8) lsm[8 * wave + ne] = l;
   __syncthreads();
-  if (real_col) {
-    const int64_t row = (int64_t(s) * a.n_q + hk * a.group + n) * a.n_split + split;
+  if (ne < a.group) {
+    const int64_t row = (int64_t(s) * a.n_q + hk * a.group + ne) * a.n_split + split;
     float* dst = a.partial + row * D;
 #pragma unroll
     for (int mi = 0; mi < MTV; ++mi)
-      *reinterpret_cast<float4*>(dst + CPW * wave + 16 * mi + 4 * j) = float4{acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]};
-    if (wave == 0 && j == 0) a.part_ml[row] = float2{m_run, lsm[n] + lsm[8 + n] + lsm[16 + n] + lsm[24 + n]};
+      *reinterpret_cast<float4*>(dst + CPW * wave + 16 * mi + 4 * je) = float4{acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]};
+    if (wave == 0 && je == 0) a.part_ml[row] = float2{m_run, lsm[ne] + lsm[8 + ne] + lsm[16 + ne] + lsm[24 + ne]};
   }
 }
 
