@@ -480,14 +480,16 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
   __shared__ __align__(16) float xk[HP][2 * DM + 16];   // key, storage order, zero past d_eff
   __shared__ __align__(16) float xv[HP][DM];       // value
   __shared__ float nrm[HP][kMaxGroups + 1];        // group norms, value norm last
-  __shared__ uint8_t cd[HP][2 * DM];               // key codes (storage order), value codes at DM
+  __shared__ uint32_t kw[HP][kMaxRecordDwords];    // the slot's key record, assembled with atomic ors
   const int si = blockIdx.x, s = a.seq_begin + si;
   const int tid = threadIdx.x, hp = tid >> 9, t = tid & 511;
   const int d = a.d, bv = a.v_bits;
   // ---- inputs that do not depend on the sequence length
+#pragma unroll 2
   for (int i = tid; i < kAppendThrFloats; i += 1024) thr[i] = (&c_thr[0][0])[i];
   if (STAGE_V) {
     const float4* src = reinterpret_cast<const float4*>(a.rot_v);
+#pragma unroll 4
     for (int i = tid; i < d * d / 4; i += 1024) {
       const float4 v = src[i];
       const int row = (4 * i) / d, col = 4 * i - row * d;
@@ -530,6 +532,7 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
     for (int g = 0; g < ng; ++g) mmax = L.g_m[g] > mmax ? L.g_m[g] : mmax;
     mmax = (mmax + 15) & ~15;
     for (int i = t; i < 2 * DM + 16; i += 512) xk[hp][i] = i < d_eff ? ko[hp][L.perm[i]] : 0.0f;
+    if (t < kMaxRecordDwords) kw[hp][t] = 0u;
     __syncthreads();
     // norms run beside the rotations when the head has threads to spare (always for d <= 128)
     const bool norms_beside = d + d_eff + ng + 1 <= 512;
@@ -550,34 +553,25 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
       else if (act && t == ng) nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
     }
     __syncthreads();
+    // codes: a value code goes straight into the slot's dwords (read before any arithmetic);
+    // key codes are ored into the slot's record, assembled in LDS
     if (act && t < d) {
       const float nv = nrm[hp][kMaxGroups];
-      cd[hp][DM + t] = uint8_t(nv != 0.0f ? code_of(thr + (bv - 1) * 255, bv, (acc / nv) * sqrtf(float(d))) : 0);
+      const uint32_t code = nv != 0.0f ? code_of(thr + (bv - 1) * 255, bv, (acc / nv) * sqrtf(float(d))) : 0u;
+      vseg[t * 2 * bv + vw] = (old0 & ~(vmask << vsh)) | (code << vsh);
+      if (vsplit) vseg[t * 2 * bv + vw + 1] = (old1 & ~(vmask >> (32 - vsh))) | (code >> (32 - vsh));
     } else if (t >= d && t < d + d_eff) {
       const int p = t - d, g = L.group[p], w = L.g_width[g], m = L.g_m[g];
       const float nv = nrm[hp][g];
-      cd[hp][p] = uint8_t(nv != 0.0f ? code_of(thr + (w - 1) * 255, w, (acc / nv) * sqrtf(float(m))) : 0);
+      const uint32_t code = nv != 0.0f ? code_of(thr + (w - 1) * 255, w, (acc / nv) * sqrtf(float(m))) : 0u;
+      const int off = L.offset[p], wd = off >> 5, sh = off & 31;
+      atomicOr(&kw[hp][wd], code << sh);
+      if (sh + w > 32) atomicOr(&kw[hp][wd + 1], code >> (32 - sh));
     }
     __syncthreads();
     if (act) {
-      // key record dwords of the slot
       uint32_t* kc = reinterpret_cast<uint32_t*>(a.k_codes) + (reg * tiles + tile) * a.chunks * kTile * 4;
-      if (t < 4 * a.chunks) {
-        const int w = t;
-        uint32_t v = 0u;
-        for (int p = L.dw_first[w]; p < L.dw_end[w]; ++p) {
-          const uint32_t c = cd[hp][p];
-          const int o = int(L.offset[p]) - 32 * w;
-          v |= o >= 0 ? (c << o) : (c >> (-o));
-        }
-        kc[((w >> 2) * kTile + slot) * 4 + (w & 3)] = v;
-      }
-      // value segment bits of the slot (the dwords were read before any arithmetic)
-      if (t < d) {
-        const uint32_t code = cd[hp][DM + t];
-        vseg[t * 2 * bv + vw] = (old0 & ~(vmask << vsh)) | (code << vsh);
-        if (vsplit) vseg[t * 2 * bv + vw + 1] = (old1 & ~(vmask >> (32 - vsh))) | (code >> (32 - vsh));
-      }
+      if (t < 4 * a.chunks) kc[((t >> 2) * kTile + slot) * 4 + (t & 3)] = kw[hp][t];
       uint16_t* kn = a.k_norms + (reg * tiles + tile) * kMaxGroups * kTile;
       if (t >= 256 && t < 256 + ng) kn[(t - 256) * kTile + slot] = f32_to_f16_bits(fminf(nrm[hp][t - 256], 65504.0f));
       if (t == 256 + kMaxGroups)
