@@ -58,6 +58,8 @@ _SIGNATURES = {
     "bgtq_quantize_append": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _vp]),
     "bgtq_decode_attention": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _f64, _f32, _vp, _vp, _vp, _sz, _vp]),
     "bgtq_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i64]),
+    "bgtq_decode_step": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _f64, _f32, _vp, _vp, _vp,
+                                _sz, _vp]),
     "bgtq_cache_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _vp]),
     "bgtq_codebook": (_i32, [_i32, _vp, _vp, _vp]),
     "bgtq_init": (_i32, []),
@@ -282,4 +284,39 @@ def bgtq_decode_attention(quantizer: Quantizer, cache: PackedCache, q: torch.Ten
     _check(lib().bgtq_decode_attention(_c.byref(quantizer), _c.byref(desc), hq, q.data_ptr(), _dtype_code(q),
                                        _ptr(q_pos), float(rope_theta), float(scale), out.data_ptr(), _ptr(lg),
                                        workspace.data_ptr(), workspace.numel(), _stream()))
+    return (out, lg) if logits is not False else out
+
+
+def bgtq_decode_step(quantizer: Quantizer, cache: PackedCache, q: torch.Tensor, k_new: torch.Tensor,
+                     v_new: torch.Tensor, rope_theta: float, softmax_scale: float | None = None,
+                     out: torch.Tensor | None = None, logits: bool | torch.Tensor = False,
+                     workspace: torch.Tensor | None = None):
+    """Append one token per sequence (k_new, v_new [batch, n_kv_heads, 1, head_dim], same strides)
+    and attend with q [batch, n_q_heads, head_dim] at its position, in one call."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, n_q_heads, head_dim] tensor")
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same shape, strides and dtype")
+    b, hq, d = q.shape
+    if k_new.dim() != 4 or k_new.shape[0] != b or k_new.shape[1] != cache.n_kv_heads or k_new.shape[2] != 1 \
+            or k_new.shape[3] != d or k_new.stride(3) != 1:
+        raise ValueError("k_new must be [batch, n_kv_heads, 1, head_dim] with a contiguous last dimension")
+    if b != cache.batch or d != cache.head_dim:
+        raise ValueError("q does not match the cache geometry")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+    lg = None
+    if isinstance(logits, torch.Tensor):
+        lg = logits
+    elif logits:
+        lg = torch.full((b, hq, cache.capacity), float("nan"), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(decode_workspace_bytes(b, hq, cache.n_kv_heads, d, cache.capacity),
+                                dtype=torch.uint8, device=q.device)
+    desc = cache.desc()
+    _check(lib().bgtq_decode_step(_c.byref(quantizer), _c.byref(desc), hq, q.data_ptr(), _dtype_code(q),
+                                  k_new.data_ptr(), v_new.data_ptr(), _dtype_code(k_new), k_new.stride(0),
+                                  k_new.stride(1), float(rope_theta), float(scale), out.data_ptr(), _ptr(lg),
+                                  workspace.data_ptr(), workspace.numel(), _stream()))
     return (out, lg) if logits is not False else out

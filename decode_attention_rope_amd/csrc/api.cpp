@@ -173,9 +173,9 @@ bgtq_status bgtq_allocate_bits(const double* energy, int n_heads, int head_dim, 
                     "allocate launch");
 }
 
-bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cache, int seq_begin, int n_seqs,
-                                 const void* keys, const void* values, bgtq_dtype dtype, int64_t n_new,
-                                 int64_t stride_seq, int64_t stride_head, int64_t stride_token, bgtq_stream stream) {
+static bgtq_status prepare_append(const bgtq_quantizer* qz, const bgtq_cache* cache, int seq_begin, int n_seqs,
+                                  const void* keys, const void* values, bgtq_dtype dtype, int64_t n_new,
+                                  int64_t stride_seq, int64_t stride_head, int64_t stride_token, AppendArgs& a) {
   if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
   if (!qz || !qz->rot_bank || !qz->rot_v || !qz->rot_bank_t || !qz->rot_v_t)
     return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
@@ -190,8 +190,8 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
                                            (long long)n_new, (long long)cache->capacity);
   if (stride_token < cache->head_dim || stride_head < 1 || stride_seq < 1)
     return fail(BGTQ_ERR_INVALID_ARG, "strides must be positive and not overlap a row");
-  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
-  AppendArgs a{};
+  a = AppendArgs{};
+  a.advance = 1;
   a.rot_bank = qz->rot_bank;
   a.rot_v = qz->rot_v;
   a.rot_bank_t = qz->rot_bank_t;
@@ -215,6 +215,18 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
   a.d = cache->head_dim;
   a.v_bits = cache->v_bits;
   a.chunks = record_chunks(cache->k_width_sum);
+  return BGTQ_OK;
+}
+
+bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cache, int seq_begin, int n_seqs,
+                                 const void* keys, const void* values, bgtq_dtype dtype, int64_t n_new,
+                                 int64_t stride_seq, int64_t stride_head, int64_t stride_token, bgtq_stream stream) {
+  AppendArgs a;
+  if (bgtq_status st = prepare_append(qz, cache, seq_begin, n_seqs, keys, values, dtype, n_new, stride_seq,
+                                      stride_head, stride_token, a);
+      st != BGTQ_OK)
+    return st;
+  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
   return hip_status(launch_append(a, dtype, n_seqs, static_cast<hipStream_t>(stream)), "quantize-append launch");
 }
 
@@ -223,13 +235,14 @@ size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
   const int splits = decode_splits(batch, n_kv_heads, capacity, true);
   const size_t part = align256(size_t(batch) * n_q_heads * splits * head_dim * 4) +
                       align256(size_t(batch) * n_q_heads * splits * 8);
-  return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + part;
+  return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + part +
+         align256(decode_qpre_bytes(batch, n_kv_heads, head_dim));
 }
 
-bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
+static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
                                   bgtq_dtype q_dtype, const int64_t* q_pos, double rope_theta, float softmax_scale,
                                   float* out, float* logits_out, void* workspace, size_t workspace_bytes,
-                                  bgtq_stream stream) {
+                                  DecodeArgs& a) {
   if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
   if (!qz || !qz->rot_bank || !qz->rot_v || !qz->rot_bank_t || !qz->rot_v_t)
     return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
@@ -247,8 +260,7 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
   const size_t need = bgtq_decode_workspace_bytes(cache->batch, n_q_heads, cache->n_kv_heads, d, cache->capacity);
   if (!workspace || workspace_bytes < need)
     return fail(BGTQ_ERR_WORKSPACE, "decode workspace needs %zu bytes", need);
-  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
-  DecodeArgs a{};
+  a = DecodeArgs{};
   a.rot_bank = qz->rot_bank;
   a.rot_v = qz->rot_v;
   a.rot_bank_t = qz->rot_bank_t;
@@ -270,6 +282,7 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.qrot = reinterpret_cast<float*>(ws);
   a.partial = reinterpret_cast<float*>(ws + qrot_b);
   a.part_ml = reinterpret_cast<float2*>(ws + qrot_b + align256(size_t(cache->batch) * n_q_heads * a.n_split * d * 4));
+  a.qpre = nullptr;   // set by the decode step (the workspace's last region)
   a.rope_theta = rope_theta;
   for (int j = 0; j < d / 2; ++j) a.inv_freq[j] = rope_theta > 0.0 ? std::pow(rope_theta, -2.0 * j / d) : 0.0;
   a.scale = softmax_scale;
@@ -282,7 +295,53 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.v_bits = cache->v_bits;
   a.chunks = record_chunks(cache->k_width_sum);
   a.pairing = cache->pairing;
+  return BGTQ_OK;
+}
+
+bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
+                                  bgtq_dtype q_dtype, const int64_t* q_pos, double rope_theta, float softmax_scale,
+                                  float* out, float* logits_out, void* workspace, size_t workspace_bytes,
+                                  bgtq_stream stream) {
+  DecodeArgs a;
+  if (bgtq_status st = prepare_decode(qz, cache, n_q_heads, q, q_dtype, q_pos, rope_theta, softmax_scale, out,
+                                      logits_out, workspace, workspace_bytes, a);
+      st != BGTQ_OK)
+    return st;
+  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
   return hip_status(launch_decode(a, q_dtype, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
+                             bgtq_dtype q_dtype, const void* keys, const void* values, bgtq_dtype kv_dtype,
+                             int64_t stride_seq, int64_t stride_head, double rope_theta, float softmax_scale,
+                             float* out, float* logits_out, void* workspace, size_t workspace_bytes,
+                             bgtq_stream stream) {
+  if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
+  AppendArgs aa;
+  if (bgtq_status st = prepare_append(qz, cache, 0, cache->batch, keys, values, kv_dtype, 1, stride_seq, stride_head,
+                                      cache->head_dim, aa);
+      st != BGTQ_OK)
+    return st;
+  DecodeArgs da;
+  if (bgtq_status st = prepare_decode(qz, cache, n_q_heads, q, q_dtype, nullptr, rope_theta, softmax_scale, out,
+                                      logits_out, workspace, workspace_bytes, da);
+      st != BGTQ_OK)
+    return st;
+  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!da.use_mfma) {   // vector-ALU path: the two calls in sequence
+    if (bgtq_status st = hip_status(launch_append(aa, kv_dtype, cache->batch, s), "decode-step append launch");
+        st != BGTQ_OK)
+      return st;
+    return hip_status(launch_decode(da, q_dtype, s), "decode-step attention launch");
+  }
+  const size_t need = bgtq_decode_workspace_bytes(cache->batch, n_q_heads, cache->n_kv_heads, cache->head_dim,
+                                                  cache->capacity);
+  aa.advance = 0;
+  da.step = 1;
+  da.qpre = reinterpret_cast<uint4*>(static_cast<char*>(workspace) + need -
+                                     align256(decode_qpre_bytes(cache->batch, cache->n_kv_heads, cache->head_dim)));
+  return hip_status(launch_decode_step(aa, da, kv_dtype, q_dtype, s), "decode-step launch");
 }
 
 }  // extern "C"

@@ -111,6 +111,7 @@ struct AppendArgs {
   int d;
   int v_bits;
   int chunks;
+  int advance;        // the one-token kernel advances lengths[] (a decode step leaves that to the merge)
 };
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s);
 
@@ -124,21 +125,28 @@ struct DecodeArgs {
   const uint16_t* k_norms;
   const uint8_t* v_codes;
   const uint16_t* v_norms;
-  const int32_t* lengths;
+  int32_t* lengths;
   const HeadLayout* layouts;
   float* out;
   float* logits;
   float* qrot;        // [batch][n_kv][d][kQPad] fp32 (vector-ALU kernel)
   float* partial;     // [batch][n_q][n_split][d] split accumulators
   float2* part_ml;    // [batch][n_q][n_split] split (running max, row sum)
+  uint4* qpre;        // matrix-core B operands [batch][n_kv][k-steps][hi, lo][64 lanes], or null
   double rope_theta;
   double inv_freq[BGTQ_MAX_HEAD_DIM / 2];   // rope_theta^(-2j/d), fp64, computed on the host
   float scale;
   int64_t capacity;
   int batch, n_q, n_kv, group, d, v_bits, chunks, n_split, pairing;
+  int step;           // decode step: one token was appended after lengths were read (see k_step_front)
   int use_mfma;
 };
 hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s);
+// decode step on the matrix-core path: append one token per sequence and attend (da.qpre set,
+// da.step = 1, aa.advance = 0)
+hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, bgtq_dtype kv_dt, bgtq_dtype q_dt,
+                              hipStream_t s);
+size_t decode_qpre_bytes(int batch, int n_kv_heads, int d);
 
 hipError_t launch_transpose_rotations(const float* rot_bank, const float* rot_v, int d, float* rot_bank_t,
                                       float* rot_v_t, hipStream_t s);

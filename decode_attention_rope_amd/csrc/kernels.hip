@@ -469,10 +469,9 @@ __host__ __device__ inline size_t append_one_lds_bytes(int d, bool stage_v) {
 }
 
 template <typename T, bool STAGE_V>
-__global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
+__device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float* dyn) {
   constexpr int HP = 2;
   constexpr int DM = BGTQ_MAX_HEAD_DIM;
-  extern __shared__ __align__(16) float dyn[];
   float* thr = dyn;                                // [8][255]
   float* rv = dyn + kAppendThrFloats;              // [d][d + 1] (STAGE_V)
   __shared__ HeadLayout Ls[HP];
@@ -481,7 +480,7 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
   __shared__ __align__(16) float xv[HP][DM];       // value
   __shared__ float nrm[HP][kMaxGroups + 1];        // group norms, value norm last
   __shared__ uint32_t kw[HP][kMaxRecordDwords];    // the slot's key record, assembled with atomic ors
-  const int si = blockIdx.x, s = a.seq_begin + si;
+  const int s = a.seq_begin + si;
   const int tid = threadIdx.x, hp = tid >> 9, t = tid & 511;
   const int d = a.d, bv = a.v_bits;
   // ---- inputs that do not depend on the sequence length
@@ -579,7 +578,13 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
     }
     __syncthreads();
   }
-  if (tid == 0) a.lengths[s] = int32_t(len + 1);
+  if (tid == 0 && a.advance) a.lengths[s] = int32_t(len + 1);
+}
+
+template <typename T, bool STAGE_V>
+__global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
+  extern __shared__ __align__(16) float dyn[];
+  append_one_wg<T, STAGE_V>(a, blockIdx.x, dyn);
 }
 
 __global__ void k_advance(int32_t* __restrict__ lengths, int seq_begin, int n_seqs, int64_t n_new,
@@ -971,7 +976,168 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // Byte offset, in the per-wave K staging [chunk][16 slots][16 B], of record dword wd.
 __device__ __forceinline__ uint32_t kdw_off(uint32_t wd) { return (wd >> 2) * 256u + (wd & 3u) * 4u; }
 
-template <int D, bool NARROW, typename QT>
+// ---- rotated query, shared by the matrix-core kernel's prologue and the decode step's query
+// workgroups.  q' = RoPE(q, pos) with the angle formed and reduced modulo 2 pi in fp64;
+// q''[h][p] = (softmax_scale * log2(e) / sqrt(m)) * sum_k R_m[p - first][k] q'[h][perm[first + k]]
+// (m and first of storage position p's width group), split into an fp16 high part and an fp16
+// remainder and scattered into the B operand layout: lane 16 j + c of k-step s holds k indices
+// 32 s + 8 j + e, column c < 8 is head c for the k-step's first width group, c + 8 head c for
+// its second; every other entry (other column half, heads >= G, unused k indices) is 0.  The
+// helpers run on 256 threads (tid < 256).
+template <int D>
+struct QShape {
+  static constexpr int NP = D / 2;
+  static constexpr int QI = 8 * NP / 256 > 0 ? 8 * NP / 256 : 1;   // (head, pair) items per thread
+  static constexpr int RR = D / 4 < 16 ? D / 4 : 16;                // rotation-row float2 per batch
+};
+
+// q of the thread's items (head h, pair jx): idx = tid + 256 it, jx = idx % NP, h = idx / NP;
+// zero for heads >= G
+template <int D, typename QT>
+__device__ __forceinline__ void q_load(const DecodeArgs& a, int s, int hk, int tid, float (&x0)[QShape<D>::QI],
+                                       float (&x1)[QShape<D>::QI]) {
+  constexpr int NP = QShape<D>::NP;
+  static_assert(256 % NP == 0 || NP % 256 == 0, "pair index of a thread's items");
+  const QT* qg = static_cast<const QT*>(a.q) + (int64_t(s) * a.n_q + int64_t(hk) * a.group) * D;
+#pragma unroll
+  for (int it = 0; it < QShape<D>::QI; ++it) {
+    const int idx = tid + 256 * it, jx = idx % NP, h = idx / NP;
+    x0[it] = 0.0f;
+    x1[it] = 0.0f;
+    if (h < a.group) {
+      x0[it] = load_f(qg + h * D, a.pairing ? 2 * jx : jx);
+      x1[it] = load_f(qg + h * D, a.pairing ? 2 * jx + 1 : jx + NP);
+    }
+  }
+}
+
+// q' of the thread's items into qc [coordinate][8 heads]; fr = inv_freq[tid % NP]
+template <int D>
+__device__ __forceinline__ void q_rope(const DecodeArgs& a, int64_t pos, double fr, int tid,
+                                       const float (&x0)[QShape<D>::QI], const float (&x1)[QShape<D>::QI], float* qc) {
+  constexpr int NP = QShape<D>::NP;
+  float cv = 1.0f, sv = 0.0f;
+  if (a.rope_theta > 0.0) {
+    const double ang = double(pos) * fr;
+    sincosf(float(ang - kTwoPi * floor(ang * (1.0 / kTwoPi))), &sv, &cv);
+  }
+#pragma unroll
+  for (int it = 0; it < QShape<D>::QI; ++it) {
+    const int idx = tid + 256 * it, jx = idx % NP, h = idx / NP;
+    if (h < 8) {
+      const double a0 = x0[it], a1 = x1[it];   // zero for heads >= G
+      qc[8 * (a.pairing ? 2 * jx : jx) + h] = float(a0 * cv - a1 * sv);
+      qc[8 * (a.pairing ? 2 * jx + 1 : jx + NP) + h] = float(a0 * sv + a1 * cv);
+    }
+  }
+}
+
+// The matrix-core kernel takes the layout's k-steps in a different order: the narrow ones
+// (every segment at most 4 bits wide) first, in layout order, then the wide ones.  The mask
+// marks the layout's wide k-steps (a ballot: every lane of the wave takes part).
+__device__ __forceinline__ uint32_t wide_ksteps(const HeadLayout* Ls, int nks, int lane) {
+  bool wd = false;
+  if (lane < nks) {
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) wd = wd || ((Ls->seg[4 * lane + sl] >> 16) & 15u) > 4u;
+  }
+  return uint32_t(__ballot(wd));
+}
+// place of layout k-step ks in the kernel's order (nn narrow k-steps)
+__device__ __forceinline__ int kperm_of(uint32_t wmask, int nn, int ks) {
+  const int below = __popc(wmask & ((1u << ks) - 1u));
+  return ((wmask >> ks) & 1u) ? nn + below : ks - below;
+}
+
+// B operand storage: high parts of k-steps < 8 [ks][lane], their remainders [ks][lane], both
+// parts of later k-steps [ks - 8][hi, lo][lane]
+__device__ __forceinline__ void qops_zero(uint4* qhi, uint4* qlo, uint4* qlate, int nks, int tid) {
+  for (int i = tid; i < 64 * nks; i += 256) {
+    const uint4 z = uint4{0u, 0u, 0u, 0u};
+    if (i < 64 * kQRegSteps) {
+      qhi[i] = z;
+      qlo[i] = z;
+    } else {
+      qlate[2 * (i - 64 * kQRegSteps) - (i & 63)] = z;            // [ks - 8][0][lane]
+      qlate[2 * (i - 64 * kQRegSteps) - (i & 63) + 64] = z;       // [ks - 8][1][lane]
+    }
+  }
+}
+
+// q'' of storage position p = p0 + tid / 2 (every 128 positions): the thread pair splits the
+// rotation row in two halves and covers all 8 heads, then each thread scatters 4 heads.
+// qc = q' [coordinate][8 heads] and the layout copy Ls are in LDS.
+template <int D>
+__device__ __forceinline__ void qops_scatter(const DecodeArgs& a, const HeadLayout* Ls, const float* qc, uint32_t wmask,
+                                             int nn, int tid, uint4* qhi, uint4* qlo, uint4* qlate) {
+  constexpr int RR = QShape<D>::RR;
+  const int d_eff = Ls->d_eff, kh = tid & 1, G = a.group;
+  const float kscale = a.scale * kLog2e;
+  float2 rr[RR];
+  for (int p0 = 0; p0 < d_eff; p0 += 128) {
+    const int p = p0 + (tid >> 1);
+    int m = 2, first = 0;
+    const float2* R2 = nullptr;
+    if (p < d_eff) {
+      const int g = Ls->group[p];
+      m = Ls->g_m[g];
+      first = Ls->g_first[g];
+      R2 = reinterpret_cast<const float2*>(a.rot_bank + bank_offset(m) + size_t(p - first) * m) + kh * (m / 4);
+    }
+    const int nh = p < d_eff ? (kh == 0 ? m / 4 : m / 2 - m / 4) : 0;   // float2 of this half
+    const uint8_t* pm = Ls->perm + first + 2 * kh * (m / 4);           // its coordinates
+    float acc[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
+    for (int b0 = 0; b0 < nh; b0 += RR) {         // one batch unless m > 4 RR
+#pragma unroll
+      for (int i = 0; i < RR; ++i)
+        if (b0 + i < nh) rr[i] = R2[b0 + i];
+#pragma unroll
+      for (int i = 0; i < RR; ++i) {
+        if (b0 + i < nh) {
+          const float4* xa = reinterpret_cast<const float4*>(qc + 8 * pm[2 * (b0 + i)]);
+          const float4* xb = reinterpret_cast<const float4*>(qc + 8 * pm[2 * (b0 + i) + 1]);
+          const float4 a0 = xa[0], a1 = xa[1], c0 = xb[0], c1 = xb[1];
+          const float r0 = rr[i].x, r1 = rr[i].y;
+          acc[0] = fmaf(r0, a0.x, acc[0]); acc[1] = fmaf(r0, a0.y, acc[1]);
+          acc[2] = fmaf(r0, a0.z, acc[2]); acc[3] = fmaf(r0, a0.w, acc[3]);
+          acc[4] = fmaf(r0, a1.x, acc[4]); acc[5] = fmaf(r0, a1.y, acc[5]);
+          acc[6] = fmaf(r0, a1.z, acc[6]); acc[7] = fmaf(r0, a1.w, acc[7]);
+          acc[0] = fmaf(r1, c0.x, acc[0]); acc[1] = fmaf(r1, c0.y, acc[1]);
+          acc[2] = fmaf(r1, c0.z, acc[2]); acc[3] = fmaf(r1, c0.w, acc[3]);
+          acc[4] = fmaf(r1, c1.x, acc[4]); acc[5] = fmaf(r1, c1.y, acc[5]);
+          acc[6] = fmaf(r1, c1.z, acc[6]); acc[7] = fmaf(r1, c1.w, acc[7]);
+        }
+      }
+    }
+    // the pair's two halves, lower coordinates first; this thread keeps heads 4 kh .. 4 kh + 3
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float mine = acc[4 * kh + e], give = acc[4 * (1 - kh) + e];
+      const float other = __shfl_xor(give, 1);
+      v[e] = (kh == 0 ? mine + other : other + mine) * (kscale / sqrtf(float(m)));
+    }
+    if (p < d_eff) {
+      const int kx = Ls->kpos[p], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm_of(wmask, nn, ks0);
+      const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks0 + jj] >> 28) & 1u);
+      uint16_t* h16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qhi + 64 * ks : qlate + 128 * (ks - kQRegSteps));
+      uint16_t* l16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qlo + 64 * ks : qlate + 128 * (ks - kQRegSteps) + 64);
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const int h = 4 * kh + hh;
+        if (h < G) {
+          const uint16_t hi = f32_to_f16_bits(v[hh]);
+          h16[(lb + h) * 8 + e] = hi;
+          l16[(lb + h) * 8 + e] = f32_to_f16_bits(v[hh] - f16_bits_to_f32(hi));
+        }
+      }
+    }
+  }
+}
+
+template <int D, bool NARROW, typename QT, bool PRE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_mfma(DecodeArgs a) {
   constexpr int CPW = D / 4;                          // value coordinates per wave
   constexpr int MTV = CPW / 16;                       // value M-tiles per wave
@@ -981,7 +1147,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
-  const int len = a.lengths[s];
+  // in a decode step the new token was appended after lengths[] were read; lengths[] is
+  // advanced by the merge kernel, so it still holds the old length here
+  const int len0 = a.lengths[s];
+  const int len = a.step && len0 + 1 <= a.capacity ? len0 + 1 : len0;
   const int tiles = (len + kTile - 1) / kTile;
   // split i takes tiles [i T / n, (i + 1) T / n): counts differ by at most one
   const int t0 = int(int64_t(split) * tiles / a.n_split);
@@ -1044,28 +1213,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int i = 0; i < MAXNV; ++i) *reinterpret_cast<uint4*>(buf + geo.v_off + vdst[i]) = pv[i];
   };
-  // ---- workgroup set-up and query prologue.  The rotated query of this (sequence, KV head) is
-  // computed here: q' = RoPE(q, pos) (angle formed and reduced modulo 2 pi in fp64),
-  // q''[h][p] = (softmax_scale * log2(e) / sqrt(m)) * sum_k R_m[p - first][k] q'[h][perm[first + k]]
-  // (m and first of storage position p's width group), split into an fp16 high part and an
-  // fp16 remainder and scattered into the B operand layout: lane 16 j + c of k-step s holds
-  // k indices 32 s + 8 j + e, column c < 8 is head c for the k-step's first width group,
-  // c + 8 head c for its second; every other entry (other column half, heads >= G, unused k
-  // indices) is 0.  Global reads come in two rounds: everything that does not depend on the
-  // layout descriptor (descriptor, level tables, query, first tile), then the rotation rows.
-  constexpr int NP = D / 2;
-  constexpr int QI = 8 * NP / 256 > 0 ? 8 * NP / 256 : 1;   // (head, pair) items per thread
-  constexpr int RR = D / 4 < 16 ? D / 4 : 16;     // rotation-row float2 per batch (half a row of m <= 64)
+  // ---- workgroup set-up and query prologue.  Global reads come in two rounds: everything
+  // that does not depend on the layout descriptor (descriptor, level tables, query, first
+  // tile), then the rotation rows.  With PRE the rotated query's B operands were written by
+  // the decode step's query workgroups and are read in the first round instead.
+  constexpr int NP = QShape<D>::NP, QI = QShape<D>::QI;
   constexpr int PW = (kPairWords + 255) / 256, SW = (kSingleHalves + 255) / 256;
   static_assert(BGTQ_LAYOUT_BYTES == 256 * 16, "one 16-byte piece of the layout per thread");
-  static_assert(256 % NP == 0 || NP % 256 == 0, "pair index of a thread's items");
-  const int G = a.group;
   uint8_t* const pro = lds + kTcRing;             // aliases the ring, first written in the loop
   HeadLayout* const Ls = reinterpret_cast<HeadLayout*>(pro);
   float* const qc = reinterpret_cast<float*>(pro + BGTQ_LAYOUT_BYTES);           // q' [coordinate][8 heads]
   uint4* const qhi = reinterpret_cast<uint4*>(pro + tc_qhi_off(D));                // [k-step < 8][lane]
   uint4* const qlo = reinterpret_cast<uint4*>(lds + tc_qlo_off(D, chunks, bv));     // [k-step < 8][lane]
   uint4* const qlate = qlo + 64 * kQRegSteps;                                       // [k-step - 8][hi, lo][lane]
+  const uint4* const qpre = PRE ? a.qpre + reg * tc_ksteps(D) * 128 : nullptr;     // [k-step][hi, lo][lane]
+  f16x8 qh[kQRegSteps];
   {
     const uint4 lw = reinterpret_cast<const uint4*>(L)[tid];
     uint32_t pt[PW];
@@ -1076,20 +1238,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int i = 0; i < SW; ++i)
       if (tid + 256 * i < kSingleHalves) st[i] = c_single[tid + 256 * i];
-    // items (head h, pair jx): idx = tid + 256 it, jx = idx % NP, h = idx / NP
-    const QT* qg = static_cast<const QT*>(a.q) + (int64_t(s) * a.n_q + int64_t(hk) * G) * D;
     float x0[QI], x1[QI];
+    double fr = 0.0;
+    if (PRE) {
 #pragma unroll
-    for (int it = 0; it < QI; ++it) {
-      const int idx = tid + 256 * it, jx = idx % NP, h = idx / NP;
-      x0[it] = 0.0f;
-      x1[it] = 0.0f;
-      if (h < G) {
-        x0[it] = load_f(qg + h * D, a.pairing ? 2 * jx : jx);
-        x1[it] = load_f(qg + h * D, a.pairing ? 2 * jx + 1 : jx + NP);
+      for (int ks = 0; ks < kQRegSteps; ++ks) {
+        const uint4 z = uint4{0u, 0u, 0u, 0u};
+        qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qpre[ks * 128 + lane] : z);
       }
+      for (int i = tid; i < 64 * nks; i += 256) {
+        const int ks = i >> 6, ln = i & 63;
+        if (ks < kQRegSteps) qlo[i] = qpre[ks * 128 + 64 + ln];
+        else {
+          qlate[(ks - kQRegSteps) * 128 + ln] = qpre[ks * 128 + ln];
+          qlate[(ks - kQRegSteps) * 128 + 64 + ln] = qpre[ks * 128 + 64 + ln];
+        }
+      }
+    } else {
+      q_load<D, QT>(a, s, hk, tid, x0, x1);
+      fr = a.rope_theta > 0.0 ? a.inv_freq[tid % NP] : 0.0;
     }
-    const double fr = a.rope_theta > 0.0 ? a.inv_freq[tid % NP] : 0.0;
     if (count > 0) load_tile(0);
     reinterpret_cast<uint4*>(Ls)[tid] = lw;
     uint32_t* ptab = reinterpret_cast<uint32_t*>(lds);
@@ -1105,50 +1273,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const int ln = (i >> 2) & 63;      // lane of the 16-byte B operand
       if ((ln & 15) >= 8) pw[i] = 0u;
     }
-    for (int i = tid; i < 64 * nks; i += 256) {
-      const uint4 z = uint4{0u, 0u, 0u, 0u};
-      if (i < 64 * kQRegSteps) {
-        qhi[i] = z;
-        qlo[i] = z;
-      } else {
-        qlate[2 * (i - 64 * kQRegSteps) - (i & 63)] = z;            // [ks - 8][0][lane]
-        qlate[2 * (i - 64 * kQRegSteps) - (i & 63) + 64] = z;       // [ks - 8][1][lane]
-      }
-    }
-    const int64_t pos = a.q_pos ? a.q_pos[s] : int64_t(len) - 1;
-    float cv = 1.0f, sv = 0.0f;
-    if (a.rope_theta > 0.0) {
-      const double ang = double(pos) * fr;
-      sincosf(float(ang - kTwoPi * floor(ang * (1.0 / kTwoPi))), &sv, &cv);
-    }
-#pragma unroll
-    for (int it = 0; it < QI; ++it) {
-      const int idx = tid + 256 * it, jx = idx % NP, h = idx / NP;
-      if (h < 8) {
-        const double a0 = x0[it], a1 = x1[it];   // zero for heads >= G
-        qc[8 * (a.pairing ? 2 * jx : jx) + h] = float(a0 * cv - a1 * sv);
-        qc[8 * (a.pairing ? 2 * jx + 1 : jx + NP) + h] = float(a0 * sv + a1 * cv);
-      }
+    if (!PRE) {
+      qops_zero(qhi, qlo, qlate, nks, tid);
+      q_rope<D>(a, a.q_pos ? a.q_pos[s] : int64_t(len) - 1, fr, tid, x0, x1, qc);
     }
   }
   lds_barrier();
-  // This kernel takes the layout's k-steps in a different order: the narrow ones (every
-  // segment at most 4 bits wide) first, in layout order, then the wide ones.  wmask marks
-  // the layout's wide k-steps; kperm maps a layout k-step to its place here.
-  uint32_t wmask;
-  {
-    bool wd = false;
-    if (lane < nks) {
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) wd = wd || ((Ls->seg[4 * lane + sl] >> 16) & 15u) > 4u;
-    }
-    wmask = uint32_t(__ballot(wd));
-  }
+  const uint32_t wmask = wide_ksteps(Ls, nks, lane);
   const int nn = nks - __popc(wmask);               // narrow k-steps
-  auto kperm = [&](int ks) {
-    const int below = __popc(wmask & ((1u << ks) - 1u));
-    return ((wmask >> ks) & 1u) ? nn + below : ks - below;
-  };
   // per segment: x = byte offset of the window's first record dword, y = control of the
   // 4-bit-or-narrower decode (shift | 2w << 8 | pair table << 16; wider segments get a
   // harmless width-1 control), z = control of the any-width decode (shift | w << 8 | single
@@ -1163,90 +1295,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const uint32_t tbp = 4u * uint32_t(pair_base(int(w)));
       const uint32_t tbs = 4u * kPairWords + 2u * uint32_t(single_base(int(w)));
       const uint32_t fast = w <= 4 ? ((o & 31u) | ((2u * w) << 8) | (tbp << 16)) : (2u << 8);
-      kd[i < 4 * nks ? 4 * kperm(i >> 2) + (i & 3) : i] = uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tbs << 16), 0u};
+      kd[i < 4 * nks ? 4 * kperm_of(wmask, nn, i >> 2) + (i & 3) : i] =
+          uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tbs << 16), 0u};
     }
     uint32_t* kn = reinterpret_cast<uint32_t*>(lds + kTcNorm);
     for (int i = tid; i < kMaxKSteps; i += 256) {
       const uint32_t kg = i < nks ? Ls->kgroups[i] : 0u;
-      kn[i < nks ? kperm(i) : i] = (32u * (kg & 0xffu)) | ((32u * ((kg >> 8) & 0xffu)) << 16);
+      kn[i < nks ? kperm_of(wmask, nn, i) : i] = (32u * (kg & 0xffu)) | ((32u * ((kg >> 8) & 0xffu)) << 16);
     }
   }
-  // q'' of storage position p = p0 + tid / 2 (every 128 positions): the thread pair splits
-  // the rotation row in two halves and covers all 8 heads, then each thread scatters 4 heads
-  {
-    const int d_eff = Ls->d_eff, kh = tid & 1;
-    const float kscale = a.scale * kLog2e;
-    float2 rr[RR];
-    for (int p0 = 0; p0 < d_eff; p0 += 128) {
-      const int p = p0 + (tid >> 1);
-      int m = 2, first = 0;
-      const float2* R2 = nullptr;
-      if (p < d_eff) {
-        const int g = Ls->group[p];
-        m = Ls->g_m[g];
-        first = Ls->g_first[g];
-        R2 = reinterpret_cast<const float2*>(a.rot_bank + bank_offset(m) + size_t(p - first) * m) + kh * (m / 4);
-      }
-      const int nh = p < d_eff ? (kh == 0 ? m / 4 : m / 2 - m / 4) : 0;   // float2 of this half
-      const uint8_t* pm = Ls->perm + first + 2 * kh * (m / 4);           // its coordinates
-      float acc[8];
-#pragma unroll
-      for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
-      for (int b0 = 0; b0 < nh; b0 += RR) {         // one batch unless m > 4 RR
-#pragma unroll
-        for (int i = 0; i < RR; ++i)
-          if (b0 + i < nh) rr[i] = R2[b0 + i];
-#pragma unroll
-        for (int i = 0; i < RR; ++i) {
-          if (b0 + i < nh) {
-            const float4* xa = reinterpret_cast<const float4*>(qc + 8 * pm[2 * (b0 + i)]);
-            const float4* xb = reinterpret_cast<const float4*>(qc + 8 * pm[2 * (b0 + i) + 1]);
-            const float4 a0 = xa[0], a1 = xa[1], c0 = xb[0], c1 = xb[1];
-            const float r0 = rr[i].x, r1 = rr[i].y;
-            acc[0] = fmaf(r0, a0.x, acc[0]); acc[1] = fmaf(r0, a0.y, acc[1]);
-            acc[2] = fmaf(r0, a0.z, acc[2]); acc[3] = fmaf(r0, a0.w, acc[3]);
-            acc[4] = fmaf(r0, a1.x, acc[4]); acc[5] = fmaf(r0, a1.y, acc[5]);
-            acc[6] = fmaf(r0, a1.z, acc[6]); acc[7] = fmaf(r0, a1.w, acc[7]);
-            acc[0] = fmaf(r1, c0.x, acc[0]); acc[1] = fmaf(r1, c0.y, acc[1]);
-            acc[2] = fmaf(r1, c0.z, acc[2]); acc[3] = fmaf(r1, c0.w, acc[3]);
-            acc[4] = fmaf(r1, c1.x, acc[4]); acc[5] = fmaf(r1, c1.y, acc[5]);
-            acc[6] = fmaf(r1, c1.z, acc[6]); acc[7] = fmaf(r1, c1.w, acc[7]);
-          }
-        }
-      }
-      // the pair's two halves, lower coordinates first; this thread keeps heads 4 kh .. 4 kh + 3
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float mine = acc[4 * kh + e], give = acc[4 * (1 - kh) + e];
-        const float other = __shfl_xor(give, 1);
-        v[e] = (kh == 0 ? mine + other : other + mine) * (kscale / sqrtf(float(m)));
-      }
-      if (p < d_eff) {
-        const int kx = Ls->kpos[p], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm(ks0);
-        const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks0 + jj] >> 28) & 1u);
-        uint16_t* h16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qhi + 64 * ks : qlate + 128 * (ks - kQRegSteps));
-        uint16_t* l16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qlo + 64 * ks : qlate + 128 * (ks - kQRegSteps) + 64);
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          const int h = 4 * kh + hh;
-          if (h < G) {
-            const uint16_t hi = f32_to_f16_bits(v[hh]);
-            h16[(lb + h) * 8 + e] = hi;
-            l16[(lb + h) * 8 + e] = f32_to_f16_bits(v[hh] - f16_bits_to_f32(hi));
-          }
-        }
-      }
-    }
-  }
+  if (!PRE) qops_scatter<D>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlate);
   __syncthreads();   // also orders the prologue's reads of the ring before the first staging store
 
   // ---- query operands of the first k-steps in registers (zero past the last one)
-  f16x8 qh[kQRegSteps];
+  if (!PRE) {
 #pragma unroll
-  for (int ks = 0; ks < kQRegSteps; ++ks) {
-    const uint4 z = uint4{0u, 0u, 0u, 0u};
-    qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qhi[ks * 64 + lane] : z);
+    for (int ks = 0; ks < kQRegSteps; ++ks) {
+      const uint4 z = uint4{0u, 0u, 0u, 0u};
+      qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qhi[ks * 64 + lane] : z);
+    }
   }
 
   const uint4* kd = reinterpret_cast<const uint4*>(lds + kTcDesc);
@@ -1448,6 +1515,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 }
 
+// ---- decode step, first launch: the one-token append (workgroups 0 .. n_seqs - 1) beside the
+// rotated query of every (sequence, KV head) (the remaining workgroups), which depends only on
+// the layout and on the query position, not on the appended token.  The query workgroups
+// write the matrix-core B operands [k-step][hi, lo][64 lanes] to the workspace; lengths[] is
+// left to the merge kernel, so both roles read the old length: the query sits at that
+// position unless the append overflows the capacity (then at the last cached token, as a
+// separate decode call would place it).
+template <int D, typename QT>
+__device__ __forceinline__ void query_wg(const DecodeArgs& a, int s, int hk, uint8_t* lds) {
+  constexpr int NP = QShape<D>::NP, QI = QShape<D>::QI;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool mine = tid < 256;                       // waves 0-3 do the work
+  const size_t reg = size_t(s) * a.n_kv + hk;
+  const HeadLayout* L = a.layouts + reg;
+  const int nks = L->n_ksteps;
+  HeadLayout* const Ls = reinterpret_cast<HeadLayout*>(lds);
+  float* const qc = reinterpret_cast<float*>(lds + BGTQ_LAYOUT_BYTES);
+  uint4* const qhi = reinterpret_cast<uint4*>(lds + tc_qhi_off(D));
+  uint4* const qlo = qhi + 64 * kQRegSteps;
+  uint4* const qlate = qlo + 64 * kQRegSteps;
+  if (mine) {
+    const uint4 lw = reinterpret_cast<const uint4*>(L)[tid];
+    float x0[QI], x1[QI];
+    q_load<D, QT>(a, s, hk, tid, x0, x1);
+    const double fr = a.rope_theta > 0.0 ? a.inv_freq[tid % NP] : 0.0;
+    const int len0 = a.lengths[s];
+    const int64_t pos = len0 + 1 <= a.capacity ? int64_t(len0) : int64_t(len0) - 1;
+    reinterpret_cast<uint4*>(Ls)[tid] = lw;
+    qops_zero(qhi, qlo, qlate, nks, tid);
+    q_rope<D>(a, pos, fr, tid, x0, x1, qc);
+  }
+  __syncthreads();
+  if (mine) {
+    const uint32_t wmask = wide_ksteps(Ls, nks, lane);
+    qops_scatter<D>(a, Ls, qc, wmask, nks - __popc(wmask), tid, qhi, qlo, qlate);
+  }
+  __syncthreads();
+  uint4* dst = a.qpre + reg * tc_ksteps(D) * 128;
+  for (int i = tid; i < 128 * nks; i += blockDim.x) {
+    const int ks = i >> 7, part = (i >> 6) & 1, ln = i & 63;
+    dst[i] = ks < kQRegSteps ? (part == 0 ? qhi : qlo)[ks * 64 + ln] : qlate[(ks - kQRegSteps) * 128 + part * 64 + ln];
+  }
+}
+
+template <typename T, bool STAGE_V, int D, typename QT>
+__global__ __launch_bounds__(1024) void k_step_front(AppendArgs aa, DecodeArgs da, int n_seqs) {
+  extern __shared__ __align__(16) uint8_t lds8[];
+  if (int(blockIdx.x) < n_seqs) {
+    append_one_wg<T, STAGE_V>(aa, blockIdx.x, reinterpret_cast<float*>(lds8));
+  } else {
+    const int r = blockIdx.x - n_seqs;
+    query_wg<D, QT>(da, r / da.n_kv, r % da.n_kv, lds8);
+  }
+}
+
 // Merge the splits of one query head and undo the value rotation:
 // out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t], from the per-split
 // (m, l) pairs and accumulators; split i is weighted by exp2(m_i - max m).  Every split's
@@ -1528,6 +1650,10 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
     a.out[(int64_t(s) * a.n_q + h) * D + tid] = o * inv;
   }
+  if (a.step && h == 0 && tid == 0) {     // the decode step's length advance, after every reader
+    const int len0 = a.lengths[s];
+    if (len0 + 1 <= a.capacity) a.lengths[s] = len0 + 1;
+  }
 }
 
 template <int D>
@@ -1536,8 +1662,10 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st)
   if (a.use_mfma) {
     const int lds = tc_lds_bytes(D, a.chunks, a.v_bits);
     const bool narrow = a.chunks <= 4 && a.v_bits <= 4, bf16 = q_dt == BGTQ_BF16;
-    void (*fn)(DecodeArgs) = narrow ? (bf16 ? k_decode_mfma<D, true, uint16_t> : k_decode_mfma<D, true, float>)
-                                    : (bf16 ? k_decode_mfma<D, false, uint16_t> : k_decode_mfma<D, false, float>);
+    void (*fn)(DecodeArgs) =
+        a.qpre ? (narrow ? k_decode_mfma<D, true, float, true> : k_decode_mfma<D, false, float, true>)
+               : narrow ? (bf16 ? k_decode_mfma<D, true, uint16_t, false> : k_decode_mfma<D, true, float, false>)
+                        : (bf16 ? k_decode_mfma<D, false, uint16_t, false> : k_decode_mfma<D, false, float, false>);
     if (lds > 64 * 1024) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1569,9 +1697,45 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st)
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_step_front(const AppendArgs& aa, const DecodeArgs& da, bgtq_dtype kv_dt, bgtq_dtype q_dt,
+                             int n_seqs, hipStream_t st) {
+  constexpr bool SV = D <= 128;
+  const size_t q_lds = size_t(tc_qhi_off(D)) + size_t(1024) * (2 * kQRegSteps) +
+                       size_t(2048) * (tc_ksteps(D) > kQRegSteps ? tc_ksteps(D) - kQRegSteps : 0);
+  const size_t a_lds = append_one_lds_bytes(D, SV);
+  const size_t lds = q_lds > a_lds ? q_lds : a_lds;
+  const bool kb = kv_dt == BGTQ_BF16, qb = q_dt == BGTQ_BF16;
+  void (*fn)(AppendArgs, DecodeArgs, int) =
+      kb ? (qb ? k_step_front<uint16_t, SV, D, uint16_t> : k_step_front<uint16_t, SV, D, float>)
+         : (qb ? k_step_front<float, SV, D, uint16_t> : k_step_front<float, SV, D, float>);
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(n_seqs + da.batch * da.n_kv), dim3(1024), lds, st, aa, da, n_seqs);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // ===================================================================== launchers
+
+hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, bgtq_dtype kv_dt, bgtq_dtype q_dt,
+                              hipStream_t st) {
+  hipError_t e = hipSuccess;
+  switch (da.d) {
+    case 64: e = launch_step_front<64>(aa, da, kv_dt, q_dt, da.batch, st); break;
+    case 128: e = launch_step_front<128>(aa, da, kv_dt, q_dt, da.batch, st); break;
+    case 256: e = launch_step_front<256>(aa, da, kv_dt, q_dt, da.batch, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  return launch_decode(da, q_dt, st);
+}
+
+size_t decode_qpre_bytes(int batch, int n_kv_heads, int d) {
+  return size_t(batch) * n_kv_heads * tc_ksteps(d) * 2048;
+}
 
 hipError_t upload_tables(const Tables& t) {
   hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(c_thr), t.thr, sizeof(t.thr));

@@ -25,6 +25,6 @@ def prefill(quantizer, cache: bgtq.PackedCache, keys: torch.Tensor, values: torc
 def decode_step(quantizer, cache: bgtq.PackedCache, k_new: torch.Tensor, v_new: torch.Tensor,
                 q: torch.Tensor, rope_theta: float, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """k_new, v_new [batch, n_kv_heads, 1, head_dim]; q [batch, n_q_heads, head_dim] (pre-RoPE)."""
-    bgtq.bgtq_quantize_append(quantizer, cache, k_new, v_new, seq_begin=0)
-    return bgtq.bgtq_decode_attention(quantizer, cache, q, rope_theta, out=out, workspace=workspace)
+    """k_new, v_new [batch, n_kv_heads, 1, head_dim]; q [batch, n_q_heads, head_dim] (pre-RoPE).
+    One bgtq_decode_step call: the same result as appending, then attending."""
+    return bgtq.bgtq_decode_step(quantizer, cache, q, k_new, v_new, rope_theta, out=out, workspace=workspace)

@@ -215,6 +215,25 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
 size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                    int64_t capacity);
 
+/* One decode step (abstract: the serving path decodes token by token from the packed
+ * cache): for every sequence s of the cache, quantize and append one new key/value
+ * token, then attend with q at that token's position.  The result equals
+ * bgtq_quantize_append(n_new = 1, all sequences) followed by
+ * bgtq_decode_attention(q_pos = NULL), cache contents, lengths, status and out
+ * included; the rotated query is computed beside the append instead of after it.
+ *   keys, values  [batch][n_kv_heads][head_dim] of kv_dtype, element (s, h, c) at
+ *                 s * stride_seq + h * stride_head + c.
+ *   q, out, logits_out, workspace: as for bgtq_decode_attention (the same workspace
+ *   size serves both calls).
+ * A sequence whose append would exceed the capacity sets cache->status, keeps its
+ * length and is attended without the new token.
+ * Errors: those of the two calls it stands for. */
+bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads,
+                             const void* q, bgtq_dtype q_dtype, const void* keys, const void* values,
+                             bgtq_dtype kv_dtype, int64_t stride_seq, int64_t stride_head,
+                             double rope_theta, float softmax_scale, float* out, float* logits_out,
+                             void* workspace, size_t workspace_bytes, bgtq_stream stream);
+
 /* Bytes of each cache array for the given geometry (k_codes, k_norms, v_codes,
  * v_norms, in that order, written to out4); returns the total, 0 if invalid. */
 size_t bgtq_cache_bytes(int batch, int n_kv_heads, int head_dim, int k_width_sum, int v_bits,

@@ -143,6 +143,25 @@ def test_decode_validation():
     assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
 
 
+def test_decode_step_validation():
+    lib = bgtq.lib()
+    need = lib.bgtq_decode_workspace_bytes(1, 16, 2, 128, 256)
+
+    def call(desc, n_q=16, ws=need, qz=None, scale=0.088, kv=FAKE, kv_dtype=0, stride_head=128):
+        qz = qz or _quantizer()
+        return lib.bgtq_decode_step(ctypes.byref(qz), ctypes.byref(desc), n_q, FAKE, 0, kv, kv, kv_dtype,
+                                    256, stride_head, 1e6, scale, FAKE, None, FAKE, ws, None)
+
+    assert call(_desc(), n_q=15) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), n_q=34) == bgtq.ERR_UNSUPPORTED
+    assert call(_desc(), ws=need - 1) == bgtq.ERR_WORKSPACE
+    assert call(_desc(), scale=0.0) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), kv=None) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), kv_dtype=7) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), stride_head=0) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
+
+
 def test_status_strings():
     lib = bgtq.lib()
     for s in range(7):
