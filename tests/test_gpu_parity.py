@@ -200,7 +200,7 @@ def test_append_one_token_per_step_bit_exact(d, k_bits, v_bits, h_kv, prefill, s
 # ---------------------------------------------------------------- decode
 
 def _decode_vs_oracle(wl, t_lens, qz, bank, rv, dtype=torch.float32, append_then_attend=False, pairing=0,
-                      theta=None, check_logits=True):
+                      theta=None, check_logits=True, check_seqs=None):
     dev = _cuda()
     d, h_kv, g = wl.d, wl.h_kv, wl.group
     theta = wl.theta if theta is None else theta
@@ -225,6 +225,8 @@ def _decode_vs_oracle(wl, t_lens, qz, bank, rv, dtype=torch.float32, append_then
     out, logits = out.cpu().numpy(), logits.cpu().numpy()
     worst = 0.0
     for s, t_len in enumerate(t_lens):
+        if check_seqs is not None and s not in check_seqs:
+            continue
         k, v = kv[s]
         kx = torch.from_numpy(k).to(dtype).float().numpy()
         vx = torch.from_numpy(v).to(dtype).float().numpy()
@@ -330,3 +332,25 @@ def test_decode_qwen3b_layer_128k_full_size(rot128):
     bank, rv, qz = rot128
     wl = synth.QWEN3B_128K
     _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=True)
+
+
+def test_decode_qwen3b_layer_512k_full_size(rot128):
+    """The same shape at 512K context: prefill 524288 tokens, append one, attend over 524289."""
+    _say("decode qwen3b 512K full size")
+    bank, rv, qz = rot128
+    wl = synth.QWEN3B_512K
+    _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=False)
+
+
+def test_decode_qwen7b_ragged_batch_full_size(rot128):
+    """One layer of the 7B-Qwen-shaped ragged batch: 16 sequences of 8K..64K tokens, 28 q / 4 kv heads
+    (group 7), K3V2, all decoded in one call after a one-token append; the oracle checks the shortest,
+    the longest and two other sequences, every head."""
+    _say("decode qwen7b ragged batch of 16")
+    bank, rv, qz = rot128
+    wl = synth.QWEN7B_RAGGED
+    lens = list(wl.seq_lens)
+    order = sorted(range(len(lens)), key=lambda i: lens[i])
+    check = {order[0], order[-1], order[len(lens) // 3], order[2 * len(lens) // 3]}
+    _decode_vs_oracle(wl, [t + 1 for t in lens], qz, bank, rv, append_then_attend=True, check_logits=False,
+                      check_seqs=check)
