@@ -60,6 +60,9 @@ _SIGNATURES = {
     "bgtq_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i64]),
     "bgtq_decode_step": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _f64, _f32, _vp, _vp, _vp,
                                 _sz, _vp]),
+    "bgtq_logit_error": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64,
+                                _i32, _f64, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "bgtq_logit_error_workspace_bytes": (_sz, [_i32, _i32, _i64]),
     "bgtq_cache_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _vp]),
     "bgtq_codebook": (_i32, [_i32, _vp, _vp, _vp]),
     "bgtq_init": (_i32, []),
@@ -320,3 +323,43 @@ def bgtq_decode_step(quantizer: Quantizer, cache: PackedCache, q: torch.Tensor, 
                                   k_new.stride(1), float(rope_theta), float(scale), out.data_ptr(), _ptr(lg),
                                   workspace.data_ptr(), workspace.numel(), _stream()))
     return (out, lg) if logits is not False else out
+
+
+def logit_error_workspace_bytes(batch, n_q_heads, capacity) -> int:
+    return int(lib().bgtq_logit_error_workspace_bytes(batch, n_q_heads, capacity))
+
+
+def bgtq_logit_error(q: torch.Tensor, keys: torch.Tensor, lengths: torch.Tensor, logits: torch.Tensor,
+                     rope_theta: float, softmax_scale: float | None = None, q_pos: torch.Tensor | None = None,
+                     pairing: int = PAIR_HALF, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Mean |logits - exact logits| per (sequence, query head), fp64 [batch, n_q_heads].
+
+    q [batch, n_q_heads, head_dim] pre-RoPE; keys [batch, n_kv_heads, tokens, head_dim] post-RoPE
+    (last dimension contiguous); lengths int32 [batch]; logits fp32 [batch, n_q_heads, capacity]."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, n_q_heads, head_dim] tensor")
+    b, hq, d = q.shape
+    if keys.dim() != 4 or keys.shape[0] != b or keys.shape[3] != d or keys.stride(3) != 1:
+        raise ValueError("keys must be [batch, n_kv_heads, tokens, head_dim] with a contiguous last dimension")
+    if logits.dim() != 3 or logits.shape[:2] != (b, hq) or not logits.is_contiguous() \
+            or logits.dtype != torch.float32:
+        raise ValueError("logits must be contiguous fp32 [batch, n_q_heads, capacity]")
+    if lengths.dtype != torch.int32 or lengths.numel() != b:
+        raise ValueError("lengths must be int32 [batch]")
+    if q_pos is not None and (q_pos.dtype != torch.int64 or q_pos.numel() != b):
+        raise ValueError("q_pos must be int64 [batch]")
+    cap = logits.shape[2]
+    if keys.shape[2] < cap:
+        raise ValueError("keys must hold capacity tokens (only those below lengths are read)")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if out is None:
+        out = torch.empty((b, hq), dtype=torch.float64, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(logit_error_workspace_bytes(b, hq, cap), dtype=torch.uint8, device=q.device)
+    _check(lib().bgtq_logit_error(q.data_ptr(), _dtype_code(q), _ptr(q_pos), keys.data_ptr(), _dtype_code(keys), b,
+                                  hq, keys.shape[1], d, keys.stride(0), keys.stride(1), keys.stride(2),
+                                  lengths.data_ptr(), cap, pairing, float(rope_theta), float(scale),
+                                  logits.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                  _stream()))
+    return out

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbgtq.so")
-SOURCES = ["api.cpp", "lloyd_max.cpp", "kernels.hip"]
+SOURCES = ["api.cpp", "lloyd_max.cpp", "kernels.hip", "diagnostic.hip"]
 
 ARCH = os.environ.get("BGTQ_OFFLOAD_ARCH", "gfx950")
 

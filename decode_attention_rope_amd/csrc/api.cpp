@@ -344,4 +344,63 @@ bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, 
   return hip_status(launch_decode_step(aa, da, kv_dtype, q_dtype, s), "decode-step launch");
 }
 
+size_t bgtq_logit_error_workspace_bytes(int batch, int n_q_heads, int64_t capacity) {
+  if (batch < 1 || n_q_heads < 1 || capacity < 1) return 0;
+  return align256(size_t(batch) * n_q_heads * size_t((capacity + kErrChunk - 1) / kErrChunk) * 8);
+}
+
+bgtq_status bgtq_logit_error(const void* q, bgtq_dtype q_dtype, const int64_t* q_pos, const void* keys,
+                             bgtq_dtype k_dtype, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                             int64_t stride_seq, int64_t stride_head, int64_t stride_token,
+                             const int32_t* lengths, int64_t capacity, bgtq_pairing pairing,
+                             double rope_theta, float softmax_scale, const float* logits, double* mae_out,
+                             void* workspace, size_t workspace_bytes, bgtq_stream stream) {
+  if (!q || !keys || !lengths || !logits || !mae_out)
+    return fail(BGTQ_ERR_INVALID_ARG, "q, keys, lengths, logits and mae_out must not be NULL");
+  if (q_dtype != BGTQ_F32 && q_dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad q dtype");
+  if (k_dtype != BGTQ_F32 && k_dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad key dtype");
+  if (pairing != BGTQ_PAIR_HALF && pairing != BGTQ_PAIR_INTERLEAVED) return fail(BGTQ_ERR_INVALID_ARG, "bad pairing");
+  if (batch < 1 || n_kv_heads < 1) return fail(BGTQ_ERR_INVALID_ARG, "batch and n_kv_heads must be >= 1");
+  if (n_q_heads < n_kv_heads || n_q_heads % n_kv_heads)
+    return fail(BGTQ_ERR_INVALID_ARG, "n_q_heads %d must be a multiple of n_kv_heads %d", n_q_heads, n_kv_heads);
+  const int group = n_q_heads / n_kv_heads;
+  if (group > BGTQ_MAX_GROUP) return fail(BGTQ_ERR_UNSUPPORTED, "group size %d > %d", group, BGTQ_MAX_GROUP);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(BGTQ_ERR_UNSUPPORTED, "the logit error is built for head_dim 64/128/256");
+  if (capacity < 1) return fail(BGTQ_ERR_INVALID_ARG, "capacity must be >= 1");
+  if (capacity % 4) return fail(BGTQ_ERR_INVALID_ARG, "capacity must be a multiple of 4");
+  if (stride_seq < 0 || stride_head < 0 || stride_token < head_dim || stride_seq % 4 || stride_head % 4 ||
+      stride_token % 4)
+    return fail(BGTQ_ERR_INVALID_ARG, "key strides must be multiples of 4 with stride_token >= head_dim");
+  const uintptr_t kal = k_dtype == BGTQ_F32 ? 16 : 8;
+  if (reinterpret_cast<uintptr_t>(keys) % kal || reinterpret_cast<uintptr_t>(logits) % 16)
+    return fail(BGTQ_ERR_INVALID_ARG, "keys or logits misaligned");
+  if (!(softmax_scale > 0.0f)) return fail(BGTQ_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  const size_t need = bgtq_logit_error_workspace_bytes(batch, n_q_heads, capacity);
+  if (!workspace || workspace_bytes < need) return fail(BGTQ_ERR_WORKSPACE, "logit-error workspace needs %zu bytes", need);
+  LogitErrArgs a{};
+  a.q = q;
+  a.q_pos = q_pos;
+  a.keys = keys;
+  a.stride_seq = stride_seq;
+  a.stride_head = stride_head;
+  a.stride_token = stride_token;
+  a.lengths = lengths;
+  a.logits = logits;
+  a.partial = static_cast<double*>(workspace);
+  a.mae = mae_out;
+  a.rope_theta = rope_theta;
+  for (int j = 0; j < head_dim / 2; ++j) a.inv_freq[j] = rope_theta > 0.0 ? std::pow(rope_theta, -2.0 * j / head_dim) : 0.0;
+  a.scale = softmax_scale;
+  a.capacity = capacity;
+  a.batch = batch;
+  a.n_q = n_q_heads;
+  a.n_kv = n_kv_heads;
+  a.group = group;
+  a.d = head_dim;
+  a.pairing = pairing;
+  a.n_chunk = int((capacity + kErrChunk - 1) / kErrChunk);
+  return hip_status(launch_logit_error(a, k_dtype, q_dtype, static_cast<hipStream_t>(stream)), "logit-error launch");
+}
+
 }  // extern "C"

@@ -148,6 +148,25 @@ hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, bgtq_d
                               hipStream_t s);
 size_t decode_qpre_bytes(int batch, int n_kv_heads, int d);
 
+// key-only logit error (diagnostic.hip)
+constexpr int kErrChunk = 256;       // tokens per workgroup and per partial sum
+struct LogitErrArgs {
+  const void* q;
+  const int64_t* q_pos;
+  const void* keys;
+  int64_t stride_seq, stride_head, stride_token;
+  const int32_t* lengths;
+  const float* logits;
+  double* partial;    // [batch][n_q][n_chunk] per-chunk sums of |error|
+  double* mae;        // [batch][n_q]
+  double rope_theta;
+  double inv_freq[BGTQ_MAX_HEAD_DIM / 2];
+  float scale;
+  int64_t capacity;
+  int batch, n_q, n_kv, group, d, pairing, n_chunk;
+};
+hipError_t launch_logit_error(const LogitErrArgs& a, bgtq_dtype k_dt, bgtq_dtype q_dt, hipStream_t s);
+
 hipError_t launch_transpose_rotations(const float* rot_bank, const float* rot_v, int d, float* rot_bank_t,
                                       float* rot_v_t, hipStream_t s);
 

@@ -98,6 +98,23 @@ def qwen7b_ragged(seed: int = 0) -> Workload:
 
 QWEN7B_RAGGED = qwen7b_ragged()
 
+def diagnostic_panel(tokens: int = 4096, layers: int = 4) -> list:
+    """Synthetic stand-ins for a panel of models in the key-only logit-error diagnostic: five
+    head shapes (head_dim 64/128/256, group sizes 1 to 8) and the three energy profiles, one
+    sequence of `tokens` cached tokens, `layers` layers each (k_bits is overridden per run)."""
+    def w(name, wid, d, h_q, h_kv, theta, profile, key_dtype="f32", outliers=2, elem_p=0.0):
+        return Workload(name, wid, d=d, h_q=h_q, h_kv=h_kv, theta=theta, layers=layers, seq_lens=(tokens,),
+                        k_bits=3, v_bits=3, key_dtype=key_dtype, profile=profile, outlier_blocks=outliers,
+                        elem_outlier_p=elem_p)
+    return [
+        w("panel_d128_g4_loguniform_bf16", 21, 128, 32, 8, 5e5, "loguniform", "bf16", 0, 0.01),
+        w("panel_d128_g8_decay_jitter", 22, 128, 16, 2, 1e6, "decay_jitter"),
+        w("panel_d128_g7_decay", 23, 128, 28, 4, 1e6, "decay"),
+        w("panel_d64_g1_decay", 24, 64, 8, 8, 1e4, "decay"),
+        w("panel_d256_g8_decay_jitter", 25, 256, 8, 1, 1e6, "decay_jitter"),
+    ]
+
+
 WORKLOADS = {w.name: w for w in (TINY, LLAMA8B_LAYER, QWEN3B_128K, QWEN3B_512K, QWEN7B_RAGGED)}
 
 

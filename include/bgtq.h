@@ -234,6 +234,36 @@ bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, 
                              double rope_theta, float softmax_scale, float* out, float* logits_out,
                              void* workspace, size_t workspace_bytes, bgtq_stream stream);
 
+/* Key-only logit error (abstract: Block-GTQ is judged on how well it keeps the RoPE
+ * query-key logits, as the per-layer mean absolute logit error when only keys are quantized,
+ * at 2 and 3 bits per coordinate, against uniform TQ-MSE at the same budget).
+ * For every sequence s and query head h (KV head h / (n_q_heads/n_kv_heads)), with
+ * T_s = min(lengths[s], capacity): q' = RoPE(q[s][h], pos) as in bgtq_decode_attention (fp64
+ * angles reduced modulo 2*pi), exact logits e_t = softmax_scale * q' . k_t from the unquantized
+ * post-RoPE keys, and
+ *     mae_out[s][h] = (1/T_s) * sum_{t < T_s} |logits[s][h][t] - e_t|   (0 when T_s == 0),
+ * where `logits` is what bgtq_decode_attention wrote to logits_out for the same q, q_pos,
+ * rope_theta and softmax_scale over the quantized cache.  The exact logits are fp32 products
+ * and sums; the absolute errors are summed in fp64 in a fixed order (reproducible).
+ *   q           [batch][n_q_heads][head_dim] of q_dtype, pre-RoPE (contiguous).
+ *   q_pos       int64 [batch] (device) or NULL for lengths[s] - 1.
+ *   keys        post-RoPE keys of k_dtype, element (s, h, t, c) at
+ *               s * stride_seq + h * stride_head + t * stride_token + c; tokens t < T_s are read.
+ *               Strides must be multiples of 4 and the pointer 16-byte aligned (8 for bf16).
+ *   lengths     int32 [batch] (device), e.g. the cache's lengths.
+ *   logits      fp32 [batch][n_q_heads][capacity], 16-byte aligned.
+ *   mae_out     fp64 [batch][n_q_heads].
+ *   workspace   >= bgtq_logit_error_workspace_bytes(batch, n_q_heads, capacity); no
+ *               initial contents needed.
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim not 64/128/256, group size > 16), WORKSPACE, HIP. */
+bgtq_status bgtq_logit_error(const void* q, bgtq_dtype q_dtype, const int64_t* q_pos, const void* keys,
+                             bgtq_dtype k_dtype, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                             int64_t stride_seq, int64_t stride_head, int64_t stride_token,
+                             const int32_t* lengths, int64_t capacity, bgtq_pairing pairing,
+                             double rope_theta, float softmax_scale, const float* logits, double* mae_out,
+                             void* workspace, size_t workspace_bytes, bgtq_stream stream);
+size_t bgtq_logit_error_workspace_bytes(int batch, int n_q_heads, int64_t capacity);
+
 /* Bytes of each cache array for the given geometry (k_codes, k_norms, v_codes,
  * v_norms, in that order, written to out4); returns the total, 0 if invalid. */
 size_t bgtq_cache_bytes(int batch, int n_kv_heads, int head_dim, int k_width_sum, int v_bits,

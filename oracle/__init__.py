@@ -19,7 +19,9 @@ mirrored on the other pages.  The abstract fixes the structure of the method:
 * keys are quantized with TurboQuant-MSE at those widths and values at a
   uniform width (``codebook``, ``layout``, ``quantize``);
 * a packed-cache serving path attends directly over the packed cache
-  (``pack``, ``decode``).
+  (``pack``, ``decode``);
+* the method is judged by the key-only RoPE logit error against uniform
+  TQ-MSE at the same budget (``diagnostic``).
 
 Everything numeric that the abstract leaves open is a stated reading; each
 function names the reading it follows.  Floating point is fp64 except where
@@ -31,4 +33,4 @@ closed form, a textbook value, brute force or a library routine; none is
 which is not available.
 """
 
-# submodules: codebook, rope, energy, allocate, layout, quantize, pack, decode
+# submodules: codebook, rope, energy, allocate, layout, quantize, pack, decode, diagnostic

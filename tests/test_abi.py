@@ -162,6 +162,33 @@ def test_decode_step_validation():
     assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
 
 
+def test_logit_error_validation():
+    lib = bgtq.lib()
+    need = lib.bgtq_logit_error_workspace_bytes(2, 16, 1024)
+    assert need == 2 * 16 * 4 * 8
+    assert lib.bgtq_logit_error_workspace_bytes(0, 16, 1024) == 0
+
+    def call(q=FAKE, keys=FAKE, n_q=16, n_kv=2, d=128, strides=(2 * 1024 * 128, 1024 * 128, 128), cap=1024,
+             ws=need, scale=0.088, k_dtype=0, pairing=0, logits=FAKE):
+        return lib.bgtq_logit_error(q, 0, None, keys, k_dtype, 2, n_q, n_kv, d, *strides, FAKE, cap, pairing, 1e6,
+                                    scale, logits, FAKE, FAKE, ws, None)
+
+    assert call(q=None) == bgtq.ERR_INVALID_ARG
+    assert call(keys=None) == bgtq.ERR_INVALID_ARG
+    assert call(n_q=15) == bgtq.ERR_INVALID_ARG
+    assert call(n_q=34) == bgtq.ERR_UNSUPPORTED
+    assert call(d=96, strides=(96, 96, 96)) == bgtq.ERR_UNSUPPORTED
+    assert call(ws=need - 1) == bgtq.ERR_WORKSPACE
+    assert call(scale=0.0) == bgtq.ERR_INVALID_ARG
+    assert call(k_dtype=3) == bgtq.ERR_INVALID_ARG
+    assert call(pairing=2) == bgtq.ERR_INVALID_ARG
+    assert call(strides=(0, 0, 64)) == bgtq.ERR_INVALID_ARG          # stride_token < head_dim
+    assert call(strides=(0, 0, 130)) == bgtq.ERR_INVALID_ARG         # not a multiple of 4
+    assert call(cap=1022) == bgtq.ERR_INVALID_ARG
+    assert call(keys=FAKE + 4) == bgtq.ERR_INVALID_ARG               # misaligned fp32 keys
+    assert call(logits=FAKE + 8) == bgtq.ERR_INVALID_ARG
+
+
 def test_status_strings():
     lib = bgtq.lib()
     for s in range(7):
