@@ -27,6 +27,7 @@ PAIR_HALF, PAIR_INTERLEAVED = 0, 1
 TILE = 64
 MAX_GROUPS = 8
 LAYOUT_BYTES = 4096
+MAX_WINDOW = 4096
 
 _c = ctypes
 _vp, _i32, _i64, _sz, _f32, _f64 = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_size_t, _c.c_float, _c.c_double
@@ -46,7 +47,8 @@ class CacheDesc(_c.Structure):
     _fields_ = [("batch", _i32), ("n_kv_heads", _i32), ("head_dim", _i32), ("k_width_sum", _i32),
                 ("v_bits", _i32), ("capacity", _i64), ("pairing", _i32),
                 ("k_codes", _vp), ("k_norms", _vp), ("v_codes", _vp), ("v_norms", _vp),
-                ("lengths", _vp), ("widths", _vp), ("layouts", _vp), ("status", _vp)]
+                ("lengths", _vp), ("widths", _vp), ("layouts", _vp), ("status", _vp),
+                ("window", _i32), ("k_window", _vp)]
 
 
 _SIGNATURES = {
@@ -172,6 +174,7 @@ class PackedCache:
     capacity: int
     pairing: int = PAIR_HALF
     device: str = "cuda"
+    window: int = 0           # fp16 recent-key window in tokens (0: none)
 
     def __post_init__(self):
         _, (kc, kn, vc, vn) = cache_bytes(self.batch, self.n_kv_heads, self.head_dim, self.k_width_sum,
@@ -186,6 +189,9 @@ class PackedCache:
         self.layouts = torch.zeros((self.batch, self.n_kv_heads, LAYOUT_BYTES), dtype=torch.uint8, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.k_chunks = -(-2 * self.k_width_sum // 128)
+        # fp16 keys of the newest `window` tokens, token t at slot t % window (as uint16 bits)
+        self.k_window = (torch.zeros((self.batch, self.n_kv_heads, self.window, self.head_dim), dtype=torch.int16,
+                                     device=dev) if self.window > 0 else None)
 
     @property
     def nbytes(self) -> int:
@@ -196,7 +202,8 @@ class PackedCache:
         return CacheDesc(self.batch, self.n_kv_heads, self.head_dim, self.k_width_sum, self.v_bits,
                          self.capacity, self.pairing, self.k_codes.data_ptr(), self.k_norms.data_ptr(),
                          self.v_codes.data_ptr(), self.v_norms.data_ptr(), self.lengths.data_ptr(),
-                         self.widths.data_ptr(), self.layouts.data_ptr(), self.status.data_ptr())
+                         self.widths.data_ptr(), self.layouts.data_ptr(), self.status.data_ptr(), self.window,
+                         _ptr(self.k_window))
 
     def region(self, seq: int, head: int) -> dict:
         """Host copies of one (sequence, KV head) region, shaped like the oracle's pack_region."""

@@ -66,6 +66,9 @@ bgtq_status check_cache(const bgtq_cache* c, bool need_layout) {
   if (!c->k_norms || !c->v_codes || !c->v_norms || !c->lengths)
     return fail(BGTQ_ERR_INVALID_ARG, "cache arrays must not be NULL");
   if (need_layout && !c->layouts) return fail(BGTQ_ERR_INVALID_ARG, "layouts is NULL");
+  if (c->window < 0 || c->window > BGTQ_MAX_WINDOW)
+    return fail(BGTQ_ERR_INVALID_ARG, "window %d outside [0, %d]", c->window, BGTQ_MAX_WINDOW);
+  if (c->window > 0 && !c->k_window) return fail(BGTQ_ERR_INVALID_ARG, "k_window is NULL");
   return BGTQ_OK;
 }
 
@@ -215,6 +218,8 @@ static bgtq_status prepare_append(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.d = cache->head_dim;
   a.v_bits = cache->v_bits;
   a.chunks = record_chunks(cache->k_width_sum);
+  a.window = cache->window;
+  a.k_window = cache->window > 0 ? cache->k_window : nullptr;
   return BGTQ_OK;
 }
 
@@ -232,7 +237,7 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
 
 size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t capacity) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || capacity < kTile) return 0;
-  const int splits = decode_splits(batch, n_kv_heads, capacity, true);
+  const int splits = decode_splits(batch, n_kv_heads, capacity, true) + kMaxWindowSplits;
   const size_t part = align256(size_t(batch) * n_q_heads * splits * head_dim * 4) +
                       align256(size_t(batch) * n_q_heads * splits * 8);
   return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + part +
@@ -276,7 +281,12 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.logits = logits_out;
   const char* which = std::getenv("BGTQ_DECODE_KERNEL");
   a.use_mfma = group <= 8 && !(which && std::strcmp(which, "valu") == 0);
-  a.n_split = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma);
+  if (cache->window > 0 && !a.use_mfma)
+    return fail(BGTQ_ERR_UNSUPPORTED, "the recent-key window is built on the matrix-core decode (group size <= 8)");
+  a.window = cache->window;
+  a.k_window = cache->window > 0 ? cache->k_window : nullptr;
+  a.n_wsplit = window_splits(cache->window);
+  a.n_split = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma) + a.n_wsplit;
   char* ws = static_cast<char*>(workspace);
   const size_t qrot_b = align256(decode_qrot_bytes(cache->batch, cache->n_kv_heads, d));
   a.qrot = reinterpret_cast<float*>(ws);

@@ -77,6 +77,9 @@ inline size_t rot_bank_offset(int m) {  // floats before the m x m matrix (m eve
   return o;
 }
 int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma);
+// splits that attend over a window of w tokens (at most two 64-token tiles each)
+inline int window_splits(int w) { return w > 0 ? ((w + kTile - 1) / kTile + 2) / 2 : 0; }
+constexpr int kMaxWindowSplits = (BGTQ_MAX_WINDOW / kTile + 2) / 2;
 size_t decode_qrot_bytes(int batch, int n_kv_heads, int d);
 
 // ---------------------------------------------------------------- launchers (kernels.hip)
@@ -112,6 +115,8 @@ struct AppendArgs {
   int v_bits;
   int chunks;
   int advance;        // the one-token kernel advances lengths[] (a decode step leaves that to the merge)
+  uint16_t* k_window; // fp16 recent keys [batch][n_kv][window][d], token t at slot t % window
+  int window;         // 0: no window
 };
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s);
 
@@ -140,6 +145,9 @@ struct DecodeArgs {
   int batch, n_q, n_kv, group, d, v_bits, chunks, n_split, pairing;
   int step;           // decode step: one token was appended after lengths were read (see k_step_front)
   int use_mfma;
+  const uint16_t* k_window;   // fp16 recent keys (see AppendArgs)
+  int window;                 // 0: no window
+  int n_wsplit;               // the last n_wsplit splits attend over the window's tokens
 };
 hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s);
 // decode step on the matrix-core path: append one token per sequence and attend (da.qpre set,

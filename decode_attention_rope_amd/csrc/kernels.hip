@@ -39,6 +39,10 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t u) {
   return (float)__builtin_bit_cast(_Float16, u);
 }
+// fp16 of a key kept in the recent-key window: nearest-even, saturated at +-65504
+__device__ __forceinline__ uint16_t f16_sat_bits(float x) {
+  return f32_to_f16_bits(fminf(fmaxf(x, -65504.0f), 65504.0f));
+}
 
 // Orders LDS traffic between lanes of one wavefront (all lanes run in lockstep).
 __device__ __forceinline__ void wave_sync() {
@@ -468,7 +472,7 @@ __host__ __device__ inline size_t append_one_lds_bytes(int d, bool stage_v) {
   return size_t(kAppendThrFloats) * 4 + (stage_v ? size_t(d) * (d + 1) * 4 : 0);
 }
 
-template <typename T, bool STAGE_V>
+template <typename T, bool STAGE_V, bool WIN>
 __device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float* dyn) {
   constexpr int HP = 2;
   constexpr int DM = BGTQ_MAX_HEAD_DIM;
@@ -575,16 +579,36 @@ __device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float
       if (t >= 256 && t < 256 + ng) kn[(t - 256) * kTile + slot] = f32_to_f16_bits(fminf(nrm[hp][t - 256], 65504.0f));
       if (t == 256 + kMaxGroups)
         a.v_norms[(reg * tiles + tile) * kTile + slot] = f32_to_f16_bits(fminf(nrm[hp][kMaxGroups], 65504.0f));
+      // the key's fp16 copy in the recent-key window, last (off the path of the packed stores)
+      if (WIN && t >= 512 - d)
+        a.k_window[(reg * a.window + len % a.window) * d + (t - (512 - d))] = f16_sat_bits(ko[hp][t - (512 - d)]);
     }
     __syncthreads();
   }
   if (tid == 0 && a.advance) a.lengths[s] = int32_t(len + 1);
 }
 
-template <typename T, bool STAGE_V>
+template <typename T, bool STAGE_V, bool WIN>
 __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
   extern __shared__ __align__(16) float dyn[];
-  append_one_wg<T, STAGE_V>(a, blockIdx.x, dyn);
+  append_one_wg<T, STAGE_V, WIN>(a, blockIdx.x, dyn);
+}
+
+// fp16 keys of the appended tokens that end up among the newest `window` (the last
+// min(n_new, window) of them), at slot t % window; runs before the length advance.
+template <typename T>
+__global__ __launch_bounds__(256) void k_window_store(AppendArgs a) {
+  const int si = blockIdx.z, s = a.seq_begin + si, hk = blockIdx.y;
+  const int64_t len = a.lengths[s];
+  if (len + a.n_new > a.capacity) return;          // the append itself is skipped
+  const int64_t m = a.n_new < a.window ? a.n_new : a.window;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= m * a.d) return;
+  const int64_t i = a.n_new - m + idx / a.d;       // token of the append
+  const int c = int(idx % a.d);
+  const T* kin = static_cast<const T*>(a.keys) + si * a.stride_seq + int64_t(hk) * a.stride_head;
+  const size_t reg = size_t(s) * a.n_kv_heads + hk;
+  a.k_window[(reg * a.window + (len + i) % a.window) * a.d + c] = f16_sat_bits(load_f(kin, i * a.stride_token + c));
 }
 
 __global__ void k_advance(int32_t* __restrict__ lengths, int seq_begin, int n_seqs, int64_t n_new,
@@ -1137,7 +1161,7 @@ __device__ __forceinline__ void qops_scatter(const DecodeArgs& a, const HeadLayo
   }
 }
 
-template <int D, bool NARROW, typename QT, bool PRE>
+template <int D, bool NARROW, typename QT, bool PRE, bool WIN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_mfma(DecodeArgs a) {
   constexpr int CPW = D / 4;                          // value coordinates per wave
   constexpr int MTV = CPW / 16;                       // value M-tiles per wave
@@ -1151,10 +1175,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // advanced by the merge kernel, so it still holds the old length here
   const int len0 = a.lengths[s];
   const int len = a.step && len0 + 1 <= a.capacity ? len0 + 1 : len0;
-  const int tiles = (len + kTile - 1) / kTile;
-  // split i takes tiles [i T / n, (i + 1) T / n): counts differ by at most one
-  const int t0 = int(int64_t(split) * tiles / a.n_split);
-  const int t1 = int(int64_t(split + 1) * tiles / a.n_split);
+  // Tokens [0, pend) are attended from the packed keys by the first n_split - n_wsplit
+  // splits; with a window (WIN), the window's tokens [pend, len) from their fp16 keys by the
+  // last n_wsplit splits (workgroup-uniform role).  Each role's tiles are shared out so that
+  // split i of n takes tiles [i T / n, (i + 1) T / n) of the role's T tiles: counts differ by
+  // at most one.
+  const int pend = !WIN ? len : (len > a.window ? len - a.window : 0);
+  const int n_ps = WIN ? a.n_split - a.n_wsplit : a.n_split;
+  const bool win = WIN && split >= n_ps;
+  int t0, t1, vlo, vhi;                              // tiles, and the role's token range
+  if (!win) {
+    const int tiles = (pend + kTile - 1) / kTile;
+    t0 = int(int64_t(split) * tiles / n_ps);
+    t1 = int(int64_t(split + 1) * tiles / n_ps);
+    vlo = 0;
+    vhi = pend;
+  } else {
+    const int first = pend / kTile, tiles = pend < len ? (len + kTile - 1) / kTile - first : 0;
+    t0 = first + int(int64_t(split - n_ps) * tiles / a.n_wsplit);
+    t1 = first + int(int64_t(split - n_ps + 1) * tiles / a.n_wsplit);
+    vlo = pend;
+    vhi = len;
+  }
   const int count = t1 - t0;
   const int bv = a.v_bits, chunks = a.chunks;
   const TcStage geo = tc_stage(D, chunks, bv);
@@ -1174,7 +1216,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // Every lane loads and stores (no divergent memory operations): lanes past the last
   // 16-byte unit repeat the last unit, writing the same bytes to the same place.  A head
   // whose K budget is zero has no K records (chunks == 0): nothing is staged for K.
-  const bool has_k = chunks > 0;
+  const bool has_k = chunks > 0 && !win;
   uint32_t ksrc[MAXNK], kdst[MAXNK], vdst[MAXNV];
 #pragma unroll
   for (int i = 0; i < MAXNK; ++i) {
@@ -1240,7 +1282,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       if (tid + 256 * i < kSingleHalves) st[i] = c_single[tid + 256 * i];
     float x0[QI], x1[QI];
     double fr = 0.0;
-    if (PRE) {
+    if (PRE && !win) {
 #pragma unroll
       for (int ks = 0; ks < kQRegSteps; ++ks) {
         const uint4 z = uint4{0u, 0u, 0u, 0u};
@@ -1273,7 +1315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const int ln = (i >> 2) & 63;      // lane of the 16-byte B operand
       if ((ln & 15) >= 8) pw[i] = 0u;
     }
-    if (!PRE) {
+    if (!PRE || win) {
       qops_zero(qhi, qlo, qlate, nks, tid);
       q_rope<D>(a, a.q_pos ? a.q_pos[s] : int64_t(len) - 1, fr, tid, x0, x1, qc);
     }
@@ -1304,16 +1346,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       kn[i < nks ? kperm_of(wmask, nn, i) : i] = (32u * (kg & 0xffu)) | ((32u * ((kg >> 8) & 0xffu)) << 16);
     }
   }
-  if (!PRE) qops_scatter<D>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlate);
+  if (WIN && win) {
+    // window role: B operand of k-step ks (coordinates 32 ks .. 32 ks + 31 in their original
+    // order), lane (n, j): q'[head n][32 ks + 8 j + e] * softmax_scale * log2(e), fp16 high
+    // part in registers and remainder in LDS; heads >= G and columns 8..15 are zero
+    const float kscale = a.scale * kLog2e;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      f16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = n < a.group ? qc[8 * (32 * ks + 8 * j + e) + n] * kscale : 0.0f;
+        hi[e] = (_Float16)v;
+        lo[e] = (_Float16)(v - float(hi[e]));
+      }
+      qh[ks] = hi;
+      qlo[ks * 64 + lane] = __builtin_bit_cast(uint4, lo);
+    }
+  } else if (!PRE) {
+    qops_scatter<D>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlate);
+  }
   __syncthreads();   // also orders the prologue's reads of the ring before the first staging store
 
   // ---- query operands of the first k-steps in registers (zero past the last one)
-  if (!PRE) {
+  if (!PRE && !win) {
 #pragma unroll
     for (int ks = 0; ks < kQRegSteps; ++ks) {
       const uint4 z = uint4{0u, 0u, 0u, 0u};
       qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qhi[ks * 64 + lane] : z);
     }
+    // the high parts sit in the ring's space: when some wave's staging reaches them, every
+    // wave must hold its operands before the first staging store
+    if (4 * geo.bytes > tc_qhi_off(D)) __syncthreads();
   }
 
   const uint4* kd = reinterpret_cast<const uint4*>(lds + kTcDesc);
@@ -1335,87 +1399,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const bool real_col = n < a.group;
   float* mx = reinterpret_cast<float*>(lds + kTcMx);   // [8 heads][4 waves][4 lane groups]
 
-  // every load issued so far (query operands, set-up reads) is complete here, so the only
-  // loads in flight inside the loop are the next tile's
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int it = 0; it < count; ++it) {
-    const int tile = t0 + it;
-    const int valid = len - tile * kTile < kTile ? len - tile * kTile : kTile;
-    store_tile();                             // this wave's staging is read only by this wave
-    asm volatile("" ::: "memory");            // issue the next tile's loads after these stores
-    if (it + 1 < count) load_tile(it + 1);
-
-    // ---- logits of tokens 16 wave + n (A rows).  Pass A issues a chunk's window reads and
-    // level lookups (k-steps narrower than 5 bits), pass B runs the matrix cores on them;
-    // wide k-steps are decoded separately afterwards.
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-    auto mfma_kstep = [&](const u32x4& raw, const f16x8& bh, const f16x8& bl, const f16x4& nv) {
-      const f16x8 A = __builtin_bit_cast(f16x8, raw);
-      f32x4 T = {0.f, 0.f, 0.f, 0.f};
-      T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, T, 0, 0, 0);
-      T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, T, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[r] = fmaf(T[r], float(nv[r]), S[r]);
-    };
-    // narrow k-steps in chunks of 4, 2 and 2 (a chunk past the last narrow k-step is skipped;
-    // inside the last one, slots past it are decoded but not multiplied)
-    auto narrow_chunk = [&](auto kc_c, auto kn_c) {
-      constexpr int kc = decltype(kc_c)::value, KC = decltype(kn_c)::value;
-      {
-        u32x4 raw[KC];
-        f16x4 nrm[KC];
-        uint32_t wd0[KC], wd1[KC], ctl[KC];
-#pragma unroll
-        for (int q = 0; q < KC; ++q) {
-          const uint2 d = *reinterpret_cast<const uint2*>(kd + 4 * (kc + q) + j);
-          ctl[q] = d.y;
-          wd0[q] = lds_u32(buf, krec + d.x);
-          wd1[q] = lds_u32(buf, krec + d.x + 4);
-          nrm[q] = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[kc + q] >> nsh) & 0xffffu));
-        }
-#pragma unroll
-        for (int q = 0; q < KC; ++q) {
-          const uint32_t x = __builtin_amdgcn_alignbit(wd1[q], wd0[q], ctl[q]);   // shift = ctl & 31
-          const uint32_t w2 = ctl[q] >> 8;                                          // low 5 bits: 2w
-          const uint32_t o4 = w2 << 1, o6 = w2 + o4, tb = ctl[q] >> 16;
-          raw[q][0] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, 0u, w2));
-          raw[q][1] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, w2, w2));
-          raw[q][2] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, o4, w2));
-          raw[q][3] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, o6, w2));
-        }
-#pragma unroll
-        for (int q = 0; q < KC; ++q)
-          if (kc + q < nn) mfma_kstep(raw[q], qh[kc + q], __builtin_bit_cast(f16x8, qlo[(kc + q) * 64 + lane]), nrm[q]);
-      }
-    };
-    static_assert(kQRegSteps == 8, "chunks 4 + 2 + 2");
-    if (0 < nn) narrow_chunk(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
-    if (4 < nn) narrow_chunk(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
-    if (6 < nn) narrow_chunk(std::integral_constant<int, 6>{}, std::integral_constant<int, 2>{});
-    // wide k-steps (codes of 5..8 bits in some segment): general decode
-#pragma unroll
-    for (int ks = 0; ks < kQRegSteps; ++ks) {
-      if (wide & (1u << ks)) {
-        const uint4 d = kd[4 * ks + j];
-        const int w = int((d.z >> 8) & 15u);
-        const uint32_t ka = krec + d.x;
-        const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
-        const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
-        mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16), qh[ks],
-                   __builtin_bit_cast(f16x8, qlo[ks * 64 + lane]), nv);
-      }
-    }
-    for (int ks = kQRegSteps; ks < nks; ++ks) {   // k-steps beyond the register-resident ones
-      const uint4 d = kd[4 * ks + j];
-      const int w = int((d.z >> 8) & 15u);
-      const uint32_t ka = krec + d.x;
-      const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
-      const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
-      mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16),
-                 __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + lane]),
-                 __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + 64 + lane]), nv);
-    }
-
+  // ---- softmax and P V of one tile from its logits S (rows: tokens 16 wave + 4 j + r, columns:
+  // heads and the second group half); slots [vlo_t, valid) of the tile count (the window
+  // role's first tile can start mid-tile; for the packed role vlo_t <= 0)
+  auto finish_tile = [&](const f32x4& S, int tile, int valid, int vlo_t) {
     // ---- online softmax (base 2); head c = column c + column c + 8 (rotate the 16-lane row
     // by 8 with DPP); the tile maximum per head goes through LDS
     float v[4];
@@ -1425,7 +1412,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const float sr = S[r];
       const float other = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sr), 0x128, 0xf, 0xf, false));
       v[r] = sr + other;
-      if (16 * wave + 4 * j + r >= valid) v[r] = -INFINITY;
+      if (16 * wave + 4 * j + r >= valid || (WIN && 16 * wave + 4 * j + r < vlo_t)) v[r] = -INFINITY;
       lm = fmaxf(lm, v[r]);
     }
     if (a.logits && real_col) {
@@ -1433,7 +1420,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
                   16 * wave + 4 * j;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (16 * wave + 4 * j + r < valid) lg[r] = v[r] * kLn2;
+        if (16 * wave + 4 * j + r < valid && (!WIN || 16 * wave + 4 * j + r >= vlo_t)) lg[r] = v[r] * kLn2;
     }
     if (n < 8) mx[16 * n + 4 * wave + j] = lm;
     lds_barrier();
@@ -1488,8 +1475,117 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         }
       }
     }
-    // the P operands and maxima of this tile are overwritten only after the next tile's first
-    // barrier, which every wave reaches after finishing this tile
+  };
+
+  // every load issued so far (query operands, set-up reads) is complete here, so the only
+  // loads in flight inside the loop are the next tile's
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int it = 0; it < count; ++it) {
+    const int tile = t0 + it;
+    // tokens of this tile in the role's range: slots [vlo - 64 tile, valid)
+    const int valid = vhi - tile * kTile < kTile ? vhi - tile * kTile : kTile;
+    store_tile();                             // this wave's staging is read only by this wave
+    asm volatile("" ::: "memory");            // issue the next tile's loads after these stores
+    if (it + 1 < count) load_tile(it + 1);
+
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    if (WIN && win) {
+      // ---- window role: logits of tokens 16 wave + n from their fp16 keys (A rows; slots
+      // outside the role's range read a valid slot and are masked).  The lane index is taken
+      // afresh (opaque copy) so that no per-lane address of this branch is kept through the
+      // loop.
+      int wl = lane;
+      asm volatile("" : "+v"(wl));
+      const int tk = tile * kTile + 16 * wave + (wl & 15);
+      const int tc = tk < vlo ? vlo : (tk >= vhi ? vhi - 1 : tk);
+      const uint16_t* kr = a.k_window + (int64_t(reg) * a.window + tc % a.window) * D + 8 * (wl >> 4);
+      constexpr int KB = D / 32 < 4 ? D / 32 : 4;     // k-steps whose keys are loaded together
+#pragma unroll
+      for (int k0 = 0; k0 < D / 32; k0 += KB) {
+        uint4 kw[KB];
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks) kw[ks] = *reinterpret_cast<const uint4*>(kr + 32 * (k0 + ks));
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks) {
+          const f16x8 A = __builtin_bit_cast(f16x8, kw[ks]);
+          S = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh[k0 + ks], S, 0, 0, 0);
+          S = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(f16x8, qlo[(k0 + ks) * 64 + wl]), S, 0,
+                                                     0, 0);
+        }
+      }
+    } else {
+      // ---- logits of tokens 16 wave + n (A rows).  Pass A issues a chunk's window reads and
+      // level lookups (k-steps narrower than 5 bits), pass B runs the matrix cores on them;
+      // wide k-steps are decoded separately afterwards.
+      auto mfma_kstep = [&](const u32x4& raw, const f16x8& bh, const f16x8& bl, const f16x4& nv) {
+        const f16x8 A = __builtin_bit_cast(f16x8, raw);
+        f32x4 T = {0.f, 0.f, 0.f, 0.f};
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, T, 0, 0, 0);
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, T, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[r] = fmaf(T[r], float(nv[r]), S[r]);
+      };
+      // narrow k-steps in chunks of 4, 2 and 2 (a chunk past the last narrow k-step is skipped;
+      // inside the last one, slots past it are decoded but not multiplied)
+      auto narrow_chunk = [&](auto kc_c, auto kn_c) {
+        constexpr int kc = decltype(kc_c)::value, KC = decltype(kn_c)::value;
+        {
+          u32x4 raw[KC];
+          f16x4 nrm[KC];
+          uint32_t wd0[KC], wd1[KC], ctl[KC];
+#pragma unroll
+          for (int q = 0; q < KC; ++q) {
+            const uint2 d = *reinterpret_cast<const uint2*>(kd + 4 * (kc + q) + j);
+            ctl[q] = d.y;
+            wd0[q] = lds_u32(buf, krec + d.x);
+            wd1[q] = lds_u32(buf, krec + d.x + 4);
+            nrm[q] = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[kc + q] >> nsh) & 0xffffu));
+          }
+#pragma unroll
+          for (int q = 0; q < KC; ++q) {
+            const uint32_t x = __builtin_amdgcn_alignbit(wd1[q], wd0[q], ctl[q]);   // shift = ctl & 31
+            const uint32_t w2 = ctl[q] >> 8;                                          // low 5 bits: 2w
+            const uint32_t o4 = w2 << 1, o6 = w2 + o4, tb = ctl[q] >> 16;
+            raw[q][0] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, 0u, w2));
+            raw[q][1] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, w2, w2));
+            raw[q][2] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, o4, w2));
+            raw[q][3] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, o6, w2));
+          }
+#pragma unroll
+          for (int q = 0; q < KC; ++q)
+            if (kc + q < nn) mfma_kstep(raw[q], qh[kc + q], __builtin_bit_cast(f16x8, qlo[(kc + q) * 64 + lane]), nrm[q]);
+        }
+      };
+      static_assert(kQRegSteps == 8, "chunks 4 + 2 + 2");
+      if (0 < nn) narrow_chunk(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+      if (4 < nn) narrow_chunk(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
+      if (6 < nn) narrow_chunk(std::integral_constant<int, 6>{}, std::integral_constant<int, 2>{});
+      // wide k-steps (codes of 5..8 bits in some segment): general decode
+#pragma unroll
+      for (int ks = 0; ks < kQRegSteps; ++ks) {
+        if (wide & (1u << ks)) {
+          const uint4 d = kd[4 * ks + j];
+          const int w = int((d.z >> 8) & 15u);
+          const uint32_t ka = krec + d.x;
+          const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
+          const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
+          mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16), qh[ks],
+                     __builtin_bit_cast(f16x8, qlo[ks * 64 + lane]), nv);
+        }
+      }
+      for (int ks = kQRegSteps; ks < nks; ++ks) {   // k-steps beyond the register-resident ones
+        const uint4 d = kd[4 * ks + j];
+        const int w = int((d.z >> 8) & 15u);
+        const uint32_t ka = krec + d.x;
+        const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
+        const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
+        mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16),
+                   __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + lane]),
+                   __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + 64 + lane]), nv);
+      }
+
+    }
+    finish_tile(S, tile, valid, WIN ? vlo - tile * kTile : 0);
   }
 
   // ---- partial result of this split: lane (n, j) holds head n, coordinates
@@ -1559,11 +1655,11 @@ __device__ __forceinline__ void query_wg(const DecodeArgs& a, int s, int hk, uin
   }
 }
 
-template <typename T, bool STAGE_V, int D, typename QT>
+template <typename T, bool STAGE_V, int D, typename QT, bool WIN>
 __global__ __launch_bounds__(1024) void k_step_front(AppendArgs aa, DecodeArgs da, int n_seqs) {
   extern __shared__ __align__(16) uint8_t lds8[];
   if (int(blockIdx.x) < n_seqs) {
-    append_one_wg<T, STAGE_V>(aa, blockIdx.x, reinterpret_cast<float*>(lds8));
+    append_one_wg<T, STAGE_V, WIN>(aa, blockIdx.x, reinterpret_cast<float*>(lds8));
   } else {
     const int r = blockIdx.x - n_seqs;
     query_wg<D, QT>(da, r / da.n_kv, r % da.n_kv, lds8);
@@ -1656,16 +1752,23 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
   }
 }
 
+// the matrix-core kernel for a cache's record widths, query dtype and pass (with the query
+// operands precomputed by a decode step or not); with WIN, the window role is built in
+template <int D, bool WIN>
+auto mfma_kernel(bool narrow, bool bf16, bool pre) -> void (*)(DecodeArgs) {
+  if (pre) return narrow ? k_decode_mfma<D, true, float, true, WIN> : k_decode_mfma<D, false, float, true, WIN>;
+  return narrow ? (bf16 ? k_decode_mfma<D, true, uint16_t, false, WIN> : k_decode_mfma<D, true, float, false, WIN>)
+                : (bf16 ? k_decode_mfma<D, false, uint16_t, false, WIN> : k_decode_mfma<D, false, float, false, WIN>);
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st) {
   const dim3 grid(a.n_split, a.n_kv, a.batch);
   if (a.use_mfma) {
     const int lds = tc_lds_bytes(D, a.chunks, a.v_bits);
     const bool narrow = a.chunks <= 4 && a.v_bits <= 4, bf16 = q_dt == BGTQ_BF16;
-    void (*fn)(DecodeArgs) =
-        a.qpre ? (narrow ? k_decode_mfma<D, true, float, true> : k_decode_mfma<D, false, float, true>)
-               : narrow ? (bf16 ? k_decode_mfma<D, true, uint16_t, false> : k_decode_mfma<D, true, float, false>)
-                        : (bf16 ? k_decode_mfma<D, false, uint16_t, false> : k_decode_mfma<D, false, float, false>);
+    void (*fn)(DecodeArgs) = a.window > 0 ? mfma_kernel<D, true>(narrow, bf16, a.qpre != nullptr)
+                                          : mfma_kernel<D, false>(narrow, bf16, a.qpre != nullptr);
     if (lds > 64 * 1024) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1707,8 +1810,11 @@ hipError_t launch_step_front(const AppendArgs& aa, const DecodeArgs& da, bgtq_dt
   const size_t lds = q_lds > a_lds ? q_lds : a_lds;
   const bool kb = kv_dt == BGTQ_BF16, qb = q_dt == BGTQ_BF16;
   void (*fn)(AppendArgs, DecodeArgs, int) =
-      kb ? (qb ? k_step_front<uint16_t, SV, D, uint16_t> : k_step_front<uint16_t, SV, D, float>)
-         : (qb ? k_step_front<float, SV, D, uint16_t> : k_step_front<float, SV, D, float>);
+      aa.window > 0
+          ? (kb ? (qb ? k_step_front<uint16_t, SV, D, uint16_t, true> : k_step_front<uint16_t, SV, D, float, true>)
+                : (qb ? k_step_front<float, SV, D, uint16_t, true> : k_step_front<float, SV, D, float, true>))
+          : (kb ? (qb ? k_step_front<uint16_t, SV, D, uint16_t, false> : k_step_front<uint16_t, SV, D, float, false>)
+                : (qb ? k_step_front<float, SV, D, uint16_t, false> : k_step_front<float, SV, D, float, false>));
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
@@ -1770,24 +1876,25 @@ hipError_t launch_allocate(const double* energy, int n_heads, int n_blocks, int 
   return hipGetLastError();
 }
 
+namespace {
+// the one-token append kernel for the input dtype, value staging and window
+template <bool WIN>
+auto append_one_kernel(bool bf16, bool stage_v) -> void (*)(AppendArgs) {
+  return bf16 ? (stage_v ? k_append_one<uint16_t, true, WIN> : k_append_one<uint16_t, false, WIN>)
+              : (stage_v ? k_append_one<float, true, WIN> : k_append_one<float, false, WIN>);
+}
+}  // namespace
+
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s) {
   if (a.n_new == 1) {   // decode step: one token per sequence, length advanced in the same kernel
     const bool stage_v = a.d <= 128;
     const size_t lds = append_one_lds_bytes(a.d, stage_v);
-    const void* fn = dt == BGTQ_BF16
-        ? (stage_v ? reinterpret_cast<const void*>(&k_append_one<uint16_t, true>)
-                   : reinterpret_cast<const void*>(&k_append_one<uint16_t, false>))
-        : (stage_v ? reinterpret_cast<const void*>(&k_append_one<float, true>)
-                   : reinterpret_cast<const void*>(&k_append_one<float, false>));
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    void (*fn)(AppendArgs) =
+        a.window > 0 ? append_one_kernel<true>(dt == BGTQ_BF16, stage_v) : append_one_kernel<false>(dt == BGTQ_BF16, stage_v);
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
-    if (dt == BGTQ_BF16) {
-      if (stage_v) hipLaunchKernelGGL((k_append_one<uint16_t, true>), dim3(n_seqs), dim3(1024), lds, s, a);
-      else hipLaunchKernelGGL((k_append_one<uint16_t, false>), dim3(n_seqs), dim3(1024), lds, s, a);
-    } else {
-      if (stage_v) hipLaunchKernelGGL((k_append_one<float, true>), dim3(n_seqs), dim3(1024), lds, s, a);
-      else hipLaunchKernelGGL((k_append_one<float, false>), dim3(n_seqs), dim3(1024), lds, s, a);
-    }
+    hipLaunchKernelGGL(fn, dim3(n_seqs), dim3(1024), lds, s, a);
     return hipGetLastError();
   }
   const int halves = int((a.n_new + kHalf - 1) / kHalf) + 1;
@@ -1798,6 +1905,14 @@ hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStre
     hipLaunchKernelGGL(k_append<uint16_t>, grid, dim3(256), lds, s, a);
   else
     hipLaunchKernelGGL(k_append<float>, grid, dim3(256), lds, s, a);
+  if (a.window > 0) {
+    const int64_t m = a.n_new < a.window ? a.n_new : a.window;
+    const dim3 wgrid(unsigned((m * a.d + 255) / 256), a.n_kv_heads, n_seqs);
+    if (dt == BGTQ_BF16)
+      hipLaunchKernelGGL(k_window_store<uint16_t>, wgrid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_window_store<float>, wgrid, dim3(256), 0, s, a);
+  }
   hipLaunchKernelGGL(k_advance, dim3((n_seqs + 63) / 64), dim3(64), 0, s, a.lengths, a.seq_begin, n_seqs, a.n_new,
                      a.capacity);
   return hipGetLastError();

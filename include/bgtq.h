@@ -59,6 +59,7 @@ typedef void* bgtq_stream;
 #define BGTQ_MAX_GROUP 16        /* query heads per KV head */
 #define BGTQ_TILE 64             /* token slots per cache tile */
 #define BGTQ_LAYOUT_BYTES 4096   /* size of one per-head layout descriptor */
+#define BGTQ_MAX_WINDOW 4096     /* tokens in the fp16 recent-key window */
 
 /* Random rotations the quantizer draws (TQ-MSE rotates before scalar coding).
  * Device memory, caller-owned, read-only, shared by all layers and heads.
@@ -108,6 +109,15 @@ bgtq_status bgtq_transpose_rotations(const float* rot_bank, const float* rot_v, 
  *            bgtq_allocate_bits at prefill and read by the other calls.
  *   status   int32  [1], nullable: a kernel sets bit 0 when an append would
  *            pass capacity (that append is then skipped for that sequence).
+ *   window, k_window  the fp16 recent-key window (abstract: the AIME run is stated to be
+ *            without an fp16 recent-key buffer, so the serving path has one as an option).
+ *            Reading: the keys of the newest `window` tokens of a sequence, t in
+ *            [lengths[s] - window, lengths[s]), are also kept as fp16 (nearest-even,
+ *            saturated at +-65504) and attention uses them in place of their quantized
+ *            reconstruction; their values stay quantized.  window = 0 turns it off
+ *            (k_window may then be NULL); otherwise 1 <= window <= BGTQ_MAX_WINDOW and
+ *            k_window is fp16 [batch][n_kv_heads][window][head_dim], token t of a sequence
+ *            at slot t mod window.  Every token is still quantized into the packed arrays.
  * Unused slots may hold anything; only slots below lengths[s] are read. */
 typedef struct {
   int batch;
@@ -125,6 +135,8 @@ typedef struct {
   uint8_t* widths;
   void* layouts;
   int32_t* status;
+  int32_t window;       /* fp16 recent-key window in tokens; 0 = none */
+  uint16_t* k_window;
 } bgtq_cache;
 
 /* Energy score of every RoPE block, computed from keys alone (abstract: one
@@ -174,7 +186,9 @@ bgtq_status bgtq_allocate_bits(const double* energy, int n_heads, int head_dim, 
  * head_dim with rot_v at v_bits.  Codes, norms and packed bytes are
  * reproducible bit for bit.
  * Appends n_new tokens to each sequence s in [seq_begin, seq_begin + n_seqs):
- * token i of s goes to slot lengths[s] + i, then lengths[s] += n_new.
+ * token i of s goes to slot lengths[s] + i, then lengths[s] += n_new.  With a window,
+ * the appended tokens that end up among the newest `window` also get their fp16 key
+ * written to the window.
  *   keys, values  [n_seqs][n_kv_heads][n_new][head_dim] of `dtype` with strides
  *                 (stride_seq, stride_head, stride_token, 1); keys post-RoPE.
  * The sequence's widths/layouts must already be written by bgtq_allocate_bits.
@@ -204,9 +218,11 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
  *               are left untouched.
  *   workspace   >= bgtq_decode_workspace_bytes(...); must be zero-filled before
  *               its first use; every call leaves it ready for the next.
+ * With a window, the logits of the newest min(window, lengths[s]) tokens use their fp16
+ * keys, q' . k16_t, instead of k_hat_t; the softmax runs over all tokens at once.
  * A sequence with lengths[s] == 0 gets out = 0.
- * Errors: INVALID_ARG, UNSUPPORTED (group size > 16, head_dim not 64/128/256),
- * WORKSPACE, HIP. */
+ * Errors: INVALID_ARG, UNSUPPORTED (group size > 16, head_dim not 64/128/256; with a
+ * window, group size > 8), WORKSPACE, HIP. */
 bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads,
                                   const void* q, bgtq_dtype q_dtype, const int64_t* q_pos,
                                   double rope_theta, float softmax_scale, float* out,

@@ -76,7 +76,7 @@ def test_allocate_validation():
 def _desc(**over):
     base = dict(batch=1, n_kv_heads=2, head_dim=128, k_width_sum=192, v_bits=3, capacity=256, pairing=0,
                 k_codes=FAKE, k_norms=FAKE, v_codes=FAKE, v_norms=FAKE, lengths=FAKE, widths=FAKE,
-                layouts=FAKE, status=None)
+                layouts=FAKE, status=None, window=0, k_window=None)
     base.update(over)
     return bgtq.CacheDesc(*[base[f] for f, _ in bgtq.CacheDesc._fields_])
 
@@ -160,6 +160,25 @@ def test_decode_step_validation():
     assert call(_desc(), kv_dtype=7) == bgtq.ERR_INVALID_ARG
     assert call(_desc(), stride_head=0) == bgtq.ERR_INVALID_ARG
     assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
+
+
+def test_window_validation():
+    lib = bgtq.lib()
+    need = lib.bgtq_decode_workspace_bytes(1, 16, 2, 128, 256)
+
+    def decode(desc):
+        return lib.bgtq_decode_attention(ctypes.byref(_quantizer()), ctypes.byref(desc), 16, FAKE, 0, None, 1e6,
+                                         0.088, FAKE, None, FAKE, need, None)
+
+    assert decode(_desc(window=4097, k_window=FAKE)) == bgtq.ERR_INVALID_ARG
+    assert decode(_desc(window=-1, k_window=FAKE)) == bgtq.ERR_INVALID_ARG
+    assert decode(_desc(window=64, k_window=None)) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_quantize_append(ctypes.byref(_quantizer()), ctypes.byref(_desc(window=64, k_window=None)), 0, 1,
+                                    FAKE, FAKE, 0, 1, 256, 128, 128, None) == bgtq.ERR_INVALID_ARG
+    # a window is attended by the matrix-core decode only (groups of at most 8 query heads)
+    assert lib.bgtq_decode_attention(ctypes.byref(_quantizer()), ctypes.byref(_desc(window=64, k_window=FAKE)), 32,
+                                     FAKE, 0, None, 1e6, 0.088, FAKE, None, FAKE,
+                                     lib.bgtq_decode_workspace_bytes(1, 32, 2, 128, 256), None) == bgtq.ERR_UNSUPPORTED
 
 
 def test_logit_error_validation():
