@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--workload", default="qwen3b_36L_128k_K3V3")
     p.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--window", type=int, default=0,
+                   help="fp16 recent-key window in tokens (0: none, the default workload)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="after timing, run one plain device copy of this many MiB (scale for PMC byte counters)")
     return p.parse_args()
@@ -139,7 +141,7 @@ def main():
     pre_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     pre_ms = 0.0
     for layer in range(wl.layers):
-        cache = bgtq.PackedCache(1, wl.h_kv, wl.d, wl.budget, wl.v_bits, cap, device=dev)
+        cache = bgtq.PackedCache(1, wl.h_kv, wl.d, wl.budget, wl.v_bits, cap, device=dev, window=args.window)
         kv = [synth.keys_values_device(wl, 0, layer, h, t_len, dev) for h in range(wl.h_kv)]
         k = torch.stack([x[0] for x in kv]).contiguous()
         v = torch.stack([x[1] for x in kv]).contiguous()
@@ -212,7 +214,10 @@ def main():
     torch.cuda.synchronize()
     us_per_launch = e0.elapsed_time(e1) * 1e3 / (args.kernel_reps * wl.layers)
     ctx = lengths[0]
-    bytes_per_launch = float(np.mean([sum(b) for b in layer_bytes])) * ctx
+    # tokens in the window are read as fp16 keys plus their packed values and value norms
+    n_win = min(args.window, ctx)
+    win_bytes = wl.h_kv * n_win * (2 * wl.d + wl.v_bits * wl.d // 8 + 2)
+    bytes_per_launch = float(np.mean([sum(b) for b in layer_bytes])) * (ctx - n_win) + win_bytes
     achieved = bytes_per_launch / (us_per_launch * 1e-6) / 1e9
 
     if args.copy_mb > 0:   # a plain copy kernel of known size, for counter calibration
@@ -238,9 +243,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": wl.layers, "q_heads": wl.h_q, "kv_heads": wl.h_kv,
                    "head_dim": wl.d, "context": ctx, "batch": 1, "budget": f"K{wl.k_bits}V{wl.v_bits}",
-                   "capacity": cap},
+                   "capacity": cap, "recent_key_window": args.window},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(wl.name) if args.window == 0 else None,
                      "kernel": "decode attention: one bgtq_decode_attention call per layer "
                                "(k_decode_mfma + k_decode_combine)",
                      "us_per_launch": us_per_launch, "alg_bytes_per_launch": bytes_per_launch},

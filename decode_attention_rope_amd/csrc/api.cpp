@@ -237,7 +237,7 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
 
 size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t capacity) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || capacity < kTile) return 0;
-  const int splits = decode_splits(batch, n_kv_heads, capacity, true) + kMaxWindowSplits;
+  const int splits = decode_splits(batch, n_kv_heads, capacity, true) + kMaxWindowSplits;   // an upper bound
   const size_t part = align256(size_t(batch) * n_q_heads * splits * head_dim * 4) +
                       align256(size_t(batch) * n_q_heads * splits * 8);
   return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + part +
@@ -285,8 +285,11 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
     return fail(BGTQ_ERR_UNSUPPORTED, "the recent-key window is built on the matrix-core decode (group size <= 8)");
   a.window = cache->window;
   a.k_window = cache->window > 0 ? cache->k_window : nullptr;
+  // the window's splits come out of the same workgroup budget (a grid that fits the GPU at
+  // once), the packed keys keep at least one split
   a.n_wsplit = window_splits(cache->window);
-  a.n_split = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma) + a.n_wsplit;
+  const int base = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma);
+  a.n_split = (base - a.n_wsplit > 1 ? base - a.n_wsplit : 1) + a.n_wsplit;
   char* ws = static_cast<char*>(workspace);
   const size_t qrot_b = align256(decode_qrot_bytes(cache->batch, cache->n_kv_heads, d));
   a.qrot = reinterpret_cast<float*>(ws);

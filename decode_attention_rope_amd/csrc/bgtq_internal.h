@@ -147,7 +147,7 @@ struct DecodeArgs {
   int use_mfma;
   const uint16_t* k_window;   // fp16 recent keys (see AppendArgs)
   int window;                 // 0: no window
-  int n_wsplit;               // the last n_wsplit splits attend over the window's tokens
+  int n_wsplit;               // the first n_wsplit splits attend over the window's tokens
 };
 hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s);
 // decode step on the matrix-core path: append one token per sequence and attend (da.qpre set,

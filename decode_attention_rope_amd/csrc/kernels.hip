@@ -1175,25 +1175,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // advanced by the merge kernel, so it still holds the old length here
   const int len0 = a.lengths[s];
   const int len = a.step && len0 + 1 <= a.capacity ? len0 + 1 : len0;
-  // Tokens [0, pend) are attended from the packed keys by the first n_split - n_wsplit
+  // Tokens [0, pend) are attended from the packed keys by the last n_split - n_wsplit
   // splits; with a window (WIN), the window's tokens [pend, len) from their fp16 keys by the
-  // last n_wsplit splits (workgroup-uniform role).  Each role's tiles are shared out so that
-  // split i of n takes tiles [i T / n, (i + 1) T / n) of the role's T tiles: counts differ by
-  // at most one.
+  // first n_wsplit splits (workgroup-uniform role; dispatched first, as their prologue is the
+  // longer one).  Each role's tiles are shared out so that split i of n takes tiles
+  // [i T / n, (i + 1) T / n) of the role's T tiles: counts differ by at most one.
   const int pend = !WIN ? len : (len > a.window ? len - a.window : 0);
-  const int n_ps = WIN ? a.n_split - a.n_wsplit : a.n_split;
-  const bool win = WIN && split >= n_ps;
+  const int nw = WIN ? a.n_wsplit : 0, n_ps = a.n_split - nw;
+  const bool win = WIN && split < nw;
   int t0, t1, vlo, vhi;                              // tiles, and the role's token range
   if (!win) {
     const int tiles = (pend + kTile - 1) / kTile;
-    t0 = int(int64_t(split) * tiles / n_ps);
-    t1 = int(int64_t(split + 1) * tiles / n_ps);
+    t0 = int(int64_t(split - nw) * tiles / n_ps);
+    t1 = int(int64_t(split - nw + 1) * tiles / n_ps);
     vlo = 0;
     vhi = pend;
   } else {
     const int first = pend / kTile, tiles = pend < len ? (len + kTile - 1) / kTile - first : 0;
-    t0 = first + int(int64_t(split - n_ps) * tiles / a.n_wsplit);
-    t1 = first + int(int64_t(split - n_ps + 1) * tiles / a.n_wsplit);
+    t0 = first + int(int64_t(split) * tiles / nw);
+    t1 = first + int(int64_t(split + 1) * tiles / nw);
     vlo = pend;
     vhi = len;
   }
