@@ -26,7 +26,7 @@ import numpy as np
 
 GEN_BLOCK = 8192          # tokens per independently seeded key/value block
 
-_STREAMS = {"profile": 1, "k": 2, "v": 3, "q": 4, "len": 5, "rot": 6, "rotv": 7, "outl": 8}
+_STREAMS = {"profile": 1, "k": 2, "v": 3, "q": 4, "len": 5, "rot": 6, "rotv": 7, "outl": 8, "givens": 9}
 
 
 @dataclass(frozen=True)
@@ -260,3 +260,43 @@ def keys_values_device(wl: Workload, seq: int, layer: int, head: int, t_len: int
     v = torch.randn((t_len, wl.d), generator=g, device=device, dtype=torch.float64)
     dt = torch.float32 if wl.key_dtype == "f32" else torch.bfloat16
     return k.to(dt), v.to(dt)
+
+
+# ---------------------------------------------------------------- structured rotations
+
+GIVENS_HEADER = 128      # header entries: one per even size m = 2 .. 256
+
+
+def givens_layer_count(m: int) -> int:
+    """Layers drawn for size m: 2 ceil(log2 m) - 1 (odd, so that a size-2 rotation is not a
+    signed permutation: 1 for m = 2, 13 for m = 128)."""
+    return 2 * max(1, (m - 1).bit_length()) - 1
+
+
+def givens_bank(d: int, seed: int = 0) -> np.ndarray:
+    """Random Givens-layer rotations for every even size m = 2 .. d, packed as uint32 [N, 4].
+
+    Size m gets givens_layer_count(m) layers; a layer is a uniformly random perfect matching of
+    the m coordinates (a random permutation read in pairs) and one angle per pair, uniform over
+    pi/4 + k pi/2 (k = 0..3: an equal split of the pair's mass with a random sign pattern, which
+    spreads sparse vectors as evenly as possible per layer), stored as fp32 cos and sin.  Layout: GIVENS_HEADER header rows, row m/2 - 1 =
+    (first record row of size m, layer count, 0, 0) (zeros for sizes above d); then the
+    records (a | b << 16, bits of cos, bits of sin, 0), size by size, layer by layer."""
+    header = np.zeros((GIVENS_HEADER, 4), dtype=np.uint32)
+    recs = []
+    row = GIVENS_HEADER
+    for m in range(2, d + 1, 2):
+        rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(_STREAMS["givens"], m)))
+        n_layers = givens_layer_count(m)
+        header[m // 2 - 1] = (row, n_layers, 0, 0)
+        for _ in range(n_layers):
+            perm = rng.permutation(m)
+            theta = math.pi / 4 + (math.pi / 2) * rng.integers(0, 4, size=m // 2)
+            r = np.zeros((m // 2, 4), dtype=np.uint32)
+            r[:, 0] = perm[0::2].astype(np.uint32) | (perm[1::2].astype(np.uint32) << 16)
+            r[:, 1] = np.cos(theta).astype(np.float32).view(np.uint32)
+            r[:, 2] = np.sin(theta).astype(np.float32).view(np.uint32)
+            recs.append(r)
+            row += m // 2
+    return np.concatenate([header] + recs)
+
