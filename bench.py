@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--workload", default="qwen3b_36L_128k_K3V3")
     p.add_argument("--kernel-reps", type=int, default=20, help="graph replays for the kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--rotation", choices=("dense", "givens"), default="dense",
+                   help="TQ-MSE rotation kind: dense Haar matrices (default) or structured Givens layers")
     p.add_argument("--window", type=int, default=0,
                    help="fp16 recent-key window in tokens (0: none, the default workload)")
     p.add_argument("--copy-mb", type=int, default=0,
@@ -131,9 +133,13 @@ def main():
     t_len = wl.seq_lens[0]
     steps_total = args.warmup + args.steps + 1
     cap = -(-(t_len + steps_total) // 64) * 64
-    bank = torch.from_numpy(synth.rotation_bank(wl.d)).to(dev)
-    rv = torch.from_numpy(synth.rotation_v(wl.d)).to(dev)
-    qz = bgtq.make_quantizer(bank, rv, wl.d)
+    if args.rotation == "givens":
+        giv = torch.from_numpy(synth.givens_bank(wl.d).view(np.int32)).to(dev)
+        qz = bgtq.make_quantizer(None, None, wl.d, givens=giv)
+    else:
+        bank = torch.from_numpy(synth.rotation_bank(wl.d)).to(dev)
+        rv = torch.from_numpy(synth.rotation_v(wl.d)).to(dev)
+        qz = bgtq.make_quantizer(bank, rv, wl.d)
 
     # ---------------- prefill every layer (setup, not timed in the metric)
     log(f"prefill {wl.layers} layers x {wl.h_kv} KV heads x {t_len} tokens")
@@ -243,10 +249,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": wl.layers, "q_heads": wl.h_q, "kv_heads": wl.h_kv,
                    "head_dim": wl.d, "context": ctx, "batch": 1, "budget": f"K{wl.k_bits}V{wl.v_bits}",
-                   "capacity": cap, "recent_key_window": args.window},
+                   "capacity": cap, "recent_key_window": args.window, "rotation": args.rotation},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(wl.name) if args.window == 0 else None,
+                     "traffic": measured_traffic(wl.name) if args.window == 0 and args.rotation == "dense" else None,
                      "kernel": "decode attention: one bgtq_decode_attention call per layer "
                                "(k_decode_mfma + k_decode_combine)",
                      "us_per_launch": us_per_launch, "alg_bytes_per_launch": bytes_per_launch},

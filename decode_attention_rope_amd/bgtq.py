@@ -24,6 +24,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "bgtq.h")
 OK, ERR_INVALID_ARG, ERR_BUDGET, ERR_CAPACITY, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(7)
 F32, BF16 = 0, 1
 PAIR_HALF, PAIR_INTERLEAVED = 0, 1
+ROT_DENSE, ROT_GIVENS = 0, 1
 TILE = 64
 MAX_GROUPS = 8
 LAYOUT_BYTES = 4096
@@ -40,7 +41,8 @@ class BgtqError(RuntimeError):
 
 
 class Quantizer(_c.Structure):
-    _fields_ = [("rot_bank", _vp), ("rot_v", _vp), ("rot_bank_t", _vp), ("rot_v_t", _vp), ("head_dim", _i32)]
+    _fields_ = [("rot_bank", _vp), ("rot_v", _vp), ("rot_bank_t", _vp), ("rot_v_t", _vp), ("head_dim", _i32),
+                ("rotation", _i32), ("givens", _vp)]
 
 
 class CacheDesc(_c.Structure):
@@ -147,8 +149,17 @@ def init() -> None:
 
 # ------------------------------------------------------------------ device objects
 
-def make_quantizer(rot_bank: torch.Tensor, rot_v: torch.Tensor, head_dim: int):
-    """C descriptor of the rotations; the library writes their transposed copies (kept alive with it)."""
+def make_quantizer(rot_bank: torch.Tensor | None, rot_v: torch.Tensor | None, head_dim: int,
+                   givens: torch.Tensor | None = None):
+    """C descriptor of the rotations (kept alive with it).  Dense: the Haar bank and the value
+    rotation, whose transposed copies the library writes.  Structured: `givens`, the packed
+    Givens-layer records (uint32 [rows, 4] bits in an int32 tensor)."""
+    if givens is not None:
+        if givens.dtype != torch.int32 or givens.dim() != 2 or givens.shape[1] != 4 or not givens.is_contiguous():
+            raise ValueError("givens must be a contiguous int32 [rows, 4] tensor")
+        q = Quantizer(None, None, None, None, head_dim, ROT_GIVENS, givens.data_ptr())
+        q._keep = (givens,)
+        return q
     n = int(lib().bgtq_rotation_bank_floats(head_dim))
     if n == 0 or rot_bank.numel() != n or rot_v.numel() != head_dim * head_dim:
         raise ValueError("rotation bank / value rotation do not match head_dim")
@@ -158,7 +169,8 @@ def make_quantizer(rot_bank: torch.Tensor, rot_v: torch.Tensor, head_dim: int):
     bank_t, rv_t = torch.empty_like(rot_bank), torch.empty_like(rot_v)
     _check(lib().bgtq_transpose_rotations(rot_bank.data_ptr(), rot_v.data_ptr(), head_dim, bank_t.data_ptr(),
                                           rv_t.data_ptr(), _stream()))
-    q = Quantizer(rot_bank.data_ptr(), rot_v.data_ptr(), bank_t.data_ptr(), rv_t.data_ptr(), head_dim)
+    q = Quantizer(rot_bank.data_ptr(), rot_v.data_ptr(), bank_t.data_ptr(), rv_t.data_ptr(), head_dim, ROT_DENSE,
+                  None)
     q._keep = (rot_bank, rot_v, bank_t, rv_t)
     return q
 

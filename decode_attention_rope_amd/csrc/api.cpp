@@ -74,6 +74,19 @@ bgtq_status check_cache(const bgtq_cache* c, bool need_layout) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+bgtq_status check_quantizer(const bgtq_quantizer* qz) {
+  if (!qz) return fail(BGTQ_ERR_INVALID_ARG, "quantizer is NULL");
+  if (qz->rotation == BGTQ_ROT_DENSE) {
+    if (!qz->rot_bank || !qz->rot_v || !qz->rot_bank_t || !qz->rot_v_t)
+      return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
+  } else if (qz->rotation == BGTQ_ROT_GIVENS) {
+    if (!qz->givens) return fail(BGTQ_ERR_INVALID_ARG, "quantizer givens records are NULL");
+  } else {
+    return fail(BGTQ_ERR_INVALID_ARG, "bad rotation kind %d", int(qz->rotation));
+  }
+  return BGTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,8 +193,7 @@ static bgtq_status prepare_append(const bgtq_quantizer* qz, const bgtq_cache* ca
                                   const void* keys, const void* values, bgtq_dtype dtype, int64_t n_new,
                                   int64_t stride_seq, int64_t stride_head, int64_t stride_token, AppendArgs& a) {
   if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
-  if (!qz || !qz->rot_bank || !qz->rot_v || !qz->rot_bank_t || !qz->rot_v_t)
-    return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
+  if (bgtq_status st = check_quantizer(qz); st != BGTQ_OK) return st;
   if (qz->head_dim != cache->head_dim) return fail(BGTQ_ERR_INVALID_ARG, "quantizer head_dim != cache head_dim");
   if (!keys || !values) return fail(BGTQ_ERR_INVALID_ARG, "keys and values must not be NULL");
   if (dtype != BGTQ_F32 && dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad dtype");
@@ -220,6 +232,7 @@ static bgtq_status prepare_append(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.chunks = record_chunks(cache->k_width_sum);
   a.window = cache->window;
   a.k_window = cache->window > 0 ? cache->k_window : nullptr;
+  a.givens = qz->rotation == BGTQ_ROT_GIVENS ? reinterpret_cast<const uint4*>(qz->givens) : nullptr;
   return BGTQ_OK;
 }
 
@@ -249,8 +262,7 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
                                   float* out, float* logits_out, void* workspace, size_t workspace_bytes,
                                   DecodeArgs& a) {
   if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
-  if (!qz || !qz->rot_bank || !qz->rot_v || !qz->rot_bank_t || !qz->rot_v_t)
-    return fail(BGTQ_ERR_INVALID_ARG, "quantizer rotations are NULL");
+  if (bgtq_status st = check_quantizer(qz); st != BGTQ_OK) return st;
   if (qz->head_dim != cache->head_dim) return fail(BGTQ_ERR_INVALID_ARG, "quantizer head_dim != cache head_dim");
   if (!q || !out) return fail(BGTQ_ERR_INVALID_ARG, "q and out must not be NULL");
   if (q_dtype != BGTQ_F32 && q_dtype != BGTQ_BF16) return fail(BGTQ_ERR_INVALID_ARG, "bad q dtype");
@@ -296,6 +308,7 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.partial = reinterpret_cast<float*>(ws + qrot_b);
   a.part_ml = reinterpret_cast<float2*>(ws + qrot_b + align256(size_t(cache->batch) * n_q_heads * a.n_split * d * 4));
   a.qpre = nullptr;   // set by the decode step (the workspace's last region)
+  a.givens = qz->rotation == BGTQ_ROT_GIVENS ? reinterpret_cast<const uint4*>(qz->givens) : nullptr;
   a.rope_theta = rope_theta;
   for (int j = 0; j < d / 2; ++j) a.inv_freq[j] = rope_theta > 0.0 ? std::pow(rope_theta, -2.0 * j / d) : 0.0;
   a.scale = softmax_scale;

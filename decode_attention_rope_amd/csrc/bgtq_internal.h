@@ -117,6 +117,7 @@ struct AppendArgs {
   int advance;        // the one-token kernel advances lengths[] (a decode step leaves that to the merge)
   uint16_t* k_window; // fp16 recent keys [batch][n_kv][window][d], token t at slot t % window
   int window;         // 0: no window
+  const uint4* givens;  // structured rotations (header, then records), or null for dense ones
 };
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s);
 
@@ -148,6 +149,7 @@ struct DecodeArgs {
   const uint16_t* k_window;   // fp16 recent keys (see AppendArgs)
   int window;                 // 0: no window
   int n_wsplit;               // the first n_wsplit splits attend over the window's tokens
+  const uint4* givens;        // structured rotations (see AppendArgs), or null for dense ones
 };
 hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s);
 // decode step on the matrix-core path: append one token per sequence and attend (da.qpre set,

@@ -77,6 +77,71 @@ __device__ __forceinline__ size_t bank_offset(int m) {  // sum of k*k for even k
   return 4 * (h * (h + 1) * (2 * h + 1) / 6);
 }
 
+// Layers per size the kernels apply; the records' header must not name more.
+constexpr int kMaxGivensLayers = 16;
+
+// Structured (Givens-layer) rotations: header row m/2 - 1 = (first record row of size m,
+// layer count); record (a | b << 16, cos, sin) of pair slot i of layer l of size m at row
+// first + l * m/2 + i.  One pair rotation in place: y_a = c x_a - s x_b, y_b = s x_a + c x_b,
+// every product and sum rounded (this file is compiled without contraction).
+__device__ __forceinline__ void givens_pair(float* x, uint4 rec) {
+  const int ia = int(rec.x & 0xffffu), ib = int(rec.x >> 16);
+  const float c = __uint_as_float(rec.y), s = __uint_as_float(rec.z);
+  const float xa = x[ia], xb = x[ib];
+  x[ia] = c * xa - s * xb;
+  x[ib] = s * xa + c * xb;
+}
+// record of pair slot q (storage positions 2q, 2q + 1 lie in one width group) in layer l, or
+// a zero record when the group's size has fewer layers
+__device__ __forceinline__ bool givens_slot(const uint4* G, const HeadLayout& L, int q, int l, uint4& rec, int& first) {
+  const int g = L.group[2 * q], m = L.g_m[g];
+  first = L.g_first[g];
+  const uint4 h = G[m / 2 - 1];
+  if (l >= min(int(h.y), kMaxGivensLayers)) return false;
+  rec = G[h.x + l * (m / 2) + (q - first / 2)];
+  return true;
+}
+__device__ __forceinline__ int givens_count(const uint4* G, int m) { return min(int(G[m / 2 - 1].y), kMaxGivensLayers); }
+// most layers among a layout's width groups
+__device__ __forceinline__ int givens_layers(const uint4* G, const HeadLayout& L) {
+  int n = 0;
+  for (int g = 0; g < L.n_groups; ++g) n = max(n, givens_count(G, L.g_m[g]));
+  return n;
+}
+// One thread's pair slot through the layers of size m: the records of the next kGivensAhead
+// layers are kept in registers and refilled as layers are applied, so the layers run without
+// waiting on memory.  Every index is a compile-time constant once the layer loop is unrolled.
+constexpr int kGivensAhead = 8;
+struct GivensSlot {
+  uint32_t ab[kGivensAhead];
+  float c[kGivensAhead], s[kGivensAhead];
+  const uint4* rec;    // record of layer 0; layer l at rec[l * stride]
+  int stride, n;
+  __device__ __forceinline__ void fetch(int l) {
+    if (l < n) {
+      const uint4 r = rec[l * stride];
+      ab[l % kGivensAhead] = r.x;
+      c[l % kGivensAhead] = __uint_as_float(r.y);
+      s[l % kGivensAhead] = __uint_as_float(r.z);
+    }
+  }
+  // layer l on x (forward, exact rounding sequence); then the record kGivensAhead layers on
+  __device__ __forceinline__ void apply(float* x, int l) {
+    const int k = l % kGivensAhead, ia = int(ab[k] & 0xffffu), ib = int(ab[k] >> 16);
+    const float xa = x[ia], xb = x[ib];
+    x[ia] = c[k] * xa - s[k] * xb;
+    x[ib] = s[k] * xa + c[k] * xb;
+  }
+};
+__device__ __forceinline__ void givens_fetch(const uint4* G, int m, int slot, GivensSlot& g) {
+  const uint4 h = G[m / 2 - 1];
+  g.n = min(int(h.y), kMaxGivensLayers);
+  g.rec = G + h.x + slot;
+  g.stride = m / 2;
+#pragma unroll
+  for (int l = 0; l < kGivensAhead; ++l) g.fetch(l);
+}
+
 // ===================================================================== block energy
 // Label-free energy of RoPE block j (abstract: one score per RoPE block, per layer and KV
 // head, no labels needed).  Reading: mean over tokens of the squared norm of the block's
@@ -302,12 +367,38 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     knrm[r * kMaxGroups + g] = sqrtf(ss);
   }
   __syncthreads();
+  const uint4* const giv = a.givens;
+  if (giv) {
+    // structured rotations, in place, layer by layer: thread (pair slot q, row parity) takes
+    // its slot's records of every layer at once and applies them to half of the rows
+    const int q = tid >> 1, hf = tid & 1;
+    GivensSlot gs;
+    gs.n = 0;
+    int first = 0;
+    if (q < d_eff / 2) {
+      const int g = L.group[2 * q];
+      first = L.g_first[g];
+      givens_fetch(giv, L.g_m[g], q - first / 2, gs);
+    }
+    const int nl = givens_layers(giv, L);
+#pragma unroll
+    for (int l = 0; l < kMaxGivensLayers; ++l) {
+      if (l < nl) {
+        if (l < gs.n) {
+          for (int r = r0 + hf; r < r0 + nrows; r += 2) gs.apply(xg + r * XS + first, l);
+          if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
+        }
+        __syncthreads();
+      }
+    }
+  }
   // key codes, storage order
   for (int it = tid; it < nrows * d_eff; it += nt) {
     const int r = r0 + (by_pos ? it / d_eff : it % nrows);
     const int p = by_pos ? it % d_eff : it / nrows;
     const int g = L.group[p], w = L.g_width[g], m = L.g_m[g], first = L.g_first[g];
-    const float acc = seq_dot(a.rot_bank + bank_offset(m) + size_t(p - first) * m, xg + r * XS + first, m);
+    const float acc = giv ? xg[r * XS + p]
+                          : seq_dot(a.rot_bank + bank_offset(m) + size_t(p - first) * m, xg + r * XS + first, m);
     const float nv = knrm[r * kMaxGroups + g];
     int code = 0;
     if (nv != 0.0f) code = code_of(thr + (w - 1) * 255, w, (acc / nv) * sqrtf(float(m)));
@@ -325,11 +416,28 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     vnrm[r] = sqrtf(ss);
   }
   __syncthreads();
+  if (giv) {
+    const int q = tid >> 1, hf = tid & 1;
+    GivensSlot gs;
+    gs.n = 0;
+    if (q < d / 2) givens_fetch(giv, d, q, gs);
+    const int nl = givens_count(giv, d);
+#pragma unroll
+    for (int l = 0; l < kMaxGivensLayers; ++l) {
+      if (l < nl) {
+        if (l < gs.n) {
+          for (int r = r0 + hf; r < r0 + nrows; r += 2) gs.apply(xs + r * XS, l);
+          if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
+        }
+        __syncthreads();
+      }
+    }
+  }
   const float sd = sqrtf(float(d));
   for (int it = tid; it < nrows * d; it += nt) {
     const int r = r0 + (by_pos ? it / d : it % nrows);
     const int i = by_pos ? it % d : it / nrows;
-    const float acc = seq_dot(a.rot_v + size_t(i) * d, xs + r * XS, d);
+    const float acc = giv ? xs[r * XS + i] : seq_dot(a.rot_v + size_t(i) * d, xs + r * XS, d);
     const float nv = vnrm[r];
     int code = 0;
     if (nv != 0.0f) code = code_of(thr + (a.v_bits - 1) * 255, a.v_bits, (acc / nv) * sd);
@@ -472,7 +580,7 @@ __host__ __device__ inline size_t append_one_lds_bytes(int d, bool stage_v) {
   return size_t(kAppendThrFloats) * 4 + (stage_v ? size_t(d) * (d + 1) * 4 : 0);
 }
 
-template <typename T, bool STAGE_V, bool WIN>
+template <typename T, bool STAGE_V, bool WIN, bool GIV>
 __device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float* dyn) {
   constexpr int HP = 2;
   constexpr int DM = BGTQ_MAX_HEAD_DIM;
@@ -490,7 +598,7 @@ __device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float
   // ---- inputs that do not depend on the sequence length
 #pragma unroll 2
   for (int i = tid; i < kAppendThrFloats; i += 1024) thr[i] = (&c_thr[0][0])[i];
-  if (STAGE_V) {
+  if (STAGE_V && !GIV) {
     const float4* src = reinterpret_cast<const float4*>(a.rot_v);
 #pragma unroll 4
     for (int i = tid; i < d * d / 4; i += 1024) {
@@ -537,23 +645,58 @@ __device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float
     for (int i = t; i < 2 * DM + 16; i += 512) xk[hp][i] = i < d_eff ? ko[hp][L.perm[i]] : 0.0f;
     if (t < kMaxRecordDwords) kw[hp][t] = 0u;
     __syncthreads();
-    // norms run beside the rotations when the head has threads to spare (always for d <= 128)
-    const bool norms_beside = d + d_eff + ng + 1 <= 512;
     float acc = 0.0f;
-    if (act && t < d) {                                  // value rotation, row t
-      acc = STAGE_V ? dot_rows_lds(rv, d + 1, d, t, xv[hp]) : dot_rows_t(a.rot_v_t, d, d, t, xv[hp]);
-    } else if (t >= d && t < d + d_eff) {                // key position p, row p - first of its group
-      const int p = t - d, g = L.group[p], m = L.g_m[g], first = L.g_first[g];
-      acc = dot_rows_t(a.rot_bank_t + bank_offset(m), m, mmax, p - first, xk[hp] + first);
-    } else if (norms_beside && t >= d + d_eff && t < d + d_eff + ng) {   // group norm
-      const int g = t - d - d_eff;
-      nrm[hp][g] = sqrtf(seq_sumsq(xk[hp] + L.g_first[g], L.g_m[g]));
-    } else if (act && norms_beside && t == d + d_eff + ng) {             // value norm
-      nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
-    }
-    if (!norms_beside) {
+    if constexpr (GIV) {
+      // structured rotations: norms of the unrotated vectors, then the layers in place (both
+      // heads of the pair in lockstep, as many layers as the longest needs)
       if (t < ng) nrm[hp][t] = sqrtf(seq_sumsq(xk[hp] + L.g_first[t], L.g_m[t]));
       else if (act && t == ng) nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
+      // one pair slot per thread: value slot t, or key slot t - 256 of its width group
+      GivensSlot gs;
+      gs.n = 0;
+      float* gx = nullptr;
+      if (act && t < d / 2) {
+        givens_fetch(a.givens, d, t, gs);
+        gx = xv[hp];
+      } else if (t >= 256 && t < 256 + d_eff / 2) {
+        const int q = t - 256, g = L.group[2 * q], first = L.g_first[g];
+        givens_fetch(a.givens, L.g_m[g], q - first / 2, gs);
+        gx = xk[hp] + first;
+      }
+      int nl = givens_count(a.givens, d);
+      for (int hh = 0; hh < HP; ++hh)
+        if (h0 + hh < a.n_kv_heads) nl = max(nl, givens_layers(a.givens, Ls[hh]));
+      __syncthreads();
+#pragma unroll
+      for (int l = 0; l < kMaxGivensLayers; ++l) {
+        if (l < nl) {
+          if (l < gs.n) {
+            gs.apply(gx, l);
+            if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
+          }
+          __syncthreads();
+        }
+      }
+      if (act && t < d) acc = xv[hp][t];
+      else if (t >= d && t < d + d_eff) acc = xk[hp][t - d];
+    } else {
+      // norms run beside the rotations when the head has threads to spare (always for d <= 128)
+      const bool norms_beside = d + d_eff + ng + 1 <= 512;
+      if (act && t < d) {                                  // value rotation, row t
+        acc = STAGE_V ? dot_rows_lds(rv, d + 1, d, t, xv[hp]) : dot_rows_t(a.rot_v_t, d, d, t, xv[hp]);
+      } else if (t >= d && t < d + d_eff) {                // key position p, row p - first of its group
+        const int p = t - d, g = L.group[p], m = L.g_m[g], first = L.g_first[g];
+        acc = dot_rows_t(a.rot_bank_t + bank_offset(m), m, mmax, p - first, xk[hp] + first);
+      } else if (norms_beside && t >= d + d_eff && t < d + d_eff + ng) {   // group norm
+        const int g = t - d - d_eff;
+        nrm[hp][g] = sqrtf(seq_sumsq(xk[hp] + L.g_first[g], L.g_m[g]));
+      } else if (act && norms_beside && t == d + d_eff + ng) {             // value norm
+        nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
+      }
+      if (!norms_beside) {
+        if (t < ng) nrm[hp][t] = sqrtf(seq_sumsq(xk[hp] + L.g_first[t], L.g_m[t]));
+        else if (act && t == ng) nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
+      }
     }
     __syncthreads();
     // codes: a value code goes straight into the slot's dwords (read before any arithmetic);
@@ -588,10 +731,10 @@ __device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float
   if (tid == 0 && a.advance) a.lengths[s] = int32_t(len + 1);
 }
 
-template <typename T, bool STAGE_V, bool WIN>
+template <typename T, bool STAGE_V, bool WIN, bool GIV>
 __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
   extern __shared__ __align__(16) float dyn[];
-  append_one_wg<T, STAGE_V, WIN>(a, blockIdx.x, dyn);
+  append_one_wg<T, STAGE_V, WIN, GIV>(a, blockIdx.x, dyn);
 }
 
 // fp16 keys of the appended tokens that end up among the newest `window` (the last
@@ -663,10 +806,24 @@ __global__ __launch_bounds__(256) void k_decode_prep(DecodeArgs a) {
     qp[h * QS + p] = qs[h * d + L.perm[p]];
   }
   __syncthreads();
+  if (a.givens) {   // structured rotations: every group of every head in place, layer by layer
+    const int nl = givens_layers(a.givens, L);
+    for (int l = 0; l < nl; ++l) {
+      for (int idx = tid; idx < G * (d_eff / 2); idx += 256) {
+        const int h = idx / (d_eff / 2), q = idx - h * (d_eff / 2);
+        uint4 rec;
+        int first;
+        if (givens_slot(a.givens, L, q, l, rec, first)) givens_pair(qp + h * QS + first, rec);
+      }
+      __syncthreads();
+    }
+  }
   const float kscale = a.scale * kLog2e;
-  // q'' of position p and head h: the group's rotation row times q' (fp32 fused multiply-adds)
+  // q'' of position p and head h: the group's rotation row times q' (fp32 fused multiply-adds),
+  // or the rotated q' itself for structured rotations
   auto qpp = [&](int p, int h) {
     const int g = L.group[p], m = L.g_m[g], first = L.g_first[g];
+    if (a.givens) return qp[h * QS + p] * (kscale / sqrtf(float(m)));
     const float2* R2 = reinterpret_cast<const float2*>(a.rot_bank + bank_offset(m) + size_t(p - first) * m);
     const float* x = qp + h * QS + first;
     float acc = 0.0f;
@@ -1091,6 +1248,25 @@ __device__ __forceinline__ void qops_zero(uint4* qhi, uint4* qlo, uint4* qlate, 
 // q'' of storage position p = p0 + tid / 2 (every 128 positions): the thread pair splits the
 // rotation row in two halves and covers all 8 heads, then each thread scatters 4 heads.
 // qc = q' [coordinate][8 heads] and the layout copy Ls are in LDS.
+// q'' of storage position p for heads 4 kh .. 4 kh + 3 (v) into the B operand slots of its
+// k-step, fp16 high part and remainder; heads >= G stay zero
+__device__ __forceinline__ void qops_put(const HeadLayout* Ls, uint32_t wmask, int nn, int p, int kh, int G,
+                                         const float (&v)[4], uint4* qhi, uint4* qlo, uint4* qlate) {
+  const int kx = Ls->kpos[p], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm_of(wmask, nn, ks0);
+  const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks0 + jj] >> 28) & 1u);
+  uint16_t* h16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qhi + 64 * ks : qlate + 128 * (ks - kQRegSteps));
+  uint16_t* l16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qlo + 64 * ks : qlate + 128 * (ks - kQRegSteps) + 64);
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    const int h = 4 * kh + hh;
+    if (h < G) {
+      const uint16_t hi = f32_to_f16_bits(v[hh]);
+      h16[(lb + h) * 8 + e] = hi;
+      l16[(lb + h) * 8 + e] = f32_to_f16_bits(v[hh] - f16_bits_to_f32(hi));
+    }
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void qops_scatter(const DecodeArgs& a, const HeadLayout* Ls, const float* qc, uint32_t wmask,
                                              int nn, int tid, uint4* qhi, uint4* qlo, uint4* qlate) {
@@ -1143,20 +1319,61 @@ __device__ __forceinline__ void qops_scatter(const DecodeArgs& a, const HeadLayo
       const float other = __shfl_xor(give, 1);
       v[e] = (kh == 0 ? mine + other : other + mine) * (kscale / sqrtf(float(m)));
     }
-    if (p < d_eff) {
-      const int kx = Ls->kpos[p], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm_of(wmask, nn, ks0);
-      const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks0 + jj] >> 28) & 1u);
-      uint16_t* h16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qhi + 64 * ks : qlate + 128 * (ks - kQRegSteps));
-      uint16_t* l16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qlo + 64 * ks : qlate + 128 * (ks - kQRegSteps) + 64);
+    if (p < d_eff) qops_put(Ls, wmask, nn, p, kh, G, v, qhi, qlo, qlate);
+  }
+}
+
+// Structured rotations of q' (qc [coordinate][8 heads]) into every width group's frame, in
+// place: the pair slots of a group act on original coordinates perm[first + a] and
+// perm[first + b]; thread tid < d_eff takes pair slot tid / 2 and four heads (nt >= d_eff
+// threads).  Every thread of the workgroup calls it (it holds the barriers).
+__device__ __forceinline__ void qops_givens_rotate(const DecodeArgs& a, const HeadLayout* Ls, float* qc, int tid,
+                                                   int nt) {
+  const int d_eff = Ls->d_eff, q = tid >> 1;        // thread: pair slot q, heads 4 (tid & 1) ..
+  GivensSlot gs;
+  gs.n = 0;
+  int first = 0;
+  if (tid < d_eff && tid < nt) {
+    const int g = Ls->group[2 * q];
+    first = Ls->g_first[g];
+    givens_fetch(a.givens, Ls->g_m[g], q - first / 2, gs);
+  }
+  const int nl = givens_layers(a.givens, *Ls);
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const int h = 4 * kh + hh;
-        if (h < G) {
-          const uint16_t hi = f32_to_f16_bits(v[hh]);
-          h16[(lb + h) * 8 + e] = hi;
-          l16[(lb + h) * 8 + e] = f32_to_f16_bits(v[hh] - f16_bits_to_f32(hi));
-        }
+  for (int l = 0; l < kMaxGivensLayers; ++l) {
+    if (l < nl) {
+      if (l < gs.n) {
+        const int k = l % kGivensAhead;
+        const int ca = Ls->perm[first + int(gs.ab[k] & 0xffffu)], cb = Ls->perm[first + int(gs.ab[k] >> 16)];
+        const float c = gs.c[k], sn = gs.s[k];
+        float4* pa = reinterpret_cast<float4*>(qc + 8 * ca + 4 * (tid & 1));
+        float4* pb = reinterpret_cast<float4*>(qc + 8 * cb + 4 * (tid & 1));
+        const float4 xa = *pa, xb = *pb;
+        *pa = float4{fmaf(c, xa.x, -sn * xb.x), fmaf(c, xa.y, -sn * xb.y), fmaf(c, xa.z, -sn * xb.z),
+                     fmaf(c, xa.w, -sn * xb.w)};
+        *pb = float4{fmaf(sn, xa.x, c * xb.x), fmaf(sn, xa.y, c * xb.y), fmaf(sn, xa.z, c * xb.z),
+                     fmaf(sn, xa.w, c * xb.w)};
+        if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
       }
+      __syncthreads();
+    }
+  }
+}
+
+// B operands from q' already rotated into the group frames (qops_givens_rotate):
+// q''_p = q'[perm[p]] * softmax_scale * log2(e) / sqrt(m); 256 threads, as qops_scatter.
+__device__ __forceinline__ void qops_scatter_rotated(const DecodeArgs& a, const HeadLayout* Ls, const float* qc,
+                                                     uint32_t wmask, int nn, int tid, uint4* qhi, uint4* qlo,
+                                                     uint4* qlate) {
+  const int d_eff = Ls->d_eff, kh = tid & 1, G = a.group;
+  const float kscale = a.scale * kLog2e;
+  for (int p0 = 0; p0 < d_eff; p0 += 128) {
+    const int p = p0 + (tid >> 1);
+    if (p < d_eff) {
+      const float f = kscale / sqrtf(float(Ls->g_m[Ls->group[p]]));
+      const float4 x = *reinterpret_cast<const float4*>(qc + 8 * Ls->perm[p] + 4 * kh);
+      const float v[4] = {x.x * f, x.y * f, x.z * f, x.w * f};
+      qops_put(Ls, wmask, nn, p, kh, G, v, qhi, qlo, qlate);
     }
   }
 }
@@ -1364,7 +1581,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       qlo[ks * 64 + lane] = __builtin_bit_cast(uint4, lo);
     }
   } else if (!PRE) {
-    qops_scatter<D>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlate);
+    if (a.givens) {
+      qops_givens_rotate(a, Ls, qc, tid, 256);
+      qops_scatter_rotated(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlate);
+    } else {
+      qops_scatter<D>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlate);
+    }
   }
   __syncthreads();   // also orders the prologue's reads of the ring before the first staging store
 
@@ -1643,9 +1865,11 @@ __device__ __forceinline__ void query_wg(const DecodeArgs& a, int s, int hk, uin
     q_rope<D>(a, pos, fr, tid, x0, x1, qc);
   }
   __syncthreads();
+  if (a.givens) qops_givens_rotate(a, Ls, qc, tid, int(blockDim.x));
   if (mine) {
     const uint32_t wmask = wide_ksteps(Ls, nks, lane);
-    qops_scatter<D>(a, Ls, qc, wmask, nks - __popc(wmask), tid, qhi, qlo, qlate);
+    if (a.givens) qops_scatter_rotated(a, Ls, qc, wmask, nks - __popc(wmask), tid, qhi, qlo, qlate);
+    else qops_scatter<D>(a, Ls, qc, wmask, nks - __popc(wmask), tid, qhi, qlo, qlate);
   }
   __syncthreads();
   uint4* dst = a.qpre + reg * tc_ksteps(D) * 128;
@@ -1655,11 +1879,11 @@ __device__ __forceinline__ void query_wg(const DecodeArgs& a, int s, int hk, uin
   }
 }
 
-template <typename T, bool STAGE_V, int D, typename QT, bool WIN>
+template <typename T, bool STAGE_V, int D, typename QT, bool WIN, bool GIV>
 __global__ __launch_bounds__(1024) void k_step_front(AppendArgs aa, DecodeArgs da, int n_seqs) {
   extern __shared__ __align__(16) uint8_t lds8[];
   if (int(blockIdx.x) < n_seqs) {
-    append_one_wg<T, STAGE_V, WIN>(aa, blockIdx.x, reinterpret_cast<float*>(lds8));
+    append_one_wg<T, STAGE_V, WIN, GIV>(aa, blockIdx.x, reinterpret_cast<float*>(lds8));
   } else {
     const int r = blockIdx.x - n_seqs;
     query_wg<D, QT>(da, r / da.n_kv, r % da.n_kv, lds8);
@@ -1718,6 +1942,19 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     if (g + NG * b < ns) add(x[b], mlv[b]);
   for (int i = g + NG * NB; i < ns; i += NG) add(acc4[size_t(i) * C4 + c4], ml[i]);
   part4[tid] = v;
+  // structured value rotation: this thread's pair slot records, requested before the
+  // reduction below so that their latency overlaps it
+  // (the transpose runs the layers backwards: the slot walks them from the last one)
+  GivensSlot gs;
+  gs.n = 0;
+  if (a.givens && tid < D / 2) {
+    const uint4 hv = a.givens[D / 2 - 1];
+    gs.n = min(int(hv.y), kMaxGivensLayers);
+    gs.rec = a.givens + hv.x + (gs.n - 1) * (D / 2) + tid;
+    gs.stride = -(D / 2);
+#pragma unroll
+    for (int l = 0; l < kGivensAhead; ++l) gs.fetch(l);
+  }
   __syncthreads();
   float ltot = 0.0f;
 #pragma unroll
@@ -1731,20 +1968,44 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     accs[4 * tid] = t.x; accs[4 * tid + 1] = t.y; accs[4 * tid + 2] = t.z; accs[4 * tid + 3] = t.w;
   }
   __syncthreads();
-  {
-    const int r = tid % D, qq = tid / D;
-    float o = 0.0f;
-#pragma unroll 8
-    for (int c = qq * (D / RS); c < (qq + 1) * (D / RS); ++c) o = fmaf(a.rot_v[c * D + r], accs[c], o);
-    outp[tid] = o;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float o = 0.0f;
+  if (a.givens) {
+    // structured rotations: the transpose, layers in reverse order, each pair as
+    // [[c, s], [-s, c]]; thread t < D/2 owns pair slot t (records fetched above)
+    const int nl = givens_count(a.givens, D);
 #pragma unroll
-    for (int qq = 0; qq < RS; ++qq) o += outp[qq * D + tid];
-    const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
-    a.out[(int64_t(s) * a.n_q + h) * D + tid] = o * inv;
+    for (int i = 0; i < kMaxGivensLayers; ++i) {   // i-th layer from the last
+      if (i < nl) {
+        if (i < gs.n) {
+          const int k = i % kGivensAhead;
+          const int ia = int(gs.ab[k] & 0xffffu), ib = int(gs.ab[k] >> 16);
+          const float xa = accs[ia], xb = accs[ib];
+          accs[ia] = fmaf(gs.c[k], xa, gs.s[k] * xb);
+          accs[ib] = fmaf(gs.c[k], xb, -gs.s[k] * xa);
+          if (i + kGivensAhead < kMaxGivensLayers) gs.fetch(i + kGivensAhead);
+        }
+        __syncthreads();
+      }
+    }
+    if (tid < D) {
+      const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
+      a.out[(int64_t(s) * a.n_q + h) * D + tid] = accs[tid] * inv;
+    }
+  } else {
+    {
+      const int r = tid % D, qq = tid / D;
+      float o = 0.0f;
+#pragma unroll 8
+      for (int c = qq * (D / RS); c < (qq + 1) * (D / RS); ++c) o = fmaf(a.rot_v[c * D + r], accs[c], o);
+      outp[tid] = o;
+    }
+    __syncthreads();
+    if (tid < D) {
+      float o = 0.0f;
+#pragma unroll
+      for (int qq = 0; qq < RS; ++qq) o += outp[qq * D + tid];
+      const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
+      a.out[(int64_t(s) * a.n_q + h) * D + tid] = o * inv;
+    }
   }
   if (a.step && h == 0 && tid == 0) {     // the decode step's length advance, after every reader
     const int len0 = a.lengths[s];
@@ -1800,6 +2061,13 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st)
   return hipGetLastError();
 }
 
+// the decode step's first kernel for the input dtypes, window and rotation kind
+template <bool SV, int D, bool WIN, bool GIV>
+auto step_front_kernel(bool kb, bool qb) -> void (*)(AppendArgs, DecodeArgs, int) {
+  return kb ? (qb ? k_step_front<uint16_t, SV, D, uint16_t, WIN, GIV> : k_step_front<uint16_t, SV, D, float, WIN, GIV>)
+            : (qb ? k_step_front<float, SV, D, uint16_t, WIN, GIV> : k_step_front<float, SV, D, float, WIN, GIV>);
+}
+
 template <int D>
 hipError_t launch_step_front(const AppendArgs& aa, const DecodeArgs& da, bgtq_dtype kv_dt, bgtq_dtype q_dt,
                              int n_seqs, hipStream_t st) {
@@ -1808,13 +2076,10 @@ hipError_t launch_step_front(const AppendArgs& aa, const DecodeArgs& da, bgtq_dt
                        size_t(2048) * (tc_ksteps(D) > kQRegSteps ? tc_ksteps(D) - kQRegSteps : 0);
   const size_t a_lds = append_one_lds_bytes(D, SV);
   const size_t lds = q_lds > a_lds ? q_lds : a_lds;
-  const bool kb = kv_dt == BGTQ_BF16, qb = q_dt == BGTQ_BF16;
+  const bool kb = kv_dt == BGTQ_BF16, qb = q_dt == BGTQ_BF16, w = aa.window > 0;
   void (*fn)(AppendArgs, DecodeArgs, int) =
-      aa.window > 0
-          ? (kb ? (qb ? k_step_front<uint16_t, SV, D, uint16_t, true> : k_step_front<uint16_t, SV, D, float, true>)
-                : (qb ? k_step_front<float, SV, D, uint16_t, true> : k_step_front<float, SV, D, float, true>))
-          : (kb ? (qb ? k_step_front<uint16_t, SV, D, uint16_t, false> : k_step_front<uint16_t, SV, D, float, false>)
-                : (qb ? k_step_front<float, SV, D, uint16_t, false> : k_step_front<float, SV, D, float, false>));
+      aa.givens ? (w ? step_front_kernel<SV, D, true, true>(kb, qb) : step_front_kernel<SV, D, false, true>(kb, qb))
+                : (w ? step_front_kernel<SV, D, true, false>(kb, qb) : step_front_kernel<SV, D, false, false>(kb, qb));
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
@@ -1878,10 +2143,10 @@ hipError_t launch_allocate(const double* energy, int n_heads, int n_blocks, int 
 
 namespace {
 // the one-token append kernel for the input dtype, value staging and window
-template <bool WIN>
+template <bool WIN, bool GIV>
 auto append_one_kernel(bool bf16, bool stage_v) -> void (*)(AppendArgs) {
-  return bf16 ? (stage_v ? k_append_one<uint16_t, true, WIN> : k_append_one<uint16_t, false, WIN>)
-              : (stage_v ? k_append_one<float, true, WIN> : k_append_one<float, false, WIN>);
+  return bf16 ? (stage_v ? k_append_one<uint16_t, true, WIN, GIV> : k_append_one<uint16_t, false, WIN, GIV>)
+              : (stage_v ? k_append_one<float, true, WIN, GIV> : k_append_one<float, false, WIN, GIV>);
 }
 }  // namespace
 
@@ -1889,8 +2154,9 @@ hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStre
   if (a.n_new == 1) {   // decode step: one token per sequence, length advanced in the same kernel
     const bool stage_v = a.d <= 128;
     const size_t lds = append_one_lds_bytes(a.d, stage_v);
-    void (*fn)(AppendArgs) =
-        a.window > 0 ? append_one_kernel<true>(dt == BGTQ_BF16, stage_v) : append_one_kernel<false>(dt == BGTQ_BF16, stage_v);
+    const bool bf = dt == BGTQ_BF16, w = a.window > 0;
+    void (*fn)(AppendArgs) = a.givens ? (w ? append_one_kernel<true, true>(bf, stage_v) : append_one_kernel<false, true>(bf, stage_v))
+                                      : (w ? append_one_kernel<true, false>(bf, stage_v) : append_one_kernel<false, false>(bf, stage_v));
     const hipError_t e =
         hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;

@@ -61,6 +61,13 @@ typedef void* bgtq_stream;
 #define BGTQ_LAYOUT_BYTES 4096   /* size of one per-head layout descriptor */
 #define BGTQ_MAX_WINDOW 4096     /* tokens in the fp16 recent-key window */
 
+/* Rotation kinds.  The abstract builds on TQ-MSE, which rotates before scalar coding, and
+ * fixes no rotation type.  DENSE: one Haar matrix per size (m x m multiply-adds per
+ * vector).  GIVENS: a structured rotation per size m, a product of layers that each rotate
+ * the pairs of a perfect matching of the m coordinates by their own angle, O(m log m) per
+ * vector.  The two give different codes; a cache is written and read with one kind. */
+typedef enum { BGTQ_ROT_DENSE = 0, BGTQ_ROT_GIVENS = 1 } bgtq_rotation;
+
 /* Random rotations the quantizer draws (TQ-MSE rotates before scalar coding).
  * Device memory, caller-owned, read-only, shared by all layers and heads.
  *   rot_bank:   Haar matrices for the key width groups, m = 2, 4, ..., head_dim,
@@ -70,13 +77,25 @@ typedef void* bgtq_stream;
  *   rot_bank_t, rot_v_t: the same matrices transposed (each block column-major),
  *               written by bgtq_transpose_rotations; kernels that form one
  *               output row per lane read these so that a wavefront's loads are
- *               contiguous. */
+ *               contiguous.
+ *   (the four matrices are read with rotation = BGTQ_ROT_DENSE and may be NULL otherwise)
+ *   givens      with rotation = BGTQ_ROT_GIVENS: uint32 rows of 4.  Rows 0..127 are a
+ *               header, row m/2 - 1 = (first record row of size m, layer count L_m, 0, 0)
+ *               for every even m <= head_dim; a record row is (a | b << 16, fp32 bits of
+ *               c, fp32 bits of s, 0), and size m has L_m layers of m/2 records, layer by
+ *               layer.  Layer l maps y_a = c x_a - s x_b, y_b = s x_a + c x_b for each of
+ *               its pairs (a, b), which must form a perfect matching of 0..m-1; every
+ *               product, difference and sum is rounded to fp32 (no fused multiply-add), so
+ *               codes are reproducible bit for bit.  Values use size head_dim.  Keys are
+ *               rotated per width group in storage order. */
 typedef struct {
   const float* rot_bank;
   const float* rot_v;
   const float* rot_bank_t;
   const float* rot_v_t;
   int head_dim;
+  bgtq_rotation rotation;
+  const uint32_t* givens;
 } bgtq_quantizer;
 
 /* Floats in a rotation bank for head_dim (sum of m*m over even m <= head_dim), 0 if

@@ -162,6 +162,24 @@ def test_decode_step_validation():
     assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
 
 
+def test_rotation_kind_validation():
+    lib = bgtq.lib()
+    need = lib.bgtq_decode_workspace_bytes(1, 16, 2, 128, 256)
+
+    def decode(qz):
+        return lib.bgtq_decode_attention(ctypes.byref(qz), ctypes.byref(_desc()), 16, FAKE, 0, None, 1e6, 0.0,
+                                         FAKE, None, FAKE, need, None)
+
+    # a valid quantizer gets as far as the softmax-scale check (scale 0 is invalid)
+    assert decode(bgtq.Quantizer(None, None, None, None, 128, bgtq.ROT_GIVENS, FAKE)) == bgtq.ERR_INVALID_ARG
+    assert b"softmax_scale" in lib.bgtq_last_error()
+    assert decode(bgtq.Quantizer(None, None, None, None, 128, bgtq.ROT_GIVENS, None)) == bgtq.ERR_INVALID_ARG
+    assert b"givens" in lib.bgtq_last_error()
+    assert decode(bgtq.Quantizer(FAKE, FAKE, FAKE, FAKE, 128, 2, FAKE)) == bgtq.ERR_INVALID_ARG
+    assert b"rotation kind" in lib.bgtq_last_error()
+    assert decode(bgtq.Quantizer(None, FAKE, FAKE, FAKE, 128, bgtq.ROT_DENSE, FAKE)) == bgtq.ERR_INVALID_ARG
+
+
 def test_window_validation():
     lib = bgtq.lib()
     need = lib.bgtq_decode_workspace_bytes(1, 16, 2, 128, 256)
