@@ -64,6 +64,8 @@ _SIGNATURES = {
     "bgtq_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i64]),
     "bgtq_decode_step": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _f64, _f32, _vp, _vp, _vp,
                                 _sz, _vp]),
+    "bgtq_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "bgtq_prefill_workspace_bytes": (_sz, [_i32, _i64, _i32]),
     "bgtq_logit_error": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64,
                                 _i32, _f64, _f32, _vp, _vp, _vp, _sz, _vp]),
     "bgtq_logit_error_workspace_bytes": (_sz, [_i32, _i32, _i64]),
@@ -277,6 +279,29 @@ def bgtq_quantize_append(quantizer: Quantizer, cache: PackedCache, keys: torch.T
     _check(lib().bgtq_quantize_append(_c.byref(quantizer), _c.byref(desc), seq_begin, n_seqs, keys.data_ptr(),
                                       values.data_ptr(), _dtype_code(keys), n_new, keys.stride(0), keys.stride(1),
                                       keys.stride(2), _stream()))
+
+
+def bgtq_prefill(quantizer: Quantizer, cache: PackedCache, keys: torch.Tensor, values: torch.Tensor, seq: int,
+                 b_min: int = 0, b_max: int = 8, energy_out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> None:
+    """keys, values [n_kv_heads, T, head_dim] (same strides, last dim contiguous) of sequence `seq`:
+    energies, widths and layouts, and the quantize-and-append of the T tokens, in one call."""
+    if keys.shape != values.shape or keys.stride() != values.stride() or keys.dtype != values.dtype:
+        raise ValueError("keys and values must have the same shape, strides and dtype")
+    if keys.dim() != 3 or keys.stride(2) != 1:
+        raise ValueError("keys must be [n_kv_heads, n_tokens, head_dim] with a contiguous last dimension")
+    h, t, d = keys.shape
+    if h != cache.n_kv_heads or d != cache.head_dim:
+        raise ValueError("keys do not match the cache geometry")
+    if energy_out is not None and (energy_out.dtype != torch.float64 or energy_out.numel() != h * (d // 2)):
+        raise ValueError("energy_out must be fp64 [n_kv_heads, head_dim/2]")
+    if workspace is None:
+        workspace = torch.empty(max(int(lib().bgtq_prefill_workspace_bytes(h, t, d)), 8), dtype=torch.uint8,
+                                device=keys.device)
+    desc = cache.desc()
+    _check(lib().bgtq_prefill(_c.byref(quantizer), _c.byref(desc), seq, keys.data_ptr(), values.data_ptr(),
+                              _dtype_code(keys), t, keys.stride(0), keys.stride(1), b_min, b_max, _ptr(energy_out),
+                              workspace.data_ptr(), workspace.numel(), _stream()))
 
 
 def bgtq_decode_attention(quantizer: Quantizer, cache: PackedCache, q: torch.Tensor, rope_theta: float,

@@ -248,6 +248,45 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
   return hip_status(launch_append(a, dtype, n_seqs, static_cast<hipStream_t>(stream)), "quantize-append launch");
 }
 
+size_t bgtq_prefill_workspace_bytes(int n_kv_heads, int64_t n_tokens, int head_dim) {
+  return bgtq_energy_workspace_bytes(n_kv_heads, n_tokens, head_dim);
+}
+
+bgtq_status bgtq_prefill(const bgtq_quantizer* qz, const bgtq_cache* cache, int seq, const void* keys,
+                         const void* values, bgtq_dtype dtype, int64_t n_tokens, int64_t stride_head,
+                         int64_t stride_token, int b_min, int b_max, double* energy_out, void* workspace,
+                         size_t workspace_bytes, bgtq_stream stream) {
+  if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
+  if (seq < 0 || seq >= cache->batch) return fail(BGTQ_ERR_INVALID_ARG, "sequence %d outside batch %d", seq, cache->batch);
+  if (!cache->widths) return fail(BGTQ_ERR_INVALID_ARG, "widths is NULL");
+  const int d = cache->head_dim, n = d / 2;
+  if (b_min < 0 || b_max < b_min || b_max > BGTQ_MAX_BITS)
+    return fail(BGTQ_ERR_BUDGET, "need 0 <= b_min <= b_max <= 8 (got %d, %d)", b_min, b_max);
+  if (cache->k_width_sum < n * b_min || cache->k_width_sum > n * b_max)
+    return fail(BGTQ_ERR_BUDGET, "k_width_sum %d outside [%d, %d]", cache->k_width_sum, n * b_min, n * b_max);
+  if (n_tokens < 1) return fail(BGTQ_ERR_INVALID_ARG, "n_tokens must be >= 1");
+  if (cache->n_kv_heads > 1 && stride_head < 1) return fail(BGTQ_ERR_INVALID_ARG, "stride_head must be >= 1");
+  AppendArgs aa;
+  if (bgtq_status st = prepare_append(qz, cache, seq, 1, keys, values, dtype, n_tokens,
+                                      stride_head * cache->n_kv_heads > 0 ? stride_head * cache->n_kv_heads : 1,
+                                      stride_head > 0 ? stride_head : 1, stride_token, aa);
+      st != BGTQ_OK)
+    return st;
+  const size_t need = bgtq_prefill_workspace_bytes(cache->n_kv_heads, n_tokens, d);
+  if (!workspace || workspace_bytes < need) return fail(BGTQ_ERR_WORKSPACE, "prefill workspace needs %zu bytes", need);
+  if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t reg = size_t(seq) * cache->n_kv_heads;
+  if (bgtq_status st = hip_status(
+          launch_prefill_alloc(keys, dtype, cache->n_kv_heads, n_tokens, d, stride_head, stride_token, cache->pairing,
+                               static_cast<double*>(workspace), cache->k_width_sum - n * b_min, b_min, b_max,
+                               energy_out, cache->widths + reg * n, static_cast<HeadLayout*>(cache->layouts) + reg, s),
+          "prefill energy/allocation launch");
+      st != BGTQ_OK)
+    return st;
+  return hip_status(launch_append(aa, dtype, 1, s), "prefill quantize-append launch");
+}
+
 size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t capacity) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || capacity < kTile) return 0;
   const int splits = decode_splits(batch, n_kv_heads, capacity, true) + kMaxWindowSplits;   // an upper bound

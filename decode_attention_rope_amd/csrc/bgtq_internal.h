@@ -89,6 +89,12 @@ hipError_t launch_energy(const void* keys, bgtq_dtype dt, int n_heads, int64_t n
                          int64_t sh, int64_t st, int pairing, double* energy, double* partial,
                          hipStream_t s);
 
+// prefill of one sequence's heads: energy partials, then the final sums and the allocation
+// in one kernel (per-head widths and layouts written at `widths`, `layouts`)
+hipError_t launch_prefill_alloc(const void* keys, bgtq_dtype dt, int n_heads, int64_t n_tokens, int d, int64_t sh,
+                               int64_t st, int pairing, double* partial, int increments, int b_min, int b_max,
+                               double* energy_out, uint8_t* widths, HeadLayout* layouts, hipStream_t s);
+
 hipError_t launch_allocate(const double* energy, int n_heads, int n_blocks, int increments, int b_min,
                            int b_max, int pairing, uint8_t* widths, HeadLayout* layouts, hipStream_t s);
 

@@ -172,14 +172,28 @@ __global__ void k_energy_partial(const T* __restrict__ keys, int n_heads, int64_
   part[(int64_t(h) * n_chunks + c) * n + j] = acc;
 }
 
+// Sum of a block's chunk partials in ascending chunk order (p: the block's first partial,
+// consecutive chunks n apart); eight loads are requested before their adds.
+__device__ __forceinline__ double chunk_sum(const double* __restrict__ p, int n_chunks, int n) {
+  double tot = 0.0;
+  int c = 0;
+  for (; c + 8 <= n_chunks; c += 8) {
+    double v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[int64_t(c + i) * n];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tot = tot + v[i];
+  }
+  for (; c < n_chunks; ++c) tot = tot + p[int64_t(c) * n];
+  return tot;
+}
+
 __global__ void k_energy_final(const double* __restrict__ part, int n_heads, int n_chunks, int n,
                                int64_t n_tokens, double* __restrict__ out) {
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n_heads * n) return;
   const int h = gid / n, j = gid % n;
-  double tot = 0.0;
-  for (int c = 0; c < n_chunks; ++c) tot = tot + part[(int64_t(h) * n_chunks + c) * n + j];
-  out[gid] = tot / (double)n_tokens;
+  out[gid] = chunk_sum(part + int64_t(h) * n_chunks * n + j, n_chunks, n) / (double)n_tokens;
 }
 
 // ===================================================================== greedy allocation
@@ -189,16 +203,15 @@ __global__ void k_energy_final(const double* __restrict__ part, int n_heads, int
 // among blocks below b_max, ties to the lowest j.  One wavefront per head, block j on
 // lane j % 64; the arg-max runs over the wave with a (gain, -j) order.  Lane 0 then
 // derives the width groups and the K record layout.
-__global__ __launch_bounds__(64) void k_allocate(const double* __restrict__ energy, int n, int increments,
-                                                 int b_min, int b_max, int pairing,
-                                                 uint8_t* __restrict__ widths,
-                                                 HeadLayout* __restrict__ layouts) {
+// One wavefront allocates one head from its energies e0 (block lane) and e1 (block lane + 64)
+// and writes the widths and the layout descriptor.
+__device__ __forceinline__ void allocate_wave(double e0, double e1, int n, int increments, int b_min, int b_max,
+                                              int pairing, uint8_t* __restrict__ widths_h,
+                                              HeadLayout* __restrict__ layout_h) {
   __shared__ int w_s[128];
   __shared__ HeadLayout lay;
-  const int h = blockIdx.x, lane = threadIdx.x;
+  const int lane = threadIdx.x;
   const int j0 = lane, j1 = lane + 64;
-  const double e0 = j0 < n ? energy[int64_t(h) * n + j0] : 0.0;
-  const double e1 = j1 < n ? energy[int64_t(h) * n + j1] : 0.0;
   int w0 = b_min, w1 = b_min;
   for (int it = 0; it < increments; ++it) {
     const double g0 = (j0 < n && w0 < b_max) ? e0 * c_dgain[w0] : -1.0;
@@ -215,8 +228,8 @@ __global__ __launch_bounds__(64) void k_allocate(const double* __restrict__ ener
     if (j == j0) ++w0;
     else if (j == j1) ++w1;
   }
-  if (j0 < n) { w_s[j0] = w0; widths[int64_t(h) * n + j0] = uint8_t(w0); }
-  if (j1 < n) { w_s[j1] = w1; widths[int64_t(h) * n + j1] = uint8_t(w1); }
+  if (j0 < n) { w_s[j0] = w0; widths_h[j0] = uint8_t(w0); }
+  if (j1 < n) { w_s[j1] = w1; widths_h[j1] = uint8_t(w1); }
   uint32_t* lw = reinterpret_cast<uint32_t*>(&lay);
   for (int i = lane; i < int(sizeof(HeadLayout) / 4); i += 64) lw[i] = 0;
   __syncthreads();
@@ -273,8 +286,35 @@ __global__ __launch_bounds__(64) void k_allocate(const double* __restrict__ ener
       if (lay.seg[i] == 0u) lay.seg[i] = 1u << 16;   // unused slot: width 1 at bit 0
   }
   __syncthreads();
-  uint32_t* dst = reinterpret_cast<uint32_t*>(layouts + h);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(layout_h);
   for (int i = lane; i < int(sizeof(HeadLayout) / 4); i += 64) dst[i] = lw[i];
+}
+
+__global__ __launch_bounds__(64) void k_allocate(const double* __restrict__ energy, int n, int increments,
+                                                 int b_min, int b_max, int pairing,
+                                                 uint8_t* __restrict__ widths,
+                                                 HeadLayout* __restrict__ layouts) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  const double e0 = lane < n ? energy[int64_t(h) * n + lane] : 0.0;
+  const double e1 = lane + 64 < n ? energy[int64_t(h) * n + lane + 64] : 0.0;
+  allocate_wave(e0, e1, n, increments, b_min, b_max, pairing, widths + int64_t(h) * n, layouts + h);
+}
+
+// Prefill: the energy's final reduction and the allocation of one head in one wavefront
+// (the same sums in the same order as k_energy_final, then k_allocate's arithmetic).
+__global__ __launch_bounds__(64) void k_energy_allocate(const double* __restrict__ part, int n_chunks,
+                                                        int64_t n_tokens, int n, int increments, int b_min,
+                                                        int b_max, int pairing, double* __restrict__ energy_out,
+                                                        uint8_t* __restrict__ widths, HeadLayout* __restrict__ layouts) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  const double* p = part + int64_t(h) * n_chunks * n;
+  const double e0 = lane < n ? chunk_sum(p + lane, n_chunks, n) / (double)n_tokens : 0.0;
+  const double e1 = lane + 64 < n ? chunk_sum(p + lane + 64, n_chunks, n) / (double)n_tokens : 0.0;
+  if (energy_out) {
+    if (lane < n) energy_out[int64_t(h) * n + lane] = e0;
+    if (lane + 64 < n) energy_out[int64_t(h) * n + lane + 64] = e1;
+  }
+  allocate_wave(e0, e1, n, increments, b_min, b_max, pairing, widths + int64_t(h) * n, layouts + h);
 }
 
 // ===================================================================== quantize + append
@@ -2131,6 +2171,24 @@ hipError_t launch_energy(const void* keys, bgtq_dtype dt, int n_heads, int64_t n
                        n_heads, n_tokens, n, sh, st, pairing, n_chunks, partial);
   hipLaunchKernelGGL(k_energy_final, dim3((n_heads * n + 255) / 256), dim3(256), 0, s, partial, n_heads,
                      n_chunks, n, n_tokens, energy);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_alloc(const void* keys, bgtq_dtype dt, int n_heads, int64_t n_tokens, int d, int64_t sh,
+                               int64_t st, int pairing, double* partial, int increments, int b_min, int b_max,
+                               double* energy_out, uint8_t* widths, HeadLayout* layouts, hipStream_t s) {
+  const int n = d / 2;
+  const int n_chunks = int((n_tokens + kEnergyChunk - 1) / kEnergyChunk);
+  const int64_t total = int64_t(n_heads) * n_chunks * n;
+  const dim3 grid(unsigned((total + 255) / 256));
+  if (dt == BGTQ_BF16)
+    hipLaunchKernelGGL(k_energy_partial<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(keys),
+                       n_heads, n_tokens, n, sh, st, pairing, n_chunks, partial);
+  else
+    hipLaunchKernelGGL(k_energy_partial<float>, grid, dim3(256), 0, s, static_cast<const float*>(keys),
+                       n_heads, n_tokens, n, sh, st, pairing, n_chunks, partial);
+  hipLaunchKernelGGL(k_energy_allocate, dim3(n_heads), dim3(64), 0, s, partial, n_chunks, n_tokens, n, increments,
+                     b_min, b_max, pairing, energy_out, widths, layouts);
   return hipGetLastError();
 }
 

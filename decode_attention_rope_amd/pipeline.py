@@ -1,9 +1,10 @@
-"""Prefill and decode steps composed from the four library calls.
+"""Prefill and decode steps of the library.
 
 Prefill of one sequence (per layer): block energy of its keys, greedy widths
-under the K budget, then quantize-and-append of the whole prompt.  A decode
-step: append the new token's key and value, then attend (the query's own
-token is the newest cached one).  Every step runs in the HIP library.
+under the K budget, then quantize-and-append of the whole prompt, in one
+bgtq_prefill call.  A decode step: append the new token's key and value, then
+attend (the query's own token is the newest cached one), in one
+bgtq_decode_step call.  Every step runs in the HIP library.
 """
 
 from __future__ import annotations
@@ -16,10 +17,7 @@ from . import bgtq
 def prefill(quantizer, cache: bgtq.PackedCache, keys: torch.Tensor, values: torch.Tensor, seq: int,
             b_min: int = 0, b_max: int = 8) -> None:
     """keys, values [n_kv_heads, T, head_dim] of sequence `seq` (post-RoPE keys)."""
-    energy = bgtq.bgtq_block_energy(keys, cache.pairing)
-    bgtq.bgtq_allocate_bits(energy, cache.k_width_sum, b_min, b_max, cache.pairing,
-                            widths_out=cache.widths[seq], layouts_out=cache.layouts[seq])
-    bgtq.bgtq_quantize_append(quantizer, cache, keys.unsqueeze(0), values.unsqueeze(0), seq_begin=seq)
+    bgtq.bgtq_prefill(quantizer, cache, keys, values, seq, b_min, b_max)
 
 
 def decode_step(quantizer, cache: bgtq.PackedCache, k_new: torch.Tensor, v_new: torch.Tensor,

@@ -218,6 +218,24 @@ bgtq_status bgtq_quantize_append(const bgtq_quantizer* qz, const bgtq_cache* cac
                                  int64_t n_new, int64_t stride_seq, int64_t stride_head,
                                  int64_t stride_token, bgtq_stream stream);
 
+/* Prefill of one sequence: the method's three steps in one call (abstract: per layer and
+ * KV head, block energies from the keys, greedy integer widths under the K budget, TQ-MSE
+ * quantization into the packed cache).  The result equals bgtq_block_energy over the given
+ * keys, bgtq_allocate_bits with the cache's k_width_sum (widths and layouts of sequence
+ * `seq`), then bgtq_quantize_append of the tokens to `seq`, bit for bit; the energies' final
+ * reduction and the allocation run in one kernel.  Keys are read twice (energy, then
+ * quantization): no width is known before every key has been scored.
+ *   keys, values  [n_kv_heads][n_tokens][head_dim] of dtype with strides
+ *                 (stride_head, stride_token, 1); keys post-RoPE.
+ *   energy_out    nullable fp64 [n_kv_heads][head_dim/2].
+ *   workspace     >= bgtq_prefill_workspace_bytes(n_kv_heads, n_tokens, head_dim).
+ * Errors: those of the three calls. */
+bgtq_status bgtq_prefill(const bgtq_quantizer* qz, const bgtq_cache* cache, int seq, const void* keys,
+                         const void* values, bgtq_dtype dtype, int64_t n_tokens, int64_t stride_head,
+                         int64_t stride_token, int b_min, int b_max, double* energy_out, void* workspace,
+                         size_t workspace_bytes, bgtq_stream stream);
+size_t bgtq_prefill_workspace_bytes(int n_kv_heads, int64_t n_tokens, int head_dim);
+
 /* Decode attention straight from the packed cache (abstract: RoPE query-key
  * logits; the serving path attends over a packed K3V3 cache at 128K context).
  * For every sequence s and query head h (KV head h / (n_q_heads/n_kv_heads)):

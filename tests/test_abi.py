@@ -162,6 +162,25 @@ def test_decode_step_validation():
     assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
 
 
+def test_prefill_validation():
+    lib = bgtq.lib()
+    need = lib.bgtq_prefill_workspace_bytes(2, 1000, 128)
+    assert need == lib.bgtq_energy_workspace_bytes(2, 1000, 128)
+
+    def call(desc=None, seq=0, b_min=0, b_max=8, ws=need, n=100, qz=None):
+        return lib.bgtq_prefill(ctypes.byref(qz or _quantizer()), ctypes.byref(desc or _desc()), seq, FAKE, FAKE, 0, n,
+                                1024 * 128, 128, b_min, b_max, None, FAKE, ws, None)
+
+    assert call(seq=1) == bgtq.ERR_INVALID_ARG                     # batch of one
+    assert call(b_min=4) == bgtq.ERR_BUDGET                        # 192 < 64 * 4
+    assert call(b_max=2) == bgtq.ERR_BUDGET                        # 192 > 64 * 2
+    assert call(b_max=9) == bgtq.ERR_BUDGET
+    assert call(n=0) == bgtq.ERR_INVALID_ARG
+    assert call(n=257) == bgtq.ERR_CAPACITY                        # capacity 256
+    assert call(ws=lib.bgtq_prefill_workspace_bytes(2, 100, 128) - 1) == bgtq.ERR_WORKSPACE
+    assert call(qz=bgtq.Quantizer(None, None, None, None, 128, bgtq.ROT_GIVENS, None)) == bgtq.ERR_INVALID_ARG
+
+
 def test_rotation_kind_validation():
     lib = bgtq.lib()
     need = lib.bgtq_decode_workspace_bytes(1, 16, 2, 128, 256)
