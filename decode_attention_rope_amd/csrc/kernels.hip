@@ -1982,6 +1982,15 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     if (g + NG * b < ns) add(x[b], mlv[b]);
   for (int i = g + NG * NB; i < ns; i += NG) add(acc4[size_t(i) * C4 + c4], ml[i]);
   part4[tid] = v;
+  // dense value rotation: this thread's rows of R_v for the un-rotation below, requested now
+  // so that their latency overlaps the reduction over groups
+  constexpr int RC = D / RS;
+  const int r_out = tid % D, q_out = tid / D;
+  float rvr[RC];
+  if (!a.givens) {
+#pragma unroll
+    for (int k = 0; k < RC; ++k) rvr[k] = a.rot_v[(q_out * RC + k) * D + r_out];
+  }
   // structured value rotation: this thread's pair slot records, requested before the
   // reduction below so that their latency overlaps it
   // (the transpose runs the layers backwards: the slot walks them from the last one)
@@ -1999,12 +2008,19 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
   float ltot = 0.0f;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) ltot += red[1][w];
-  if (tid < C4) {
-    float4 t = part4[tid];
-    for (int gg = 1; gg < NG; ++gg) {
-      const float4 y = part4[gg * C4 + tid];
+  // the NG groups' weighted sums, pairwise in a fixed tree
+#pragma unroll
+  for (int span = NG / 2; span >= 1; span >>= 1) {
+    if (g < span) {
+      const float4 y = part4[tid + span * C4];
+      float4 t = part4[tid];
       t.x += y.x; t.y += y.y; t.z += y.z; t.w += y.w;
+      part4[tid] = t;
     }
+    __syncthreads();
+  }
+  if (tid < C4) {
+    const float4 t = part4[tid];
     accs[4 * tid] = t.x; accs[4 * tid + 1] = t.y; accs[4 * tid + 2] = t.z; accs[4 * tid + 3] = t.w;
   }
   __syncthreads();
@@ -2032,10 +2048,9 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     }
   } else {
     {
-      const int r = tid % D, qq = tid / D;
       float o = 0.0f;
-#pragma unroll 8
-      for (int c = qq * (D / RS); c < (qq + 1) * (D / RS); ++c) o = fmaf(a.rot_v[c * D + r], accs[c], o);
+#pragma unroll
+      for (int k = 0; k < RC; ++k) o = fmaf(rvr[k], accs[q_out * RC + k], o);
       outp[tid] = o;
     }
     __syncthreads();
