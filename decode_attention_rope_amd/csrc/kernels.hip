@@ -1449,8 +1449,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     vhi = pend;
   } else {
     const int first = pend / kTile, tiles = pend < len ? (len + kTile - 1) / kTile - first : 0;
-    t0 = first + int(int64_t(split) * tiles / nw);
-    t1 = first + int(int64_t(split + 1) * tiles / nw);
+    const int nwd = nw > 0 ? nw : 1;               // nw > 0 whenever this role runs
+    t0 = first + int(int64_t(split) * tiles / nwd);
+    t1 = first + int(int64_t(split + 1) * tiles / nwd);
     vlo = pend;
     vhi = len;
   }
