@@ -1194,9 +1194,6 @@ __device__ __forceinline__ u32x4 decode8_any(uint32_t d0, uint32_t d1, uint32_t 
 // outstanding global loads, so staging loads for later tiles stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Byte offset, in the per-wave K staging [chunk][16 slots][16 B], of record dword wd.
-__device__ __forceinline__ uint32_t kdw_off(uint32_t wd) { return (wd >> 2) * 256u + (wd & 3u) * 4u; }
-
 // ---- rotated query, shared by the matrix-core kernel's prologue and the decode step's query
 // workgroups.  q' = RoPE(q, pos) with the angle formed and reduced modulo 2 pi in fp64;
 // q''[h][p] = (softmax_scale * log2(e) / sqrt(m)) * sum_k R_m[p - first][k] q'[h][perm[first + k]]
