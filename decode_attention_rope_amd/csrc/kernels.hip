@@ -51,6 +51,31 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One DPP move of a double (both halves with the same control; lanes without a source, or in
+// rows outside row_mask, keep their own value).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = __double_as_longlong(v);
+  const int lo = int(uint32_t(u)), hi = int(uint32_t(u >> 32));
+  const int lo2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
+  const int hi2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double((long long)((unsigned long long)uint32_t(hi2) << 32 | uint32_t(lo2)));
+}
+// Maximum of a double over the wavefront, in every lane: a prefix maximum within each row of 16
+// lanes (row_shr 1, 2, 4, 8), rows combined by the row broadcasts of lanes 15 and 31, the
+// result read from lane 63.
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dpp_f64<0x111, 0xf>(v));
+  v = fmax(v, dpp_f64<0x112, 0xf>(v));
+  v = fmax(v, dpp_f64<0x114, 0xf>(v));
+  v = fmax(v, dpp_f64<0x118, 0xf>(v));
+  v = fmax(v, dpp_f64<0x142, 0xa>(v));
+  v = fmax(v, dpp_f64<0x143, 0xc>(v));
+  const unsigned long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(int(uint32_t(u)), 63), hi = __builtin_amdgcn_readlane(int(uint32_t(u >> 32)), 63);
+  return __longlong_as_double((long long)((unsigned long long)uint32_t(hi) << 32 | uint32_t(lo)));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -173,18 +198,24 @@ __global__ void k_energy_partial(const T* __restrict__ keys, int n_heads, int64_
 }
 
 // Sum of a block's chunk partials in ascending chunk order (p: the block's first partial,
-// consecutive chunks n apart); eight loads are requested before their adds.
+// consecutive chunks n apart).  The partials come from another kernel's workgroups on every
+// XCD, so each load is a far one: B of them are kept in flight ahead of the adds.
+template <int B>
 __device__ __forceinline__ double chunk_sum(const double* __restrict__ p, int n_chunks, int n) {
   double tot = 0.0;
-  int c = 0;
-  for (; c + 8 <= n_chunks; c += 8) {
-    double v[8];
+  double cur[B];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = p[int64_t(c + i) * n];
+  for (int i = 0; i < B; ++i) cur[i] = i < n_chunks ? p[int64_t(i) * n] : 0.0;
+  for (int c = 0; c < n_chunks; c += B) {
+    double nxt[B];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tot = tot + v[i];
+    for (int i = 0; i < B; ++i) nxt[i] = c + B + i < n_chunks ? p[int64_t(c + B + i) * n] : 0.0;
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+      if (c + i < n_chunks) tot = tot + cur[i];
+#pragma unroll
+    for (int i = 0; i < B; ++i) cur[i] = nxt[i];
   }
-  for (; c < n_chunks; ++c) tot = tot + p[int64_t(c) * n];
   return tot;
 }
 
@@ -193,7 +224,7 @@ __global__ void k_energy_final(const double* __restrict__ part, int n_heads, int
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n_heads * n) return;
   const int h = gid / n, j = gid % n;
-  out[gid] = chunk_sum(part + int64_t(h) * n_chunks * n + j, n_chunks, n) / (double)n_tokens;
+  out[gid] = chunk_sum<8>(part + int64_t(h) * n_chunks * n + j, n_chunks, n) / (double)n_tokens;
 }
 
 // ===================================================================== greedy allocation
@@ -201,87 +232,131 @@ __global__ void k_energy_final(const double* __restrict__ part, int n_heads, int
 // energy is high, matched budget).  Reading: every block starts at b_min; each of the
 // `increments` steps gives one bit to the block of largest fp64 gain E_j*(D(b_j)-D(b_j+1))
 // among blocks below b_max, ties to the lowest j.  One wavefront per head, block j on
-// lane j % 64; the arg-max runs over the wave with a (gain, -j) order.  Lane 0 then
-// derives the width groups and the K record layout.
+// lane j % 64; each step takes the wave's largest gain, then the lowest block index at it.
+// The width groups and the K record layout follow from the number of blocks per width.
 // One wavefront allocates one head from its energies e0 (block lane) and e1 (block lane + 64)
 // and writes the widths and the layout descriptor.
 __device__ __forceinline__ void allocate_wave(double e0, double e1, int n, int increments, int b_min, int b_max,
                                               int pairing, uint8_t* __restrict__ widths_h,
                                               HeadLayout* __restrict__ layout_h) {
-  __shared__ int w_s[128];
   __shared__ HeadLayout lay;
+  __shared__ double dg[kMaxBits];          // D(b) - D(b + 1)
   const int lane = threadIdx.x;
   const int j0 = lane, j1 = lane + 64;
+  if (lane < kMaxBits) dg[lane] = c_dgain[lane];
+  __syncthreads();
+  auto gain = [&](double e, int w) { return e * dg[w]; };   // w < kMaxBits
   int w0 = b_min, w1 = b_min;
   for (int it = 0; it < increments; ++it) {
-    const double g0 = (j0 < n && w0 < b_max) ? e0 * c_dgain[w0] : -1.0;
-    const double g1 = (j1 < n && w1 < b_max) ? e1 * c_dgain[w1] : -1.0;
-    double g = g0;
-    int j = j0;
-    if (g1 > g0) { g = g1; j = j1; }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const double go = __shfl_xor(g, off);
-      const int jo = __shfl_xor(j, off);
-      if (go > g || (go == g && jo < j)) { g = go; j = jo; }
-    }
-    if (j == j0) ++w0;
-    else if (j == j1) ++w1;
+    const double g0 = (j0 < n && w0 < b_max) ? gain(e0, w0) : -1.0;
+    const double g1 = (j1 < n && w1 < b_max) ? gain(e1, w1) : -1.0;
+    const bool up = g1 > g0;               // the lane's better block (j0 on a tie)
+    const double g = up ? g1 : g0;
+    const double gm = wave_max_f64(g);
+    // the lowest block index among the lanes at the maximum: blocks j0 < 64 <= j1
+    const unsigned long long m_lo = __ballot(g == gm && !up), m_hi = __ballot(g == gm && up);
+    const int win = m_lo ? __ffsll(m_lo) - 1 : 64 + __ffsll(m_hi) - 1;
+    if (win == j0) ++w0;
+    else if (win == j1) ++w1;
   }
-  if (j0 < n) { w_s[j0] = w0; widths_h[j0] = uint8_t(w0); }
-  if (j1 < n) { w_s[j1] = w1; widths_h[j1] = uint8_t(w1); }
+  if (j0 < n) widths_h[j0] = uint8_t(w0);
+  if (j1 < n) widths_h[j1] = uint8_t(w1);
   uint32_t* lw = reinterpret_cast<uint32_t*>(&lay);
   for (int i = lane; i < int(sizeof(HeadLayout) / 4); i += 64) lw[i] = 0;
+  // Width groups in descending width, blocks of one width in ascending index: from the
+  // blocks per width, each group's first storage position and record bit, and each block's
+  // rank within its width.
+  unsigned long long mk0[kMaxBits + 1], mk1[kMaxBits + 1];
+  int cnt[kMaxBits + 1], gidx[kMaxBits + 1], fpos[kMaxBits + 1], fbit[kMaxBits + 1];
+#pragma unroll
+  for (int w = 1; w <= kMaxBits; ++w) {
+    mk0[w] = __ballot(j0 < n && w0 == w);
+    mk1[w] = __ballot(j1 < n && w1 == w);
+    cnt[w] = __popcll(mk0[w]) + __popcll(mk1[w]);
+  }
+  int ng = 0, pos = 0, bit = 0;
+#pragma unroll
+  for (int w = kMaxBits; w >= 1; --w) {
+    gidx[w] = ng;
+    fpos[w] = pos;
+    fbit[w] = bit;
+    if (cnt[w] > 0) ++ng;
+    pos += 2 * cnt[w];
+    bit += 2 * w * cnt[w];
+  }
   __syncthreads();
   if (lane == 0) {
-    int pos = 0, bit = 0, g = 0;
+#pragma unroll
     for (int w = kMaxBits; w >= 1; --w) {
-      const int first = pos, bit0 = bit;
-      for (int jj = 0; jj < n; ++jj) {
-        if (w_s[jj] != w) continue;
-        const int ca = pairing ? 2 * jj : jj, cb = pairing ? 2 * jj + 1 : jj + n;
-        lay.perm[pos] = uint8_t(ca); lay.group[pos] = uint8_t(g); lay.offset[pos] = uint16_t(bit);
-        bit += w; ++pos;
-        lay.perm[pos] = uint8_t(cb); lay.group[pos] = uint8_t(g); lay.offset[pos] = uint16_t(bit);
-        bit += w; ++pos;
-      }
-      if (pos > first) {
-        lay.g_width[g] = w; lay.g_first[g] = first; lay.g_m[g] = pos - first; lay.g_bitoff[g] = bit0;
-        ++g;
+      if (cnt[w] > 0) {
+        const int g = gidx[w];
+        lay.g_width[g] = w; lay.g_first[g] = fpos[w]; lay.g_m[g] = 2 * cnt[w]; lay.g_bitoff[g] = fbit[w];
       }
     }
-    lay.n_groups = g; lay.d_eff = pos; lay.code_bits = bit; lay.chunks = (bit + 127) / 128;
+    lay.n_groups = ng; lay.d_eff = pos; lay.code_bits = bit; lay.chunks = (bit + 127) / 128;
+  }
+  const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  auto place = [&](int j, int w, int rank) {     // block j (width w >= 1) at its rank among width w
+    int g = 0, p = 0, b = 0;
+#pragma unroll
+    for (int ww = 1; ww <= kMaxBits; ++ww)
+      if (w == ww) { g = gidx[ww]; p = fpos[ww]; b = fbit[ww]; }
+    p += 2 * rank;
+    b += 2 * w * rank;
+    const int ca = pairing ? 2 * j : j, cb = pairing ? 2 * j + 1 : j + n;
+    lay.perm[p] = uint8_t(ca); lay.group[p] = uint8_t(g); lay.offset[p] = uint16_t(b);
+    lay.perm[p + 1] = uint8_t(cb); lay.group[p + 1] = uint8_t(g); lay.offset[p + 1] = uint16_t(b + w);
+  };
+  {
+    unsigned long long s0 = 0, a0 = 0, s1 = 0;
+#pragma unroll
+    for (int w = 1; w <= kMaxBits; ++w) {
+      if (w0 == w) s0 = mk0[w];
+      if (w1 == w) { a0 = mk0[w]; s1 = mk1[w]; }
+    }
+    if (j0 < n && w0 >= 1) place(j0, w0, __popcll(s0 & below));
+    if (j1 < n && w1 >= 1) place(j1, w1, __popcll(a0) + __popcll(s1 & below));
+  }
+  // storage positions with bits in record dword `lane`: each group holds positions at bits
+  // bitoff + i * w, so the counts below a bit are closed forms per group
+  if (lane < 4 * ((bit + 127) / 128)) {
+    const int b_lo = 32 * lane, b_hi = b_lo + 32;
+    int first = 0, end = 0;
+#pragma unroll
+    for (int w = 1; w <= kMaxBits; ++w) {
+      const int m = 2 * cnt[w], bo = fbit[w];
+      const int c_end = b_hi > bo ? (b_hi - bo + w - 1) / w : 0;     // positions starting below b_hi
+      const int c_first = b_lo >= bo ? (b_lo - bo) / w : 0;          // positions ending at or below b_lo
+      end += c_end < m ? c_end : m;
+      first += c_first < m ? c_first : m;
+    }
+    lay.dw_first[lane] = uint16_t(first);
+    lay.dw_end[lane] = uint16_t(end);
+  }
+  __syncthreads();
+  if (lane == 0) {
     // matrix-core view: segments of at most 8 positions in storage order; a k-step takes up to
     // 4 consecutive segments from at most two groups (the two halves of the output columns)
     int ks = -1, slot = 4, ga = -1, gb = -1;
-    for (int gg = 0; gg < g; ++gg) {
-      const int w = lay.g_width[gg];
-      for (int s0 = 0; s0 < lay.g_m[gg]; s0 += kSegLen) {
+    for (int gg = 0; gg < ng; ++gg) {
+      const int w = lay.g_width[gg], m = lay.g_m[gg], first = lay.g_first[gg], bo = lay.g_bitoff[gg];
+      for (int s0 = 0; s0 < m; s0 += kSegLen) {
         if (slot == 4 || (gg != ga && gg != gb && gb >= 0)) {
           if (ks >= 0) lay.kgroups[ks] = uint32_t(ga) | uint32_t(gb >= 0 ? gb : ga) << 8;
           ++ks; slot = 0; ga = gg; gb = -1;
         } else if (gg != ga && gb < 0) {
           gb = gg;
         }
-        const int cnt = lay.g_m[gg] - s0 < kSegLen ? lay.g_m[gg] - s0 : kSegLen;
+        const int cnt_s = m - s0 < kSegLen ? m - s0 : kSegLen;
         const uint32_t half = gg == ga ? 0u : 1u;
-        lay.seg[4 * ks + slot] = uint32_t(lay.g_bitoff[gg] + s0 * w) | uint32_t(w) << 16 | uint32_t(gg) << 20 |
-                                 uint32_t(cnt) << 24 | half << 28;
-        for (int e = 0; e < cnt; ++e)
-          lay.kpos[lay.g_first[gg] + s0 + e] = uint16_t(32 * ks + kSegLen * slot + e);
+        lay.seg[4 * ks + slot] = uint32_t(bo + s0 * w) | uint32_t(w) << 16 | uint32_t(gg) << 20 |
+                                 uint32_t(cnt_s) << 24 | half << 28;
+        for (int e = 0; e < cnt_s; ++e) lay.kpos[first + s0 + e] = uint16_t(32 * ks + kSegLen * slot + e);
         ++slot;
       }
     }
     if (ks >= 0) lay.kgroups[ks] = uint32_t(ga) | uint32_t(gb >= 0 ? gb : ga) << 8;
     lay.n_ksteps = ks + 1;
-    // storage positions with bits in record dword w (offsets ascend with the position)
-    for (int w = 0, p0 = 0, p1 = 0; w < 4 * lay.chunks; ++w) {
-      while (p0 < pos && int(lay.offset[p0]) + lay.g_width[lay.group[p0]] <= 32 * w) ++p0;
-      if (p1 < p0) p1 = p0;
-      while (p1 < pos && int(lay.offset[p1]) < 32 * w + 32) ++p1;
-      lay.dw_first[w] = uint16_t(p0);
-      lay.dw_end[w] = uint16_t(p1);
-    }
     for (int i = 0; i < 4 * lay.n_ksteps; ++i)
       if (lay.seg[i] == 0u) lay.seg[i] = 1u << 16;   // unused slot: width 1 at bit 0
   }
@@ -308,8 +383,8 @@ __global__ __launch_bounds__(64) void k_energy_allocate(const double* __restrict
                                                         uint8_t* __restrict__ widths, HeadLayout* __restrict__ layouts) {
   const int h = blockIdx.x, lane = threadIdx.x;
   const double* p = part + int64_t(h) * n_chunks * n;
-  const double e0 = lane < n ? chunk_sum(p + lane, n_chunks, n) / (double)n_tokens : 0.0;
-  const double e1 = lane + 64 < n ? chunk_sum(p + lane + 64, n_chunks, n) / (double)n_tokens : 0.0;
+  const double e0 = lane < n ? chunk_sum<32>(p + lane, n_chunks, n) / (double)n_tokens : 0.0;
+  const double e1 = lane + 64 < n ? chunk_sum<32>(p + lane + 64, n_chunks, n) / (double)n_tokens : 0.0;
   if (energy_out) {
     if (lane < n) energy_out[int64_t(h) * n + lane] = e0;
     if (lane + 64 < n) energy_out[int64_t(h) * n + lane + 64] = e1;
@@ -327,34 +402,128 @@ __global__ __launch_bounds__(64) void k_energy_allocate(const double* __restrict
 // atomics are needed.  Slots that are not being appended keep their bits.
 constexpr int kHalf = 32;
 
-// Sequential fp32 dot product sum_k R[k] * x[k] (ascending k, no fused multiply-add).  R is
-// read as float2 (m is even and every row starts 8-byte aligned), 64 values per batch with
-// all of a batch's loads issued before the first add, so one memory latency covers 64 terms.
-__device__ __forceinline__ float seq_dot(const float* __restrict__ R, const float* x, int m) {
-  const float2* R2 = reinterpret_cast<const float2*>(R);
-  float acc = 0.0f;
-  for (int k0 = 0; k0 < m; k0 += 64) {
-    float2 r[32];
+// Slot geometry of k_append: each of the four waves owns 8 of the workgroup's 32 slots, and
+// everything per slot (norms, rotations, codes) runs inside the owning wave, ordered by
+// wave_sync() alone.  Keys or values of the 32 slots sit in LDS coordinate-major,
+// xt[c * kXTS + r] (row stride 36 floats, 16-byte aligned), so one coordinate of a wave's 8
+// slots is two 16-byte reads.
+constexpr int kWaveSlots = 8;
+constexpr int kXTS = kHalf + 4;
+
+// Sequential fp32 dot products of two matrix rows (o, o + 1 of an m x m matrix stored
+// transposed: element (o, k) at rt[k * ld], (o + 1, k) next to it) with the coordinates of 8
+// slots, x[k * kXTS + j]: k ascending from 0, every product and sum rounded.  The matrix pairs
+// are requested 8 k-steps ahead of their use.
+__device__ __forceinline__ void dot_pair8(const float* __restrict__ rt, int ld, int m, const float* x,
+                                          float (&acc)[2][kWaveSlots]) {
+  constexpr int KB = 8;
+  float2 rc[KB];
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if (k0 + 2 * i < m) r[i] = R2[k0 / 2 + i];
+  for (int i = 0; i < KB; ++i)
+    rc[i] = i < m ? *reinterpret_cast<const float2*>(rt + size_t(i) * ld) : make_float2(0.0f, 0.0f);
+  for (int k0 = 0; k0 < m; k0 += KB) {
+    float2 rn[KB];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (k0 + 2 * i < m) {
-        acc = acc + r[i].x * x[k0 + 2 * i];
-        acc = acc + r[i].y * x[k0 + 2 * i + 1];
+    for (int i = 0; i < KB; ++i)
+      rn[i] = k0 + KB + i < m ? *reinterpret_cast<const float2*>(rt + size_t(k0 + KB + i) * ld)
+                              : make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if (k0 + i < m) {
+        const float4* x4 = reinterpret_cast<const float4*>(x + (k0 + i) * kXTS);
+        const float4 xa = x4[0], xb = x4[1];
+        const float xv[kWaveSlots] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int j = 0; j < kWaveSlots; ++j) {
+          acc[0][j] = acc[0][j] + rc[i].x * xv[j];
+          acc[1][j] = acc[1][j] + rc[i].y * xv[j];
+        }
       }
     }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) rc[i] = rn[i];
   }
-  return acc;
 }
 
-template <typename T>
+// One structured-rotation layer of a pair slot on 8 slots: x points at coordinate 0 of the
+// slot's width group (coordinate-major, stride kXTS); same rounding as GivensSlot::apply.
+__device__ __forceinline__ void givens_apply8(float* x, const GivensSlot& gs, int l) {
+  const int k = l % kGivensAhead, ia = int(gs.ab[k] & 0xffffu), ib = int(gs.ab[k] >> 16);
+  const float c = gs.c[k], sn = gs.s[k];
+  float4* pa = reinterpret_cast<float4*>(x + ia * kXTS);
+  float4* pb = reinterpret_cast<float4*>(x + ib * kXTS);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float4 xa = pa[h], xb = pb[h];
+    float4 ya, yb;
+    ya.x = c * xa.x - sn * xb.x; yb.x = sn * xa.x + c * xb.x;
+    ya.y = c * xa.y - sn * xb.y; yb.y = sn * xa.y + c * xb.y;
+    ya.z = c * xa.z - sn * xb.z; yb.z = sn * xa.z + c * xb.z;
+    ya.w = c * xa.w - sn * xb.w; yb.w = sn * xa.w + c * xb.w;
+    pa[h] = ya;
+    pb[h] = yb;
+  }
+}
+
+// Sequential fp32 sum of squares of m coordinates of one slot (x[k * kXTS], k ascending).
+__device__ __forceinline__ float sum_sq_slot(const float* x, int m) {
+  float ss = 0.0f;
+  int k = 0;
+  for (; k + 8 <= m; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = x[(k + i) * kXTS];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = ss + v[i] * v[i];
+  }
+  for (; k < m; ++k) ss = ss + x[k * kXTS] * x[k * kXTS];
+  return ss;
+}
+
+// LDS of k_append for head dim d (at most DM): the slot tile, thresholds, norms, key and value
+// codes, layout descriptor.
+__host__ __device__ constexpr size_t append_lds_bytes(int d, int dm) {
+  return size_t(d) * kXTS * 4 + kMaxBits * 255 * 4 + kHalf * kMaxGroups * 4 + kHalf * 4 + 2 * size_t(kHalf) * dm +
+         sizeof(HeadLayout);
+}
+
+// Codes of a wave's 8 slots at one storage position or coordinate: z = (y / n) * fl32(sqrt(m)),
+// code = number of thresholds below z (0 for a zero norm).  The 8 binary searches advance
+// together, so each step's threshold reads are independent of one another.
+__device__ __forceinline__ void codes8(const float* y, const float* nrm, int nstride, const float* thr, int bits,
+                                       float sq, int rw, int ra, int rb, uint8_t* dst, int dstride) {
+  float z[kWaveSlots];
+  bool zero[kWaveSlots];
+  int code[kWaveSlots];
+#pragma unroll
+  for (int j = 0; j < kWaveSlots; ++j) {
+    const float nv = nrm[(rw + j) * nstride];
+    zero[j] = nv == 0.0f;
+    z[j] = (y[j] / nv) * sq;
+    code[j] = 0;
+  }
+  for (int b = bits - 1; b >= 0; --b) {
+#pragma unroll
+    for (int j = 0; j < kWaveSlots; ++j) {
+      const int cand = code[j] | (1 << b);
+      if (z[j] > thr[cand - 1]) code[j] = cand;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kWaveSlots; ++j) {
+    const int r = rw + j;
+    if (r >= ra && r < rb) dst[r * dstride] = uint8_t(zero[j] ? 0 : code[j]);
+  }
+}
+
+template <typename T, int DM, bool GIV>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
-  extern __shared__ float sm[];
+  extern __shared__ __align__(16) float sm[];
+  constexpr int QL = (DM / 2 + 63) / 64;           // pair slots per lane
+  constexpr int PL = DM / 64;                      // coordinates per lane
   const int d = a.d;
   const int si = blockIdx.z, s = a.seq_begin + si, hk = blockIdx.y;
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t len = a.lengths[s];
   if (len + a.n_new > a.capacity) {
     if (blockIdx.x == 0 && hk == 0 && tid == 0 && a.status) atomicOr(a.status, 1);
@@ -364,170 +533,240 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   const int64_t lo = len > ht * kHalf ? len : ht * kHalf;
   const int64_t hi = (len + a.n_new) < (ht + 1) * kHalf ? (len + a.n_new) : (ht + 1) * kHalf;
   if (lo >= hi) return;
-  const int r0 = int(lo - ht * kHalf), nrows = int(hi - lo);   // active rows r0 .. r0 + nrows - 1
+  const int r0 = int(lo - ht * kHalf), r1 = int(hi - ht * kHalf);   // appended slots r0 .. r1 - 1
   const int64_t tile = ht / 2;
   const int half = int(ht & 1);
-  const int XS = d + 1;
-  float* xg = sm;                                   // [32][d+1] keys in storage order
-  float* xs = sm;                                   // same buffer, later: values in original order
-  float* thr = xg + kHalf * XS;                     // [8][255]
+  float* xt = sm;                                   // [d][kXTS] keys (storage order), then values
+  float* thr = xt + d * kXTS;                       // [8][255]
   float* knrm = thr + kMaxBits * 255;               // [32][8]
   float* vnrm = knrm + kHalf * kMaxGroups;          // [32]
-  uint8_t* kcode = reinterpret_cast<uint8_t*>(vnrm + kHalf);             // [32][256]
-  uint8_t* vcode = kcode + kHalf * BGTQ_MAX_HEAD_DIM;                      // [32][256]
-  HeadLayout* Ls = reinterpret_cast<HeadLayout*>(vcode + kHalf * BGTQ_MAX_HEAD_DIM);   // LDS copy
+  uint8_t* kcode = reinterpret_cast<uint8_t*>(vnrm + kHalf);   // [32][DM]
+  uint8_t* vcode = kcode + kHalf * DM;                          // [32][DM]
+  HeadLayout* Ls = reinterpret_cast<HeadLayout*>(vcode + kHalf * DM);
 
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(a.layouts + int64_t(s) * a.n_kv_heads + hk);
-    uint4* dst = reinterpret_cast<uint4*>(Ls);
-    for (int i = tid; i < int(sizeof(HeadLayout) / 16); i += nt) dst[i] = src[i];
-  }
-  const HeadLayout& L = *Ls;
+  static_assert(BGTQ_LAYOUT_BYTES == 256 * 16, "one 16-byte piece of the layout per thread");
+  reinterpret_cast<uint4*>(Ls)[tid] = reinterpret_cast<const uint4*>(a.layouts + int64_t(s) * a.n_kv_heads + hk)[tid];
+  for (int i = tid; i < kMaxBits * 255; i += 256) thr[i] = c_thr[i / 255][i % 255];
   __syncthreads();
+  const HeadLayout& L = *Ls;
   const int ng = L.n_groups, d_eff = L.d_eff, n_dw = 4 * a.chunks;
   const size_t reg = size_t(s) * a.n_kv_heads + hk;
   const int64_t tiles = a.capacity / kTile;
-  // few rows (decode): spread one row's outputs over the threads; many rows: lanes run over rows
-  const bool by_pos = nrows <= 4;
-
-  for (int i = tid; i < kMaxBits * 255; i += nt) thr[i] = c_thr[i / 255][i % 255];
   const T* kin = static_cast<const T*>(a.keys) + si * a.stride_seq + hk * a.stride_head;
   const T* vin = static_cast<const T*>(a.values) + si * a.stride_seq + hk * a.stride_head;
-  for (int idx = tid; idx < nrows * d_eff; idx += nt) {
-    const int r = r0 + idx / d_eff, p = idx % d_eff;
-    xg[r * XS + p] = load_f(kin, (ht * kHalf + r - len) * a.stride_token + L.perm[p]);
-  }
-  __syncthreads();
-  // key group norms: sequential fp32 sum of squares in storage order
-  for (int it = tid; it < nrows * ng; it += nt) {
-    const int r = r0 + it % nrows, g = it / nrows;
-    const float* x = xg + r * XS + L.g_first[g];
-    float ss = 0.0f;
-    for (int k = 0; k < L.g_m[g]; ++k) ss = ss + x[k] * x[k];
-    knrm[r * kMaxGroups + g] = sqrtf(ss);
-  }
-  __syncthreads();
-  const uint4* const giv = a.givens;
-  if (giv) {
-    // structured rotations, in place, layer by layer: thread (pair slot q, row parity) takes
-    // its slot's records of every layer at once and applies them to half of the rows
-    const int q = tid >> 1, hf = tid & 1;
-    GivensSlot gs;
-    gs.n = 0;
-    int first = 0;
-    if (q < d_eff / 2) {
-      const int g = L.group[2 * q];
-      first = L.g_first[g];
-      givens_fetch(giv, L.g_m[g], q - first / 2, gs);
-    }
-    const int nl = givens_layers(giv, L);
+  const int64_t tok0 = ht * kHalf - len;            // input token of slot 0
+  const int rw = kWaveSlots * wave;                 // this wave's slots rw .. rw + 7
+  const int ra = max(r0, rw), rb = min(r1, rw + kWaveSlots);   // of which appended: ra .. rb - 1
+  const bool busy = ra < rb;
+  float* const xw = xt + rw;                        // this wave's column of the slot tile
+
+  // ---- keys, in the owning wave: load (storage order; slots not appended hold zeros), group
+  // norms, rotation, codes
+  if (busy) {
+    float kv[kWaveSlots][PL];
 #pragma unroll
-    for (int l = 0; l < kMaxGivensLayers; ++l) {
-      if (l < nl) {
-        if (l < gs.n) {
-          for (int r = r0 + hf; r < r0 + nrows; r += 2) gs.apply(xg + r * XS + first, l);
-          if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
+    for (int j = 0; j < kWaveSlots; ++j) {
+      const int r = rw + j;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int p = lane + 64 * i;
+        kv[j][i] = (r >= ra && r < rb && p < d_eff) ? load_f(kin, (tok0 + r) * a.stride_token + L.perm[p]) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kWaveSlots; ++j) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int p = lane + 64 * i;
+        if (p < d_eff) xw[p * kXTS + j] = kv[j][i];
+      }
+    }
+    wave_sync();
+    {
+      const int j = lane & 7, g = lane >> 3, r = rw + j;
+      if (g < ng && r >= ra && r < rb) knrm[r * kMaxGroups + g] = sqrtf(sum_sq_slot(xw + L.g_first[g] * kXTS + j, L.g_m[g]));
+    }
+    wave_sync();
+    if constexpr (GIV) {
+      const uint4* const giv = a.givens;
+      GivensSlot gs[QL];
+      int first[QL];
+#pragma unroll
+      for (int i = 0; i < QL; ++i) {
+        const int q = lane + 64 * i;
+        gs[i].n = 0;
+        first[i] = 0;
+        if (q < d_eff / 2) {
+          const int g = L.group[2 * q];
+          first[i] = L.g_first[g];
+          givens_fetch(giv, L.g_m[g], q - first[i] / 2, gs[i]);
         }
-        __syncthreads();
+      }
+      const int nl = givens_layers(giv, L);
+#pragma unroll
+      for (int l = 0; l < kMaxGivensLayers; ++l) {
+        if (l < nl) {
+#pragma unroll
+          for (int i = 0; i < QL; ++i) {
+            if (l < gs[i].n) {
+              givens_apply8(xw + first[i] * kXTS, gs[i], l);
+              if (l + kGivensAhead < kMaxGivensLayers) gs[i].fetch(l + kGivensAhead);
+            }
+          }
+          wave_sync();
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int p = lane + 64 * i;
+        if (p < d_eff) {
+          const int g = L.group[p], w = L.g_width[g];
+          const float4* x4 = reinterpret_cast<const float4*>(xw + p * kXTS);
+          const float4 xa = x4[0], xb = x4[1];
+          const float y[kWaveSlots] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+          codes8(y, knrm + g, kMaxGroups, thr + (w - 1) * 255, w, sqrtf(float(L.g_m[g])), rw, ra, rb, kcode + p, DM);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < QL; ++i) {
+        const int q = lane + 64 * i;
+        if (q < d_eff / 2) {
+          const int p = 2 * q, g = L.group[p], m = L.g_m[g], first = L.g_first[g], w = L.g_width[g];
+          float acc[2][kWaveSlots] = {};
+          dot_pair8(a.rot_bank_t + bank_offset(m) + (p - first), m, m, xw + first * kXTS, acc);
+          const float sq = sqrtf(float(m));
+          codes8(acc[0], knrm + g, kMaxGroups, thr + (w - 1) * 255, w, sq, rw, ra, rb, kcode + p, DM);
+          codes8(acc[1], knrm + g, kMaxGroups, thr + (w - 1) * 255, w, sq, rw, ra, rb, kcode + p + 1, DM);
+        }
       }
     }
   }
-  // key codes, storage order
-  for (int it = tid; it < nrows * d_eff; it += nt) {
-    const int r = r0 + (by_pos ? it / d_eff : it % nrows);
-    const int p = by_pos ? it % d_eff : it / nrows;
-    const int g = L.group[p], w = L.g_width[g], m = L.g_m[g], first = L.g_first[g];
-    const float acc = giv ? xg[r * XS + p]
-                          : seq_dot(a.rot_bank + bank_offset(m) + size_t(p - first) * m, xg + r * XS + first, m);
-    const float nv = knrm[r * kMaxGroups + g];
-    int code = 0;
-    if (nv != 0.0f) code = code_of(thr + (w - 1) * 255, w, (acc / nv) * sqrtf(float(m)));
-    kcode[r * BGTQ_MAX_HEAD_DIM + p] = uint8_t(code);
-  }
   __syncthreads();
-  for (int idx = tid; idx < nrows * d; idx += nt) {
-    const int r = r0 + idx / d, c = idx % d;
-    xs[r * XS + c] = load_f(vin, (ht * kHalf + r - len) * a.stride_token + c);
-  }
-  __syncthreads();
-  for (int r = r0 + tid; r < r0 + nrows; r += nt) {
-    float ss = 0.0f;
-    for (int k = 0; k < d; ++k) ss = ss + xs[r * XS + k] * xs[r * XS + k];
-    vnrm[r] = sqrtf(ss);
-  }
-  __syncthreads();
-  if (giv) {
-    const int q = tid >> 1, hf = tid & 1;
-    GivensSlot gs;
-    gs.n = 0;
-    if (q < d / 2) givens_fetch(giv, d, q, gs);
-    const int nl = givens_count(giv, d);
+
+  // ---- values, in the owning wave (loads requested before the key records are packed)
+  float vv[kWaveSlots][PL];
+  if (busy) {
 #pragma unroll
-    for (int l = 0; l < kMaxGivensLayers; ++l) {
-      if (l < nl) {
-        if (l < gs.n) {
-          for (int r = r0 + hf; r < r0 + nrows; r += 2) gs.apply(xs + r * XS, l);
-          if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
-        }
-        __syncthreads();
+    for (int j = 0; j < kWaveSlots; ++j) {
+      const int r = rw + j;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int c = lane + 64 * i;
+        vv[j][i] = (r >= ra && r < rb && c < d) ? load_f(vin, (tok0 + r) * a.stride_token + c) : 0.0f;
       }
     }
   }
-  const float sd = sqrtf(float(d));
-  for (int it = tid; it < nrows * d; it += nt) {
-    const int r = r0 + (by_pos ? it / d : it % nrows);
-    const int i = by_pos ? it % d : it / nrows;
-    const float acc = giv ? xs[r * XS + i] : seq_dot(a.rot_v + size_t(i) * d, xs + r * XS, d);
-    const float nv = vnrm[r];
-    int code = 0;
-    if (nv != 0.0f) code = code_of(thr + (a.v_bits - 1) * 255, a.v_bits, (acc / nv) * sd);
-    vcode[r * BGTQ_MAX_HEAD_DIM + i] = uint8_t(code);
-  }
-  __syncthreads();
-  // pack key records (one thread per (slot, record dword))
+  // pack key records (one thread per (slot, record dword)) and key norms
   uint32_t* kc = reinterpret_cast<uint32_t*>(a.k_codes) + reg * tiles * a.chunks * kTile * 4;
-  for (int it = tid; it < nrows * n_dw; it += nt) {
+  const int nrows = r1 - r0;
+  for (int it = tid; it < nrows * n_dw; it += 256) {
     const int r = r0 + it % nrows, w = it / nrows;
     const int64_t slot = ht * kHalf + r;
     uint32_t v = 0;
     for (int p = L.dw_first[w]; p < L.dw_end[w]; ++p) {
-      const uint32_t c = kcode[r * BGTQ_MAX_HEAD_DIM + p];
+      const uint32_t c = kcode[r * DM + p];
       const int o = int(L.offset[p]) - 32 * w;
       v |= o >= 0 ? (c << o) : (c >> (-o));
     }
     kc[((tile * a.chunks + w / 4) * kTile + (slot % kTile)) * 4 + (w % 4)] = v;
   }
+  uint16_t* kn = a.k_norms + reg * tiles * kMaxGroups * kTile;
+  for (int it = tid; it < nrows * ng; it += 256) {
+    const int r = r0 + it % nrows, g = it / nrows;
+    const int64_t slot = ht * kHalf + r;
+    kn[(tile * kMaxGroups + g) * kTile + slot % kTile] = f32_to_f16_bits(fminf(knrm[r * kMaxGroups + g], 65504.0f));
+  }
+  if (busy) {
+#pragma unroll
+    for (int j = 0; j < kWaveSlots; ++j) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int c = lane + 64 * i;
+        if (c < d) xw[c * kXTS + j] = vv[j][i];
+      }
+    }
+    wave_sync();
+    if (lane < kWaveSlots) {
+      const int r = rw + lane;
+      if (r >= ra && r < rb) vnrm[r] = sqrtf(sum_sq_slot(xw + lane, d));
+    }
+    wave_sync();
+    const int bv = a.v_bits;
+    const float sd = sqrtf(float(d));
+    if constexpr (GIV) {
+      const uint4* const giv = a.givens;
+      GivensSlot gs[QL];
+#pragma unroll
+      for (int i = 0; i < QL; ++i) {
+        const int q = lane + 64 * i;
+        gs[i].n = 0;
+        if (q < d / 2) givens_fetch(giv, d, q, gs[i]);
+      }
+      const int nl = givens_count(giv, d);
+#pragma unroll
+      for (int l = 0; l < kMaxGivensLayers; ++l) {
+        if (l < nl) {
+#pragma unroll
+          for (int i = 0; i < QL; ++i) {
+            if (l < gs[i].n) {
+              givens_apply8(xw, gs[i], l);
+              if (l + kGivensAhead < kMaxGivensLayers) gs[i].fetch(l + kGivensAhead);
+            }
+          }
+          wave_sync();
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int c = lane + 64 * i;
+        if (c < d) {
+          const float4* x4 = reinterpret_cast<const float4*>(xw + c * kXTS);
+          const float4 xa = x4[0], xb = x4[1];
+          const float y[kWaveSlots] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+          codes8(y, vnrm, 1, thr + (bv - 1) * 255, bv, sd, rw, ra, rb, vcode + c, DM);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < QL; ++i) {
+        const int q = lane + 64 * i;
+        if (q < d / 2) {
+          float acc[2][kWaveSlots] = {};
+          dot_pair8(a.rot_v_t + 2 * q, d, d, xw, acc);
+          codes8(acc[0], vnrm, 1, thr + (bv - 1) * 255, bv, sd, rw, ra, rb, vcode + 2 * q, DM);
+          codes8(acc[1], vnrm, 1, thr + (bv - 1) * 255, bv, sd, rw, ra, rb, vcode + 2 * q + 1, DM);
+        }
+      }
+    }
+  }
+  __syncthreads();
   // pack value segments (one thread per (coordinate, segment dword) of this half tile)
   const int bv = a.v_bits;
   uint32_t* vc = reinterpret_cast<uint32_t*>(a.v_codes) + reg * tiles * d * 2 * bv;
   const uint32_t vmask = (1u << bv) - 1u;
-  for (int it = tid; it < d * bv; it += nt) {
+  for (int it = tid; it < d * bv; it += 256) {
     const int i = it / bv, w = half * bv + it % bv;
     uint32_t* addr = vc + (size_t(tile) * d + i) * 2 * bv + w;
     const int bit0 = 32 * w;
     const int j_lo = bit0 / bv, j_hi = (bit0 + 31) / bv;
-    // only dwords that hold bits of an appended slot are rewritten
+    // only dwords that hold bits of an appended slot are rewritten; one whose every slot is
+    // appended is not read first
     if (tile * kTile + j_hi < lo || tile * kTile + j_lo >= hi) continue;
-    uint32_t v = *addr;
+    const bool whole = tile * kTile + j_lo >= lo && tile * kTile + j_hi < hi;
+    uint32_t v = whole ? 0u : *addr;
     for (int j = j_lo; j <= j_hi; ++j) {
       const int64_t slot = tile * kTile + j;
       if (slot < lo || slot >= hi) continue;
-      const uint32_t c = vcode[int(slot - ht * kHalf) * BGTQ_MAX_HEAD_DIM + i];
+      const uint32_t c = vcode[int(slot - ht * kHalf) * DM + i];
       const int o = j * bv - bit0;
       if (o >= 0) v = (v & ~(vmask << o)) | (c << o);
       else v = (v & ~(vmask >> (-o))) | (c >> (-o));
     }
     *addr = v;
   }
-  // norms
-  uint16_t* kn = a.k_norms + reg * tiles * kMaxGroups * kTile;
   uint16_t* vn = a.v_norms + reg * tiles * kTile;
-  for (int it = tid; it < nrows * ng; it += nt) {
-    const int r = r0 + it % nrows, g = it / nrows;
-    const int64_t slot = ht * kHalf + r;
-    kn[(tile * kMaxGroups + g) * kTile + slot % kTile] = f32_to_f16_bits(fminf(knrm[r * kMaxGroups + g], 65504.0f));
-  }
-  for (int r = r0 + tid; r < r0 + nrows; r += nt) {
+  for (int r = r0 + tid; r < r1; r += 256) {
     const int64_t slot = ht * kHalf + r;
     vn[tile * kTile + slot % kTile] = f32_to_f16_bits(fminf(vnrm[r], 65504.0f));
   }
@@ -2221,6 +2460,22 @@ auto append_one_kernel(bool bf16, bool stage_v) -> void (*)(AppendArgs) {
 }
 }  // namespace
 
+// k_append for head dims up to DM, the input dtype and the rotation kind
+template <int DM>
+hipError_t launch_append_many(const AppendArgs& a, bgtq_dtype dt, dim3 grid, hipStream_t s) {
+  const bool bf = dt == BGTQ_BF16;
+  void (*fn)(AppendArgs) = a.givens ? (bf ? k_append<uint16_t, DM, true> : k_append<float, DM, true>)
+                                    : (bf ? k_append<uint16_t, DM, false> : k_append<float, DM, false>);
+  const size_t lds = append_lds_bytes(a.d, DM);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, grid, dim3(256), lds, s, a);
+  return hipSuccess;
+}
+
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s) {
   if (a.n_new == 1) {   // decode step: one token per sequence, length advanced in the same kernel
     const bool stage_v = a.d <= 128;
@@ -2236,12 +2491,10 @@ hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStre
   }
   const int halves = int((a.n_new + kHalf - 1) / kHalf) + 1;
   const dim3 grid(halves, a.n_kv_heads, n_seqs);
-  const size_t lds = size_t(kHalf) * (a.d + 1) * 4 + kMaxBits * 255 * 4 + kHalf * kMaxGroups * 4 + kHalf * 4 +
-                     2 * kHalf * BGTQ_MAX_HEAD_DIM + sizeof(HeadLayout);
-  if (dt == BGTQ_BF16)
-    hipLaunchKernelGGL(k_append<uint16_t>, grid, dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL(k_append<float>, grid, dim3(256), lds, s, a);
+  const hipError_t e = a.d <= 64 ? launch_append_many<64>(a, dt, grid, s)
+                       : a.d <= 128 ? launch_append_many<128>(a, dt, grid, s)
+                                    : launch_append_many<256>(a, dt, grid, s);
+  if (e != hipSuccess) return e;
   if (a.window > 0) {
     const int64_t m = a.n_new < a.window ? a.n_new : a.window;
     const dim3 wgrid(unsigned((m * a.d + 255) / 256), a.n_kv_heads, n_seqs);
