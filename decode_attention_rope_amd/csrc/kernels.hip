@@ -174,7 +174,7 @@ __device__ __forceinline__ void givens_fetch(const uint4* G, int m, int slot, Gi
 // ascending order.  Pass 1: one thread per (head, chunk, block); lanes run over blocks
 // so every token row is read coalesced.  Pass 2: one thread per (head, block).
 template <typename T>
-__global__ void k_energy_partial(const T* __restrict__ keys, int n_heads, int64_t n_tokens, int n,
+__global__ __launch_bounds__(256) void k_energy_partial(const T* __restrict__ keys, int n_heads, int64_t n_tokens, int n,
                                  int64_t sh, int64_t st, int pairing, int n_chunks,
                                  double* __restrict__ part) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -188,7 +188,24 @@ __global__ void k_energy_partial(const T* __restrict__ keys, int n_heads, int64_
   const int64_t t0 = int64_t(c) * kEnergyChunk;
   const int64_t t1 = t0 + kEnergyChunk < n_tokens ? t0 + kEnergyChunk : n_tokens;
   double acc = 0.0;
-  for (int64_t t = t0; t < t1; ++t) {
+  int64_t t = t0;
+  // 16 tokens' loads are requested before their adds, which keep ascending token order
+  for (; t + 16 <= t1; t += 16) {
+    float xa[16], xb[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      xa[i] = load_f(base, (t + i) * st + ca);
+      xb[i] = load_f(base, (t + i) * st + cb);
+    }
+    __builtin_amdgcn_sched_barrier(0);     // every load issued before the first add
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const double x0 = (double)xa[i], x1 = (double)xb[i];
+      const double e = x0 * x0 + x1 * x1;
+      acc = acc + e;
+    }
+  }
+  for (; t < t1; ++t) {
     const double x0 = (double)load_f(base, t * st + ca);
     const double x1 = (double)load_f(base, t * st + cb);
     const double e = x0 * x0 + x1 * x1;
@@ -198,24 +215,20 @@ __global__ void k_energy_partial(const T* __restrict__ keys, int n_heads, int64_
 }
 
 // Sum of a block's chunk partials in ascending chunk order (p: the block's first partial,
-// consecutive chunks n apart).  The partials come from another kernel's workgroups on every
-// XCD, so each load is a far one: B of them are kept in flight ahead of the adds.
+// consecutive chunks n apart); B loads are requested before their adds.
 template <int B>
 __device__ __forceinline__ double chunk_sum(const double* __restrict__ p, int n_chunks, int n) {
   double tot = 0.0;
-  double cur[B];
+  int c = 0;
+  for (; c + B <= n_chunks; c += B) {
+    double v[B];
 #pragma unroll
-  for (int i = 0; i < B; ++i) cur[i] = i < n_chunks ? p[int64_t(i) * n] : 0.0;
-  for (int c = 0; c < n_chunks; c += B) {
-    double nxt[B];
+    for (int i = 0; i < B; ++i) v[i] = p[int64_t(c + i) * n];
+    __builtin_amdgcn_sched_barrier(0);     // every load issued before the first add
 #pragma unroll
-    for (int i = 0; i < B; ++i) nxt[i] = c + B + i < n_chunks ? p[int64_t(c + B + i) * n] : 0.0;
-#pragma unroll
-    for (int i = 0; i < B; ++i)
-      if (c + i < n_chunks) tot = tot + cur[i];
-#pragma unroll
-    for (int i = 0; i < B; ++i) cur[i] = nxt[i];
+    for (int i = 0; i < B; ++i) tot = tot + v[i];
   }
+  for (; c < n_chunks; ++c) tot = tot + p[int64_t(c) * n];
   return tot;
 }
 
@@ -573,6 +586,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
         kv[j][i] = (r >= ra && r < rb && p < d_eff) ? load_f(kin, (tok0 + r) * a.stride_token + L.perm[p]) : 0.0f;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);     // every load issued before the first store
 #pragma unroll
     for (int j = 0; j < kWaveSlots; ++j) {
 #pragma unroll
