@@ -120,7 +120,7 @@ struct AppendArgs {
   int d;
   int v_bits;
   int chunks;
-  int advance;        // the one-token kernel advances lengths[] (a decode step leaves that to the merge)
+  int advance;        // lengths[] advanced after the append (a decode step leaves that to the merge)
   uint16_t* k_window; // fp16 recent keys [batch][n_kv][window][d], token t at slot t % window
   int window;         // 0: no window
   const uint4* givens;  // structured rotations (header, then records), or null for dense ones

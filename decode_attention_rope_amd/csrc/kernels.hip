@@ -787,12 +787,14 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 }
 
 // Decode-time append of one token to each sequence (n_new == 1), same arithmetic as
-// k_append.  One workgroup per sequence; its KV heads run two at a time on 512 threads each
-// (threads 0..d-1 rotate the value, d..d+d_eff-1 the key positions, the next ones form the
-// norms).  Every input is requested before any arithmetic: the layout, key and value of each
-// head, the quantizer thresholds (copied to LDS) and, for head_dim <= 128, the value rotation
-// (copied to LDS with rows padded to d + 1 floats, so lanes on consecutive rows hit distinct
-// banks).  The sequence length is advanced by the same workgroup once all heads are written.
+// k_append.  One workgroup of 1024 threads per (sequence, KV head): threads 0..d-1 rotate the
+// value, d..d+d_eff-1 the key positions, 768.. form the norms.  Reads come in two rounds: first
+// everything that depends neither on the sequence length nor on the layout (layout, key, value,
+// quantizer thresholds and, for head_dim <= 128, the value rotation), then the slot's old value
+// dwords and, with dense rotations and head_dim <= 128, the key groups' matrices.  Both
+// rotations are staged in LDS with rows padded to m + 1 floats, so lanes on consecutive rows hit
+// distinct banks.  The sequence length is advanced afterwards (k_advance, or the decode step's
+// merge).
 //
 // Sequential fp32 dot product of row `row` of an m x m matrix stored transposed (element
 // (row, k) at Rt[k * m + row]) with x, k ascending, no fused multiply-add; lanes on
@@ -830,21 +832,26 @@ __device__ __forceinline__ float dot_rows_t(const float* __restrict__ Rt, int m,
 }
 
 // Sequential fp32 dot product of row `row` of an LDS matrix with row stride ld and x (both in
-// LDS), k ascending over [0, m), m a multiple of 16.
-__device__ __forceinline__ float dot_rows_lds(const float* R, int ld, int m, int row, const float* x) {
+// LDS), k ascending over [0, m).  Terms past m in the last chunk of 16 are exact zeros, which
+// leave the sum's value (and so every code) unchanged.  x is 8-byte aligned and readable to
+// the end of that chunk.
+__device__ __forceinline__ float dot_rows_lds_any(const float* R, int ld, int m, int row, const float* x) {
   float acc = 0.0f;
   const float* rr = R + row * ld;
   for (int k0 = 0; k0 < m; k0 += 16) {
     float r[16], xv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = rr[k0 + i];
+    for (int i = 0; i < 16; ++i) r[i] = rr[k0 + i < m ? k0 + i : m - 1];   // every read issued
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const float2 v = *reinterpret_cast<const float2*>(x + k0 + i);
       xv[i] = v.x; xv[i + 1] = v.y;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc = acc + r[i] * xv[i];
+    for (int i = 0; i < 16; ++i) {
+      const bool in = k0 + i < m;
+      acc = acc + (in ? r[i] : 0.0f) * (in ? xv[i] : 0.0f);
+    }
   }
   return acc;
 }
@@ -867,43 +874,74 @@ __device__ __forceinline__ float seq_sumsq(const float* x, int m) {
   return ss;
 }
 
-// Dynamic LDS of k_append_one: thresholds, then (STAGE_V) the padded value rotation.
+// Dynamic LDS of the one-token append: thresholds, then (STAGE_V) the padded value rotation
+// and, with dense rotations, the key groups' matrices (rows padded to m + 1 floats; at most
+// d (d + 1) floats in all, the case of a single group).
 constexpr int kAppendThrFloats = kMaxBits * 255;
-__host__ __device__ inline size_t append_one_lds_bytes(int d, bool stage_v) {
-  return size_t(kAppendThrFloats) * 4 + (stage_v ? size_t(d) * (d + 1) * 4 : 0);
+__host__ __device__ inline size_t append_one_lds_bytes(int d, bool stage_v, bool stage_k) {
+  return size_t(kAppendThrFloats) * 4 + (stage_v ? size_t(d) * (d + 1) * 4 : 0) +
+         (stage_k ? size_t(d) * (d + 1) * 4 : 0);
 }
 
 template <typename T, bool STAGE_V, bool WIN, bool GIV>
-__device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float* dyn) {
-  constexpr int HP = 2;
+__device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, int hk, float* dyn) {
   constexpr int DM = BGTQ_MAX_HEAD_DIM;
-  float* thr = dyn;                                // [8][255]
-  float* rv = dyn + kAppendThrFloats;              // [d][d + 1] (STAGE_V)
-  __shared__ HeadLayout Ls[HP];
-  __shared__ __align__(16) float ko[HP][DM];       // key, original coordinate order
-  __shared__ __align__(16) float xk[HP][2 * DM + 16];   // key, storage order, zero past d_eff
-  __shared__ __align__(16) float xv[HP][DM];       // value
-  __shared__ float nrm[HP][kMaxGroups + 1];        // group norms, value norm last
-  __shared__ uint32_t kw[HP][kMaxRecordDwords];    // the slot's key record, assembled with atomic ors
-  const int s = a.seq_begin + si;
-  const int tid = threadIdx.x, hp = tid >> 9, t = tid & 511;
+  constexpr bool STAGE_K = STAGE_V && !GIV;        // key matrices staged beside the value rotation
   const int d = a.d, bv = a.v_bits;
-  // ---- inputs that do not depend on the sequence length
-#pragma unroll 2
-  for (int i = tid; i < kAppendThrFloats; i += 1024) thr[i] = (&c_thr[0][0])[i];
+  float* thr = dyn;                                // [8][255]
+  float* rv = dyn + kAppendThrFloats;              // [d][d + 1] (STAGE_V, dense)
+  float* rk = rv + d * (d + 1);                    // group g's matrix from rko[g], rows m_g + 1 apart
+  __shared__ HeadLayout L;
+  __shared__ __align__(16) float ko[DM];           // key, original coordinate order
+  __shared__ __align__(16) float xk[2 * DM + 16];  // key, storage order, zero past d_eff
+  __shared__ __align__(16) float xv[DM + 16];      // value, zero past d
+  __shared__ float nrm[kMaxGroups + 1];            // group norms, value norm last
+  __shared__ uint32_t kw[kMaxRecordDwords];        // the slot's key record, assembled with atomic ors
+  __shared__ int rko[kMaxGroups + 1];              // float offsets of the staged key matrices
+  const int s = a.seq_begin + si, t = threadIdx.x;
+  const size_t reg = size_t(s) * a.n_kv_heads + hk;
+  const T* kin = static_cast<const T*>(a.keys) + si * a.stride_seq + int64_t(hk) * a.stride_head;
+  const T* vin = static_cast<const T*>(a.values) + si * a.stride_seq + int64_t(hk) * a.stride_head;
+  // ---- first round of reads: everything that depends neither on the length nor on the layout
+  uint4 lw = uint4{0u, 0u, 0u, 0u};
+  if (t < 256) lw = reinterpret_cast<const uint4*>(a.layouts + reg)[t];
+  const float kval = t < d ? load_f(kin, t) : 0.0f;
+  const float vval = t < d ? load_f(vin, t) : 0.0f;
+  float tv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) tv[i] = t + 1024 * i < kAppendThrFloats ? (&c_thr[0][0])[t + 1024 * i] : 0.0f;
+  float4 rvq[4];                                  // d <= 128: at most 4096 pieces
   if (STAGE_V && !GIV) {
     const float4* src = reinterpret_cast<const float4*>(a.rot_v);
-#pragma unroll 4
-    for (int i = tid; i < d * d / 4; i += 1024) {
-      const float4 v = src[i];
-      const int row = (4 * i) / d, col = 4 * i - row * d;
-      float* dst = rv + row * (d + 1) + col;
-      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = t + 1024 * i;
+      rvq[i] = q < d * d / 4 ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   const int64_t len = a.lengths[s];
-  if (len + 1 > a.capacity) {
-    if (tid == 0 && a.status) atomicOr(a.status, 1);
+  __builtin_amdgcn_sched_barrier(0);      // every read above issued before the first store
+  if (t < 256) reinterpret_cast<uint4*>(&L)[t] = lw;
+  if (t < DM) { ko[t] = kval; xv[t] = vval; }
+  if (t < 16) xv[DM + t] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (t + 1024 * i < kAppendThrFloats) thr[t + 1024 * i] = tv[i];
+  if (STAGE_V && !GIV) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = t + 1024 * i;
+      if (q < d * d / 4) {
+        const int row = (4 * q) / d, col = 4 * q - row * d;
+        float* dst = rv + row * (d + 1) + col;
+        dst[0] = rvq[i].x; dst[1] = rvq[i].y; dst[2] = rvq[i].z; dst[3] = rvq[i].w;
+      }
+    }
+  }
+  if (t < kMaxRecordDwords) kw[t] = 0u;
+  __syncthreads();
+  if (len + 1 > a.capacity) {                     // the same for every thread
+    if (t == 0 && hk == 0 && a.status) atomicOr(a.status, 1);
     return;
   }
   const int64_t tiles = a.capacity / kTile;
@@ -912,122 +950,145 @@ __device__ __forceinline__ void append_one_wg(const AppendArgs& a, int si, float
   const uint32_t vmask = (1u << bv) - 1u;
   const int vbit = slot * bv, vw = vbit >> 5, vsh = vbit & 31;
   const bool vsplit = vsh + bv > 32;
-  for (int h0 = 0; h0 < a.n_kv_heads; h0 += HP) {
-    const int hk = h0 + hp;
-    const bool act = hk < a.n_kv_heads;
-    const size_t reg = size_t(s) * a.n_kv_heads + (act ? hk : 0);
-    HeadLayout& L = Ls[hp];
-    const T* kin = static_cast<const T*>(a.keys) + si * a.stride_seq + int64_t(act ? hk : 0) * a.stride_head;
-    const T* vin = static_cast<const T*>(a.values) + si * a.stride_seq + int64_t(act ? hk : 0) * a.stride_head;
-    uint32_t* vseg = reinterpret_cast<uint32_t*>(a.v_codes) + (reg * tiles + tile) * d * 2 * bv;
-    uint32_t old0 = 0u, old1 = 0u;
-    if (act) {
-      if (t < 256) reinterpret_cast<uint4*>(&L)[t] = reinterpret_cast<const uint4*>(a.layouts + reg)[t];
-      if (t < d) {
-        ko[hp][t] = load_f(kin, t);
-        xv[hp][t] = load_f(vin, t);
-        old0 = vseg[t * 2 * bv + vw];
-        if (vsplit) old1 = vseg[t * 2 * bv + vw + 1];
+  uint32_t* vseg = reinterpret_cast<uint32_t*>(a.v_codes) + (reg * tiles + tile) * d * 2 * bv;
+  const int ng = L.n_groups, d_eff = L.d_eff;
+  // ---- second round: the slot's old value dwords (by the length), the key matrices (by the layout)
+  uint32_t old0 = 0u, old1 = 0u;
+  if (t < d) {
+    old0 = vseg[t * 2 * bv + vw];
+    if (vsplit) old1 = vseg[t * 2 * bv + vw + 1];
+  }
+  if constexpr (STAGE_K) {
+    // group g's m x m matrix (row-major in the bank) to rk + rko[g], rows padded to m + 1
+    int pre[kMaxGroups + 1];
+    pre[0] = 0;
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) pre[g + 1] = pre[g] + (g < ng ? L.g_m[g] * L.g_m[g] : 0);
+    if (t <= kMaxGroups) {
+      int o = 0;
+      for (int g = 0; g < t && g < ng; ++g) o += L.g_m[g] * (L.g_m[g] + 1);
+      rko[t] = o;
+    }
+    constexpr int KQ = 4;                       // float4 pieces per thread (d <= 128: at most 4096)
+    float4 kq[KQ];
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) {
+      const int q = t + 1024 * i;
+      kq[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * q < pre[kMaxGroups]) {
+        int g = 0;
+#pragma unroll
+        for (int gg = 1; gg < kMaxGroups; ++gg) g += 4 * q >= pre[gg] && gg < ng ? 1 : 0;
+        const int m = L.g_m[g];
+        kq[i] = *reinterpret_cast<const float4*>(a.rot_bank + bank_offset(m) + (4 * q - pre[g]));
       }
     }
-    __syncthreads();
-    const int ng = act ? L.n_groups : 0, d_eff = act ? L.d_eff : 0;
-    int mmax = 0;
-    for (int g = 0; g < ng; ++g) mmax = L.g_m[g] > mmax ? L.g_m[g] : mmax;
-    mmax = (mmax + 15) & ~15;
-    for (int i = t; i < 2 * DM + 16; i += 512) xk[hp][i] = i < d_eff ? ko[hp][L.perm[i]] : 0.0f;
-    if (t < kMaxRecordDwords) kw[hp][t] = 0u;
-    __syncthreads();
-    float acc = 0.0f;
-    if constexpr (GIV) {
-      // structured rotations: norms of the unrotated vectors, then the layers in place (both
-      // heads of the pair in lockstep, as many layers as the longest needs)
-      if (t < ng) nrm[hp][t] = sqrtf(seq_sumsq(xk[hp] + L.g_first[t], L.g_m[t]));
-      else if (act && t == ng) nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
-      // one pair slot per thread: value slot t, or key slot t - 256 of its width group
-      GivensSlot gs;
-      gs.n = 0;
-      float* gx = nullptr;
-      if (act && t < d / 2) {
-        givens_fetch(a.givens, d, t, gs);
-        gx = xv[hp];
-      } else if (t >= 256 && t < 256 + d_eff / 2) {
-        const int q = t - 256, g = L.group[2 * q], first = L.g_first[g];
-        givens_fetch(a.givens, L.g_m[g], q - first / 2, gs);
-        gx = xk[hp] + first;
-      }
-      int nl = givens_count(a.givens, d);
-      for (int hh = 0; hh < HP; ++hh)
-        if (h0 + hh < a.n_kv_heads) nl = max(nl, givens_layers(a.givens, Ls[hh]));
-      __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int l = 0; l < kMaxGivensLayers; ++l) {
-        if (l < nl) {
-          if (l < gs.n) {
-            gs.apply(gx, l);
-            if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
-          }
-          __syncthreads();
+    for (int i = 0; i < KQ; ++i) {
+      const int q = t + 1024 * i;
+      if (4 * q < pre[kMaxGroups]) {
+        int g = 0, o = 0;
+#pragma unroll
+        for (int gg = 1; gg < kMaxGroups; ++gg) g += 4 * q >= pre[gg] && gg < ng ? 1 : 0;
+#pragma unroll
+        for (int gg = 0; gg < kMaxGroups; ++gg) o += gg < g ? L.g_m[gg] * (L.g_m[gg] + 1) : 0;
+        const int m = L.g_m[g], e0 = 4 * q - pre[g];
+        // row = e0 / m (e0 < m * m, m <= 128): the exact quotient of e0 + 1/2 is at least 1/(2m)
+        // away from an integer, far more than the rounding error of the float division
+        int row = int((float(e0) + 0.5f) / float(m)), col = e0 - row * m;
+        const float e[4] = {kq[i].x, kq[i].y, kq[i].z, kq[i].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          rk[o + row * (m + 1) + col] = e[c];
+          if (++col == m) { col = 0; ++row; }
         }
       }
-      if (act && t < d) acc = xv[hp][t];
-      else if (t >= d && t < d + d_eff) acc = xk[hp][t - d];
-    } else {
-      // norms run beside the rotations when the head has threads to spare (always for d <= 128)
-      const bool norms_beside = d + d_eff + ng + 1 <= 512;
-      if (act && t < d) {                                  // value rotation, row t
-        acc = STAGE_V ? dot_rows_lds(rv, d + 1, d, t, xv[hp]) : dot_rows_t(a.rot_v_t, d, d, t, xv[hp]);
-      } else if (t >= d && t < d + d_eff) {                // key position p, row p - first of its group
-        const int p = t - d, g = L.group[p], m = L.g_m[g], first = L.g_first[g];
-        acc = dot_rows_t(a.rot_bank_t + bank_offset(m), m, mmax, p - first, xk[hp] + first);
-      } else if (norms_beside && t >= d + d_eff && t < d + d_eff + ng) {   // group norm
-        const int g = t - d - d_eff;
-        nrm[hp][g] = sqrtf(seq_sumsq(xk[hp] + L.g_first[g], L.g_m[g]));
-      } else if (act && norms_beside && t == d + d_eff + ng) {             // value norm
-        nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
-      }
-      if (!norms_beside) {
-        if (t < ng) nrm[hp][t] = sqrtf(seq_sumsq(xk[hp] + L.g_first[t], L.g_m[t]));
-        else if (act && t == ng) nrm[hp][kMaxGroups] = sqrtf(seq_sumsq(xv[hp], d));
-      }
     }
-    __syncthreads();
-    // codes: a value code goes straight into the slot's dwords (read before any arithmetic);
-    // key codes are ored into the slot's record, assembled in LDS
-    if (act && t < d) {
-      const float nv = nrm[hp][kMaxGroups];
-      const uint32_t code = nv != 0.0f ? code_of(thr + (bv - 1) * 255, bv, (acc / nv) * sqrtf(float(d))) : 0u;
-      vseg[t * 2 * bv + vw] = (old0 & ~(vmask << vsh)) | (code << vsh);
-      if (vsplit) vseg[t * 2 * bv + vw + 1] = (old1 & ~(vmask >> (32 - vsh))) | (code >> (32 - vsh));
-    } else if (t >= d && t < d + d_eff) {
-      const int p = t - d, g = L.group[p], w = L.g_width[g], m = L.g_m[g];
-      const float nv = nrm[hp][g];
-      const uint32_t code = nv != 0.0f ? code_of(thr + (w - 1) * 255, w, (acc / nv) * sqrtf(float(m))) : 0u;
-      const int off = L.offset[p], wd = off >> 5, sh = off & 31;
-      atomicOr(&kw[hp][wd], code << sh);
-      if (sh + w > 32) atomicOr(&kw[hp][wd + 1], code >> (32 - sh));
-    }
-    __syncthreads();
-    if (act) {
-      uint32_t* kc = reinterpret_cast<uint32_t*>(a.k_codes) + (reg * tiles + tile) * a.chunks * kTile * 4;
-      if (t < 4 * a.chunks) kc[((t >> 2) * kTile + slot) * 4 + (t & 3)] = kw[hp][t];
-      uint16_t* kn = a.k_norms + (reg * tiles + tile) * kMaxGroups * kTile;
-      if (t >= 256 && t < 256 + ng) kn[(t - 256) * kTile + slot] = f32_to_f16_bits(fminf(nrm[hp][t - 256], 65504.0f));
-      if (t == 256 + kMaxGroups)
-        a.v_norms[(reg * tiles + tile) * kTile + slot] = f32_to_f16_bits(fminf(nrm[hp][kMaxGroups], 65504.0f));
-      // the key's fp16 copy in the recent-key window, last (off the path of the packed stores)
-      if (WIN && t >= 512 - d)
-        a.k_window[(reg * a.window + len % a.window) * d + (t - (512 - d))] = f16_sat_bits(ko[hp][t - (512 - d)]);
-    }
-    __syncthreads();
   }
-  if (tid == 0 && a.advance) a.lengths[s] = int32_t(len + 1);
+  int mmax = 0;
+  for (int g = 0; g < ng; ++g) mmax = L.g_m[g] > mmax ? L.g_m[g] : mmax;
+  mmax = (mmax + 15) & ~15;
+  for (int i = t; i < 2 * DM + 16; i += 1024) xk[i] = i < d_eff ? ko[L.perm[i]] : 0.0f;
+  __syncthreads();
+  float acc = 0.0f;
+  if constexpr (GIV) {
+    // structured rotations: norms of the unrotated vectors, then the layers in place
+    if (t < ng) nrm[t] = sqrtf(seq_sumsq(xk + L.g_first[t], L.g_m[t]));
+    else if (t == ng) nrm[kMaxGroups] = sqrtf(seq_sumsq(xv, d));
+    // one pair slot per thread: value slot t, or key slot t - 512 of its width group
+    GivensSlot gs;
+    gs.n = 0;
+    float* gx = nullptr;
+    if (t < d / 2) {
+      givens_fetch(a.givens, d, t, gs);
+      gx = xv;
+    } else if (t >= 512 && t < 512 + d_eff / 2) {
+      const int q = t - 512, g = L.group[2 * q], first = L.g_first[g];
+      givens_fetch(a.givens, L.g_m[g], q - first / 2, gs);
+      gx = xk + first;
+    }
+    const int nl = max(givens_count(a.givens, d), givens_layers(a.givens, L));
+    __syncthreads();
+#pragma unroll
+    for (int l = 0; l < kMaxGivensLayers; ++l) {
+      if (l < nl) {
+        if (l < gs.n) {
+          gs.apply(gx, l);
+          if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
+        }
+        __syncthreads();
+      }
+    }
+    if (t < d) acc = xv[t];
+    else if (t >= d && t < d + d_eff) acc = xk[t - d];
+  } else {
+    // norms run beside the rotations
+    if (t < d) {                                        // value rotation, row t
+      acc = STAGE_V ? dot_rows_lds_any(rv, d + 1, d, t, xv) : dot_rows_t(a.rot_v_t, d, d, t, xv);
+    } else if (t >= d && t < d + d_eff) {               // key position p, row p - first of its group
+      const int p = t - d, g = L.group[p], m = L.g_m[g], first = L.g_first[g];
+      acc = STAGE_K ? dot_rows_lds_any(rk + rko[g], m + 1, m, p - first, xk + first)
+                    : dot_rows_t(a.rot_bank_t + bank_offset(m), m, mmax, p - first, xk + first);
+    } else if (t >= 768 && t < 768 + ng) {              // group norm
+      const int g = t - 768;
+      nrm[g] = sqrtf(seq_sumsq(xk + L.g_first[g], L.g_m[g]));
+    } else if (t == 768 + kMaxGroups) {                 // value norm
+      nrm[kMaxGroups] = sqrtf(seq_sumsq(xv, d));
+    }
+  }
+  __syncthreads();
+  // codes: a value code goes straight into the slot's dwords (read before any arithmetic);
+  // key codes are ored into the slot's record, assembled in LDS
+  if (t < d) {
+    const float nv = nrm[kMaxGroups];
+    const uint32_t code = nv != 0.0f ? code_of(thr + (bv - 1) * 255, bv, (acc / nv) * sqrtf(float(d))) : 0u;
+    vseg[t * 2 * bv + vw] = (old0 & ~(vmask << vsh)) | (code << vsh);
+    if (vsplit) vseg[t * 2 * bv + vw + 1] = (old1 & ~(vmask >> (32 - vsh))) | (code >> (32 - vsh));
+  } else if (t >= d && t < d + d_eff) {
+    const int p = t - d, g = L.group[p], w = L.g_width[g], m = L.g_m[g];
+    const float nv = nrm[g];
+    const uint32_t code = nv != 0.0f ? code_of(thr + (w - 1) * 255, w, (acc / nv) * sqrtf(float(m))) : 0u;
+    const int off = L.offset[p], wd = off >> 5, sh = off & 31;
+    atomicOr(&kw[wd], code << sh);
+    if (sh + w > 32) atomicOr(&kw[wd + 1], code >> (32 - sh));
+  }
+  __syncthreads();
+  uint32_t* kc = reinterpret_cast<uint32_t*>(a.k_codes) + (reg * tiles + tile) * a.chunks * kTile * 4;
+  if (t < 4 * a.chunks) kc[((t >> 2) * kTile + slot) * 4 + (t & 3)] = kw[t];
+  uint16_t* kn = a.k_norms + (reg * tiles + tile) * kMaxGroups * kTile;
+  if (t >= 256 && t < 256 + ng) kn[(t - 256) * kTile + slot] = f32_to_f16_bits(fminf(nrm[t - 256], 65504.0f));
+  if (t == 256 + kMaxGroups)
+    a.v_norms[(reg * tiles + tile) * kTile + slot] = f32_to_f16_bits(fminf(nrm[kMaxGroups], 65504.0f));
+  // the key's fp16 copy in the recent-key window, last (off the path of the packed stores)
+  if (WIN && t >= 1024 - d)
+    a.k_window[(reg * a.window + len % a.window) * d + (t - (1024 - d))] = f16_sat_bits(ko[t - (1024 - d)]);
 }
 
 template <typename T, bool STAGE_V, bool WIN, bool GIV>
 __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
   extern __shared__ __align__(16) float dyn[];
-  append_one_wg<T, STAGE_V, WIN, GIV>(a, blockIdx.x, dyn);
+  append_one_wg<T, STAGE_V, WIN, GIV>(a, blockIdx.x / a.n_kv_heads, blockIdx.x % a.n_kv_heads, dyn);
 }
 
 // fp16 keys of the appended tokens that end up among the newest `window` (the last
@@ -2124,13 +2185,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 }
 
-// ---- decode step, first launch: the one-token append (workgroups 0 .. n_seqs - 1) beside the
-// rotated query of every (sequence, KV head) (the remaining workgroups), which depends only on
-// the layout and on the query position, not on the appended token.  The query workgroups
-// write the matrix-core B operands [k-step][hi, lo][64 lanes] to the workspace; lengths[] is
-// left to the merge kernel, so both roles read the old length: the query sits at that
-// position unless the append overflows the capacity (then at the last cached token, as a
-// separate decode call would place it).
+// ---- decode step, first launch: the one-token append (workgroups 0 .. n_seqs * n_kv - 1, one
+// per (sequence, KV head)) beside the rotated query of every (sequence, KV head) (the remaining
+// workgroups), which depends only on the layout and on the query position, not on the appended
+// token.  The query workgroups write the matrix-core B operands [k-step][hi, lo][64 lanes] to
+// the workspace; lengths[] is left to the merge kernel, so both roles read the old length: the
+// query sits at that position unless the append overflows the capacity (then at the last
+// cached token, as a separate decode call would place it).
 template <int D, typename QT>
 __device__ __forceinline__ void query_wg(const DecodeArgs& a, int s, int hk, uint8_t* lds) {
   constexpr int NP = QShape<D>::NP, QI = QShape<D>::QI;
@@ -2173,10 +2234,12 @@ __device__ __forceinline__ void query_wg(const DecodeArgs& a, int s, int hk, uin
 template <typename T, bool STAGE_V, int D, typename QT, bool WIN, bool GIV>
 __global__ __launch_bounds__(1024) void k_step_front(AppendArgs aa, DecodeArgs da, int n_seqs) {
   extern __shared__ __align__(16) uint8_t lds8[];
-  if (int(blockIdx.x) < n_seqs) {
-    append_one_wg<T, STAGE_V, WIN, GIV>(aa, blockIdx.x, reinterpret_cast<float*>(lds8));
+  const int n_app = n_seqs * aa.n_kv_heads;
+  if (int(blockIdx.x) < n_app) {
+    append_one_wg<T, STAGE_V, WIN, GIV>(aa, blockIdx.x / aa.n_kv_heads, blockIdx.x % aa.n_kv_heads,
+                                        reinterpret_cast<float*>(lds8));
   } else {
-    const int r = blockIdx.x - n_seqs;
+    const int r = blockIdx.x - n_app;
     query_wg<D, QT>(da, r / da.n_kv, r % da.n_kv, lds8);
   }
 }
@@ -2380,7 +2443,7 @@ hipError_t launch_step_front(const AppendArgs& aa, const DecodeArgs& da, bgtq_dt
   constexpr bool SV = D <= 128;
   const size_t q_lds = size_t(tc_qhi_off(D)) + size_t(1024) * (2 * kQRegSteps) +
                        size_t(2048) * (tc_ksteps(D) > kQRegSteps ? tc_ksteps(D) - kQRegSteps : 0);
-  const size_t a_lds = append_one_lds_bytes(D, SV);
+  const size_t a_lds = append_one_lds_bytes(D, SV, SV && !aa.givens);
   const size_t lds = q_lds > a_lds ? q_lds : a_lds;
   const bool kb = kv_dt == BGTQ_BF16, qb = q_dt == BGTQ_BF16, w = aa.window > 0;
   void (*fn)(AppendArgs, DecodeArgs, int) =
@@ -2389,7 +2452,7 @@ hipError_t launch_step_front(const AppendArgs& aa, const DecodeArgs& da, bgtq_dt
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(n_seqs + da.batch * da.n_kv), dim3(1024), lds, st, aa, da, n_seqs);
+  hipLaunchKernelGGL(fn, dim3(n_seqs * aa.n_kv_heads + da.batch * da.n_kv), dim3(1024), lds, st, aa, da, n_seqs);
   return hipGetLastError();
 }
 
@@ -2491,16 +2554,19 @@ hipError_t launch_append_many(const AppendArgs& a, bgtq_dtype dt, dim3 grid, hip
 }
 
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s) {
-  if (a.n_new == 1) {   // decode step: one token per sequence, length advanced in the same kernel
+  if (a.n_new == 1) {   // one token per sequence: one workgroup per (sequence, KV head)
     const bool stage_v = a.d <= 128;
-    const size_t lds = append_one_lds_bytes(a.d, stage_v);
+    const size_t lds = append_one_lds_bytes(a.d, stage_v, stage_v && !a.givens);
     const bool bf = dt == BGTQ_BF16, w = a.window > 0;
     void (*fn)(AppendArgs) = a.givens ? (w ? append_one_kernel<true, true>(bf, stage_v) : append_one_kernel<false, true>(bf, stage_v))
                                       : (w ? append_one_kernel<true, false>(bf, stage_v) : append_one_kernel<false, false>(bf, stage_v));
     const hipError_t e =
         hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(n_seqs), dim3(1024), lds, s, a);
+    hipLaunchKernelGGL(fn, dim3(n_seqs * a.n_kv_heads), dim3(1024), lds, s, a);
+    if (a.advance)
+      hipLaunchKernelGGL(k_advance, dim3((n_seqs + 63) / 64), dim3(64), 0, s, a.lengths, a.seq_begin, n_seqs,
+                         a.n_new, a.capacity);
     return hipGetLastError();
   }
   const int halves = int((a.n_new + kHalf - 1) / kHalf) + 1;
