@@ -1746,27 +1746,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // Tokens [0, pend) are attended from the packed keys by the last n_split - n_wsplit
   // splits; with a window (WIN), the window's tokens [pend, len) from their fp16 keys by the
   // first n_wsplit splits (workgroup-uniform role; dispatched first, as their prologue is the
-  // longer one).  Each role's tiles are shared out so that split i of n takes tiles
-  // [i T / n, (i + 1) T / n) of the role's T tiles: counts differ by at most one.
+  // longer one).  Packed split i of n takes tiles i, i + n, i + 2n, ... of the role's T tiles,
+  // so its first tile is known before the length is; window split i takes the range
+  // [i T / n, (i + 1) T / n).  Either way the counts differ by at most one.
   const int pend = !WIN ? len : (len > a.window ? len - a.window : 0);
   const int nw = WIN ? a.n_wsplit : 0, n_ps = a.n_split - nw;
   const bool win = WIN && split < nw;
-  int t0, t1, vlo, vhi;                              // tiles, and the role's token range
+  int tbase, tstride, count, vlo, vhi;               // tiles tbase + it * tstride, the role's tokens
   if (!win) {
     const int tiles = (pend + kTile - 1) / kTile;
-    t0 = int(int64_t(split - nw) * tiles / n_ps);
-    t1 = int(int64_t(split - nw + 1) * tiles / n_ps);
+    tbase = split - nw;
+    tstride = n_ps;
+    count = tiles > tbase ? (tiles - tbase + n_ps - 1) / n_ps : 0;
     vlo = 0;
     vhi = pend;
   } else {
     const int first = pend / kTile, tiles = pend < len ? (len + kTile - 1) / kTile - first : 0;
     const int nwd = nw > 0 ? nw : 1;               // nw > 0 whenever this role runs
-    t0 = first + int(int64_t(split) * tiles / nwd);
-    t1 = first + int(int64_t(split + 1) * tiles / nwd);
+    tbase = first + int(int64_t(split) * tiles / nwd);
+    tstride = 1;
+    count = first + int(int64_t(split + 1) * tiles / nwd) - tbase;
     vlo = pend;
     vhi = len;
   }
-  const int count = t1 - t0;
   const int bv = a.v_bits, chunks = a.chunks;
   const TcStage geo = tc_stage(D, chunks, bv);
   const HeadLayout* L = a.layouts + int64_t(s) * a.n_kv + hk;
@@ -1774,7 +1776,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 
   // ---- staging of one tile's share of this wave, through registers: K records of the wave's
   // 16 tokens record-major ([token][chunk][16 B], unit u = token * chunks + chunk), group and
-  // value norms [g][16] fp16 (value norms at g = n_groups), value segments of the wave's
+  // value norms [g][16] fp16 (value norms at g = kMaxGroups, planes of absent groups staged
+  // too, so that no address depends on the layout), value segments of the wave's
   // D/4 coordinates.  Loads for the next tile are in flight while this tile is computed.
   const size_t reg = size_t(s) * a.n_kv + hk;
   const int64_t cap_tiles = a.capacity / kTile;
@@ -1796,13 +1799,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 #pragma unroll
   for (int i = 0; i < MAXNV; ++i) vdst[i] = uint32_t(16 * min(64 * i + lane, D * bv / 8 - 1));
-  const int nu = min(lane, 2 * ng + 1);                      // norm unit of this lane
-  const bool nu_k = nu < 2 * ng;                             // group norm (else value norm)
+  const int nu = min(lane, 2 * kMaxGroups + 1);              // norm unit of this lane
+  const bool nu_k = nu < 2 * kMaxGroups;                     // group norm (else value norm)
   const size_t nsrc = nu_k ? (size_t(nu >> 1) * kTile + 16 * wave + 8 * (nu & 1))
                            : (size_t(16 * wave + 8 * (nu & 1)));
   uint4 pk[MAXNK], pn, pv[MAXNV];
   auto load_tile = [&](int it) {
-    const int tile = t0 + it;
+    const int tile = tbase + it * tstride;
     const uint8_t* kt = kc + size_t(tile) * chunks * kTile * 16;
     if (has_k) {
 #pragma unroll
@@ -1840,6 +1843,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const uint4* const qpre = PRE ? a.qpre + reg * tc_ksteps(D) * 128 : nullptr;     // [k-step][hi, lo][lane]
   f16x8 qh[kQRegSteps];
   {
+    // a packed split's first tile depends on neither the length nor the layout: requested first
+    if (!win) load_tile(0);
     const uint4 lw = reinterpret_cast<const uint4*>(L)[tid];
     uint32_t pt[PW];
     uint16_t st[SW];
@@ -1852,12 +1857,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     float x0[QI], x1[QI];
     double fr = 0.0;
     if (PRE && !win) {
+      // every k-step of the head's operand block is read (the number in use, from the layout,
+      // is not waited for); the tile loop never reads those past it
 #pragma unroll
       for (int ks = 0; ks < kQRegSteps; ++ks) {
         const uint4 z = uint4{0u, 0u, 0u, 0u};
-        qh[ks] = __builtin_bit_cast(f16x8, ks < nks ? qpre[ks * 128 + lane] : z);
+        qh[ks] = __builtin_bit_cast(f16x8, ks < tc_ksteps(D) ? qpre[ks * 128 + lane] : z);
       }
-      for (int i = tid; i < 64 * nks; i += 256) {
+      for (int i = tid; i < 64 * tc_ksteps(D); i += 256) {
         const int ks = i >> 6, ln = i & 63;
         if (ks < kQRegSteps) qlo[i] = qpre[ks * 128 + 64 + ln];
         else {
@@ -1869,7 +1876,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       q_load<D, QT>(a, s, hk, tid, x0, x1);
       fr = a.rope_theta > 0.0 ? a.inv_freq[tid % NP] : 0.0;
     }
-    if (count > 0) load_tile(0);
+    if (win && count > 0) load_tile(0);
     reinterpret_cast<uint4*>(Ls)[tid] = lw;
     uint32_t* ptab = reinterpret_cast<uint32_t*>(lds);
 #pragma unroll
@@ -2007,7 +2014,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
     const float m_new = fmaxf(m_run, tmax);          // finite: every tile has a valid token
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const f16x4 vn = *reinterpret_cast<const f16x4*>(buf + geo.n_off + 32 * ng + 8 * j);
+    const f16x4 vn = *reinterpret_cast<const f16x4*>(buf + geo.n_off + 32 * kMaxGroups + 8 * j);
     f16x4 bp;
     float psum = 0.0f;
 #pragma unroll
@@ -2055,7 +2062,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // loads in flight inside the loop are the next tile's
   __builtin_amdgcn_s_waitcnt(0);
   for (int it = 0; it < count; ++it) {
-    const int tile = t0 + it;
+    const int tile = tbase + it * tstride;
     // tokens of this tile in the role's range: slots [vlo - 64 tile, valid)
     const int valid = vhi - tile * kTile < kTile ? vhi - tile * kTile : kTile;
     store_tile();                             // this wave's staging is read only by this wave
