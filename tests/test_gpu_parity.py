@@ -112,6 +112,8 @@ def test_allocate_bit_exact(n, seed):
     (128, 8, 8, [65]),
     (128, 0, 3, [40]),
     (256, 3, 2, [129]),
+    (72, 3, 3, [100, 1, 37, 5]),      # head dims that are not multiples of 16 or 64
+    (200, 3, 2, [70, 1, 33]),
 ])
 def test_quantize_append_bytes_bit_exact(d, k_bits, v_bits, appends):
     dev = _cuda()
@@ -162,6 +164,8 @@ def test_capacity_overflow_sets_status(rot64):
     (64, 3, 3, 3, [7, 20], 30, "f32", 1),           # only the second sequence grows
     (256, 3, 7, 1, [5], 70, "f32", 0),
     (128, 0, 3, 2, [3], 66, "f32", 0),              # zero key budget
+    (72, 3, 3, 2, [60, 5], 40, "f32", 0),           # head dims that are not multiples of 16
+    (200, 2, 3, 1, [10], 30, "bf16", 0),
 ])
 def test_append_one_token_per_step_bit_exact(d, k_bits, v_bits, h_kv, prefill, steps, dtype, seq_begin):
     """Decode-style appends (one token per sequence per call) against the oracle, byte for byte."""
