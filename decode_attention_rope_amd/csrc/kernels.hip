@@ -832,45 +832,66 @@ __device__ __forceinline__ float dot_rows_t(const float* __restrict__ Rt, int m,
 }
 
 // Sequential fp32 dot product of row `row` of an LDS matrix with row stride ld and x (both in
-// LDS), k ascending over [0, m).  Terms past m in the last chunk of 16 are exact zeros, which
-// leave the sum's value (and so every code) unchanged.  x is 8-byte aligned and readable to
-// the end of that chunk.
+// LDS), k ascending over [0, m).  Chunks of 16 terms; each chunk's reads are issued before the
+// previous chunk's adds.  Terms past m in the last chunk are exact zeros, which leave the sum's
+// value (and so every code) unchanged.  x is 8-byte aligned and readable to the end of that
+// chunk.
 __device__ __forceinline__ float dot_rows_lds_any(const float* R, int ld, int m, int row, const float* x) {
-  float acc = 0.0f;
   const float* rr = R + row * ld;
-  for (int k0 = 0; k0 < m; k0 += 16) {
-    float r[16], xv[16];
+  float acc = 0.0f;
+  float r[16], xv[16];
+  auto fetch = [&](float (&rb)[16], float (&xb)[16], int k0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = rr[k0 + i < m ? k0 + i : m - 1];   // every read issued
+    for (int i = 0; i < 16; ++i) rb[i] = rr[k0 + i < m ? k0 + i : m - 1];
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const float2 v = *reinterpret_cast<const float2*>(x + k0 + i);
-      xv[i] = v.x; xv[i + 1] = v.y;
+      xb[i] = v.x; xb[i + 1] = v.y;
     }
+  };
+  fetch(r, xv, 0);
+  int k0 = 0;
+  for (; k0 + 16 < m; k0 += 16) {           // full chunks with a chunk after them
+    float rn[16], xn[16];
+    fetch(rn, xn, k0 + 16);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool in = k0 + i < m;
-      acc = acc + (in ? r[i] : 0.0f) * (in ? xv[i] : 0.0f);
-    }
+    for (int i = 0; i < 16; ++i) acc = acc + r[i] * xv[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { r[i] = rn[i]; xv[i] = xn[i]; }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {            // the last chunk
+    const bool in = k0 + i < m;
+    acc = acc + (in ? r[i] : 0.0f) * (in ? xv[i] : 0.0f);
   }
   return acc;
 }
 
-// Sequential fp32 sum of squares of x[0..m) (m even, x 8-byte aligned).
+// Sequential fp32 sum of squares of x[0..m) (m even, x 8-byte aligned, readable to the end of
+// the last chunk of 8); each chunk's reads are issued before the previous chunk's adds.
 __device__ __forceinline__ float seq_sumsq(const float* x, int m) {
   float ss = 0.0f;
-  int k = 0;
-  for (; k + 8 <= m; k += 8) {
-    float v[8];
+  float v[8];
+  auto fetch = [&](float (&b)[8], int k) {
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
       const float2 t = *reinterpret_cast<const float2*>(x + k + i);
-      v[i] = t.x; v[i + 1] = t.y;
+      b[i] = t.x; b[i + 1] = t.y;
     }
+  };
+  fetch(v, 0);
+  int k = 0;
+  for (; k + 8 < m; k += 8) {
+    float vn[8];
+    fetch(vn, k + 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss = ss + v[i] * v[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = vn[i];
   }
-  for (; k < m; ++k) ss = ss + x[k] * x[k];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (k + i < m) ss = ss + v[i] * v[i];
   return ss;
 }
 
