@@ -340,7 +340,10 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
   // once), the packed keys keep at least one split
   a.n_wsplit = window_splits(cache->window);
   const int base = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma);
-  a.n_split = (base - a.n_wsplit > 1 ? base - a.n_wsplit : 1) + a.n_wsplit;
+  // the matrix-core pass leaves one workgroup of every (sequence, KV head) to a decode step's
+  // append role, so that a step and a decode call split the tokens alike
+  const int packed = base - a.n_wsplit - (a.use_mfma ? 1 : 0);
+  a.n_split = (packed > 1 ? packed : 1) + a.n_wsplit;
   char* ws = static_cast<char*>(workspace);
   const size_t qrot_b = align256(decode_qrot_bytes(cache->batch, cache->n_kv_heads, d));
   a.qrot = reinterpret_cast<float*>(ws);
@@ -404,8 +407,8 @@ bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, 
                                                   cache->capacity);
   aa.advance = 0;
   da.step = 1;
-  da.qpre = reinterpret_cast<uint4*>(static_cast<char*>(workspace) + need -
-                                     align256(decode_qpre_bytes(cache->batch, cache->n_kv_heads, cache->head_dim)));
+  da.step_flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need -
+                                            align256(decode_qpre_bytes(cache->batch, cache->n_kv_heads, cache->head_dim)));
   return hip_status(launch_decode_step(aa, da, kv_dtype, q_dtype, s), "decode-step launch");
 }
 

@@ -124,6 +124,7 @@ struct AppendArgs {
   uint16_t* k_window; // fp16 recent keys [batch][n_kv][window][d], token t at slot t % window
   int window;         // 0: no window
   const uint4* givens;  // structured rotations (header, then records), or null for dense ones
+  int kv_bf16;        // keys and values are bf16 (the decode step's append role)
 };
 hipError_t launch_append(const AppendArgs& a, bgtq_dtype dt, int n_seqs, hipStream_t s);
 
@@ -144,7 +145,8 @@ struct DecodeArgs {
   float* qrot;        // [batch][n_kv][d][kQPad] fp32 (vector-ALU kernel)
   float* partial;     // [batch][n_q][n_split][d] split accumulators
   float2* part_ml;    // [batch][n_q][n_split] split (running max, row sum)
-  uint4* qpre;        // matrix-core B operands [batch][n_kv][k-steps][hi, lo][64 lanes], or null
+  uint4* qpre;        // unused
+  int32_t* step_flag; // [batch][n_kv] decode step: new length once the append role's stores are released
   double rope_theta;
   double inv_freq[BGTQ_MAX_HEAD_DIM / 2];   // rope_theta^(-2j/d), fp64, computed on the host
   float scale;

@@ -1112,6 +1112,157 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
   append_one_wg<T, STAGE_V, WIN, GIV>(a, blockIdx.x / a.n_kv_heads, blockIdx.x % a.n_kv_heads, dyn);
 }
 
+// ---- decode step, append role: the one-token append of (sequence s, KV head hk) on one 256-thread
+// workgroup of the split kernel, the same arithmetic as k_append_one; the rotations read the
+// transposed matrices from global memory.  Once its stores are released, it publishes the new
+// length in step_flag[s][hk]; the split that reads the new token's tile waits for that.
+constexpr size_t kStepAppendLds =
+    size_t(kAppendThrFloats) * 4 + sizeof(HeadLayout) +
+    4 * size_t(BGTQ_MAX_HEAD_DIM + 2 * BGTQ_MAX_HEAD_DIM + 16 + BGTQ_MAX_HEAD_DIM + 16 + kMaxGroups + 1 + kMaxRecordDwords);
+constexpr int kStepSpinLimit = 1 << 22;    // bounded wait of the split that reads the new tile
+
+template <bool WIN, bool GIV>
+__device__ void step_append_role(const AppendArgs& a, int32_t* flags, int s, int hk, uint8_t* lds) {
+  constexpr int DM = BGTQ_MAX_HEAD_DIM;
+  const int t = threadIdx.x, d = a.d, bv = a.v_bits;
+  float* thr = reinterpret_cast<float*>(lds);                                   // [8][255]
+  HeadLayout* Lp = reinterpret_cast<HeadLayout*>(lds + kAppendThrFloats * 4);
+  float* ko = reinterpret_cast<float*>(Lp + 1);        // key, original order
+  float* xk = ko + DM;                                 // key, storage order, zero past d_eff
+  float* xv = xk + 2 * DM + 16;                        // value, zero past d
+  float* nrm = xv + DM + 16;                           // group norms, value norm last
+  uint32_t* kw = reinterpret_cast<uint32_t*>(nrm + kMaxGroups + 1);   // the slot's key record
+  const size_t reg = size_t(s) * a.n_kv_heads + hk;
+  const int si = s - a.seq_begin;
+  const size_t esz = a.kv_bf16 ? 2 : 4;
+  const char* kin = static_cast<const char*>(a.keys) + (si * a.stride_seq + hk * a.stride_head) * esz;
+  const char* vin = static_cast<const char*>(a.values) + (si * a.stride_seq + hk * a.stride_head) * esz;
+  auto ld = [&](const char* base, int i) {
+    return a.kv_bf16 ? load_f(reinterpret_cast<const uint16_t*>(base), i) : load_f(reinterpret_cast<const float*>(base), i);
+  };
+  // ---- first round of reads: none depends on the length or on the layout
+  const uint4 lw = reinterpret_cast<const uint4*>(a.layouts + reg)[t];
+  const float kval = t < d ? ld(kin, t) : 0.0f;
+  const float vval = t < d ? ld(vin, t) : 0.0f;
+  float tv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tv[i] = t + 256 * i < kAppendThrFloats ? (&c_thr[0][0])[t + 256 * i] : 0.0f;
+  const int64_t len = a.lengths[s];
+  __builtin_amdgcn_sched_barrier(0);
+  reinterpret_cast<uint4*>(Lp)[t] = lw;
+  ko[t] = kval;
+  xv[t] = vval;
+  if (t < 16) xv[DM + t] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (t + 256 * i < kAppendThrFloats) thr[t + 256 * i] = tv[i];
+  if (t < kMaxRecordDwords) kw[t] = 0u;
+  __syncthreads();
+  if (len + 1 > a.capacity) {                     // nothing appended; the splits do not wait
+    if (t == 0 && hk == 0 && a.status) atomicOr(a.status, 1);
+    return;
+  }
+  const HeadLayout& L = *Lp;
+  const int64_t tiles = a.capacity / kTile;
+  const int64_t tile = len / kTile;
+  const int slot = int(len - tile * kTile);
+  const uint32_t vmask = (1u << bv) - 1u;
+  const int vbit = slot * bv, vw = vbit >> 5, vsh = vbit & 31;
+  const bool vsplit = vsh + bv > 32;
+  uint32_t* vseg = reinterpret_cast<uint32_t*>(a.v_codes) + (reg * tiles + tile) * d * 2 * bv;
+  const int ng = L.n_groups, d_eff = L.d_eff;
+  uint32_t old0 = 0u, old1 = 0u;
+  if (t < d) {
+    old0 = vseg[t * 2 * bv + vw];
+    if (vsplit) old1 = vseg[t * 2 * bv + vw + 1];
+  }
+  int mmax = 0;
+  for (int g = 0; g < ng; ++g) mmax = L.g_m[g] > mmax ? L.g_m[g] : mmax;
+  mmax = (mmax + 15) & ~15;
+  for (int i = t; i < 2 * DM + 16; i += 256) xk[i] = i < d_eff ? ko[L.perm[i]] : 0.0f;
+  __syncthreads();
+  // rotations: value row r < d, key position r - d; rows t and t + 256
+  float acc[2] = {0.0f, 0.0f};
+  if constexpr (GIV) {
+    if (t < ng) nrm[t] = sqrtf(seq_sumsq(xk + L.g_first[t], L.g_m[t]));
+    else if (t == ng) nrm[kMaxGroups] = sqrtf(seq_sumsq(xv, d));
+    // one pair slot per thread: value slot t, or key slot t - 128 of its width group
+    GivensSlot gs;
+    gs.n = 0;
+    float* gx = nullptr;
+    if (t < d / 2) {
+      givens_fetch(a.givens, d, t, gs);
+      gx = xv;
+    } else if (t >= 128 && t < 128 + d_eff / 2) {
+      const int q = t - 128, g = L.group[2 * q], first = L.g_first[g];
+      givens_fetch(a.givens, L.g_m[g], q - first / 2, gs);
+      gx = xk + first;
+    }
+    const int nl = max(givens_count(a.givens, d), givens_layers(a.givens, L));
+    __syncthreads();
+#pragma unroll
+    for (int l = 0; l < kMaxGivensLayers; ++l) {
+      if (l < nl) {
+        if (l < gs.n) {
+          gs.apply(gx, l);
+          if (l + kGivensAhead < kMaxGivensLayers) gs.fetch(l + kGivensAhead);
+        }
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = t + 256 * j;
+      if (r < d) acc[j] = xv[r];
+      else if (r < d + d_eff) acc[j] = xk[r - d];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = t + 256 * j;
+      if (r < d) {
+        acc[j] = dot_rows_t(a.rot_v_t, d, d, r, xv);
+      } else if (r < d + d_eff) {
+        const int p = r - d, g = L.group[p], m = L.g_m[g], first = L.g_first[g];
+        acc[j] = dot_rows_t(a.rot_bank_t + bank_offset(m), m, mmax, p - first, xk + first);
+      }
+    }
+    if (t < ng) nrm[t] = sqrtf(seq_sumsq(xk + L.g_first[t], L.g_m[t]));
+    else if (t == ng) nrm[kMaxGroups] = sqrtf(seq_sumsq(xv, d));
+  }
+  __syncthreads();
+  // codes: a value code goes straight into the slot's dwords; key codes are ored into the record
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = t + 256 * j;
+    if (r < d) {
+      const float nv = nrm[kMaxGroups];
+      const uint32_t code = nv != 0.0f ? code_of(thr + (bv - 1) * 255, bv, (acc[j] / nv) * sqrtf(float(d))) : 0u;
+      vseg[r * 2 * bv + vw] = (old0 & ~(vmask << vsh)) | (code << vsh);
+      if (vsplit) vseg[r * 2 * bv + vw + 1] = (old1 & ~(vmask >> (32 - vsh))) | (code >> (32 - vsh));
+    } else if (r < d + d_eff) {
+      const int p = r - d, g = L.group[p], w = L.g_width[g], m = L.g_m[g];
+      const float nv = nrm[g];
+      const uint32_t code = nv != 0.0f ? code_of(thr + (w - 1) * 255, w, (acc[j] / nv) * sqrtf(float(m))) : 0u;
+      const int off = L.offset[p], wd = off >> 5, sh = off & 31;
+      atomicOr(&kw[wd], code << sh);
+      if (sh + w > 32) atomicOr(&kw[wd + 1], code >> (32 - sh));
+    }
+  }
+  __syncthreads();
+  uint32_t* kc = reinterpret_cast<uint32_t*>(a.k_codes) + (reg * tiles + tile) * a.chunks * kTile * 4;
+  if (t < 4 * a.chunks) kc[((t >> 2) * kTile + slot) * 4 + (t & 3)] = kw[t];
+  uint16_t* kn = a.k_norms + (reg * tiles + tile) * kMaxGroups * kTile;
+  if (t < ng) kn[t * kTile + slot] = f32_to_f16_bits(fminf(nrm[t], 65504.0f));
+  if (t == 255) a.v_norms[(reg * tiles + tile) * kTile + slot] = f32_to_f16_bits(fminf(nrm[kMaxGroups], 65504.0f));
+  if (WIN && t < d) a.k_window[(reg * a.window + len % a.window) * d + t] = f16_sat_bits(ko[t]);
+  // ---- publish: every store released at device scope, then the new length
+  __threadfence();
+  __syncthreads();
+  if (t == 0) __hip_atomic_store(flags + reg, int32_t(len + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+
 // fp16 keys of the appended tokens that end up among the newest `window` (the last
 // min(n_new, window) of them), at slot t % window; runs before the length advance.
 template <typename T>
@@ -1750,14 +1901,22 @@ __device__ __forceinline__ void qops_scatter_rotated(const DecodeArgs& a, const 
   }
 }
 
-template <int D, bool NARROW, typename QT, bool PRE, bool WIN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_mfma(DecodeArgs a) {
+template <int D, bool NARROW, typename QT, bool STEP, bool WIN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_mfma(DecodeArgs a, AppendArgs aa) {
   constexpr int CPW = D / 4;                          // value coordinates per wave
   constexpr int MTV = CPW / 16;                       // value M-tiles per wave
   constexpr int MAXNK = NARROW ? 1 : (D + 63) / 64;                  // K staging loads per lane
   constexpr int MAXNV = NARROW ? (D / 2 + 63) / 64 : (D + 63) / 64;  // value staging loads per lane
   extern __shared__ __align__(16) uint8_t lds[];
-  const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
+  if constexpr (STEP) {
+    // decode step: workgroup 0 of every (sequence, KV head) appends the new token
+    if (blockIdx.x == 0) {
+      if (aa.givens) step_append_role<WIN, true>(aa, a.step_flag, blockIdx.z, blockIdx.y, lds);
+      else step_append_role<WIN, false>(aa, a.step_flag, blockIdx.z, blockIdx.y, lds);
+      return;
+    }
+  }
+  const int split = int(blockIdx.x) - (STEP ? 1 : 0), hk = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
   // in a decode step the new token was appended after lengths[] were read; lengths[] is
@@ -1790,6 +1949,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     vlo = pend;
     vhi = len;
   }
+  // decode step: the split whose tiles include the new token's waits for the append role before
+  // it requests that tile (iteration it_new), with a bounded wait
+  int it_new = -1;
+  if constexpr (STEP) {
+    if (len == len0 + 1) {
+      const int dt = len0 / kTile - tbase;
+      if (dt >= 0 && dt % tstride == 0 && dt / tstride < count) it_new = dt / tstride;
+    }
+  }
+  auto wait_append = [&]() {
+    if (tid == 0) {
+      const int32_t* f = a.step_flag + (size_t(s) * a.n_kv + hk);
+      for (int i = 0; i < kStepSpinLimit; ++i) {
+        if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == len0 + 1) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  };
   const int bv = a.v_bits, chunks = a.chunks;
   const TcStage geo = tc_stage(D, chunks, bv);
   const HeadLayout* L = a.layouts + int64_t(s) * a.n_kv + hk;
@@ -1850,8 +2029,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   };
   // ---- workgroup set-up and query prologue.  Global reads come in two rounds: everything
   // that does not depend on the layout descriptor (descriptor, level tables, query, first
-  // tile), then the rotation rows.  With PRE the rotated query's B operands were written by
-  // the decode step's query workgroups and are read in the first round instead.
+  // tile), then the rotation rows.
   constexpr int NP = QShape<D>::NP, QI = QShape<D>::QI;
   constexpr int PW = (kPairWords + 255) / 256, SW = (kSingleHalves + 255) / 256;
   static_assert(BGTQ_LAYOUT_BYTES == 256 * 16, "one 16-byte piece of the layout per thread");
@@ -1861,7 +2039,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   uint4* const qhi = reinterpret_cast<uint4*>(pro + tc_qhi_off(D));                // [k-step < 8][lane]
   uint4* const qlo = reinterpret_cast<uint4*>(lds + tc_qlo_off(D, chunks, bv));     // [k-step < 8][lane]
   uint4* const qlate = qlo + 64 * kQRegSteps;                                       // [k-step - 8][hi, lo][lane]
-  const uint4* const qpre = PRE ? a.qpre + reg * tc_ksteps(D) * 128 : nullptr;     // [k-step][hi, lo][lane]
   f16x8 qh[kQRegSteps];
   {
     // a packed split's first tile depends on neither the length nor the layout: requested first
@@ -1877,23 +2054,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       if (tid + 256 * i < kSingleHalves) st[i] = c_single[tid + 256 * i];
     float x0[QI], x1[QI];
     double fr = 0.0;
-    if (PRE && !win) {
-      // every k-step of the head's operand block is read (the number in use, from the layout,
-      // is not waited for); the tile loop never reads those past it
-#pragma unroll
-      for (int ks = 0; ks < kQRegSteps; ++ks) {
-        const uint4 z = uint4{0u, 0u, 0u, 0u};
-        qh[ks] = __builtin_bit_cast(f16x8, ks < tc_ksteps(D) ? qpre[ks * 128 + lane] : z);
-      }
-      for (int i = tid; i < 64 * tc_ksteps(D); i += 256) {
-        const int ks = i >> 6, ln = i & 63;
-        if (ks < kQRegSteps) qlo[i] = qpre[ks * 128 + 64 + ln];
-        else {
-          qlate[(ks - kQRegSteps) * 128 + ln] = qpre[ks * 128 + ln];
-          qlate[(ks - kQRegSteps) * 128 + 64 + ln] = qpre[ks * 128 + 64 + ln];
-        }
-      }
-    } else {
+    {
       q_load<D, QT>(a, s, hk, tid, x0, x1);
       fr = a.rope_theta > 0.0 ? a.inv_freq[tid % NP] : 0.0;
     }
@@ -1912,7 +2073,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const int ln = (i >> 2) & 63;      // lane of the 16-byte B operand
       if ((ln & 15) >= 8) pw[i] = 0u;
     }
-    if (!PRE || win) {
+    {
       qops_zero(qhi, qlo, qlate, nks, tid);
       q_rope<D>(a, a.q_pos ? a.q_pos[s] : int64_t(len) - 1, fr, tid, x0, x1, qc);
     }
@@ -1960,7 +2121,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       qh[ks] = hi;
       qlo[ks * 64 + lane] = __builtin_bit_cast(uint4, lo);
     }
-  } else if (!PRE) {
+  } else {
     if (a.givens) {
       qops_givens_rotate(a, Ls, qc, tid, 256);
       qops_scatter_rotated(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlate);
@@ -1971,7 +2132,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   __syncthreads();   // also orders the prologue's reads of the ring before the first staging store
 
   // ---- query operands of the first k-steps in registers (zero past the last one)
-  if (!PRE && !win) {
+  if (!win) {
 #pragma unroll
     for (int ks = 0; ks < kQRegSteps; ++ks) {
       const uint4 z = uint4{0u, 0u, 0u, 0u};
@@ -2081,6 +2242,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 
   // every load issued so far (query operands, set-up reads) is complete here, so the only
   // loads in flight inside the loop are the next tile's
+  if (STEP && it_new == 0) {     // the first tile holds the new token: requested again after the append
+    wait_append();
+    load_tile(0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   for (int it = 0; it < count; ++it) {
     const int tile = tbase + it * tstride;
@@ -2088,6 +2253,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int valid = vhi - tile * kTile < kTile ? vhi - tile * kTile : kTile;
     store_tile();                             // this wave's staging is read only by this wave
     asm volatile("" ::: "memory");            // issue the next tile's loads after these stores
+    if (STEP && it + 1 == it_new) wait_append();
     if (it + 1 < count) load_tile(it + 1);
 
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
@@ -2404,35 +2570,42 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
       a.out[(int64_t(s) * a.n_q + h) * D + tid] = o * inv;
     }
   }
+  if (a.step && a.step_flag && h % a.group == 0 && tid == 0)   // ready for the next step
+    a.step_flag[int64_t(s) * a.n_kv + h / a.group] = 0;
   if (a.step && h == 0 && tid == 0) {     // the decode step's length advance, after every reader
     const int len0 = a.lengths[s];
     if (len0 + 1 <= a.capacity) a.lengths[s] = len0 + 1;
   }
 }
 
-// the matrix-core kernel for a cache's record widths, query dtype and pass (with the query
-// operands precomputed by a decode step or not); with WIN, the window role is built in
+// the matrix-core kernel for a cache's record widths, query dtype and pass (a decode step, with
+// its append role, or a decode call); with WIN, the window role is built in
 template <int D, bool WIN>
-auto mfma_kernel(bool narrow, bool bf16, bool pre) -> void (*)(DecodeArgs) {
-  if (pre) return narrow ? k_decode_mfma<D, true, float, true, WIN> : k_decode_mfma<D, false, float, true, WIN>;
+auto mfma_kernel(bool narrow, bool bf16, bool step) -> void (*)(DecodeArgs, AppendArgs) {
+  if (step)
+    return narrow ? (bf16 ? k_decode_mfma<D, true, uint16_t, true, WIN> : k_decode_mfma<D, true, float, true, WIN>)
+                  : (bf16 ? k_decode_mfma<D, false, uint16_t, true, WIN> : k_decode_mfma<D, false, float, true, WIN>);
   return narrow ? (bf16 ? k_decode_mfma<D, true, uint16_t, false, WIN> : k_decode_mfma<D, true, float, false, WIN>)
                 : (bf16 ? k_decode_mfma<D, false, uint16_t, false, WIN> : k_decode_mfma<D, false, float, false, WIN>);
 }
 
+// a decode call, or (step != null, matrix-core path) a decode step: one more workgroup per
+// (sequence, KV head), the append role, ahead of the splits
 template <int D>
-hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st) {
-  const dim3 grid(a.n_split, a.n_kv, a.batch);
+hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st, const AppendArgs* step = nullptr) {
+  const dim3 grid(a.n_split + (step ? 1 : 0), a.n_kv, a.batch);
   if (a.use_mfma) {
-    const int lds = tc_lds_bytes(D, a.chunks, a.v_bits);
+    int lds = tc_lds_bytes(D, a.chunks, a.v_bits);
+    if (step && lds < int(kStepAppendLds)) lds = int(kStepAppendLds);
     const bool narrow = a.chunks <= 4 && a.v_bits <= 4, bf16 = q_dt == BGTQ_BF16;
-    void (*fn)(DecodeArgs) = a.window > 0 ? mfma_kernel<D, true>(narrow, bf16, a.qpre != nullptr)
-                                          : mfma_kernel<D, false>(narrow, bf16, a.qpre != nullptr);
+    void (*fn)(DecodeArgs, AppendArgs) = a.window > 0 ? mfma_kernel<D, true>(narrow, bf16, step != nullptr)
+                                                      : mfma_kernel<D, false>(narrow, bf16, step != nullptr);
     if (lds > 64 * 1024) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, grid, dim3(256), size_t(lds), st, a);
+    hipLaunchKernelGGL(fn, grid, dim3(256), size_t(lds), st, a, step ? *step : AppendArgs{});
   } else {
     if (q_dt == BGTQ_BF16)
       hipLaunchKernelGGL(k_decode_prep<uint16_t>, dim3(a.n_kv, a.batch, kPrepZ), dim3(256), 0, st, a);
@@ -2490,15 +2663,14 @@ hipError_t launch_step_front(const AppendArgs& aa, const DecodeArgs& da, bgtq_dt
 
 hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, bgtq_dtype kv_dt, bgtq_dtype q_dt,
                               hipStream_t st) {
-  hipError_t e = hipSuccess;
+  AppendArgs a2 = aa;
+  a2.kv_bf16 = kv_dt == BGTQ_BF16;
   switch (da.d) {
-    case 64: e = launch_step_front<64>(aa, da, kv_dt, q_dt, da.batch, st); break;
-    case 128: e = launch_step_front<128>(aa, da, kv_dt, q_dt, da.batch, st); break;
-    case 256: e = launch_step_front<256>(aa, da, kv_dt, q_dt, da.batch, st); break;
+    case 64: return launch_decode_d<64>(da, q_dt, st, &a2);
+    case 128: return launch_decode_d<128>(da, q_dt, st, &a2);
+    case 256: return launch_decode_d<256>(da, q_dt, st, &a2);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  return launch_decode(da, q_dt, st);
 }
 
 size_t decode_qpre_bytes(int batch, int n_kv_heads, int d) {
