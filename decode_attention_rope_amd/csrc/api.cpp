@@ -293,7 +293,7 @@ size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
   const size_t part = align256(size_t(batch) * n_q_heads * splits * head_dim * 4) +
                       align256(size_t(batch) * n_q_heads * splits * 8);
   return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + part +
-         align256(decode_qpre_bytes(batch, n_kv_heads, head_dim));
+         align256(decode_step_bytes(batch, n_kv_heads));
 }
 
 static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
@@ -349,7 +349,6 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.qrot = reinterpret_cast<float*>(ws);
   a.partial = reinterpret_cast<float*>(ws + qrot_b);
   a.part_ml = reinterpret_cast<float2*>(ws + qrot_b + align256(size_t(cache->batch) * n_q_heads * a.n_split * d * 4));
-  a.qpre = nullptr;   // set by the decode step (the workspace's last region)
   a.givens = qz->rotation == BGTQ_ROT_GIVENS ? reinterpret_cast<const uint4*>(qz->givens) : nullptr;
   a.rope_theta = rope_theta;
   for (int j = 0; j < d / 2; ++j) a.inv_freq[j] = rope_theta > 0.0 ? std::pow(rope_theta, -2.0 * j / d) : 0.0;
@@ -408,7 +407,7 @@ bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, 
   aa.advance = 0;
   da.step = 1;
   da.step_flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need -
-                                            align256(decode_qpre_bytes(cache->batch, cache->n_kv_heads, cache->head_dim)));
+                                            align256(decode_step_bytes(cache->batch, cache->n_kv_heads)));
   return hip_status(launch_decode_step(aa, da, kv_dtype, q_dtype, s), "decode-step launch");
 }
 

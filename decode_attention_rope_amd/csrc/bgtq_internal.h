@@ -145,14 +145,13 @@ struct DecodeArgs {
   float* qrot;        // [batch][n_kv][d][kQPad] fp32 (vector-ALU kernel)
   float* partial;     // [batch][n_q][n_split][d] split accumulators
   float2* part_ml;    // [batch][n_q][n_split] split (running max, row sum)
-  uint4* qpre;        // unused
   int32_t* step_flag; // [batch][n_kv] decode step: new length once the append role's stores are released
   double rope_theta;
   double inv_freq[BGTQ_MAX_HEAD_DIM / 2];   // rope_theta^(-2j/d), fp64, computed on the host
   float scale;
   int64_t capacity;
   int batch, n_q, n_kv, group, d, v_bits, chunks, n_split, pairing;
-  int step;           // decode step: one token was appended after lengths were read (see k_step_front)
+  int step;           // decode step: one token is appended beside the pass (its append role)
   int use_mfma;
   const uint16_t* k_window;   // fp16 recent keys (see AppendArgs)
   int window;                 // 0: no window
@@ -160,11 +159,12 @@ struct DecodeArgs {
   const uint4* givens;        // structured rotations (see AppendArgs), or null for dense ones
 };
 hipError_t launch_decode(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t s);
-// decode step on the matrix-core path: append one token per sequence and attend (da.qpre set,
-// da.step = 1, aa.advance = 0)
+// decode step on the matrix-core path: append one token per sequence and attend (da.step = 1,
+// da.step_flag set, aa.advance = 0)
 hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, bgtq_dtype kv_dt, bgtq_dtype q_dt,
                               hipStream_t s);
-size_t decode_qpre_bytes(int batch, int n_kv_heads, int d);
+// the decode step's flags: one int per (sequence, KV head), zero between steps
+size_t decode_step_bytes(int batch, int n_kv_heads);
 
 // key-only logit error (diagnostic.hip)
 constexpr int kErrChunk = 256;       // tokens per workgroup and per partial sum

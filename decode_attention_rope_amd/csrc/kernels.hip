@@ -793,8 +793,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 // quantizer thresholds and, for head_dim <= 128, the value rotation), then the slot's old value
 // dwords and, with dense rotations and head_dim <= 128, the key groups' matrices.  Both
 // rotations are staged in LDS with rows padded to m + 1 floats, so lanes on consecutive rows hit
-// distinct banks.  The sequence length is advanced afterwards (k_advance, or the decode step's
-// merge).
+// distinct banks.  The sequence length is advanced afterwards (k_advance).
 //
 // Sequential fp32 dot product of row `row` of an m x m matrix stored transposed (element
 // (row, k) at Rt[k * m + row]) with x, k ascending, no fused multiply-add; lanes on
@@ -1680,8 +1679,7 @@ __device__ __forceinline__ u32x4 decode8_any(uint32_t d0, uint32_t d1, uint32_t 
 // outstanding global loads, so staging loads for later tiles stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// ---- rotated query, shared by the matrix-core kernel's prologue and the decode step's query
-// workgroups.  q' = RoPE(q, pos) with the angle formed and reduced modulo 2 pi in fp64;
+// ---- rotated query, formed in the matrix-core kernel's prologue.  q' = RoPE(q, pos) with the angle formed and reduced modulo 2 pi in fp64;
 // q''[h][p] = (softmax_scale * log2(e) / sqrt(m)) * sum_k R_m[p - first][k] q'[h][perm[first + k]]
 // (m and first of storage position p's width group), split into an fp16 high part and an fp16
 // remainder and scattered into the B operand layout: lane 16 j + c of k-step s holds k indices
@@ -1919,8 +1917,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int split = int(blockIdx.x) - (STEP ? 1 : 0), hk = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
-  // in a decode step the new token was appended after lengths[] were read; lengths[] is
-  // advanced by the merge kernel, so it still holds the old length here
+  // in a decode step the append role adds the new token beside this pass and the merge kernel
+  // advances lengths[], so it still holds the old length here
   const int len0 = a.lengths[s];
   const int len = a.step && len0 + 1 <= a.capacity ? len0 + 1 : len0;
   // Tokens [0, pend) are attended from the packed keys by the last n_split - n_wsplit
@@ -2379,65 +2377,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 }
 
-// ---- decode step, first launch: the one-token append (workgroups 0 .. n_seqs * n_kv - 1, one
-// per (sequence, KV head)) beside the rotated query of every (sequence, KV head) (the remaining
-// workgroups), which depends only on the layout and on the query position, not on the appended
-// token.  The query workgroups write the matrix-core B operands [k-step][hi, lo][64 lanes] to
-// the workspace; lengths[] is left to the merge kernel, so both roles read the old length: the
-// query sits at that position unless the append overflows the capacity (then at the last
-// cached token, as a separate decode call would place it).
-template <int D, typename QT>
-__device__ __forceinline__ void query_wg(const DecodeArgs& a, int s, int hk, uint8_t* lds) {
-  constexpr int NP = QShape<D>::NP, QI = QShape<D>::QI;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const bool mine = tid < 256;                       // waves 0-3 do the work
-  const size_t reg = size_t(s) * a.n_kv + hk;
-  const HeadLayout* L = a.layouts + reg;
-  const int nks = L->n_ksteps;
-  HeadLayout* const Ls = reinterpret_cast<HeadLayout*>(lds);
-  float* const qc = reinterpret_cast<float*>(lds + BGTQ_LAYOUT_BYTES);
-  uint4* const qhi = reinterpret_cast<uint4*>(lds + tc_qhi_off(D));
-  uint4* const qlo = qhi + 64 * kQRegSteps;
-  uint4* const qlate = qlo + 64 * kQRegSteps;
-  if (mine) {
-    const uint4 lw = reinterpret_cast<const uint4*>(L)[tid];
-    float x0[QI], x1[QI];
-    q_load<D, QT>(a, s, hk, tid, x0, x1);
-    const double fr = a.rope_theta > 0.0 ? a.inv_freq[tid % NP] : 0.0;
-    const int len0 = a.lengths[s];
-    const int64_t pos = len0 + 1 <= a.capacity ? int64_t(len0) : int64_t(len0) - 1;
-    reinterpret_cast<uint4*>(Ls)[tid] = lw;
-    qops_zero(qhi, qlo, qlate, nks, tid);
-    q_rope<D>(a, pos, fr, tid, x0, x1, qc);
-  }
-  __syncthreads();
-  if (a.givens) qops_givens_rotate(a, Ls, qc, tid, int(blockDim.x));
-  if (mine) {
-    const uint32_t wmask = wide_ksteps(Ls, nks, lane);
-    if (a.givens) qops_scatter_rotated(a, Ls, qc, wmask, nks - __popc(wmask), tid, qhi, qlo, qlate);
-    else qops_scatter<D>(a, Ls, qc, wmask, nks - __popc(wmask), tid, qhi, qlo, qlate);
-  }
-  __syncthreads();
-  uint4* dst = a.qpre + reg * tc_ksteps(D) * 128;
-  for (int i = tid; i < 128 * nks; i += blockDim.x) {
-    const int ks = i >> 7, part = (i >> 6) & 1, ln = i & 63;
-    dst[i] = ks < kQRegSteps ? (part == 0 ? qhi : qlo)[ks * 64 + ln] : qlate[(ks - kQRegSteps) * 128 + part * 64 + ln];
-  }
-}
-
-template <typename T, bool STAGE_V, int D, typename QT, bool WIN, bool GIV>
-__global__ __launch_bounds__(1024) void k_step_front(AppendArgs aa, DecodeArgs da, int n_seqs) {
-  extern __shared__ __align__(16) uint8_t lds8[];
-  const int n_app = n_seqs * aa.n_kv_heads;
-  if (int(blockIdx.x) < n_app) {
-    append_one_wg<T, STAGE_V, WIN, GIV>(aa, blockIdx.x / aa.n_kv_heads, blockIdx.x % aa.n_kv_heads,
-                                        reinterpret_cast<float*>(lds8));
-  } else {
-    const int r = blockIdx.x - n_app;
-    query_wg<D, QT>(da, r / da.n_kv, r % da.n_kv, lds8);
-  }
-}
-
 // Merge the splits of one query head and undo the value rotation:
 // out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t], from the per-split
 // (m, l) pairs and accumulators; split i is weighted by exp2(m_i - max m).  Every split's
@@ -2631,31 +2570,6 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st,
   return hipGetLastError();
 }
 
-// the decode step's first kernel for the input dtypes, window and rotation kind
-template <bool SV, int D, bool WIN, bool GIV>
-auto step_front_kernel(bool kb, bool qb) -> void (*)(AppendArgs, DecodeArgs, int) {
-  return kb ? (qb ? k_step_front<uint16_t, SV, D, uint16_t, WIN, GIV> : k_step_front<uint16_t, SV, D, float, WIN, GIV>)
-            : (qb ? k_step_front<float, SV, D, uint16_t, WIN, GIV> : k_step_front<float, SV, D, float, WIN, GIV>);
-}
-
-template <int D>
-hipError_t launch_step_front(const AppendArgs& aa, const DecodeArgs& da, bgtq_dtype kv_dt, bgtq_dtype q_dt,
-                             int n_seqs, hipStream_t st) {
-  constexpr bool SV = D <= 128;
-  const size_t q_lds = size_t(tc_qhi_off(D)) + size_t(1024) * (2 * kQRegSteps) +
-                       size_t(2048) * (tc_ksteps(D) > kQRegSteps ? tc_ksteps(D) - kQRegSteps : 0);
-  const size_t a_lds = append_one_lds_bytes(D, SV, SV && !aa.givens);
-  const size_t lds = q_lds > a_lds ? q_lds : a_lds;
-  const bool kb = kv_dt == BGTQ_BF16, qb = q_dt == BGTQ_BF16, w = aa.window > 0;
-  void (*fn)(AppendArgs, DecodeArgs, int) =
-      aa.givens ? (w ? step_front_kernel<SV, D, true, true>(kb, qb) : step_front_kernel<SV, D, false, true>(kb, qb))
-                : (w ? step_front_kernel<SV, D, true, false>(kb, qb) : step_front_kernel<SV, D, false, false>(kb, qb));
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(n_seqs * aa.n_kv_heads + da.batch * da.n_kv), dim3(1024), lds, st, aa, da, n_seqs);
-  return hipGetLastError();
-}
 
 }  // namespace
 
@@ -2673,9 +2587,7 @@ hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, bgtq_d
   }
 }
 
-size_t decode_qpre_bytes(int batch, int n_kv_heads, int d) {
-  return size_t(batch) * n_kv_heads * tc_ksteps(d) * 2048;
-}
+size_t decode_step_bytes(int batch, int n_kv_heads) { return size_t(batch) * n_kv_heads * 4; }
 
 hipError_t upload_tables(const Tables& t) {
   hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(c_thr), t.thr, sizeof(t.thr));

@@ -273,7 +273,9 @@ size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  * token, then attend with q at that token's position.  The result equals
  * bgtq_quantize_append(n_new = 1, all sequences) followed by
  * bgtq_decode_attention(q_pos = NULL), cache contents, lengths, status and out
- * included; the rotated query is computed beside the append instead of after it.
+ * included.  The append runs beside the attention pass, in the same launch; only the
+ * part of the pass that reads the new token's tile waits for it (a flag in the workspace,
+ * zero between calls).
  *   keys, values  [batch][n_kv_heads][head_dim] of kv_dtype, element (s, h, c) at
  *                 s * stride_seq + h * stride_head + c.
  *   q, out, logits_out, workspace: as for bgtq_decode_attention (the same workspace
