@@ -406,6 +406,11 @@ bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, 
                                                   cache->capacity);
   aa.advance = 0;
   da.step = 1;
+  // the wait of the split that reads the new token's tile is bounded (about 0.2 s at most);
+  // BGTQ_STEP_SPIN_LIMIT overrides the bound (0: no wait), to exercise the report of a wait
+  // that gave up
+  da.step_spin = 1 << 22;
+  if (const char* sl = std::getenv("BGTQ_STEP_SPIN_LIMIT")) da.step_spin = std::atoi(sl) > 0 ? std::atoi(sl) : 0;
   da.step_flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need -
                                             align256(decode_step_bytes(cache->batch, cache->n_kv_heads)));
   return hip_status(launch_decode_step(aa, da, kv_dtype, q_dtype, s), "decode-step launch");

@@ -146,6 +146,7 @@ struct DecodeArgs {
   float* partial;     // [batch][n_q][n_split][d] split accumulators
   float2* part_ml;    // [batch][n_q][n_split] split (running max, row sum)
   int32_t* step_flag; // [batch][n_kv] decode step: new length once the append role's stores are released
+  int step_spin;      // decode step: bound of the wait for the append role (spins of a few hundred cycles)
   double rope_theta;
   double inv_freq[BGTQ_MAX_HEAD_DIM / 2];   // rope_theta^(-2j/d), fp64, computed on the host
   float scale;

@@ -1118,7 +1118,6 @@ __global__ __launch_bounds__(1024) void k_append_one(AppendArgs a) {
 constexpr size_t kStepAppendLds =
     size_t(kAppendThrFloats) * 4 + sizeof(HeadLayout) +
     4 * size_t(BGTQ_MAX_HEAD_DIM + 2 * BGTQ_MAX_HEAD_DIM + 16 + BGTQ_MAX_HEAD_DIM + 16 + kMaxGroups + 1 + kMaxRecordDwords);
-constexpr int kStepSpinLimit = 1 << 22;    // bounded wait of the split that reads the new tile
 
 template <bool WIN, bool GIV>
 __device__ void step_append_role(const AppendArgs& a, int32_t* flags, int s, int hk, uint8_t* lds) {
@@ -1959,10 +1958,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   auto wait_append = [&]() {
     if (tid == 0) {
       const int32_t* f = a.step_flag + (size_t(s) * a.n_kv + hk);
-      for (int i = 0; i < kStepSpinLimit; ++i) {
+      int i = 0;
+      for (; i < a.step_spin; ++i) {
         if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == len0 + 1) break;
         __builtin_amdgcn_s_sleep(2);
       }
+      if (i == a.step_spin && aa.status) atomicOr(aa.status, 2);   // gave up: reported
     }
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");

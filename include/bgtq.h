@@ -127,7 +127,9 @@ bgtq_status bgtq_transpose_rotations(const float* rot_bank, const float* rot_v, 
  *            [batch][n_kv_heads][BGTQ_LAYOUT_BYTES]: written by
  *            bgtq_allocate_bits at prefill and read by the other calls.
  *   status   int32  [1], nullable: a kernel sets bit 0 when an append would
- *            pass capacity (that append is then skipped for that sequence).
+ *            pass capacity (that append is then skipped for that sequence), and
+ *            bit 1 when a decode step's attention pass gave up waiting for its
+ *            own append (a bounded wait; that step's output is not to be trusted).
  *   window, k_window  the fp16 recent-key window (abstract: the AIME run is stated to be
  *            without an fp16 recent-key buffer, so the serving path has one as an option).
  *            Reading: the keys of the newest `window` tokens of a sequence, t in

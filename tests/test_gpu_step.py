@@ -1,12 +1,15 @@
 """bgtq_decode_step against the two calls it stands for (GPU).
 
 One decode step appends one key/value token to every sequence and attends with the query at
-that token's position.  The fused call runs the append beside the rotated-query computation
-and advances the lengths in its merge kernel; its results must equal, bit for bit,
+that token's position.  The fused call runs the append as one workgroup of the attention pass
+(the split that reads the new token's tile waits for it) and advances the lengths in its merge
+kernel; its results must equal, bit for bit,
 bgtq_quantize_append(n_new = 1) followed by bgtq_decode_attention(q_pos = None): outputs,
 logits, every cache array, lengths and status.  The append-then-decode path itself is checked
 against the oracle by test_gpu_parity.py.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -85,3 +88,36 @@ def test_decode_step_equals_append_then_decode(d, k_bits, v_bits, h_q, h_kv, pre
             assert torch.equal(getattr(a, name), getattr(b, name)), f"step {step}: {name}"
     if extra_cap == 0:
         assert int(b.status[0]) == 1 and b.lengths.tolist() == [cap]
+
+
+def test_step_wait_that_gives_up_is_reported():
+    """The attention pass waits for its own append with a bounded spin.  With the bound forced
+    to zero from the host (the spin is skipped), the pass reports bit 1 in the cache's status;
+    with the normal bound it does not.  No wait hangs either way."""
+    dev = _cuda()
+    d, h_q, h_kv, pre = 128, 16, 2, 130
+    _say("decode step: bounded wait report")
+    wl = synth.Workload("step_wait", 96, d=d, h_q=h_q, h_kv=h_kv, theta=1e6, layers=1, seq_lens=(pre + 2,),
+                        k_bits=3, v_bits=3, key_dtype="f32", profile="decay", outlier_blocks=2)
+    bank, rv = synth.rotation_bank(d, seed=5), synth.rotation_v(d, seed=5)
+    qz = bgtq.make_quantizer(_t(bank), _t(rv), d)
+    k = np.stack([synth.keys(wl, 0, 0, h, 0, pre + 2) for h in range(h_kv)])
+    v = np.stack([synth.values(wl, 0, 0, h, 0, pre + 2) for h in range(h_kv)])
+    cache = bgtq.PackedCache(1, h_kv, d, wl.budget, wl.v_bits, 256, device=dev)
+    pipeline.prefill(qz, cache, _t(k[:, :pre]), _t(v[:, :pre]), 0)
+    ws = torch.zeros(bgtq.decode_workspace_bytes(1, h_q, h_kv, d, 256), dtype=torch.uint8, device=dev)
+    q = torch.randn((1, h_q, d), generator=torch.Generator().manual_seed(3)).to(dev)
+    os.environ["BGTQ_STEP_SPIN_LIMIT"] = "0"
+    try:
+        bgtq.bgtq_decode_step(qz, cache, q, _t(k[:, pre:pre + 1])[None].contiguous(),
+                              _t(v[:, pre:pre + 1])[None].contiguous(), 1e6, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["BGTQ_STEP_SPIN_LIMIT"]
+    assert int(cache.status[0]) & 2, "a wait that gave up was not reported"
+    assert int(cache.lengths[0]) == pre + 1
+    cache.status.zero_()
+    bgtq.bgtq_decode_step(qz, cache, q, _t(k[:, pre + 1:pre + 2])[None].contiguous(),
+                          _t(v[:, pre + 1:pre + 2])[None].contiguous(), 1e6, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(cache.status[0]) == 0 and int(cache.lengths[0]) == pre + 2
