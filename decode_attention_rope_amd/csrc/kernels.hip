@@ -1380,6 +1380,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   extern __shared__ uint32_t smem[];
   const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  if (split == 0)       // the merge adds into this (sequence, KV head)'s output rows
+    for (int i = tid; i < a.group * D; i += blockDim.x) a.out[(int64_t(s) * a.n_q + hk * a.group) * D + i] = 0.0f;
   const int len = a.lengths[s];
   const int tiles = (len + kTile - 1) / kTile;
   const int per = (tiles + a.n_split - 1) / a.n_split;
@@ -1916,6 +1918,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int split = int(blockIdx.x) - (STEP ? 1 : 0), hk = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
+  if (split == 0)       // the merge adds into this (sequence, KV head)'s output rows
+    for (int i = tid; i < a.group * D; i += 256) a.out[(int64_t(s) * a.n_q + hk * a.group) * D + i] = 0.0f;
   // in a decode step the append role adds the new token beside this pass and the merge kernel
   // advances lengths[], so it still holds the old length here
   const int len0 = a.lengths[s];
@@ -2381,26 +2385,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // Merge the splits of one query head and undo the value rotation:
 // out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t], from the per-split
 // (m, l) pairs and accumulators; split i is weighted by exp2(m_i - max m).  Every split's
-// accumulator loads are issued before the maximum is known, so they overlap.
-template <int D>
+// accumulator loads are issued before the maximum is known, so they overlap.  With dense
+// rotations the head runs on H = 2 workgroups, each owning half of acc's coordinates (half of
+// the split results to read, which is what bounds the merge) and adding its part of R_v^T acc,
+// already scaled, into out, which the split pass zeroed: a sum of two terms, the same in
+// either order.
+template <int D, int H>
 __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
-  constexpr int NT = 1024, C4 = D / 4, NG = NT / C4, RS = NT / D, NB = 16;
+  constexpr int NT = 1024, DH = D / H, C4 = DH / 4, NG = NT / C4, RS = NT / D, NB = 16;
   __shared__ float red[2][NT / 64];
   __shared__ float4 part4[NT];
   __shared__ float accs[D];
   __shared__ float outp[NT];
-  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, s = blockIdx.y, hf = H > 1 ? int(blockIdx.z) : 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_split;
   const size_t base = (size_t(s) * a.n_q + h) * ns;
   const float2* ml = a.part_ml + base;
-  const float4* acc4 = reinterpret_cast<const float4*>(a.partial + base * D);
+  const float4* acc4 = reinterpret_cast<const float4*>(a.partial + base * D) + hf * C4;   // rows D/4 apart
   const int c4 = tid % C4, g = tid / C4;
   float4 x[NB];
   float2 mlv[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {            // first NB splits of this thread's class
     const int i = g + NG * b;
-    if (i < ns) { x[b] = acc4[size_t(i) * C4 + c4]; mlv[b] = ml[i]; }
+    if (i < ns) { x[b] = acc4[size_t(i) * (D / 4) + c4]; mlv[b] = ml[i]; }
   }
   float mloc = -INFINITY;
   for (int i = tid; i < ns; i += NT) mloc = fmaxf(mloc, ml[i].x);
@@ -2428,23 +2437,23 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
 #pragma unroll
   for (int b = 0; b < NB; ++b)
     if (g + NG * b < ns) add(x[b], mlv[b]);
-  for (int i = g + NG * NB; i < ns; i += NG) add(acc4[size_t(i) * C4 + c4], ml[i]);
+  for (int i = g + NG * NB; i < ns; i += NG) add(acc4[size_t(i) * (D / 4) + c4], ml[i]);
   part4[tid] = v;
   // dense value rotation: this thread's rows of R_v for the un-rotation below, requested now
   // so that their latency overlaps the reduction over groups
-  constexpr int RC = D / RS;
+  constexpr int RC = DH / RS;                        // rows of R_v per thread, within this half
   const int r_out = tid % D, q_out = tid / D;
   float rvr[RC];
   if (!a.givens) {
 #pragma unroll
-    for (int k = 0; k < RC; ++k) rvr[k] = a.rot_v[(q_out * RC + k) * D + r_out];
+    for (int k = 0; k < RC; ++k) rvr[k] = a.rot_v[(hf * DH + q_out * RC + k) * D + r_out];
   }
   // structured value rotation: this thread's pair slot records, requested before the
   // reduction below so that their latency overlaps it
   // (the transpose runs the layers backwards: the slot walks them from the last one)
   GivensSlot gs;
   gs.n = 0;
-  if (a.givens && tid < D / 2) {
+  if (H == 1 && a.givens && tid < D / 2) {
     const uint4 hv = a.givens[D / 2 - 1];
     gs.n = min(int(hv.y), kMaxGivensLayers);
     gs.rec = a.givens + hv.x + (gs.n - 1) * (D / 2) + tid;
@@ -2472,7 +2481,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     accs[4 * tid] = t.x; accs[4 * tid + 1] = t.y; accs[4 * tid + 2] = t.z; accs[4 * tid + 3] = t.w;
   }
   __syncthreads();
-  if (a.givens) {
+  if (H == 1 && a.givens) {
     // structured rotations: the transpose, layers in reverse order, each pair as
     // [[c, s], [-s, c]]; thread t < D/2 owns pair slot t (records fetched above)
     const int nl = givens_count(a.givens, D);
@@ -2507,12 +2516,13 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
 #pragma unroll
       for (int qq = 0; qq < RS; ++qq) o += outp[qq * D + tid];
       const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
-      a.out[(int64_t(s) * a.n_q + h) * D + tid] = o * inv;
+      if (H == 1) a.out[(int64_t(s) * a.n_q + h) * D + tid] = o * inv;
+      else atomicAdd(a.out + (int64_t(s) * a.n_q + h) * D + tid, o * inv);
     }
   }
-  if (a.step && a.step_flag && h % a.group == 0 && tid == 0)   // ready for the next step
+  if (hf == 0 && a.step && a.step_flag && h % a.group == 0 && tid == 0)   // ready for the next step
     a.step_flag[int64_t(s) * a.n_kv + h / a.group] = 0;
-  if (a.step && h == 0 && tid == 0) {     // the decode step's length advance, after every reader
+  if (hf == 0 && a.step && h == 0 && tid == 0) {     // the decode step's length advance, after every reader
     const int len0 = a.lengths[s];
     if (len0 + 1 <= a.capacity) a.lengths[s] = len0 + 1;
   }
@@ -2567,7 +2577,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st,
       default: hipLaunchKernelGGL((k_decode_split<D, 16>), grid, block, lds, st, a); break;
     }
   }
-  hipLaunchKernelGGL(k_decode_combine<D>, dim3(a.n_q, a.batch), dim3(1024), 0, st, a);
+  if (a.givens) hipLaunchKernelGGL((k_decode_combine<D, 1>), dim3(a.n_q, a.batch, 1), dim3(1024), 0, st, a);
+  else hipLaunchKernelGGL((k_decode_combine<D, 2>), dim3(a.n_q, a.batch, 2), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 

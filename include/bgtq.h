@@ -252,7 +252,8 @@ size_t bgtq_prefill_workspace_bytes(int n_kv_heads, int64_t n_tokens, int head_d
  *   q_pos       int64 [batch] (device) query positions, or NULL for
  *               lengths[s] - 1 (the newest cached token).
  *   rope_theta  RoPE base; <= 0 means q is already rotated.
- *   out         fp32 [batch][n_q_heads][head_dim].
+ *   out         fp32 [batch][n_q_heads][head_dim]; must not overlap q (the attention
+ *               pass clears it before the merge adds the heads' halves into it).
  *   logits_out  nullable fp32 [batch][n_q_heads][capacity]; slots >= lengths[s]
  *               are left untouched.
  *   workspace   >= bgtq_decode_workspace_bytes(...); must be zero-filled before
