@@ -2438,7 +2438,16 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
   for (int b = 0; b < NB; ++b)
     if (g + NG * b < ns) add(x[b], mlv[b]);
   for (int i = g + NG * NB; i < ns; i += NG) add(acc4[size_t(i) * (D / 4) + c4], ml[i]);
-  part4[tid] = v;
+  // the groups within a wave (lanes C4 apart share a coordinate), by a fixed xor butterfly
+  static_assert(64 % C4 == 0, "coordinate classes must tile a wave");
+#pragma unroll
+  for (int off = C4; off < 64; off <<= 1) {
+    v.x += __shfl_xor(v.x, off);
+    v.y += __shfl_xor(v.y, off);
+    v.z += __shfl_xor(v.z, off);
+    v.w += __shfl_xor(v.w, off);
+  }
+  if (lane < C4) part4[wave * C4 + c4] = v;
   // dense value rotation: this thread's rows of R_v for the un-rotation below, requested now
   // so that their latency overlaps the reduction over groups
   constexpr int RC = DH / RS;                        // rows of R_v per thread, within this half
@@ -2465,19 +2474,13 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
   float ltot = 0.0f;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) ltot += red[1][w];
-  // the NG groups' weighted sums, pairwise in a fixed tree
+  if (tid < C4) {                           // the waves' sums, in wave order
+    float4 t = part4[tid];
 #pragma unroll
-  for (int span = NG / 2; span >= 1; span >>= 1) {
-    if (g < span) {
-      const float4 y = part4[tid + span * C4];
-      float4 t = part4[tid];
+    for (int w = 1; w < NT / 64; ++w) {
+      const float4 y = part4[w * C4 + tid];
       t.x += y.x; t.y += y.y; t.z += y.z; t.w += y.w;
-      part4[tid] = t;
     }
-    __syncthreads();
-  }
-  if (tid < C4) {
-    const float4 t = part4[tid];
     accs[4 * tid] = t.x; accs[4 * tid + 1] = t.y; accs[4 * tid + 2] = t.z; accs[4 * tid + 3] = t.w;
   }
   __syncthreads();
