@@ -2411,6 +2411,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     const int i = g + NG * b;
     if (i < ns) { x[b] = acc4[size_t(i) * (D / 4) + c4]; mlv[b] = ml[i]; }
   }
+  constexpr bool DENSE = H > 1;                      // H = 2: dense rotations, H = 1: Givens layers
   float mloc = -INFINITY;
   for (int i = tid; i < ns; i += NT) mloc = fmaxf(mloc, ml[i].x);
   mloc = wave_max(mloc);
@@ -2449,11 +2450,12 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
   }
   if (lane < C4) part4[wave * C4 + c4] = v;
   // dense value rotation: this thread's rows of R_v for the un-rotation below, requested now
-  // so that their latency overlaps the reduction over groups
+  // so that their latency overlaps the reduction over waves (requested with the split loads
+  // instead, they made the merge slower)
   constexpr int RC = DH / RS;                        // rows of R_v per thread, within this half
   const int r_out = tid % D, q_out = tid / D;
-  float rvr[RC];
-  if (!a.givens) {
+  float rvr[DENSE ? RC : 1];
+  if constexpr (DENSE) {
 #pragma unroll
     for (int k = 0; k < RC; ++k) rvr[k] = a.rot_v[(hf * DH + q_out * RC + k) * D + r_out];
   }
@@ -2462,7 +2464,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
   // (the transpose runs the layers backwards: the slot walks them from the last one)
   GivensSlot gs;
   gs.n = 0;
-  if (H == 1 && a.givens && tid < D / 2) {
+  if (!DENSE && tid < D / 2) {
     const uint4 hv = a.givens[D / 2 - 1];
     gs.n = min(int(hv.y), kMaxGivensLayers);
     gs.rec = a.givens + hv.x + (gs.n - 1) * (D / 2) + tid;
@@ -2484,7 +2486,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     accs[4 * tid] = t.x; accs[4 * tid + 1] = t.y; accs[4 * tid + 2] = t.z; accs[4 * tid + 3] = t.w;
   }
   __syncthreads();
-  if (H == 1 && a.givens) {
+  if constexpr (!DENSE) {
     // structured rotations: the transpose, layers in reverse order, each pair as
     // [[c, s], [-s, c]]; thread t < D/2 owns pair slot t (records fetched above)
     const int nl = givens_count(a.givens, D);
@@ -2519,8 +2521,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
 #pragma unroll
       for (int qq = 0; qq < RS; ++qq) o += outp[qq * D + tid];
       const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
-      if (H == 1) a.out[(int64_t(s) * a.n_q + h) * D + tid] = o * inv;
-      else atomicAdd(a.out + (int64_t(s) * a.n_q + h) * D + tid, o * inv);
+      atomicAdd(a.out + (int64_t(s) * a.n_q + h) * D + tid, o * inv);
     }
   }
   if (hf == 0 && a.step && a.step_flag && h % a.group == 0 && tid == 0)   // ready for the next step
