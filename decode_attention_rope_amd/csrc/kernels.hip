@@ -2385,33 +2385,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // Merge the splits of one query head and undo the value rotation:
 // out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t], from the per-split
 // (m, l) pairs and accumulators; split i is weighted by exp2(m_i - max m).  Every split's
-// accumulator loads are issued before the maximum is known, so they overlap.  With dense
-// rotations the head runs on H = 2 workgroups, each owning half of acc's coordinates (half of
-// the split results to read, which is what bounds the merge) and adding its part of R_v^T acc,
-// already scaled, into out, which the split pass zeroed: a sum of two terms, the same in
-// either order.
-template <int D, int H>
+// accumulator loads are issued before the maximum is known, so they overlap.  Each head runs
+// on two workgroups, each reading half of the split results (what bounds the merge) and adding
+// its part of out, already scaled by the global maximum and sum of all splits, into out, which
+// the split pass zeroed: a sum of two terms, the same in either order.  With dense rotations
+// a workgroup owns half of acc's coordinates (R_v^T acc is a sum over them); with Givens
+// layers, which mix all coordinates, half of the splits (the un-rotation is linear in acc).
+template <int D, bool GIV>
 __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
-  constexpr int NT = 1024, DH = D / H, C4 = DH / 4, NG = NT / C4, RS = NT / D, NB = 16;
+  constexpr int NT = 1024, DH = GIV ? D : D / 2, C4 = DH / 4, NG = NT / C4, RS = NT / D, NB = 16;
   __shared__ float red[2][NT / 64];
   __shared__ float4 part4[NT];
   __shared__ float accs[D];
   __shared__ float outp[NT];
-  const int h = blockIdx.x, s = blockIdx.y, hf = H > 1 ? int(blockIdx.z) : 0;
+  const int h = blockIdx.x, s = blockIdx.y, hf = int(blockIdx.z);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_split;
   const size_t base = (size_t(s) * a.n_q + h) * ns;
   const float2* ml = a.part_ml + base;
-  const float4* acc4 = reinterpret_cast<const float4*>(a.partial + base * D) + hf * C4;   // rows D/4 apart
+  const float4* acc4 = reinterpret_cast<const float4*>(a.partial + base * D) + (GIV ? 0 : hf * C4);   // rows D/4 apart
   const int c4 = tid % C4, g = tid / C4;
+  const int lo = GIV && hf ? ns / 2 : 0, hi = GIV && !hf ? ns / 2 : ns;   // this workgroup's splits
   float4 x[NB];
   float2 mlv[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {            // first NB splits of this thread's class
-    const int i = g + NG * b;
-    if (i < ns) { x[b] = acc4[size_t(i) * (D / 4) + c4]; mlv[b] = ml[i]; }
+    const int i = lo + g + NG * b;
+    if (i < hi) { x[b] = acc4[size_t(i) * (D / 4) + c4]; mlv[b] = ml[i]; }
   }
-  constexpr bool DENSE = H > 1;                      // H = 2: dense rotations, H = 1: Givens layers
+  constexpr bool DENSE = !GIV;
   float mloc = -INFINITY;
   for (int i = tid; i < ns; i += NT) mloc = fmaxf(mloc, ml[i].x);
   mloc = wave_max(mloc);
@@ -2437,8 +2439,8 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
   };
 #pragma unroll
   for (int b = 0; b < NB; ++b)
-    if (g + NG * b < ns) add(x[b], mlv[b]);
-  for (int i = g + NG * NB; i < ns; i += NG) add(acc4[size_t(i) * (D / 4) + c4], ml[i]);
+    if (lo + g + NG * b < hi) add(x[b], mlv[b]);
+  for (int i = lo + g + NG * NB; i < hi; i += NG) add(acc4[size_t(i) * (D / 4) + c4], ml[i]);
   // the groups within a wave (lanes C4 apart share a coordinate), by a fixed xor butterfly
   static_assert(64 % C4 == 0, "coordinate classes must tile a wave");
 #pragma unroll
@@ -2506,7 +2508,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
     }
     if (tid < D) {
       const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
-      a.out[(int64_t(s) * a.n_q + h) * D + tid] = accs[tid] * inv;
+      atomicAdd(a.out + (int64_t(s) * a.n_q + h) * D + tid, accs[tid] * inv);
     }
   } else {
     {
@@ -2581,8 +2583,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st,
       default: hipLaunchKernelGGL((k_decode_split<D, 16>), grid, block, lds, st, a); break;
     }
   }
-  if (a.givens) hipLaunchKernelGGL((k_decode_combine<D, 1>), dim3(a.n_q, a.batch, 1), dim3(1024), 0, st, a);
-  else hipLaunchKernelGGL((k_decode_combine<D, 2>), dim3(a.n_q, a.batch, 2), dim3(1024), 0, st, a);
+  if (a.givens) hipLaunchKernelGGL((k_decode_combine<D, true>), dim3(a.n_q, a.batch, 2), dim3(1024), 0, st, a);
+  else hipLaunchKernelGGL((k_decode_combine<D, false>), dim3(a.n_q, a.batch, 2), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
