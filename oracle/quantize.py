@@ -168,21 +168,31 @@ def quantize_values(v, rot_v, bits: int):
     return tq_mse(v, value_rotation(rot_v, np.asarray(v).shape[-1]), bits)
 
 
-def dequantize_keys(codes, norms, lay: Layout, bank) -> np.ndarray:
+def _levels(bits: int, levels: str) -> np.ndarray:
+    """Reconstruction levels as fp64 values: "fp16" = the fp32 centroids rounded to fp16 (the
+    reading the packed cache is decoded with), "fp32" = the fp32 centroids themselves."""
+    if levels == "fp16":
+        return codebook.levels16(bits)
+    if levels == "fp32":
+        return codebook.centroids32(bits).astype(np.float64)
+    raise ValueError(f"levels must be 'fp16' or 'fp32', not {levels!r}")
+
+
+def dequantize_keys(codes, norms, lay: Layout, bank, levels: str = "fp16") -> np.ndarray:
     """fp64 reconstruction [T, d] in original coordinate order; width-0 blocks are 0."""
     codes = np.asarray(codes)
     t_len = codes.shape[0]
     out = np.zeros((t_len, lay.d), dtype=np.float64)
     for g, grp in enumerate(lay.groups):
-        cen = codebook.levels16(grp.width)
+        cen = _levels(grp.width, levels)
         yhat = cen[codes[:, grp.first:grp.first + grp.m]] / np.sqrt(grp.m)
         xg = _unrotate(yhat, bank_matrix(bank, grp.m)) * norms[:, g].astype(np.float64)[:, None]
         out[:, lay.perm[grp.first:grp.first + grp.m]] = xg
     return out
 
 
-def dequantize_values(codes, norms, rot_v, bits: int) -> np.ndarray:
+def dequantize_values(codes, norms, rot_v, bits: int, levels: str = "fp16") -> np.ndarray:
     d = np.asarray(codes).shape[-1]
-    cen = codebook.levels16(bits)
+    cen = _levels(bits, levels)
     yhat = cen[np.asarray(codes)] / np.sqrt(d)
     return _unrotate(yhat, value_rotation(rot_v, d)) * np.asarray(norms, dtype=np.float64)[:, None]

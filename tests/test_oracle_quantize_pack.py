@@ -150,3 +150,30 @@ def test_tiny_workload_end_to_end_quantize():
     cu, nu = quantize.quantize_keys(k, lay_u, synth.rotation_bank(64))
     ku = quantize.dequantize_keys(cu, nu, lay_u, synth.rotation_bank(64))
     assert np.sum((kh - k) ** 2) < np.sum((ku - k) ** 2)
+
+
+@pytest.mark.parametrize("levels", ["fp16", "fp32"])
+def test_one_bit_reconstruction_closed_form(levels):
+    """One-bit groups with identity rotations and unit norms reconstruct every coordinate as
+    +-sqrt(2/pi)/sqrt(m): the 1-bit Lloyd-Max level of N(0, 1) in closed form, rounded to fp32
+    ("fp32" levels) or further to fp16 ("fp16", the levels the packed cache is decoded with)."""
+    d = 16
+    lay = layout.build(np.array([1, 1, 1, 1, 0, 0, 1, 1]))         # one group of six blocks, m = 12
+    bank = np.zeros(sum(m * m for m in range(2, d + 1, 2)), dtype=np.float32)
+    for m in range(2, d + 1, 2):
+        o = quantize.bank_offset(m)
+        bank[o:o + m * m] = np.eye(m, dtype=np.float32).ravel()
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 2, size=(5, lay.d_eff))
+    norms = np.ones((5, 1), dtype=np.float16)
+    x = quantize.dequantize_keys(codes, norms, lay, bank, levels=levels)
+    c = np.float32(math.sqrt(2.0 / math.pi))
+    if levels == "fp16":
+        c = np.float16(c)
+    want = np.zeros((5, d))
+    want[:, lay.perm] = np.where(codes == 1, 1.0, -1.0) * float(c) / math.sqrt(12)
+    np.testing.assert_array_equal(x, want)
+    v = quantize.dequantize_values(codes[:, :12], np.ones(5, dtype=np.float16), np.eye(12), 1, levels=levels)
+    np.testing.assert_array_equal(v, np.where(codes[:, :12] == 1, 1.0, -1.0) * float(c) / math.sqrt(12))
+    with pytest.raises(ValueError):
+        quantize.dequantize_values(codes[:, :12], np.ones(5, dtype=np.float16), np.eye(12), 1, levels="bf16")
