@@ -123,7 +123,7 @@ def main():
     import numpy as np
     import torch
 
-    from decode_attention_rope_amd import bgtq, pipeline, synth
+    from decode_attention_rope_amd import bgtq, synth
 
     wl = synth.WORKLOADS[args.workload]
     assert len(wl.seq_lens) == 1, "bench times a batch-1 workload"
@@ -153,7 +153,7 @@ def main():
         v = torch.stack([x[1] for x in kv]).contiguous()
         del kv
         pre_ev[0].record()
-        pipeline.prefill(qz, cache, k, v, 0)
+        bgtq.bgtq_prefill(qz, cache, k, v, 0)
         pre_ev[1].record()
         torch.cuda.synchronize()
         pre_ms += pre_ev[0].elapsed_time(pre_ev[1])
@@ -176,8 +176,8 @@ def main():
 
     def step():
         for layer in range(wl.layers):
-            pipeline.decode_step(qz, caches[layer], k_new[layer], v_new[layer], qs[layer], wl.theta,
-                                 out=outs[layer], workspace=wss[layer])
+            bgtq.bgtq_decode_step(qz, caches[layer], qs[layer], k_new[layer], v_new[layer], wl.theta,
+                                  out=outs[layer], workspace=wss[layer])
 
     def decode_only():
         for layer in range(wl.layers):

@@ -25,6 +25,7 @@ OK, ERR_INVALID_ARG, ERR_BUDGET, ERR_CAPACITY, ERR_WORKSPACE, ERR_UNSUPPORTED, E
 F32, BF16 = 0, 1
 PAIR_HALF, PAIR_INTERLEAVED = 0, 1
 ROT_DENSE, ROT_GIVENS = 0, 1
+OPT_DECODE_KERNEL, OPT_STEP_WAIT_LIMIT = 0, 1
 TILE = 64
 MAX_GROUPS = 8
 LAYOUT_BYTES = 4096
@@ -72,6 +73,8 @@ _SIGNATURES = {
     "bgtq_cache_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _vp]),
     "bgtq_codebook": (_i32, [_i32, _vp, _vp, _vp]),
     "bgtq_init": (_i32, []),
+    "bgtq_set_option": (_i32, [_i32, _i64]),
+    "bgtq_get_option": (_i64, [_i32]),
     "bgtq_status_string": (_c.c_char_p, [_i32]),
     "bgtq_last_error": (_c.c_char_p, []),
 }
@@ -147,6 +150,16 @@ def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, capacity) -> 
 
 def init() -> None:
     _check(lib().bgtq_init())
+
+
+def set_option(option: int, value: int) -> None:
+    """Process-wide test/diagnosis option (OPT_DECODE_KERNEL: 1 forces the vector-ALU decode;
+    OPT_STEP_WAIT_LIMIT: bound of a decode step's wait for its append)."""
+    _check(lib().bgtq_set_option(option, value))
+
+
+def get_option(option: int) -> int:
+    return int(lib().bgtq_get_option(option))
 
 
 # ------------------------------------------------------------------ device objects

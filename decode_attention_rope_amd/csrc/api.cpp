@@ -1,6 +1,7 @@
 // C ABI of the Block-GTQ packed-cache decode path: argument checks, sizes, launches.
 // Declared and documented in include/bgtq.h.
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -19,6 +20,11 @@ thread_local std::string g_last_error;
 std::mutex g_init_mutex;
 bool g_device_ready[64] = {};
 
+// process-wide options (bgtq_set_option); defaults from the environment, read once
+std::atomic<int> g_force_valu{0};
+std::atomic<int> g_step_spin{1 << 22};
+std::once_flag g_env_once;
+
 bgtq_status fail(bgtq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 bgtq_status fail(bgtq_status s, const char* fmt, ...) {
   char buf[512];
@@ -35,7 +41,14 @@ bgtq_status hip_status(hipError_t e, const char* what) {
   return fail(BGTQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The library's initialisation, once per device (the current one): the codebook tables go to
+// constant memory.  The first initialisation in the process also takes the options' defaults from the environment;
+// no other place reads it.
 bgtq_status ensure_init() {
+  std::call_once(g_env_once, [] {
+    if (const char* k = std::getenv("BGTQ_DECODE_KERNEL")) g_force_valu = std::strcmp(k, "valu") == 0 ? 1 : 0;
+    if (const char* sl = std::getenv("BGTQ_STEP_SPIN_LIMIT")) g_step_spin = std::atoi(sl) > 0 ? std::atoi(sl) : 0;
+  });
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e, "hipGetDevice");
@@ -107,6 +120,28 @@ const char* bgtq_status_string(bgtq_status s) {
 const char* bgtq_last_error(void) { return g_last_error.c_str(); }
 
 bgtq_status bgtq_init(void) { return ensure_init(); }
+
+bgtq_status bgtq_set_option(bgtq_option option, int64_t value) {
+  switch (option) {
+    case BGTQ_OPT_DECODE_KERNEL:
+      if (value != 0 && value != 1) return fail(BGTQ_ERR_INVALID_ARG, "decode kernel option must be 0 or 1");
+      g_force_valu = int(value);
+      return BGTQ_OK;
+    case BGTQ_OPT_STEP_WAIT_LIMIT:
+      if (value < 0 || value > (int64_t(1) << 30)) return fail(BGTQ_ERR_INVALID_ARG, "wait limit must be 0..2^30");
+      g_step_spin = int(value);
+      return BGTQ_OK;
+  }
+  return fail(BGTQ_ERR_INVALID_ARG, "unknown option %d", int(option));
+}
+
+int64_t bgtq_get_option(bgtq_option option) {
+  switch (option) {
+    case BGTQ_OPT_DECODE_KERNEL: return g_force_valu;
+    case BGTQ_OPT_STEP_WAIT_LIMIT: return g_step_spin;
+  }
+  return -1;
+}
 
 bgtq_status bgtq_codebook(int bits, float* thresholds, float* centroids, double* distortion) {
   if (bits < 0 || bits > BGTQ_MAX_BITS) return fail(BGTQ_ERR_INVALID_ARG, "bits must be 0..8");
@@ -330,8 +365,7 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.layouts = static_cast<const HeadLayout*>(cache->layouts);
   a.out = out;
   a.logits = logits_out;
-  const char* which = std::getenv("BGTQ_DECODE_KERNEL");
-  a.use_mfma = group <= 8 && !(which && std::strcmp(which, "valu") == 0);
+  a.use_mfma = group <= 8 && !g_force_valu;
   if (cache->window > 0 && !a.use_mfma)
     return fail(BGTQ_ERR_UNSUPPORTED, "the recent-key window is built on the matrix-core decode (group size <= 8)");
   a.window = cache->window;
@@ -406,11 +440,10 @@ bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, 
                                                   cache->capacity);
   aa.advance = 0;
   da.step = 1;
-  // the wait of the split that reads the new token's tile is bounded (about 0.2 s at most);
-  // BGTQ_STEP_SPIN_LIMIT overrides the bound (0: no wait), to exercise the report of a wait
-  // that gave up
-  da.step_spin = 1 << 22;
-  if (const char* sl = std::getenv("BGTQ_STEP_SPIN_LIMIT")) da.step_spin = std::atoi(sl) > 0 ? std::atoi(sl) : 0;
+  // the wait of the split that reads the new token's tile is bounded (about 0.2 s at most by
+  // default); the option BGTQ_OPT_STEP_WAIT_LIMIT sets the bound (0: no wait), so that the
+  // report of a wait that gave up can be exercised
+  da.step_spin = g_step_spin;
   da.step_flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need -
                                             align256(decode_step_bytes(cache->batch, cache->n_kv_heads)));
   return hip_status(launch_decode_step(aa, da, kv_dtype, q_dtype, s), "decode-step launch");

@@ -22,7 +22,7 @@ import json
 import numpy as np
 import torch
 
-from . import bgtq, pipeline, synth
+from . import bgtq, synth
 
 METHODS = ("uniform", "block_gtq")
 
@@ -54,7 +54,7 @@ def layer_mae(quantizer, wl: synth.Workload, layer: int, bits: int, method: str,
     b_min, b_max = (bits, bits) if method == "uniform" else (0, 8)
     for s, t_len in enumerate(wl.seq_lens):
         if t_len:
-            pipeline.prefill(quantizer, cache, keys[s, :, :t_len], vals[s, :, :t_len], s, b_min, b_max)
+            bgtq.bgtq_prefill(quantizer, cache, keys[s, :, :t_len], vals[s, :, :t_len], s, b_min, b_max)
     _, logits = bgtq.bgtq_decode_attention(quantizer, cache, q, wl.theta, softmax_scale=softmax_scale, logits=True)
     mae = bgtq.bgtq_logit_error(q, keys, cache.lengths, logits, wl.theta, softmax_scale=softmax_scale)
     return mae.cpu().numpy()
@@ -86,7 +86,7 @@ def time_logit_error(quantizer, device, steps: int = 20) -> dict:
     wl = synth.QWEN3B_128K
     keys, vals, q, cap = layer_inputs(wl, 0, device)
     cache = bgtq.PackedCache(1, wl.h_kv, wl.d, wl.budget, wl.v_bits, cap, device=device)
-    pipeline.prefill(quantizer, cache, keys[0], vals[0], 0)
+    bgtq.bgtq_prefill(quantizer, cache, keys[0], vals[0], 0)
     _, logits = bgtq.bgtq_decode_attention(quantizer, cache, q, wl.theta, logits=True)
     ws = torch.empty(bgtq.logit_error_workspace_bytes(1, wl.h_q, cap), dtype=torch.uint8, device=device)
     out = torch.empty((1, wl.h_q), dtype=torch.float64, device=device)

@@ -23,6 +23,8 @@
  *   - Call bgtq_init() once per device before capturing calls in a HIP graph;
  *     otherwise the first call on a device initialises it (a synchronous copy
  *     of the codebook tables to device constant memory).
+ *   - Two process-wide options exist for tests and diagnosis (bgtq_set_option);
+ *     the first initialisation reads their defaults from the environment once.
  */
 #ifndef BGTQ_H
 #define BGTQ_H
@@ -332,8 +334,26 @@ size_t bgtq_cache_bytes(int batch, int n_kv_heads, int head_dim, int k_width_sum
  * bits 0 has no tables).  Host-only, enqueues nothing. */
 bgtq_status bgtq_codebook(int bits, float* thresholds, float* centroids, double* distortion);
 
-/* Copy the frozen tables to the current device's constant memory (synchronous). */
+/* Copy the frozen tables to the current device's constant memory (synchronous).  The
+ * first call in the process also reads the options' defaults from the environment:
+ * BGTQ_DECODE_KERNEL=valu sets BGTQ_OPT_DECODE_KERNEL to 1, BGTQ_STEP_SPIN_LIMIT=n sets
+ * BGTQ_OPT_STEP_WAIT_LIMIT to n.  Nothing reads the environment afterwards. */
 bgtq_status bgtq_init(void);
+
+/* Process-wide options, for tests and diagnosis; every later call reads the value set
+ * last.  Not meant to change while calls are in flight on other threads.
+ *   BGTQ_OPT_DECODE_KERNEL    0 (default): the decode runs on the matrix cores when the
+ *                             group size is <= 8, on the vector ALU otherwise; 1: always
+ *                             on the vector ALU (then a cache with a window is refused:
+ *                             UNSUPPORTED).
+ *   BGTQ_OPT_STEP_WAIT_LIMIT  bound of a decode step's wait for its own append, in polls
+ *                             of a few hundred cycles (default 1 << 22, about 0.2 s;
+ *                             0: no wait, so the step reports through cache->status that
+ *                             it gave up, which is how that report is tested).
+ * Errors: INVALID_ARG (unknown option or value out of range). */
+typedef enum { BGTQ_OPT_DECODE_KERNEL = 0, BGTQ_OPT_STEP_WAIT_LIMIT = 1 } bgtq_option;
+bgtq_status bgtq_set_option(bgtq_option option, int64_t value);
+int64_t bgtq_get_option(bgtq_option option);
 
 const char* bgtq_status_string(bgtq_status s);
 const char* bgtq_last_error(void);

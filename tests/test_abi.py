@@ -250,3 +250,21 @@ def test_status_strings():
     for s in range(7):
         assert lib.bgtq_status_string(s)
     assert lib.bgtq_status_string(99) == b"unknown status"
+
+
+def test_options_round_trip():
+    lib = bgtq.lib()
+    old_k, old_w = bgtq.get_option(bgtq.OPT_DECODE_KERNEL), bgtq.get_option(bgtq.OPT_STEP_WAIT_LIMIT)
+    try:
+        bgtq.set_option(bgtq.OPT_DECODE_KERNEL, 1)
+        assert bgtq.get_option(bgtq.OPT_DECODE_KERNEL) == 1
+        bgtq.set_option(bgtq.OPT_STEP_WAIT_LIMIT, 0)
+        assert bgtq.get_option(bgtq.OPT_STEP_WAIT_LIMIT) == 0
+        assert lib.bgtq_set_option(bgtq.OPT_DECODE_KERNEL, 2) == bgtq.ERR_INVALID_ARG
+        assert lib.bgtq_set_option(bgtq.OPT_STEP_WAIT_LIMIT, -1) == bgtq.ERR_INVALID_ARG
+        assert lib.bgtq_set_option(7, 0) == bgtq.ERR_INVALID_ARG
+        assert lib.bgtq_get_option(7) == -1
+    finally:
+        bgtq.set_option(bgtq.OPT_DECODE_KERNEL, old_k)
+        bgtq.set_option(bgtq.OPT_STEP_WAIT_LIMIT, old_w)
+

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from decode_attention_rope_amd import bgtq, pipeline, synth
+from decode_attention_rope_amd import bgtq, synth
 from oracle import quantize
 from oracle import window as owin
 from _ref import TOL, assert_region_equal, decode_reference, head_reference, rel_err
@@ -88,7 +88,7 @@ def _decode_case(wl, t_lens, kdt=torch.float32, window=0, valu=False):
         k = np.stack([synth.keys(wl, s, 0, h, 0, t_len) for h in range(h_kv)])
         v = np.stack([synth.values(wl, s, 0, h, 0, t_len) for h in range(h_kv)])
         kv.append((torch.from_numpy(k).to(kdt).float().numpy(), torch.from_numpy(v).to(kdt).float().numpy()))
-        pipeline.prefill(qz, cache, _t(k, kdt), _t(v, kdt), s)
+        bgtq.bgtq_prefill(qz, cache, _t(k, kdt), _t(v, kdt), s)
     q = np.stack([synth.queries(wl, s, 0) for s in range(len(t_lens))])
     out, logits = bgtq.bgtq_decode_attention(qz, cache, _t(q), wl.theta, logits=True)
     torch.cuda.synchronize()
@@ -126,7 +126,8 @@ def test_decode_parity(d, h_q, h_kv, t_lens, kdt, window):
     _decode_case(wl, t_lens, kdt, window)
 
 
-@pytest.mark.parametrize("d,h_q,pre", [(128, 16, [200, 63]), (256, 4, [70])])
+@pytest.mark.parametrize("d,h_q,pre", [(128, 16, [200, 63]), (256, 4, [70]),
+                                       (128, 16, [131072])])   # full size: 511 splits per KV head
 def test_decode_step_equals_append_then_decode(d, h_q, pre):
     dev = _cuda()
     _say(f"givens step d={d} h_q={h_q} pre={pre}")
@@ -142,7 +143,7 @@ def test_decode_step_equals_append_then_decode(d, h_q, pre):
     for _ in range(2):
         c = bgtq.PackedCache(len(pre), h_kv, d, wl.budget, wl.v_bits, cap, device=dev)
         for s, p in enumerate(pre):
-            pipeline.prefill(qz, c, _t(kv[s][0][:, :p]), _t(kv[s][1][:, :p]), s)
+            bgtq.bgtq_prefill(qz, c, _t(kv[s][0][:, :p]), _t(kv[s][1][:, :p]), s)
         caches.append(c)
     a, b = caches
     ws = [torch.zeros(bgtq.decode_workspace_bytes(len(pre), h_q, h_kv, d, cap), dtype=torch.uint8, device=dev)

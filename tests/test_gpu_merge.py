@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from decode_attention_rope_amd import bgtq, pipeline, synth
+from decode_attention_rope_amd import bgtq, synth
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def test_merge_output_ignores_prior_contents_and_repeats(rotation, d, h_q, h_kv,
     for s, n in enumerate(t_lens):
         k = np.stack([synth.keys(wl, s, 0, h, 0, n) for h in range(h_kv)])
         v = np.stack([synth.values(wl, s, 0, h, 0, n) for h in range(h_kv)])
-        pipeline.prefill(qz, cache, _t(k), _t(v), s)
+        bgtq.bgtq_prefill(qz, cache, _t(k), _t(v), s)
     q = torch.randn((len(t_lens), h_q, d), generator=torch.Generator().manual_seed(5)).to(dev)
     ws = torch.zeros(bgtq.decode_workspace_bytes(len(t_lens), h_q, h_kv, d, cap), dtype=torch.uint8, device=dev)
 

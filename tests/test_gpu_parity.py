@@ -8,9 +8,9 @@ import numpy as np
 import pytest
 import torch
 
-from decode_attention_rope_amd import bgtq, pipeline, synth
+from decode_attention_rope_amd import bgtq, synth
 from oracle import allocate, codebook, energy, layout, rope
-from _ref import TOL, assert_region_equal, decode_reference, head_reference, rel_err
+from _ref import TOL, assert_region_equal, decode_reference, head_reference, oracle_heads, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -204,63 +204,99 @@ def test_append_one_token_per_step_bit_exact(d, k_bits, v_bits, h_kv, prefill, s
 # ---------------------------------------------------------------- decode
 
 def _decode_vs_oracle(wl, t_lens, qz, bank, rv, dtype=torch.float32, append_then_attend=False, pairing=0,
-                      theta=None, check_logits=True, check_seqs=None):
+                      theta=None, check_logits=True, check_seqs=None, step_twin=False, levels="fp16",
+                      bank_seed=0):
+    """Decode over a cache prefilled with the workload's keys and values, against the oracle.
+    With append_then_attend the last token of every sequence is appended (bgtq_quantize_append)
+    and the query sits at its position.  With step_twin a second cache gets the same prefill and
+    the last token through bgtq_decode_step instead; its outputs, logits, cache arrays, lengths
+    and status must equal the first cache's bit for bit.  `levels` picks the oracle's
+    reconstruction levels ("fp16": the reading the cache is decoded with; "fp32": the fp32
+    centroids).  Returns the cache and the worst relative error seen."""
     dev = _cuda()
     d, h_kv, g = wl.d, wl.h_kv, wl.group
+    assert np.array_equal(bank, synth.rotation_bank(d, seed=bank_seed)), "the oracle regenerates the rotations"
     theta = wl.theta if theta is None else theta
     batch = len(t_lens)
     cap = -(-(max(t_lens) + 1) // 64) * 64
-    cache = bgtq.PackedCache(batch, h_kv, d, wl.budget, wl.v_bits, cap, pairing=pairing, device=dev)
-    refs, kv = [], []
+    caches = [bgtq.PackedCache(batch, h_kv, d, wl.budget, wl.v_bits, cap, pairing=pairing, device=dev)
+              for _ in range(2 if step_twin else 1)]
+    tails = []
     for s, t_len in enumerate(t_lens):
         n_pre = t_len - 1 if append_then_attend else t_len
         k = np.stack([synth.keys(wl, s, 0, h, 0, t_len) for h in range(h_kv)])
         v = np.stack([synth.values(wl, s, 0, h, 0, t_len) for h in range(h_kv)])
-        kv.append((k, v))
         if n_pre > 0:
-            pipeline.prefill(qz, cache, _t(k[:, :n_pre], dtype), _t(v[:, :n_pre], dtype), s)
+            kt, vt = _t(k[:, :n_pre], dtype), _t(v[:, :n_pre], dtype)
+            for c in caches:
+                bgtq.bgtq_prefill(qz, c, kt, vt, s)
+            del kt, vt
+        tails.append((_t(k[:, -1:], dtype), _t(v[:, -1:], dtype)))
+        del k, v
+    q = _t(np.stack([synth.queries(wl, s, 0) for s in range(batch)]))
     if append_then_attend:
-        for s, (k, v) in enumerate(kv):
-            bgtq.bgtq_quantize_append(qz, cache, _t(k[:, -1:], dtype)[None], _t(v[:, -1:], dtype)[None], seq_begin=s)
-    q = np.stack([synth.queries(wl, s, 0) for s in range(batch)])
+        for s, (kn, vn) in enumerate(tails):
+            bgtq.bgtq_quantize_append(qz, caches[0], kn[None], vn[None], seq_begin=s)
     pos = None if append_then_attend else torch.tensor(t_lens, dtype=torch.int64, device=dev)
-    out, logits = bgtq.bgtq_decode_attention(qz, cache, _t(q), theta, q_pos=pos, logits=True)
+    out, logits = bgtq.bgtq_decode_attention(qz, caches[0], q, theta, q_pos=pos, logits=True)
+    if step_twin:
+        assert append_then_attend
+        kn = torch.stack([t[0] for t in tails]).contiguous()
+        vn = torch.stack([t[1] for t in tails]).contiguous()
+        out_b, lg_b = bgtq.bgtq_decode_step(qz, caches[1], q, kn, vn, theta, logits=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_b), "decode step output differs from append + decode"
+        for s, t_len in enumerate(t_lens):
+            assert torch.equal(logits[s, :, :t_len], lg_b[s, :, :t_len]), f"decode step logits differ (seq {s})"
+        a, b = caches
+        assert torch.equal(a.lengths, b.lengths) and torch.equal(a.status, b.status)
+        for name in ("k_codes", "k_norms", "v_codes", "v_norms", "widths", "layouts"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), f"decode step cache {name} differs"
+        _say(f"  decode step == append + decode, bit for bit ({batch} seqs)")
+        del out_b, lg_b
     torch.cuda.synchronize()
     out, logits = out.cpu().numpy(), logits.cpu().numpy()
-    worst = 0.0
+    cache = caches[0]
+    del caches
+    qn = q.cpu().numpy()
+    jobs, keys = [], []
     for s, t_len in enumerate(t_lens):
         if check_seqs is not None and s not in check_seqs:
             continue
-        k, v = kv[s]
-        kx = torch.from_numpy(k).to(dtype).float().numpy()
-        vx = torch.from_numpy(v).to(dtype).float().numpy()
-        n_pre = t_len - 1 if append_then_attend else t_len
-        qpos = t_len - 1 if append_then_attend else t_len
         for h in range(h_kv):
-            ref = head_reference(kx[h, :n_pre], vx[h, :n_pre], wl.budget, wl.v_bits, bank, rv, cap, pairing)
-            if append_then_attend:
-                # the appended token is quantized with the prefill allocation
-                from oracle import quantize as oq
-                kc, kn = oq.quantize_keys(kx[h, n_pre:], ref["layout"], bank)
-                vc, vn = oq.quantize_values(vx[h, n_pre:], rv, wl.v_bits)
-                ref["k_hat"] = np.concatenate([ref["k_hat"], oq.dequantize_keys(kc, kn, ref["layout"], bank)])
-                ref["v_hat"] = np.concatenate([ref["v_hat"], oq.dequantize_values(vc, vn, rv, wl.v_bits)])
-            o_ref, l_ref = decode_reference(q[s, h * g:(h + 1) * g], qpos, theta, ref, pairing=pairing)
+            jobs.append(dict(wl=wl, s=s, h=h, t_len=t_len, n_pre=t_len - 1 if append_then_attend else t_len,
+                             dtype="bf16" if dtype == torch.bfloat16 else "f32", bank_seed=bank_seed,
+                             qpos=t_len - 1 if append_then_attend else t_len, theta=theta, pairing=pairing,
+                             levels=levels, cap=cap))
+            keys.append((s, h))
+    assert np.array_equal(qn, np.stack([synth.queries(wl, s, 0) for s in range(batch)]))
+    lvls = (levels,) if isinstance(levels, str) else tuple(levels)
+    for j in jobs:
+        j["levels"] = lvls
+    worst = {lv: [0.0, 0.0] for lv in lvls}          # output, logit
+    for (s, h), res in zip(keys, oracle_heads(jobs)):
+        t_len = t_lens[s]
+        for lv in lvls:
+            o_ref, l_ref = res[lv]
             e_out = rel_err(out[s, h * g:(h + 1) * g], o_ref)
             if check_logits:
                 e_log = rel_err(logits[s, h * g:(h + 1) * g, :t_len], l_ref)
-                assert np.all(e_log <= TOL), f"seq {s} head {h}: logit error {e_log} (output error {e_out})"
-                worst = max(worst, float(e_log.max()))
-            assert np.all(e_out <= TOL), f"seq {s} head {h}: output error {e_out}"
-            worst = max(worst, float(e_out.max()))
-    _say(f"  worst rel err {worst:.2e}")
-    return cache
+                assert np.all(e_log <= TOL), f"{lv} levels, seq {s} head {h}: logit error {e_log} (output {e_out})"
+                worst[lv][1] = max(worst[lv][1], float(e_log.max()))
+            assert np.all(e_out <= TOL), f"{lv} levels, seq {s} head {h}: output error {e_out}"
+            worst[lv][0] = max(worst[lv][0], float(e_out.max()))
+    for lv in lvls:
+        _say(f"  worst rel err vs the {lv}-level oracle: output {worst[lv][0]:.2e}, logits "
+             f"{worst[lv][1]:.2e} ({len(jobs)} heads)")
+    return cache, max(max(w) for w in worst.values())
 
 
 def test_decode_tiny(rot64):
+    """Also against the oracle with fp32 reconstruction levels (the cache is decoded with the fp32
+    centroids rounded to fp16): the same 2e-3 bar holds."""
     _say("decode tiny")
     bank, rv, qz = rot64
-    _decode_vs_oracle(synth.TINY, [256], qz, bank, rv)
+    _decode_vs_oracle(synth.TINY, [256], qz, bank, rv, levels=("fp16", "fp32"))
 
 
 @pytest.mark.parametrize("t_lens", [[1], [63], [64], [65], [1000, 3, 129, 4096]])
@@ -294,7 +330,7 @@ def test_decode_llama8b_layer_32k_bf16(rot128):
     _say("decode llama8b 32K bf16")
     bank, rv, qz = rot128
     wl = synth.LLAMA8B_LAYER
-    _decode_vs_oracle(wl, list(wl.seq_lens), qz, bank, rv, dtype=torch.bfloat16)
+    _decode_vs_oracle(wl, list(wl.seq_lens), qz, bank, rv, dtype=torch.bfloat16, levels=("fp16", "fp32"))
 
 
 def test_decode_empty_sequence_and_zero_budget(rot64):
@@ -305,7 +341,7 @@ def test_decode_empty_sequence_and_zero_budget(rot64):
     rng = np.random.default_rng(0)
     k = rng.standard_normal((1, 50, 64)).astype(np.float32)
     v = rng.standard_normal((1, 50, 64)).astype(np.float32)
-    pipeline.prefill(qz, cache, _t(k), _t(v), 0)        # sequence 1 stays empty
+    bgtq.bgtq_prefill(qz, cache, _t(k), _t(v), 0)        # sequence 1 stays empty
     q = _t(rng.standard_normal((2, 1, 64)))
     out = bgtq.bgtq_decode_attention(qz, cache, q, 1e4, q_pos=torch.tensor([50, 0], device=dev))
     torch.cuda.synchronize()
@@ -321,7 +357,7 @@ def test_decode_is_deterministic(rot128):
     bank, rv, qz = rot128
     wl = synth.Workload("det", 94, d=128, h_q=8, h_kv=1, theta=1e6, layers=1, seq_lens=(5000,),
                         k_bits=3, v_bits=3, key_dtype="f32", profile="decay", outlier_blocks=2)
-    cache = _decode_vs_oracle(wl, [5000], qz, bank, rv, check_logits=False)
+    cache, _ = _decode_vs_oracle(wl, [5000], qz, bank, rv, check_logits=False)
     q = _t(synth.queries(wl, 0, 0)[None])
     a = bgtq.bgtq_decode_attention(qz, cache, q, wl.theta)
     b = bgtq.bgtq_decode_attention(qz, cache, q, wl.theta)
@@ -331,30 +367,62 @@ def test_decode_is_deterministic(rot128):
 
 def test_decode_qwen3b_layer_128k_full_size(rot128):
     """One layer of the Qwen2.5-3B-shaped 128K decode at full size (16 q / 2 kv heads, K3V3), in the
-    launch configuration the benchmark times: prefill 131072 tokens, append one, attend over 131073."""
-    _say("decode qwen3b 128K full size")
+    launch configuration the benchmark times: prefill 131072 tokens, then one decode step
+    (bgtq_decode_step: the append as one workgroup beside 511 splits per KV head, the split that
+    reads the new token's tile waiting for it) on one cache and bgtq_quantize_append +
+    bgtq_decode_attention on its twin, bit for bit equal; logits and outputs against the oracle
+    with fp16 and with fp32 reconstruction levels, every head."""
+    _say("decode qwen3b 128K full size, step and append + decode")
     bank, rv, qz = rot128
     wl = synth.QWEN3B_128K
-    _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=True)
+    _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=True,
+                      step_twin=True, levels=("fp16", "fp32"))
 
 
 def test_decode_qwen3b_layer_512k_full_size(rot128):
-    """The same shape at 512K context: prefill 524288 tokens, append one, attend over 524289."""
-    _say("decode qwen3b 512K full size")
+    """The same shape at 512K context: prefill 524288 tokens, one decode step (and its append +
+    decode twin), attend over 524289; logits and outputs of every head against the oracle."""
+    _say("decode qwen3b 512K full size, step and append + decode")
     bank, rv, qz = rot128
     wl = synth.QWEN3B_512K
-    _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=False)
+    _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=True,
+                      step_twin=True)
 
 
 def test_decode_qwen7b_ragged_batch_full_size(rot128):
     """One layer of the 7B-Qwen-shaped ragged batch: 16 sequences of 8K..64K tokens, 28 q / 4 kv heads
-    (group 7), K3V2, all decoded in one call after a one-token append; the oracle checks the shortest,
-    the longest and two other sequences, every head."""
-    _say("decode qwen7b ragged batch of 16")
+    (group 7), K3V2, one decode step for all of them (and its append + decode twin); logits and
+    outputs of every sequence and head against the oracle."""
+    _say("decode qwen7b ragged batch of 16, step and append + decode")
     bank, rv, qz = rot128
     wl = synth.QWEN7B_RAGGED
-    lens = list(wl.seq_lens)
-    order = sorted(range(len(lens)), key=lambda i: lens[i])
-    check = {order[0], order[-1], order[len(lens) // 3], order[2 * len(lens) // 3]}
-    _decode_vs_oracle(wl, [t + 1 for t in lens], qz, bank, rv, append_then_attend=True, check_logits=False,
-                      check_seqs=check)
+    _decode_vs_oracle(wl, [t + 1 for t in wl.seq_lens], qz, bank, rv, append_then_attend=True,
+                      check_logits=True, step_twin=True)
+
+
+@pytest.fixture
+def valu_decode():
+    """Forces the vector-ALU decode kernel (the no-matrix-core path) for one test."""
+    old = bgtq.get_option(bgtq.OPT_DECODE_KERNEL)
+    bgtq.set_option(bgtq.OPT_DECODE_KERNEL, 1)
+    yield
+    bgtq.set_option(bgtq.OPT_DECODE_KERNEL, old)
+
+
+@pytest.mark.parametrize("h_q,h_kv,t_lens", [(16, 2, [4097, 130]), (32, 2, [6000]), (8, 8, [3000])])
+def test_decode_valu_kernel_vs_oracle(h_q, h_kv, t_lens, rot128, valu_decode):
+    """The vector-ALU decode against the oracle: group 8 (forced; the matrix cores serve it by
+    default), group 16 (the only path for it) and group 1, multi-tile ragged lengths."""
+    _say(f"decode vector ALU {h_q}/{h_kv} {t_lens}")
+    bank, rv, qz = rot128
+    wl = synth.Workload("valu", 95, d=128, h_q=h_q, h_kv=h_kv, theta=1e6, layers=1, seq_lens=tuple(t_lens),
+                        k_bits=3, v_bits=3, key_dtype="f32", profile="decay_jitter", outlier_blocks=2)
+    _decode_vs_oracle(wl, t_lens, qz, bank, rv, append_then_attend=True, step_twin=True)
+
+
+def test_decode_valu_kernel_qwen3b_128k(rot128, valu_decode):
+    """The vector-ALU decode on the 128K Qwen2.5-3B-shaped layer (group 8), every head."""
+    _say("decode vector ALU qwen3b 128K")
+    bank, rv, qz = rot128
+    wl = synth.QWEN3B_128K
+    _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=True)

@@ -4,7 +4,7 @@ The one-call prefill (energy partials, then the energies' final sums and the all
 one kernel, then the quantize-and-append) must equal bgtq_block_energy + bgtq_allocate_bits
 + bgtq_quantize_append bit for bit: energies, widths, layouts, every cache array, lengths
 and the recent-key window.  Those three calls are checked against the oracle by
-test_gpu_parity.py; the prefill path itself is what pipeline.prefill (and so every other
+test_gpu_parity.py; the prefill path itself is what bgtq_prefill (and so every other
 parity test) uses.
 """
 

@@ -9,13 +9,11 @@ logits, every cache array, lengths and status.  The append-then-decode path itse
 against the oracle by test_gpu_parity.py.
 """
 
-import os
-
 import numpy as np
 import pytest
 import torch
 
-from decode_attention_rope_amd import bgtq, pipeline, synth
+from decode_attention_rope_amd import bgtq, synth
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +36,7 @@ def _cache(wl, prefill, cap, qz, kv, tdt, dev):
     cache = bgtq.PackedCache(len(prefill), wl.h_kv, wl.d, wl.budget, wl.v_bits, cap, device=dev)
     for s, n in enumerate(prefill):
         k, v = kv[s]
-        pipeline.prefill(qz, cache, _t(k[:, :max(n, 1)], tdt), _t(v[:, :max(n, 1)], tdt), s)
+        bgtq.bgtq_prefill(qz, cache, _t(k[:, :max(n, 1)], tdt), _t(v[:, :max(n, 1)], tdt), s)
         if n == 0:     # allocation from one token, then an empty sequence
             cache.lengths[s] = 0
     return cache
@@ -104,16 +102,17 @@ def test_step_wait_that_gives_up_is_reported():
     k = np.stack([synth.keys(wl, 0, 0, h, 0, pre + 2) for h in range(h_kv)])
     v = np.stack([synth.values(wl, 0, 0, h, 0, pre + 2) for h in range(h_kv)])
     cache = bgtq.PackedCache(1, h_kv, d, wl.budget, wl.v_bits, 256, device=dev)
-    pipeline.prefill(qz, cache, _t(k[:, :pre]), _t(v[:, :pre]), 0)
+    bgtq.bgtq_prefill(qz, cache, _t(k[:, :pre]), _t(v[:, :pre]), 0)
     ws = torch.zeros(bgtq.decode_workspace_bytes(1, h_q, h_kv, d, 256), dtype=torch.uint8, device=dev)
     q = torch.randn((1, h_q, d), generator=torch.Generator().manual_seed(3)).to(dev)
-    os.environ["BGTQ_STEP_SPIN_LIMIT"] = "0"
+    limit = bgtq.get_option(bgtq.OPT_STEP_WAIT_LIMIT)
+    bgtq.set_option(bgtq.OPT_STEP_WAIT_LIMIT, 0)
     try:
         bgtq.bgtq_decode_step(qz, cache, q, _t(k[:, pre:pre + 1])[None].contiguous(),
                               _t(v[:, pre:pre + 1])[None].contiguous(), 1e6, workspace=ws)
         torch.cuda.synchronize()
     finally:
-        del os.environ["BGTQ_STEP_SPIN_LIMIT"]
+        bgtq.set_option(bgtq.OPT_STEP_WAIT_LIMIT, limit)
     assert int(cache.status[0]) & 2, "a wait that gave up was not reported"
     assert int(cache.lengths[0]) == pre + 1
     cache.status.zero_()

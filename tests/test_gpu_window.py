@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from decode_attention_rope_amd import bgtq, pipeline, synth
+from decode_attention_rope_amd import bgtq, synth
 from oracle import allocate, energy, layout, quantize
 from oracle import window as owin
 from _ref import TOL, rel_err
@@ -64,7 +64,7 @@ def _build(wl, pre, appends, w, kdt, pairing, cap=None):
         v = np.stack([synth.values(wl, s, 0, h, 0, t_len) for h in range(wl.h_kv)])
         kv.append((torch.from_numpy(k).to(tdt).float().numpy(), torch.from_numpy(v).to(tdt).float().numpy()))
         if pre[s]:
-            pipeline.prefill(qz, cache, _t(k[:, :pre[s]], tdt), _t(v[:, :pre[s]], tdt), s)
+            bgtq.bgtq_prefill(qz, cache, _t(k[:, :pre[s]], tdt), _t(v[:, :pre[s]], tdt), s)
     start = list(pre)
     for n in appends:
         for s in range(len(pre)):
@@ -152,7 +152,7 @@ def test_decode_step_with_window_equals_append_then_decode(d, h_q, h_kv, pre, w,
     for _ in range(2):
         c = bgtq.PackedCache(len(pre), h_kv, d, wl.budget, wl.v_bits, cap, device=dev, window=w)
         for s, p in enumerate(pre):
-            pipeline.prefill(qz, c, _t(kv[s][0][:, :p], tdt), _t(kv[s][1][:, :p], tdt), s)
+            bgtq.bgtq_prefill(qz, c, _t(kv[s][0][:, :p], tdt), _t(kv[s][1][:, :p], tdt), s)
         caches.append(c)
     a, b = caches
     ws = [torch.zeros(bgtq.decode_workspace_bytes(len(pre), h_q, h_kv, d, cap), dtype=torch.uint8, device=dev)
@@ -194,7 +194,7 @@ def test_window_qwen3b_layer_128k_full_size():
     cache = bgtq.PackedCache(1, wl.h_kv, wl.d, wl.budget, wl.v_bits, cap, device=dev, window=w)
     k = np.stack([synth.keys(wl, 0, 0, h, 0, t_len) for h in range(wl.h_kv)])
     v = np.stack([synth.values(wl, 0, 0, h, 0, t_len) for h in range(wl.h_kv)])
-    pipeline.prefill(qz, cache, _t(k[:, :-1]), _t(v[:, :-1]), 0)
+    bgtq.bgtq_prefill(qz, cache, _t(k[:, :-1]), _t(v[:, :-1]), 0)
     q = synth.queries(wl, 0, 0)
     out, logits = bgtq.bgtq_decode_step(qz, cache, _t(q[None]), _t(k[None, :, -1:]), _t(v[None, :, -1:]), wl.theta,
                                         logits=True)
