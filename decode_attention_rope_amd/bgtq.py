@@ -26,6 +26,7 @@ F32, BF16 = 0, 1
 PAIR_HALF, PAIR_INTERLEAVED = 0, 1
 ROT_DENSE, ROT_GIVENS = 0, 1
 OPT_DECODE_KERNEL, OPT_STEP_WAIT_LIMIT = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20
 TILE = 64
 MAX_GROUPS = 8
 LAYOUT_BYTES = 4096
@@ -75,6 +76,8 @@ _SIGNATURES = {
     "bgtq_init": (_i32, []),
     "bgtq_set_option": (_i32, [_i32, _i64]),
     "bgtq_get_option": (_i64, [_i32]),
+    "bgtq_decode_step_noalloc": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _f64, _f32, _vp,
+                                        _vp, _vp]),
     "bgtq_status_string": (_c.c_char_p, [_i32]),
     "bgtq_last_error": (_c.c_char_p, []),
 }
@@ -380,6 +383,33 @@ def bgtq_decode_step(quantizer: Quantizer, cache: PackedCache, q: torch.Tensor, 
                                   k_new.stride(1), float(rope_theta), float(scale), out.data_ptr(), _ptr(lg),
                                   workspace.data_ptr(), workspace.numel(), _stream()))
     return (out, lg) if logits is not False else out
+
+
+def bgtq_decode_step_noalloc(quantizer: Quantizer, cache: PackedCache, q: torch.Tensor, k_new: torch.Tensor,
+                             v_new: torch.Tensor, rope_theta: float, softmax_scale: float | None = None,
+                             out: torch.Tensor | None = None, logits: torch.Tensor | None = None):
+    """bgtq_decode_step without a workspace (the library's per-GPU scratch array holds it); `out`
+    and `logits` (fp32 [batch, n_q_heads, capacity] or None) are caller-provided, so that a
+    caller who must not allocate can pass buffers it already holds."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, n_q_heads, head_dim] tensor")
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same shape, strides and dtype")
+    b, hq, d = q.shape
+    if k_new.dim() != 4 or k_new.shape[0] != b or k_new.shape[1] != cache.n_kv_heads or k_new.shape[2] != 1 \
+            or k_new.shape[3] != d or k_new.stride(3) != 1:
+        raise ValueError("k_new must be [batch, n_kv_heads, 1, head_dim] with a contiguous last dimension")
+    if b != cache.batch or d != cache.head_dim:
+        raise ValueError("q does not match the cache geometry")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+    desc = cache.desc()
+    _check(lib().bgtq_decode_step_noalloc(_c.byref(quantizer), _c.byref(desc), hq, q.data_ptr(), _dtype_code(q),
+                                          k_new.data_ptr(), v_new.data_ptr(), _dtype_code(k_new), k_new.stride(0),
+                                          k_new.stride(1), float(rope_theta), float(scale), out.data_ptr(),
+                                          _ptr(logits), _stream()))
+    return out
 
 
 def logit_error_workspace_bytes(batch, n_q_heads, capacity) -> int:

@@ -19,6 +19,7 @@ namespace {
 thread_local std::string g_last_error;
 std::mutex g_init_mutex;
 bool g_device_ready[64] = {};
+void* g_scratch[64] = {};     // device address of each GPU's allocation-free scratch
 
 // process-wide options (bgtq_set_option); defaults from the environment, read once
 std::atomic<int> g_force_valu{0};
@@ -42,7 +43,8 @@ bgtq_status hip_status(hipError_t e, const char* what) {
 }
 
 // The library's initialisation, once per device (the current one): the codebook tables go to
-// constant memory.  The first initialisation in the process also takes the options' defaults from the environment;
+// constant memory and the device address of the allocation-free scratch is looked up.  The
+// first initialisation in the process also takes the options' defaults from the environment;
 // no other place reads it.
 bgtq_status ensure_init() {
   std::call_once(g_env_once, [] {
@@ -57,6 +59,8 @@ bgtq_status ensure_init() {
   if (g_device_ready[dev]) return BGTQ_OK;
   e = upload_tables(host_tables());
   if (e != hipSuccess) return hip_status(e, "upload codebook tables");
+  e = scratch_address(&g_scratch[dev]);
+  if (e != hipSuccess) return hip_status(e, "scratch symbol address");
   g_device_ready[dev] = true;
   return BGTQ_OK;
 }
@@ -412,12 +416,26 @@ bgtq_status bgtq_decode_attention(const bgtq_quantizer* qz, const bgtq_cache* ca
   return hip_status(launch_decode(a, q_dtype, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
-bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
-                             bgtq_dtype q_dtype, const void* keys, const void* values, bgtq_dtype kv_dtype,
-                             int64_t stride_seq, int64_t stride_head, double rope_theta, float softmax_scale,
-                             float* out, float* logits_out, void* workspace, size_t workspace_bytes,
-                             bgtq_stream stream) {
+// a decode step on a given workspace; with noalloc, the workspace is the current device's
+// scratch array (looked up after the arguments are validated) and its step flags are cleared
+// first
+static bgtq_status decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
+                               bgtq_dtype q_dtype, const void* keys, const void* values, bgtq_dtype kv_dtype,
+                               int64_t stride_seq, int64_t stride_head, double rope_theta, float softmax_scale,
+                               float* out, float* logits_out, void* workspace, size_t workspace_bytes,
+                               hipStream_t s, bool noalloc) {
   if (bgtq_status st = check_cache(cache, true); st != BGTQ_OK) return st;
+  if (noalloc) {
+    const size_t need = bgtq_decode_workspace_bytes(cache->batch, n_q_heads, cache->n_kv_heads, cache->head_dim,
+                                                    cache->capacity);
+    if (need > BGTQ_NOALLOC_SCRATCH_BYTES)
+      return fail(BGTQ_ERR_WORKSPACE, "this cache needs %zu bytes of decode workspace; the allocation-free "
+                  "scratch holds %u (use bgtq_decode_step with a workspace)", need, BGTQ_NOALLOC_SCRATCH_BYTES);
+    // the arguments are validated against a stand-in address; the scratch's own address is
+    // looked up once they pass (the lookup initialises the device)
+    workspace = reinterpret_cast<void*>(uintptr_t(256));
+    workspace_bytes = BGTQ_NOALLOC_SCRATCH_BYTES;
+  }
   AppendArgs aa;
   if (bgtq_status st = prepare_append(qz, cache, 0, cache->batch, keys, values, kv_dtype, 1, stride_seq, stride_head,
                                       cache->head_dim, aa);
@@ -429,24 +447,58 @@ bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, 
       st != BGTQ_OK)
     return st;
   if (bgtq_status st = ensure_init(); st != BGTQ_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (noalloc) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e, "hipGetDevice");
+    workspace = g_scratch[dev];
+    if (bgtq_status st = prepare_decode(qz, cache, n_q_heads, q, q_dtype, nullptr, rope_theta, softmax_scale, out,
+                                        logits_out, workspace, workspace_bytes, da);
+        st != BGTQ_OK)
+      return st;
+  }
+  const size_t need = bgtq_decode_workspace_bytes(cache->batch, n_q_heads, cache->n_kv_heads, cache->head_dim,
+                                                  cache->capacity);
+  int32_t* flags = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need -
+                                              align256(decode_step_bytes(cache->batch, cache->n_kv_heads)));
+  if (noalloc) {   // the scratch keeps the last call's contents: the flags must start at zero
+    if (bgtq_status st = hip_status(launch_clear_flags(flags, cache->batch * cache->n_kv_heads, s),
+                                    "decode-step flag clear launch");
+        st != BGTQ_OK)
+      return st;
+  }
   if (!da.use_mfma) {   // vector-ALU path: the two calls in sequence
     if (bgtq_status st = hip_status(launch_append(aa, kv_dtype, cache->batch, s), "decode-step append launch");
         st != BGTQ_OK)
       return st;
     return hip_status(launch_decode(da, q_dtype, s), "decode-step attention launch");
   }
-  const size_t need = bgtq_decode_workspace_bytes(cache->batch, n_q_heads, cache->n_kv_heads, cache->head_dim,
-                                                  cache->capacity);
   aa.advance = 0;
   da.step = 1;
   // the wait of the split that reads the new token's tile is bounded (about 0.2 s at most by
   // default); the option BGTQ_OPT_STEP_WAIT_LIMIT sets the bound (0: no wait), so that the
   // report of a wait that gave up can be exercised
   da.step_spin = g_step_spin;
-  da.step_flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + need -
-                                            align256(decode_step_bytes(cache->batch, cache->n_kv_heads)));
+  da.step_flag = flags;
   return hip_status(launch_decode_step(aa, da, kv_dtype, q_dtype, s), "decode-step launch");
+}
+
+bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads, const void* q,
+                             bgtq_dtype q_dtype, const void* keys, const void* values, bgtq_dtype kv_dtype,
+                             int64_t stride_seq, int64_t stride_head, double rope_theta, float softmax_scale,
+                             float* out, float* logits_out, void* workspace, size_t workspace_bytes,
+                             bgtq_stream stream) {
+  return decode_step(qz, cache, n_q_heads, q, q_dtype, keys, values, kv_dtype, stride_seq, stride_head, rope_theta,
+                     softmax_scale, out, logits_out, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                     false);
+}
+
+bgtq_status bgtq_decode_step_noalloc(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads,
+                                     const void* q, bgtq_dtype q_dtype, const void* keys, const void* values,
+                                     bgtq_dtype kv_dtype, int64_t stride_seq, int64_t stride_head,
+                                     double rope_theta, float softmax_scale, float* out, float* logits_out,
+                                     bgtq_stream stream) {
+  return decode_step(qz, cache, n_q_heads, q, q_dtype, keys, values, kv_dtype, stride_seq, stride_head, rope_theta,
+                     softmax_scale, out, logits_out, nullptr, 0, static_cast<hipStream_t>(stream), true);
 }
 
 size_t bgtq_logit_error_workspace_bytes(int batch, int n_q_heads, int64_t capacity) {

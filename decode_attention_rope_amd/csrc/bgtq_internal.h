@@ -166,6 +166,10 @@ hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, bgtq_d
                               hipStream_t s);
 // the decode step's flags: one int per (sequence, KV head), zero between steps
 size_t decode_step_bytes(int batch, int n_kv_heads);
+// clears n step flags with a fill kernel (no memset node, so the call can be captured)
+hipError_t launch_clear_flags(int32_t* flags, int n, hipStream_t s);
+// device address of the current device's allocation-free scratch (BGTQ_NOALLOC_SCRATCH_BYTES)
+hipError_t scratch_address(void** ptr);
 
 // key-only logit error (diagnostic.hip)
 constexpr int kErrChunk = 256;       // tokens per workgroup and per partial sum

@@ -2607,6 +2607,26 @@ hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, bgtq_d
 
 size_t decode_step_bytes(int batch, int n_kv_heads) { return size_t(batch) * n_kv_heads * 4; }
 
+namespace {
+// Workspace of the allocation-free decode step: one array per GPU, part of the code object.
+// Host code must not pass the array's name to a kernel (on the host it is only a stand-in);
+// scratch_address gives the device address to use instead.
+__device__ __align__(256) uint8_t scratch[BGTQ_NOALLOC_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void k_clear_flags(int32_t* __restrict__ flags, int n) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (i < n) flags[i] = 0;
+}
+}  // namespace
+
+hipError_t scratch_address(void** ptr) { return hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch)); }
+
+hipError_t launch_clear_flags(int32_t* flags, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_clear_flags, dim3((n + 255) / 256), dim3(256), 0, s, flags, n);
+  return hipGetLastError();
+}
+
 hipError_t upload_tables(const Tables& t) {
   hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(c_thr), t.thr, sizeof(t.thr));
   if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_cen), t.cen, sizeof(t.cen));

@@ -12,7 +12,9 @@
  *
  * Conventions for every call
  *   - All tensors are device memory owned by the caller; the library never
- *     allocates, frees or keeps device memory, and keeps no per-call state.
+ *     allocates or frees device memory and keeps no per-call state.  The one
+ *     device memory it owns is the static scratch array of
+ *     bgtq_decode_step_noalloc (part of the code object, one per GPU).
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     null stream) and the call returns without waiting.
  *   - Arguments are validated on the host before anything is enqueued; a bad
@@ -294,6 +296,24 @@ bgtq_status bgtq_decode_step(const bgtq_quantizer* qz, const bgtq_cache* cache, 
                              double rope_theta, float softmax_scale, float* out, float* logits_out,
                              void* workspace, size_t workspace_bytes, bgtq_stream stream);
 
+/* bgtq_decode_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace:
+ * the split partials and the step flags live in a library-owned device array of
+ * BGTQ_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends).  The call allocates
+ * nothing; it clears the step flags with a small kernel, then runs the same kernels as
+ * bgtq_decode_step, so the results are the same bit for bit.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams, or different host
+ * threads without ordering) race and give undefined results.  Arguments as for
+ * bgtq_decode_step, minus the workspace.
+ * Errors: those of bgtq_decode_step; WORKSPACE when bgtq_decode_workspace_bytes for the
+ * cache exceeds BGTQ_NOALLOC_SCRATCH_BYTES. */
+#define BGTQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+bgtq_status bgtq_decode_step_noalloc(const bgtq_quantizer* qz, const bgtq_cache* cache, int n_q_heads,
+                                     const void* q, bgtq_dtype q_dtype, const void* keys,
+                                     const void* values, bgtq_dtype kv_dtype, int64_t stride_seq,
+                                     int64_t stride_head, double rope_theta, float softmax_scale,
+                                     float* out, float* logits_out, bgtq_stream stream);
+
 /* Key-only logit error (abstract: Block-GTQ is judged on how well it keeps the RoPE
  * query-key logits, as the per-layer mean absolute logit error when only keys are quantized,
  * at 2 and 3 bits per coordinate, against uniform TQ-MSE at the same budget).
@@ -334,8 +354,9 @@ size_t bgtq_cache_bytes(int batch, int n_kv_heads, int head_dim, int k_width_sum
  * bits 0 has no tables).  Host-only, enqueues nothing. */
 bgtq_status bgtq_codebook(int bits, float* thresholds, float* centroids, double* distortion);
 
-/* Copy the frozen tables to the current device's constant memory (synchronous).  The
- * first call in the process also reads the options' defaults from the environment:
+/* Copy the frozen tables to the current device's constant memory (synchronous) and
+ * look up the device's allocation-free scratch (bgtq_decode_step_noalloc).  The first
+ * call in the process also reads the options' defaults from the environment:
  * BGTQ_DECODE_KERNEL=valu sets BGTQ_OPT_DECODE_KERNEL to 1, BGTQ_STEP_SPIN_LIMIT=n sets
  * BGTQ_OPT_STEP_WAIT_LIMIT to n.  Nothing reads the environment afterwards. */
 bgtq_status bgtq_init(void);

@@ -268,3 +268,25 @@ def test_options_round_trip():
         bgtq.set_option(bgtq.OPT_DECODE_KERNEL, old_k)
         bgtq.set_option(bgtq.OPT_STEP_WAIT_LIMIT, old_w)
 
+
+def test_decode_step_noalloc_validation():
+    """Host checks of the allocation-free step: a cache whose decode workspace exceeds the scratch
+    is refused, and bad arguments are refused before any device is touched."""
+    lib = bgtq.lib()
+
+    def call(desc, n_q=16, scale=0.088, kv=FAKE):
+        return lib.bgtq_decode_step_noalloc(ctypes.byref(_quantizer()), ctypes.byref(desc), n_q, FAKE, 0, kv, kv, 0,
+                                            256, 128, 1e6, scale, FAKE, None, None)
+
+    big = _desc(batch=64, n_kv_heads=8, capacity=1 << 20)
+    assert lib.bgtq_decode_workspace_bytes(64, 256, 8, 128, 1 << 20) > bgtq.NOALLOC_SCRATCH_BYTES
+    assert call(big, n_q=256) == bgtq.ERR_WORKSPACE
+    assert b"scratch" in lib.bgtq_last_error()
+    assert lib.bgtq_decode_workspace_bytes(1, 16, 2, 128, 131136) <= bgtq.NOALLOC_SCRATCH_BYTES
+    assert call(_desc(), n_q=15) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), n_q=34) == bgtq.ERR_UNSUPPORTED
+    assert call(_desc(), scale=0.0) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(), kv=None) == bgtq.ERR_INVALID_ARG
+    assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
+    assert lib.bgtq_decode_step_noalloc(ctypes.byref(_quantizer()), None, 16, FAKE, 0, FAKE, FAKE, 0, 256, 128, 1e6,
+                                        0.088, FAKE, None, None) == bgtq.ERR_INVALID_ARG
