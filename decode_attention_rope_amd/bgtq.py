@@ -156,8 +156,9 @@ def init() -> None:
 
 
 def set_option(option: int, value: int) -> None:
-    """Process-wide test/diagnosis option (OPT_DECODE_KERNEL: 1 forces the vector-ALU decode;
-    OPT_STEP_WAIT_LIMIT: bound of a decode step's wait for its append)."""
+    """Process-wide test/diagnosis option (OPT_DECODE_KERNEL: 1 forces the vector-ALU decode,
+    2 the tiled matrix-core pass; OPT_STEP_WAIT_LIMIT: bound of a decode step's wait for its
+    append)."""
     _check(lib().bgtq_set_option(option, value))
 
 

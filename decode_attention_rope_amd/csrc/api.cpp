@@ -1,6 +1,7 @@
 // C ABI of the Block-GTQ packed-cache decode path: argument checks, sizes, launches.
 // Declared and documented in include/bgtq.h.
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -22,7 +23,7 @@ bool g_device_ready[64] = {};
 void* g_scratch[64] = {};     // device address of each GPU's allocation-free scratch
 
 // process-wide options (bgtq_set_option); defaults from the environment, read once
-std::atomic<int> g_force_valu{0};
+std::atomic<int> g_decode_kernel{0};   // 0 automatic, 1 vector ALU, 2 tiled matrix-core pass
 std::atomic<int> g_step_spin{1 << 22};
 std::once_flag g_env_once;
 
@@ -48,7 +49,8 @@ bgtq_status hip_status(hipError_t e, const char* what) {
 // no other place reads it.
 bgtq_status ensure_init() {
   std::call_once(g_env_once, [] {
-    if (const char* k = std::getenv("BGTQ_DECODE_KERNEL")) g_force_valu = std::strcmp(k, "valu") == 0 ? 1 : 0;
+    if (const char* k = std::getenv("BGTQ_DECODE_KERNEL"))
+      g_decode_kernel = std::strcmp(k, "valu") == 0 ? 1 : std::strcmp(k, "tiled") == 0 ? 2 : 0;
     if (const char* sl = std::getenv("BGTQ_STEP_SPIN_LIMIT")) g_step_spin = std::atoi(sl) > 0 ? std::atoi(sl) : 0;
   });
   int dev = 0;
@@ -128,8 +130,8 @@ bgtq_status bgtq_init(void) { return ensure_init(); }
 bgtq_status bgtq_set_option(bgtq_option option, int64_t value) {
   switch (option) {
     case BGTQ_OPT_DECODE_KERNEL:
-      if (value != 0 && value != 1) return fail(BGTQ_ERR_INVALID_ARG, "decode kernel option must be 0 or 1");
-      g_force_valu = int(value);
+      if (value < 0 || value > 2) return fail(BGTQ_ERR_INVALID_ARG, "decode kernel option must be 0, 1 or 2");
+      g_decode_kernel = int(value);
       return BGTQ_OK;
     case BGTQ_OPT_STEP_WAIT_LIMIT:
       if (value < 0 || value > (int64_t(1) << 30)) return fail(BGTQ_ERR_INVALID_ARG, "wait limit must be 0..2^30");
@@ -141,7 +143,7 @@ bgtq_status bgtq_set_option(bgtq_option option, int64_t value) {
 
 int64_t bgtq_get_option(bgtq_option option) {
   switch (option) {
-    case BGTQ_OPT_DECODE_KERNEL: return g_force_valu;
+    case BGTQ_OPT_DECODE_KERNEL: return g_decode_kernel;
     case BGTQ_OPT_STEP_WAIT_LIMIT: return g_step_spin;
   }
   return -1;
@@ -328,7 +330,12 @@ bgtq_status bgtq_prefill(const bgtq_quantizer* qz, const bgtq_cache* cache, int 
 
 size_t bgtq_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t capacity) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || !head_dim_ok(head_dim) || capacity < kTile) return 0;
-  const int splits = decode_splits(batch, n_kv_heads, capacity, true) + kMaxWindowSplits;   // an upper bound
+  // an upper bound of every pass's split count (the streamed matrix-core pass, the other
+  // matrix-core pass with its window splits, the vector-ALU pass)
+  const int base = std::max(std::max(decode_splits(batch, n_kv_heads, capacity, true),
+                                     decode_splits(batch, n_kv_heads, capacity, false)),
+                            decode_stream_splits(batch, n_kv_heads));
+  const int splits = base + kMaxWindowSplits;
   const size_t part = align256(size_t(batch) * n_q_heads * splits * head_dim * 4) +
                       align256(size_t(batch) * n_q_heads * splits * 8);
   return align256(decode_qrot_bytes(batch, n_kv_heads, head_dim)) + part +
@@ -369,7 +376,7 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
   a.layouts = static_cast<const HeadLayout*>(cache->layouts);
   a.out = out;
   a.logits = logits_out;
-  a.use_mfma = group <= 8 && !g_force_valu;
+  a.use_mfma = group <= 8 && g_decode_kernel != 1;
   if (cache->window > 0 && !a.use_mfma)
     return fail(BGTQ_ERR_UNSUPPORTED, "the recent-key window is built on the matrix-core decode (group size <= 8)");
   a.window = cache->window;
@@ -377,11 +384,25 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
   // the window's splits come out of the same workgroup budget (a grid that fits the GPU at
   // once), the packed keys keep at least one split
   a.n_wsplit = window_splits(cache->window);
-  const int base = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma);
-  // the matrix-core pass leaves one workgroup of every (sequence, KV head) to a decode step's
-  // append role, so that a step and a decode call split the tokens alike
-  const int packed = base - a.n_wsplit - (a.use_mfma ? 1 : 0);
-  a.n_split = (packed > 1 ? packed : 1) + a.n_wsplit;
+  a.use_stream = a.use_mfma && g_decode_kernel != 2 && cache->window == 0 &&
+                 decode_stream_fits(d, record_chunks(cache->k_width_sum), cache->v_bits);
+  if (a.use_stream) {
+    a.n_split = decode_stream_splits(cache->batch, cache->n_kv_heads);
+  } else {
+    const int base = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma);
+    // the matrix-core pass leaves one workgroup of every (sequence, KV head) to a decode step's
+    // append role, so that a step and a decode call split the tokens alike
+    const int packed = base - a.n_wsplit - (a.use_mfma ? 1 : 0);
+    a.n_split = (packed > 1 ? packed : 1) + a.n_wsplit;
+  }
+  // the partial results of this split count must fit the workspace layout (the size function
+  // bounds every pass's count)
+  const size_t used = align256(decode_qrot_bytes(cache->batch, cache->n_kv_heads, d)) +
+                      align256(size_t(cache->batch) * n_q_heads * a.n_split * d * 4) +
+                      align256(size_t(cache->batch) * n_q_heads * a.n_split * 8) +
+                      align256(decode_step_bytes(cache->batch, cache->n_kv_heads));
+  if (used > need) return fail(BGTQ_ERR_WORKSPACE, "internal: %d splits need %zu workspace bytes, sized %zu",
+                               a.n_split, used, need);
   char* ws = static_cast<char*>(workspace);
   const size_t qrot_b = align256(decode_qrot_bytes(cache->batch, cache->n_kv_heads, d));
   a.qrot = reinterpret_cast<float*>(ws);

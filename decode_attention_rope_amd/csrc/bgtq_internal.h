@@ -64,6 +64,11 @@ struct Tables {
   // levels of codes c0 (low half) and c1 (high half) of width w <= 5; single[] widths 1..8.
   uint32_t pair[kPairWords];
   uint16_t single[kSingleHalves];
+  // the same levels split as hi + lo, hi = fp16(cen), lo = fp16(cen - hi): hi + lo carries the
+  // fp32 centroid to about 2^-22 relative.  pair_hl[i] = (pair hi halves, pair lo halves);
+  // single_hl[] = hi | lo << 16, widths 1..8 at 2^w - 2.
+  uint32_t pair_hl[kPairWords][2];
+  uint32_t single_hl[kSingleHalves];
   double dgain[kMaxBits];     // dist[b] - dist[b+1], b = 0..7
   double dist[kMaxBits + 1];  // fl32(D(b)), dist[0] = 1
 };
@@ -77,6 +82,10 @@ inline size_t rot_bank_offset(int m) {  // floats before the m x m matrix (m eve
   return o;
 }
 int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma);
+// the streamed matrix-core split pass: whether it serves a cache geometry (head dims 64/128,
+// tiles that fit its staging), and its split count per (sequence, KV head)
+bool decode_stream_fits(int d, int chunks, int v_bits);
+int decode_stream_splits(int batch, int n_kv_heads);
 // splits that attend over a window of w tokens (at most two 64-token tiles each)
 inline int window_splits(int w) { return w > 0 ? ((w + kTile - 1) / kTile + 2) / 2 : 0; }
 constexpr int kMaxWindowSplits = (BGTQ_MAX_WINDOW / kTile + 2) / 2;
@@ -154,6 +163,7 @@ struct DecodeArgs {
   int batch, n_q, n_kv, group, d, v_bits, chunks, n_split, pairing;
   int step;           // decode step: one token is appended beside the pass (its append role)
   int use_mfma;
+  int use_stream;             // the streamed matrix-core split pass (no window, head dims 64/128)
   const uint16_t* k_window;   // fp16 recent keys (see AppendArgs)
   int window;                 // 0: no window
   int n_wsplit;               // the first n_wsplit splits attend over the window's tokens

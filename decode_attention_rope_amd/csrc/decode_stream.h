@@ -1,0 +1,616 @@
+// Streamed split pass of the matrix-core decode (included by kernels.hip, inside its
+// anonymous namespace, after the query prologue helpers and the decode step's append role).
+//
+// RoPE query-key logits over the packed cache, softmax and the value sum (abstract: the
+// logit is a sum of per-block 2-D RoPE terms; the serving path attends over a packed K3V3
+// cache at 128K context).  One workgroup of 8 waves per split; a split takes tiles tbase,
+// tbase + stride, ... of its (sequence, KV head), and wave w of the split takes that list's
+// entries w, w + 8, ...  Every wave works on whole 64-token tiles on its own: it stages a
+// tile's packed bytes through registers into its own LDS slot (the next tile's loads are in
+// flight meanwhile), computes the tile's logits, runs its own online softmax and accumulates
+// P V; no workgroup barrier falls inside the tile loop.  The 8 waves' results are merged once,
+// at the end, into the split's partial result (the format k_decode_combine reads).
+//
+//   logits  per k-step ks (32 storage positions of at most two width groups) and row block rb
+//           (16 tokens): lane (n, j) decodes the 8 codes of its token's segment (ks, j) into
+//           fp16 levels hi + lo (pair tables); T = A_hi B_hi + A_hi B_lo + A_lo B_hi on
+//           v_mfma_f32_16x16x32_f16, B the rotated query (columns 0-7: the G heads restricted
+//           to the k-step's first width group, columns 8-15: its second); S += T * n_group.
+//           Row r of row block rb is token 32 (rb / 2) + 8 (r / 4) + 4 (rb % 2) + r % 4 of the
+//           tile, so that lane (c, j) ends up holding tokens 8 j .. 8 j + 7 of each 32-token
+//           block: exactly the k slots of the P V operand below, with no exchange.
+//   values  A = the value levels (hi + lo) of 16 rotated coordinates x 32 tokens, B = P n_v in
+//           fp16 from the softmax registers; acc holds 16 coordinates x 16 columns per M-tile.
+// The hi + lo split carries the fp32 Lloyd-Max levels to about 2^-22 relative.
+
+constexpr int kStreamWaves = 8;
+constexpr int kStreamThreads = 64 * kStreamWaves;
+
+// One tile's staging slot in LDS (bytes): K records token-major [64][16 chunks], the K norm
+// planes [8][64] fp16, the value norms [64] fp16, the value codes [D][8 b_v] (coordinate-
+// major, as in HBM), 16 bytes of slack for window reads past the end.  A tile arrives with
+// `chunks` + 1 + v_loads direct loads of 1 KiB per wave (the last value load partial).
+struct StreamSlot {
+  int kn_off, vn_off, vc_off, bytes;
+  int v_units, v_loads;              // 16-byte value units (norms first) and their loads
+};
+__host__ __device__ inline StreamSlot stream_slot(int D, int chunks, int bv) {
+  StreamSlot g;
+  g.kn_off = 1024 * chunks;
+  g.vn_off = g.kn_off + 2 * kMaxGroups * kTile;
+  g.vc_off = g.vn_off + 2 * kTile;
+  g.bytes = g.vc_off + D * 8 * bv + 16;
+  g.v_units = 8 + D * bv / 2;
+  g.v_loads = (g.v_units + 63) / 64;
+  return g;
+}
+// Static LDS of the pass: two staging rings of one slot per wave (separate objects, so that the
+// compiler's waits for one ring's loads leave the other's in flight), decoder tables, k-step
+// descriptors, the prologue's area (layout copy, q', B operands), the merge's exchange.
+__host__ __device__ constexpr int stream_slot_max(int D) { return D == 128 ? 7424 : 5376; }
+constexpr int kSTabPair = 0;                                   // uint2 [kPairWords] hi, lo
+constexpr int kSTabSingle = kSTabPair + 8 * kPairWords;        // uint32 [kSingleHalves] hi | lo << 16
+constexpr int kSTabBytes = (kSTabSingle + 4 * kSingleHalves + 255) & ~255;
+__host__ __device__ constexpr int stream_pro_bytes(int D) {
+  return BGTQ_LAYOUT_BYTES + 32 * D + 2 * 1024 * kQRegSteps;   // layout, q' [D][8], B hi [8][64], B lo [8][64]
+}
+// whether the streamed pass serves a cache: head dims 64 and 128 without a window, K records of
+// at most 4 chunks, tiles that fit a ring slot
+__host__ __device__ inline bool stream_fits(int D, int chunks, int bv) {
+  return (D == 64 || D == 128) && chunks <= 4 && stream_slot(D, chunks, bv).bytes <= stream_slot_max(D);
+}
+
+// the window of a segment: bits [sh, sh + 32) of d1:d0 as one dword
+__device__ __forceinline__ uint32_t win32(uint32_t d0, uint32_t d1, uint32_t sh) {
+  return __builtin_amdgcn_alignbit(d1, d0, sh);
+}
+
+// 16 bytes per lane from global address p to LDS at lds + 16 lane (lds the same for the whole
+// wave) as one direct-to-LDS load.  It is issued from asm so that the compiler's wait insertion
+// does not track it: that pass cannot tell the two staging rings apart and would make every LDS
+// read of the tile loop wait for every staging load in flight, including the next tile's.  The
+// waits for these loads are therefore explicit (vmcnt, which counts vector memory operations in
+// issue order).  M0 holds the LDS address for the load and is restored afterwards.
+__device__ __forceinline__ void stage16(const void* p, const void* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds)));
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(l), "v"(p)
+      : "memory");
+}
+
+// Matrix-core operands of eight decoded codes, k slots interleaved: A1 holds the levels of codes
+// 0..3 as (hi 0, hi 1, lo 0, lo 1, hi 2, hi 3, lo 2, lo 3), A2 those of codes 4..7, so that each
+// pair lookup (hi pair, lo pair) lands in its operand as loaded.  The matching B operand repeats
+// the other factor: (x 0, x 1, x 0, x 1, x 2, x 3, x 2, x 3).  A1 B1 + A2 B2 is then the
+// product with the levels hi + lo.
+
+// Eight codes of widths w <= 4 from the window x (code e at bits [e w, (e + 1) w)), two per
+// lookup in the hi/lo pair table at byte offset tb.  o1, o2, o3 = 2w, 4w, 6w; w2 = 2w (the field
+// extracts use bits 4:0 of each).
+__device__ __forceinline__ void dec8_pairs(uint32_t x, uint32_t w2, uint32_t o1, uint32_t o2, uint32_t o3,
+                                           uint32_t tb, const uint8_t* lds, u32x4& A1, u32x4& A2) {
+  const uint32_t i0 = __builtin_amdgcn_ubfe(x, 0u, w2), i1 = __builtin_amdgcn_ubfe(x, o1, w2);
+  const uint32_t i2 = __builtin_amdgcn_ubfe(x, o2, w2), i3 = __builtin_amdgcn_ubfe(x, o3, w2);
+  const uint2 v0 = *reinterpret_cast<const uint2*>(lds + tb + 8 * i0);
+  const uint2 v1 = *reinterpret_cast<const uint2*>(lds + tb + 8 * i1);
+  const uint2 v2 = *reinterpret_cast<const uint2*>(lds + tb + 8 * i2);
+  const uint2 v3 = *reinterpret_cast<const uint2*>(lds + tb + 8 * i3);
+  A1 = u32x4{v0.x, v0.y, v1.x, v1.y};
+  A2 = u32x4{v2.x, v2.y, v3.x, v3.y};
+}
+
+// The same for widths w <= 5 from the 64-bit window xh:xl (the fourth pair can cross bit 32).
+__device__ __forceinline__ void dec8_pairs5(uint32_t xl, uint32_t xh, uint32_t w2, uint32_t o1, uint32_t o2,
+                                            uint32_t o3, uint32_t tb, const uint8_t* lds, u32x4& A1, u32x4& A2) {
+  const uint32_t x3 = __builtin_amdgcn_alignbit(xh, xl, o3);
+  const uint32_t i0 = __builtin_amdgcn_ubfe(xl, 0u, w2), i1 = __builtin_amdgcn_ubfe(xl, o1, w2);
+  const uint32_t i2 = __builtin_amdgcn_ubfe(xl, o2, w2), i3 = __builtin_amdgcn_ubfe(x3, 0u, w2);
+  const uint2 v0 = *reinterpret_cast<const uint2*>(lds + tb + 8 * i0);
+  const uint2 v1 = *reinterpret_cast<const uint2*>(lds + tb + 8 * i1);
+  const uint2 v2 = *reinterpret_cast<const uint2*>(lds + tb + 8 * i2);
+  const uint2 v3 = *reinterpret_cast<const uint2*>(lds + tb + 8 * i3);
+  A1 = u32x4{v0.x, v0.y, v1.x, v1.y};
+  A2 = u32x4{v2.x, v2.y, v3.x, v3.y};
+}
+
+// Eight codes of any width w (1..8) from the 64-bit window xh:xl, one per lookup in the hi | lo
+// single table at byte offset tb.
+__device__ __forceinline__ void dec8_singles(uint32_t xl, uint32_t xh, uint32_t w, uint32_t tb, const uint8_t* lds,
+                                             u32x4& A1, u32x4& A2) {
+  const uint64_t x = (uint64_t(xh) << 32) | xl;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t c = uint32_t(x >> (uint32_t(e) * w)) & ((1u << w) - 1u);   // e w + w <= 64
+    v[e] = *reinterpret_cast<const uint32_t*>(lds + tb + 4 * c);
+  }
+  uint32_t o[8];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    o[2 * e2] = __builtin_amdgcn_perm(v[2 * e2 + 1], v[2 * e2], 0x05040100u);       // hi of the pair
+    o[2 * e2 + 1] = __builtin_amdgcn_perm(v[2 * e2 + 1], v[2 * e2], 0x07060302u);   // lo of the pair
+  }
+  A1 = u32x4{o[0], o[1], o[2], o[3]};
+  A2 = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// B operand of the interleaved form from four values' fp16 halves packed as (x0 | x1 << 16,
+// x2 | x3 << 16)
+__device__ __forceinline__ f16x8 bdup(uint32_t x01, uint32_t x23) {
+  return __builtin_bit_cast(f16x8, u32x4{x01, x01, x23, x23});
+}
+
+// k-step class: 0 = every segment at most 4 bits wide, 1 = at most 5, 2 = wider
+__device__ __forceinline__ uint32_t seg_class(uint32_t w) { return w <= 4 ? 0u : (w == 5 ? 1u : 2u); }
+
+template <int D, typename QT, bool STEP>
+__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void k_decode_stream(DecodeArgs a, AppendArgs aa) {
+  constexpr int MT = D / 16;                         // value M-tiles (16 coordinates each)
+  constexpr int KS = tc_ksteps(D);                   // k-steps at most
+  constexpr int SLOT = stream_slot_max(D);
+  static_assert(KS <= kQRegSteps, "every k-step's operands in the prologue's B rows");
+  __shared__ __align__(16) uint8_t s_tab[kSTabBytes];
+  __shared__ __align__(16) uint4 s_kd[4 * kMaxKSteps];
+  __shared__ float s_ml[2 * kStreamWaves * 8];
+  __shared__ __align__(16) uint8_t s_pro[stream_pro_bytes(D)];
+  __shared__ __align__(16) uint8_t s_ring0[kStreamWaves * SLOT];
+  __shared__ __align__(16) uint8_t s_ring1[kStreamWaves * SLOT];
+  if constexpr (STEP) {
+    if (blockIdx.x == 0) {          // decode step: workgroup 0 of every (sequence, KV head) appends
+      if (aa.givens) step_append_role<false, true>(aa, a.step_flag, blockIdx.z, blockIdx.y, s_ring0);
+      else step_append_role<false, false>(aa, a.step_flag, blockIdx.z, blockIdx.y, s_ring0);
+      return;
+    }
+  }
+  const int split = int(blockIdx.x) - (STEP ? 1 : 0), hk = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, j = lane >> 4;
+  if (split == 0)       // the merge adds into this (sequence, KV head)'s output rows
+    for (int i = tid; i < a.group * D; i += kStreamThreads) a.out[(int64_t(s) * a.n_q + hk * a.group) * D + i] = 0.0f;
+  // in a decode step the append role adds the new token beside this pass and the merge kernel
+  // advances lengths[], so it still holds the old length here
+  const int len0 = a.lengths[s];
+  const int len = a.step && len0 + 1 <= a.capacity ? len0 + 1 : len0;
+  const int n_ps = a.n_split;
+  const int tiles = (len + kTile - 1) / kTile;
+  const int count = tiles > split ? (tiles - split + n_ps - 1) / n_ps : 0;     // this split's tiles
+  const int wcount = count > wave ? (count - wave + kStreamWaves - 1) / kStreamWaves : 0;   // this wave's
+  // a decode step: the wave whose tiles include the new token's waits for the append role
+  // before it requests that tile
+  int k_new = -1;
+  if constexpr (STEP) {
+    if (len == len0 + 1) {
+      const int dt = len0 / kTile - split;
+      if (dt >= 0 && dt % n_ps == 0 && (dt / n_ps) % kStreamWaves == wave) k_new = (dt / n_ps) / kStreamWaves;
+    }
+  }
+  const int bv = a.v_bits, chunks = a.chunks;
+  const StreamSlot geo = stream_slot(D, chunks, bv);
+  const size_t reg = size_t(s) * a.n_kv + hk;
+  const int64_t cap_tiles = a.capacity / kTile;
+  const uint8_t* kc = a.k_codes + reg * cap_tiles * chunks * kTile * 16;
+  const uint8_t* knp = reinterpret_cast<const uint8_t*>(a.k_norms + reg * cap_tiles * kMaxGroups * kTile);
+  const uint8_t* vnp = reinterpret_cast<const uint8_t*>(a.v_norms + reg * cap_tiles * kTile);
+  const uint8_t* vc = a.v_codes + reg * cap_tiles * D * 8 * bv;
+  uint8_t* const slot0 = s_ring0 + wave * SLOT;
+  uint8_t* const slot1 = s_ring1 + wave * SLOT;
+
+  // ---- a tile into a slot: direct loads, 1 KiB per wave each, lane l's 16 bytes to slot +
+  // base + 16 l.  Load i < chunks: K record unit u = 64 i + l (token u / chunks, chunk
+  // u % chunks of the chunk-major HBM layout, so the slot holds token-major records); then the
+  // 8 K norm planes; then the value units u (norms for u < 8, codes after), lanes past the last
+  // unit off.
+  const uint32_t inv_ch = (65536u + uint32_t(chunks) - 1u) / uint32_t(chunks > 0 ? chunks : 1);
+  auto load_tile = [&](int k, uint8_t* slot) {
+    const int tile = split + (wave + kStreamWaves * k) * n_ps;
+    const uint8_t* kt = kc + size_t(tile) * chunks * kTile * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < chunks) {
+        const uint32_t u = uint32_t(64 * i + lane), t = (u * inv_ch) >> 16, c = u - t * uint32_t(chunks);
+        stage16(kt + (c * kTile + t) * 16, slot + 1024 * i);
+      }
+    }
+    stage16(knp + size_t(tile) * (2 * kMaxGroups * kTile) + 16 * lane, slot + geo.kn_off);
+#pragma unroll
+    for (int i = 0; i < (D * 4 + 8 + 63) / 64; ++i) {   // up to 4 bits per value code
+      if (i < geo.v_loads) {
+        const int u = 64 * i + lane;
+        if (u < geo.v_units) {
+          const uint8_t* src = u < 8 ? vnp + size_t(tile) * (2 * kTile) + 16 * u
+                                     : vc + size_t(tile) * D * 8 * bv + 16 * (u - 8);
+          stage16(src, slot + geo.vn_off + 1024 * i);
+        }
+      }
+    }
+  };
+  auto wait_append = [&]() {        // one wave: bounded wait for the append role, then acquire
+    if (lane == 0) {
+      const int32_t* f = a.step_flag + (size_t(s) * a.n_kv + hk);
+      int i = 0;
+      for (; i < a.step_spin; ++i) {
+        if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == len0 + 1) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (i == a.step_spin && aa.status) atomicOr(aa.status, 2);   // gave up: reported
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  };
+
+  // ---- workgroup set-up and query prologue (the matrix-core pass's helpers, on the first 256
+  // threads).  Global reads in two rounds: what does not depend on the layout descriptor
+  // (descriptor, tables, query), then the rotation rows; the wave's first two tiles are
+  // requested between the two.
+  constexpr int NP = QShape<D>::NP, QI = QShape<D>::QI;
+  constexpr int PW = (kPairWords + kStreamThreads - 1) / kStreamThreads;
+  constexpr int SW = (kSingleHalves + kStreamThreads - 1) / kStreamThreads;
+  static_assert(BGTQ_LAYOUT_BYTES == 256 * 16, "one 16-byte piece of the layout per thread of the first 256");
+  HeadLayout* const Ls = reinterpret_cast<HeadLayout*>(s_pro);
+  float* const qc = reinterpret_cast<float*>(s_pro + BGTQ_LAYOUT_BYTES);                 // q' [coordinate][8 heads]
+  uint4* const qhi = reinterpret_cast<uint4*>(s_pro + BGTQ_LAYOUT_BYTES + 32 * D);       // [k-step][lane]
+  uint4* const qlo = qhi + 64 * kQRegSteps;                                            // [k-step][lane]
+  const HeadLayout* L = a.layouts + reg;
+  {
+    uint4 lw = uint4{0u, 0u, 0u, 0u};
+    if (tid < 256) lw = reinterpret_cast<const uint4*>(L)[tid];
+    uint2 pt[PW];
+    uint32_t st[SW];
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      if (tid + kStreamThreads * i < kPairWords) pt[i] = c_pair_hl[tid + kStreamThreads * i];
+#pragma unroll
+    for (int i = 0; i < SW; ++i)
+      if (tid + kStreamThreads * i < kSingleHalves) st[i] = c_single_hl[tid + kStreamThreads * i];
+    float x0[QI], x1[QI];
+    double fr = 0.0;
+    if (tid < 256) {
+      q_load<D, QT>(a, s, hk, tid, x0, x1);
+      fr = a.rope_theta > 0.0 ? a.inv_freq[tid % NP] : 0.0;
+    }
+    if (tid < 256) reinterpret_cast<uint4*>(Ls)[tid] = lw;
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      if (tid + kStreamThreads * i < kPairWords) reinterpret_cast<uint2*>(s_tab + kSTabPair)[tid + kStreamThreads * i] = pt[i];
+#pragma unroll
+    for (int i = 0; i < SW; ++i)
+      if (tid + kStreamThreads * i < kSingleHalves) reinterpret_cast<uint32_t*>(s_tab + kSTabSingle)[tid + kStreamThreads * i] = st[i];
+    if (tid < 256) {
+      qops_zero(qhi, qlo, qlo + 64 * kQRegSteps, KS, tid);
+      q_rope<D>(a, a.q_pos ? a.q_pos[s] : int64_t(len) - 1, fr, tid, x0, x1, qc);
+    }
+  }
+  if (wcount > 0 && k_new != 0) load_tile(0, slot0);
+  if (wcount > 1 && k_new != 1) load_tile(1, slot1);
+  lds_barrier();
+  const int nks = Ls->n_ksteps;
+  const uint32_t wmask = wide_ksteps(Ls, nks, lane);
+  const int nn = nks - __popc(wmask);               // narrow k-steps
+  // per k-step (kernel order: narrow ones first) and lane group j: x = byte offset of the
+  // window's first record dword, y = shift | 2w << 8 | 4w << 16 | 6w << 24, z = byte offset of
+  // the width's pair table (w <= 5), w = byte offset of its single table | w << 16 | class << 20 |
+  // first group << 24 | second group << 28 (class 0: every segment of the k-step at most 4 bits
+  // wide, 1: at most 5, 2: wider, decoded one code per lookup; the groups name the K norm planes
+  // of output columns 0-7 and 8-15)
+  for (int i = tid; i < 4 * nks; i += kStreamThreads) {
+    const int ks = i >> 2;
+    const uint32_t seg = Ls->seg[i];
+    const uint32_t o = seg & 0xffffu, w = (seg >> 16) & 15u;
+    uint32_t wmax = 0;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) wmax = max(wmax, (Ls->seg[4 * ks + sl] >> 16) & 15u);
+    const uint32_t kg = Ls->kgroups[ks];
+    const uint32_t tbp = w <= 5 ? uint32_t(kSTabPair + 8 * pair_base(int(w))) : 0u;
+    const uint32_t tbs = uint32_t(kSTabSingle + 4 * single_base(int(w)));
+    s_kd[4 * kperm_of(wmask, nn, ks) + (i & 3)] =
+        uint4{4u * (o >> 5), (o & 31u) | (2u * w) << 8 | (4u * w) << 16 | (6u * w) << 24, tbp,
+              tbs | w << 16 | seg_class(wmax) << 20 | (kg & 7u) << 24 | ((kg >> 8) & 7u) << 28};
+  }
+  if (a.givens) qops_givens_rotate(a, Ls, qc, tid, 256);   // every thread: it holds the barriers
+  if (tid < 256) {
+    if (a.givens) qops_scatter_rotated<true>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlo + 64 * kQRegSteps);
+    else qops_scatter<D, true>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlo + 64 * kQRegSteps);
+  }
+  lds_barrier();
+
+  // ---- per-lane constants
+  const uint32_t rec = uint32_t(16 * chunks);
+  const uint32_t krow = uint32_t(8 * (n >> 2) + (n & 3)) * rec;      // token 8 (n / 4) + n % 4, row block 0
+  const uint32_t kr1 = 4u * rec, kr2 = 32u * rec, kr3 = 36u * rec;   // row blocks 1..3: + 4, 32, 36 tokens
+  const uint32_t nsh = n < 8 ? 24u : 28u;                            // the lane's norm group field of d.w
+  const uint32_t knb = uint32_t(geo.kn_off + 2 * 8 * j);             // tokens 8 j .. 8 j + 7 of a norm plane
+  // value windows: coordinate 16 mt + n, tokens 32 b + 8 j .. + 7: bits (32 b + 8 j) b_v of the
+  // coordinate's segment of 8 b_v bytes
+  const uint32_t vwin = uint32_t(geo.vc_off + n * 8 * bv + 4 * ((8 * j * bv) >> 5));
+  const uint32_t vctl = uint32_t((8 * j * bv) & 31) | (2u * bv) << 8 | (4u * bv) << 16 | (6u * bv) << 24;
+  const uint32_t vmt = uint32_t(16 * 8 * bv);                        // bytes between M-tiles
+  const uint32_t vtb = bv <= 5 ? uint32_t(kSTabPair + 8 * pair_base(bv)) : uint32_t(kSTabSingle + 4 * single_base(bv));
+  const uint32_t vcls = seg_class(uint32_t(bv));
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.0f;
+  const bool real_col = n < a.group;
+
+  auto ld32 = [](const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); };
+
+  // ---- one tile from its slot: logits (4 row blocks per k-step), online softmax, P V.  Within a
+  // k-step the four row blocks' reads are issued together (the k-step's class is uniform, so the
+  // decode form is chosen once per k-step), and the next k-step's descriptor and B operands are
+  // requested before this one's lookups.
+  auto process_tile = [&](int k, const uint8_t* slot) {
+    const int tile = split + (wave + kStreamWaves * k) * n_ps;
+    const int valid = len - tile * kTile < kTile ? len - tile * kTile : kTile;
+    f32x4 S[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kw = slot + krow;
+    uint4 dn = s_kd[j];
+    uint4 qan = qhi[lane], qbn = qlo[lane];
+    for (int ks = 0; ks < nks; ++ks) {
+      const uint4 d = dn;
+      const uint4 qa = qan, qb = qbn;
+      if (ks + 1 < nks) {
+        dn = s_kd[4 * (ks + 1) + j];
+        qan = qhi[64 * (ks + 1) + lane];
+        qbn = qlo[64 * (ks + 1) + lane];
+      }
+      const uint32_t cls = (__builtin_amdgcn_readfirstlane(d.w) >> 20) & 3u;   // the same for every lane group
+      const uint8_t* np = slot + knb + 128u * ((d.w >> nsh) & 7u);
+      const uint4 n01 = *reinterpret_cast<const uint4*>(np);          // row blocks 0, 1
+      const uint4 n23 = *reinterpret_cast<const uint4*>(np + 64);     // row blocks 2, 3
+      const uint8_t* kb = kw + d.x;
+      const uint32_t w2 = d.y >> 8, o2 = d.y >> 16, o3 = d.y >> 24;   // the field extracts use bits 4:0
+      u32x4 A1[4], A2[4];
+      if (cls == 0u) {
+        uint32_t wa[4], wb[4];
+        wa[0] = ld32(kb); wb[0] = ld32(kb + 4);
+        wa[1] = ld32(kb + kr1); wb[1] = ld32(kb + kr1 + 4);
+        wa[2] = ld32(kb + kr2); wb[2] = ld32(kb + kr2 + 4);
+        wa[3] = ld32(kb + kr3); wb[3] = ld32(kb + kr3 + 4);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) dec8_pairs(win32(wa[rb], wb[rb], d.y), w2, w2, o2, o3, d.z, s_tab, A1[rb], A2[rb]);
+      } else {
+        uint32_t wa[4], wb[4], wc[4];
+        const uint32_t ro[4] = {0u, kr1, kr2, kr3};
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          wa[rb] = ld32(kb + ro[rb]);
+          wb[rb] = ld32(kb + ro[rb] + 4);
+          wc[rb] = ld32(kb + ro[rb] + 8);
+        }
+        if (cls == 1u) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            dec8_pairs5(win32(wa[rb], wb[rb], d.y), win32(wb[rb], wc[rb], d.y), w2, w2, o2, o3, d.z, s_tab, A1[rb],
+                        A2[rb]);
+        } else {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            dec8_singles(win32(wa[rb], wb[rb], d.y), win32(wb[rb], wc[rb], d.y), (d.w >> 16) & 15u, d.w & 0xffffu,
+                         s_tab, A1[rb], A2[rb]);
+        }
+      }
+      const f16x8 B1h = bdup(qa.x, qa.y), B1l = bdup(qa.z, qa.w), B2h = bdup(qb.x, qb.y), B2l = bdup(qb.z, qb.w);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const f16x8 a1 = __builtin_bit_cast(f16x8, A1[rb]), a2 = __builtin_bit_cast(f16x8, A2[rb]);
+        f32x4 T = {0.f, 0.f, 0.f, 0.f};
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, B1h, T, 0, 0, 0);
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, B2h, T, 0, 0, 0);
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, B1l, T, 0, 0, 0);
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, B2l, T, 0, 0, 0);
+        const uint4& nq = rb < 2 ? n01 : n23;
+        const f16x4 nv = __builtin_bit_cast(f16x4, (rb & 1) ? uint2{nq.z, nq.w} : uint2{nq.x, nq.y});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[rb][r] = fmaf(T[r], float(nv[r]), S[rb][r]);
+      }
+    }
+
+    // online softmax (base 2).  Head c = column c + column c + 8 (row rotation by 8, so both
+    // lanes hold the head's logit); lane (c, j) holds tokens 32 (rb / 2) + 8 j + 4 (rb % 2) + r
+    // of row block rb.
+    float v[4][4];
+    float lm = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sr = S[rb][r];
+        const float other = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sr), 0x128, 0xf, 0xf, false));
+        float x = sr + other;
+        if (32 * (rb >> 1) + 8 * j + 4 * (rb & 1) + r >= valid) x = -INFINITY;
+        v[rb][r] = x;
+        lm = fmaxf(lm, x);
+      }
+    }
+    if (a.logits && real_col) {
+      float* lg = a.logits + (int64_t(s) * a.n_q + hk * a.group + n) * a.capacity + int64_t(tile) * kTile + 8 * j;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 32 * (rb >> 1) + 4 * (rb & 1) + r;
+          if (t + 8 * j < valid) lg[t] = v[rb][r] * kLn2;
+        }
+    }
+    lm = fmaxf(lm, __shfl_xor(lm, 16));
+    lm = fmaxf(lm, __shfl_xor(lm, 32));
+    const float m_new = fmaxf(m_run, lm);            // finite: every tile has a valid token
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[rb][r] = __builtin_amdgcn_exp2f(v[rb][r] - m_new);
+        psum += v[rb][r];
+      }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+    }
+    // P V: block b (tokens 32 b ..), k slot 8 j + e = token 32 b + 8 j + e: row block 2 b
+    // (e < 4) and 2 b + 1 (e >= 4); P n_v in fp16.  The M-tiles' windows and lookups are
+    // issued together.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (32 * b < valid) {
+        const f16x8 vn = *reinterpret_cast<const f16x8*>(slot + geo.vn_off + 2 * (32 * b + 8 * j));
+        f16x8 P;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) P[e] = (_Float16)(v[2 * b + (e >> 2)][e & 3] * float(vn[e]));
+        if (valid < kTile) {       // slots past the length: p is 0, their value norm may be any bits
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (32 * b + 8 * j + e >= valid) P[e] = (_Float16)0.0f;
+        }
+        const u32x4 pw = __builtin_bit_cast(u32x4, P);
+        const f16x8 B1 = bdup(pw[0], pw[1]), B2 = bdup(pw[2], pw[3]);
+        const uint8_t* vb = slot + vwin + uint32_t(4 * b * bv);
+        u32x4 VA1[MT], VA2[MT];
+        if (vcls == 0u) {
+          uint32_t wa[MT], wb[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            wa[mt] = ld32(vb + mt * vmt);
+            wb[mt] = ld32(vb + mt * vmt + 4);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            dec8_pairs(win32(wa[mt], wb[mt], vctl), vctl >> 8, vctl >> 8, vctl >> 16, vctl >> 24, vtb, s_tab, VA1[mt],
+                       VA2[mt]);
+        } else {
+          uint32_t wa[MT], wb[MT], wc[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            wa[mt] = ld32(vb + mt * vmt);
+            wb[mt] = ld32(vb + mt * vmt + 4);
+            wc[mt] = ld32(vb + mt * vmt + 8);
+          }
+          if (vcls == 1u) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              dec8_pairs5(win32(wa[mt], wb[mt], vctl), win32(wb[mt], wc[mt], vctl), vctl >> 8, vctl >> 8, vctl >> 16,
+                          vctl >> 24, vtb, s_tab, VA1[mt], VA2[mt]);
+          } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              dec8_singles(win32(wa[mt], wb[mt], vctl), win32(wb[mt], wc[mt], vctl), uint32_t(bv), vtb, s_tab, VA1[mt],
+                           VA2[mt]);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA1[mt]), B1, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA2[mt]), B2, acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- the wave's tiles, two slots: tile k in slot k % 2.  Tile m is requested in the prologue
+  // (m < 2), once the wave has read tile m - 2 out of the same slot, or, for the new token's
+  // tile of a decode step, after the wait for the append role.  The waits for a slot's loads are
+  // explicit: with tile k + 1 requested before tile k is processed, tile k is complete once at
+  // most `ni` (tile k + 1's load count) vector memory operations are outstanding.
+  const int ni = chunks + 1 + geo.v_loads;
+  auto wait_tile = [&](int k) {
+    const bool next = k + 1 < wcount && !(STEP && (k + 1 == k_new || k == k_new));
+    if (!next) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      switch (ni) {     // the count is an immediate of the instruction
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+        case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      }
+    }
+  };
+  for (int k = 0; k < wcount; ++k) {
+    uint8_t* const slot = (k & 1) ? slot1 : slot0;
+    if (STEP && k == k_new) {      // the new token's tile: requested after the append role's release
+      wait_append();
+      load_tile(k, slot);
+    }
+    wait_tile(k);
+    process_tile(k, slot);
+    if (k + 2 < wcount && !(STEP && k + 2 == k_new)) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");     // every read of the slot done
+      load_tile(k + 2, slot);
+    }
+  }
+
+  // ---- merge of the 8 waves: running maxima and sums through LDS, then each wave's
+  // accumulator scaled to the common maximum, summed in wave order.  Lane (c, j) holds head
+  // c % 8, coordinates 16 mt + 4 j + r.  The lane indices are taken afresh (opaque copies).
+  int le = lane;
+  asm volatile("" : "+v"(le));
+  const int ne = le & 15, je = le >> 4;
+  float l = l_part;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float* mws = s_ml;                               // [8 waves][8 heads]
+  float* lws = s_ml + 8 * kStreamWaves;
+  if (je == 0 && ne < 8) {
+    mws[8 * wave + ne] = m_run;
+    lws[8 * wave + ne] = l;
+  }
+  __syncthreads();             // every wave is past its tiles: ring 0 is free for the merge
+  float mmax = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kStreamWaves; ++w) mmax = fmaxf(mmax, mws[8 * w + (ne & 7)]);
+  const float sc = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mmax);
+  float* accw = reinterpret_cast<float*>(s_ring0);  // [8 waves][8 heads][D]
+  static_assert(kStreamWaves * 8 * D * 4 <= kStreamWaves * SLOT, "the merge fits ring 0");
+  if (ne < 8) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<float4*>(accw + (8 * wave + ne) * D + 16 * mt + 4 * je) =
+          float4{acc[mt][0] * sc, acc[mt][1] * sc, acc[mt][2] * sc, acc[mt][3] * sc};
+  }
+  __syncthreads();
+  for (int i = tid; i < a.group * D; i += kStreamThreads) {
+    const int h = i / D, r = i - h * D;
+    float x = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) x += accw[(8 * w + h) * D + r];
+    const int64_t row = (int64_t(s) * a.n_q + hk * a.group + h) * a.n_split + split;
+    a.partial[row * D + r] = x;
+  }
+  if (tid < a.group) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) mx = fmaxf(mx, mws[8 * w + tid]);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) {
+      const float mw = mws[8 * w + tid];
+      lsum += mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mx) * lws[8 * w + tid];
+    }
+    const int64_t row = (int64_t(s) * a.n_q + hk * a.group + tid) * a.n_split + split;
+    a.part_ml[row] = float2{mx, lsum};
+  }
+}

@@ -23,6 +23,8 @@ __constant__ float c_cen[kMaxBits][256];
 __constant__ double c_dgain[kMaxBits];
 __constant__ uint32_t c_pair[kPairWords];
 __constant__ uint16_t c_single[kSingleHalves];
+__constant__ uint2 c_pair_hl[kPairWords];
+__constant__ uint32_t c_single_hl[kSingleHalves];
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -1119,10 +1121,13 @@ constexpr size_t kStepAppendLds =
     size_t(kAppendThrFloats) * 4 + sizeof(HeadLayout) +
     4 * size_t(BGTQ_MAX_HEAD_DIM + 2 * BGTQ_MAX_HEAD_DIM + 16 + BGTQ_MAX_HEAD_DIM + 16 + kMaxGroups + 1 + kMaxRecordDwords);
 
+// Every thread of the workgroup calls it (it holds the barriers); threads from 256 on take
+// part in the barriers only.
 template <bool WIN, bool GIV>
 __device__ void step_append_role(const AppendArgs& a, int32_t* flags, int s, int hk, uint8_t* lds) {
   constexpr int DM = BGTQ_MAX_HEAD_DIM;
   const int t = threadIdx.x, d = a.d, bv = a.v_bits;
+  const bool act = t < 256;
   float* thr = reinterpret_cast<float*>(lds);                                   // [8][255]
   HeadLayout* Lp = reinterpret_cast<HeadLayout*>(lds + kAppendThrFloats * 4);
   float* ko = reinterpret_cast<float*>(Lp + 1);        // key, original order
@@ -1139,22 +1144,24 @@ __device__ void step_append_role(const AppendArgs& a, int32_t* flags, int s, int
     return a.kv_bf16 ? load_f(reinterpret_cast<const uint16_t*>(base), i) : load_f(reinterpret_cast<const float*>(base), i);
   };
   // ---- first round of reads: none depends on the length or on the layout
-  const uint4 lw = reinterpret_cast<const uint4*>(a.layouts + reg)[t];
+  const uint4 lw = act ? reinterpret_cast<const uint4*>(a.layouts + reg)[t] : uint4{0u, 0u, 0u, 0u};
   const float kval = t < d ? ld(kin, t) : 0.0f;
   const float vval = t < d ? ld(vin, t) : 0.0f;
   float tv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) tv[i] = t + 256 * i < kAppendThrFloats ? (&c_thr[0][0])[t + 256 * i] : 0.0f;
+  for (int i = 0; i < 8; ++i) tv[i] = act && t + 256 * i < kAppendThrFloats ? (&c_thr[0][0])[t + 256 * i] : 0.0f;
   const int64_t len = a.lengths[s];
   __builtin_amdgcn_sched_barrier(0);
-  reinterpret_cast<uint4*>(Lp)[t] = lw;
-  ko[t] = kval;
-  xv[t] = vval;
-  if (t < 16) xv[DM + t] = 0.0f;
+  if (act) {
+    reinterpret_cast<uint4*>(Lp)[t] = lw;
+    ko[t] = kval;
+    xv[t] = vval;
+    if (t < 16) xv[DM + t] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (t + 256 * i < kAppendThrFloats) thr[t + 256 * i] = tv[i];
-  if (t < kMaxRecordDwords) kw[t] = 0u;
+    for (int i = 0; i < 8; ++i)
+      if (t + 256 * i < kAppendThrFloats) thr[t + 256 * i] = tv[i];
+    if (t < kMaxRecordDwords) kw[t] = 0u;
+  }
   __syncthreads();
   if (len + 1 > a.capacity) {                     // nothing appended; the splits do not wait
     if (t == 0 && hk == 0 && a.status) atomicOr(a.status, 1);
@@ -1177,7 +1184,8 @@ __device__ void step_append_role(const AppendArgs& a, int32_t* flags, int s, int
   int mmax = 0;
   for (int g = 0; g < ng; ++g) mmax = L.g_m[g] > mmax ? L.g_m[g] : mmax;
   mmax = (mmax + 15) & ~15;
-  for (int i = t; i < 2 * DM + 16; i += 256) xk[i] = i < d_eff ? ko[L.perm[i]] : 0.0f;
+  if (act)
+    for (int i = t; i < 2 * DM + 16; i += 256) xk[i] = i < d_eff ? ko[L.perm[i]] : 0.0f;
   __syncthreads();
   // rotations: value row r < d, key position r - d; rows t and t + 256
   float acc[2] = {0.0f, 0.0f};
@@ -1233,7 +1241,8 @@ __device__ void step_append_role(const AppendArgs& a, int32_t* flags, int s, int
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = t + 256 * j;
-    if (r < d) {
+    if (!act) {
+    } else if (r < d) {
       const float nv = nrm[kMaxGroups];
       const uint32_t code = nv != 0.0f ? code_of(thr + (bv - 1) * 255, bv, (acc[j] / nv) * sqrtf(float(d))) : 0u;
       vseg[r * 2 * bv + vw] = (old0 & ~(vmask << vsh)) | (code << vsh);
@@ -1401,9 +1410,9 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 
   for (int i = tid; i < 510; i += blockDim.x) {
     const int w = 31 - __clz(i + 2);
-    cbk[i] = f16_bits_to_f32(f32_to_f16_bits(c_cen[w - 1][i + 2 - (1 << w)]));   // fp16 levels
+    cbk[i] = c_cen[w - 1][i + 2 - (1 << w)];   // fp32 levels
   }
-  for (int i = tid; i < (1 << bv); i += blockDim.x) cbv[i] = f16_bits_to_f32(f32_to_f16_bits(c_cen[bv - 1][i]));
+  for (int i = tid; i < (1 << bv); i += blockDim.x) cbv[i] = c_cen[bv - 1][i];
   __syncthreads();
 
   cLayout* L = (cLayout*)(a.layouts + int64_t(s) * a.n_kv + hk);
@@ -1596,7 +1605,7 @@ __host__ __device__ inline TcStage tc_stage(int D, int chunks, int bv) {
   return g;
 }
 // Workgroup LDS (bytes): tables, k-step descriptors, P operands, softmax exchange, ring.
-constexpr int kTcTab = (4 * kPairWords + 2 * kSingleHalves + 15) & ~15;   // 6480
+constexpr int kTcTab = (8 * kPairWords + 4 * kSingleHalves + 15) & ~15;   // 12960: hi/lo pairs, hi | lo singles
 constexpr int kTcDesc = kTcTab;                                       // uint4 [kMaxKSteps][4]
 constexpr int kTcNorm = kTcDesc + 16 * 4 * kMaxKSteps;                // uint32 [kMaxKSteps]
 constexpr int kTcP = (kTcNorm + 4 * kMaxKSteps + 15) & ~15;           // [2][64][16 B]
@@ -1624,15 +1633,19 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const uint32_t*>(base + off);
 }
 
-// Eight consecutive codes of width w starting at bit sh of the window d2:d1:d0, as fp16
-// levels (low half = first code).  tb = byte offset of the width's table in LDS.
-__device__ __forceinline__ u32x4 decode8(uint32_t d0, uint32_t d1, uint32_t d2, int sh, int w, const uint8_t* lds,
-                                         uint32_t tb) {
-  u32x4 r;
+// Eight consecutive codes of width w starting at bit sh of the window d2:d1:d0, as fp16 levels
+// hi (h) and lo (l), hi + lo = the fp32 level to about 2^-22 (low half = first code).  tb = byte
+// offset of the width's table in LDS: the hi/lo pair table (w <= 5) or the hi | lo single table.
+__device__ __forceinline__ void decode8(uint32_t d0, uint32_t d1, uint32_t d2, int sh, int w, const uint8_t* lds,
+                                        uint32_t tb, u32x4& h, u32x4& l) {
   if (w <= 4) {      // 8 codes fit one 32-bit window
     const uint32_t x = __builtin_amdgcn_alignbit(d1, d0, sh);
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) r[e2] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, 2 * e2 * w, 2 * w));
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, 2 * e2 * w, 2 * w));
+      h[e2] = v.x;
+      l[e2] = v.y;
+    }
   } else {
     const uint32_t lo = __builtin_amdgcn_alignbit(d1, d0, sh);
     const uint32_t hi = __builtin_amdgcn_alignbit(d2, d1, sh);
@@ -1640,40 +1653,41 @@ __device__ __forceinline__ u32x4 decode8(uint32_t d0, uint32_t d1, uint32_t d2, 
     if (w == 5) {
       const uint32_t mask = 0x3ffu;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) r[e2] = lds_u32(lds, tb + 4 * (uint32_t(x >> (10 * e2)) & mask));
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(lds + tb + 8 * (uint32_t(x >> (10 * e2)) & mask));
+        h[e2] = v.x;
+        l[e2] = v.y;
+      }
     } else {
       const uint32_t mask = (1u << w) - 1u;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const uint32_t c0 = uint32_t(x >> (2 * e2 * w)) & mask;
         const uint32_t c1 = uint32_t(x >> ((2 * e2 + 1) * w)) & mask;
-        const uint32_t h0 = *reinterpret_cast<const uint16_t*>(lds + tb + 2 * c0);
-        const uint32_t h1 = *reinterpret_cast<const uint16_t*>(lds + tb + 2 * c1);
-        r[e2] = h0 | (h1 << 16);
+        const uint32_t v0 = lds_u32(lds, tb + 4 * c0), v1 = lds_u32(lds, tb + 4 * c1);
+        h[e2] = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
+        l[e2] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
       }
     }
   }
-  return r;
 }
 
 // Eight consecutive codes of any width w (1..8) starting at bit sh of the window d2:d1:d0, as
-// fp16 levels from the width's single-level table at byte offset tb (low half = first code).
-// One instruction sequence for every width, so lanes whose segments differ in width run it
-// together instead of one width class after another.
-__device__ __forceinline__ u32x4 decode8_any(uint32_t d0, uint32_t d1, uint32_t d2, int sh, int w,
-                                             const uint8_t* lds, uint32_t tb) {
+// fp16 levels hi and lo from the width's hi | lo single table at byte offset tb (low half =
+// first code).  One instruction sequence for every width, so lanes whose segments differ in
+// width run it together instead of one width class after another.
+__device__ __forceinline__ void decode8_any(uint32_t d0, uint32_t d1, uint32_t d2, int sh, int w, const uint8_t* lds,
+                                            uint32_t tb, u32x4& h, u32x4& l) {
   const uint64_t x = (uint64_t(__builtin_amdgcn_alignbit(d2, d1, sh)) << 32) | __builtin_amdgcn_alignbit(d1, d0, sh);
   const uint32_t mask = (1u << w) - 1u;
-  u32x4 r;
 #pragma unroll
   for (int e2 = 0; e2 < 4; ++e2) {
     const uint32_t c0 = uint32_t(x >> (2 * e2 * w)) & mask;
     const uint32_t c1 = uint32_t(x >> ((2 * e2 + 1) * w)) & mask;
-    const uint32_t h0 = *reinterpret_cast<const uint16_t*>(lds + tb + 2 * c0);
-    const uint32_t h1 = *reinterpret_cast<const uint16_t*>(lds + tb + 2 * c1);
-    r[e2] = h0 | (h1 << 16);
+    const uint32_t v0 = lds_u32(lds, tb + 4 * c0), v1 = lds_u32(lds, tb + 4 * c1);
+    h[e2] = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
+    l[e2] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
   }
-  return r;
 }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
@@ -1771,11 +1785,26 @@ __device__ __forceinline__ void qops_zero(uint4* qhi, uint4* qlo, uint4* qlate, 
 // rotation row in two halves and covers all 8 heads, then each thread scatters 4 heads.
 // qc = q' [coordinate][8 heads] and the layout copy Ls are in LDS.
 // q'' of storage position p for heads 4 kh .. 4 kh + 3 (v) into the B operand slots of its
-// k-step, fp16 high part and remainder; heads >= G stay zero
+// k-step, fp16 high part and remainder; heads >= G stay zero.  IL: the streamed pass's layout,
+// qhi = k indices e = 0..3 of a lane's 8, qlo = e = 4..7, each as 4 high parts then 4 remainders.
+template <bool IL = false>
 __device__ __forceinline__ void qops_put(const HeadLayout* Ls, uint32_t wmask, int nn, int p, int kh, int G,
                                          const float (&v)[4], uint4* qhi, uint4* qlo, uint4* qlate) {
   const int kx = Ls->kpos[p], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm_of(wmask, nn, ks0);
   const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks0 + jj] >> 28) & 1u);
+  if constexpr (IL) {
+    uint16_t* q16 = reinterpret_cast<uint16_t*>((e < 4 ? qhi : qlo) + 64 * ks);
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const int h = 4 * kh + hh;
+      if (h < G) {
+        const uint16_t hi = f32_to_f16_bits(v[hh]);
+        q16[(lb + h) * 8 + (e & 3)] = hi;
+        q16[(lb + h) * 8 + 4 + (e & 3)] = f32_to_f16_bits(v[hh] - f16_bits_to_f32(hi));
+      }
+    }
+    return;
+  }
   uint16_t* h16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qhi + 64 * ks : qlate + 128 * (ks - kQRegSteps));
   uint16_t* l16 = reinterpret_cast<uint16_t*>(ks < kQRegSteps ? qlo + 64 * ks : qlate + 128 * (ks - kQRegSteps) + 64);
 #pragma unroll
@@ -1789,7 +1818,7 @@ __device__ __forceinline__ void qops_put(const HeadLayout* Ls, uint32_t wmask, i
   }
 }
 
-template <int D>
+template <int D, bool IL = false>
 __device__ __forceinline__ void qops_scatter(const DecodeArgs& a, const HeadLayout* Ls, const float* qc, uint32_t wmask,
                                              int nn, int tid, uint4* qhi, uint4* qlo, uint4* qlate) {
   constexpr int RR = QShape<D>::RR;
@@ -1841,7 +1870,7 @@ __device__ __forceinline__ void qops_scatter(const DecodeArgs& a, const HeadLayo
       const float other = __shfl_xor(give, 1);
       v[e] = (kh == 0 ? mine + other : other + mine) * (kscale / sqrtf(float(m)));
     }
-    if (p < d_eff) qops_put(Ls, wmask, nn, p, kh, G, v, qhi, qlo, qlate);
+    if (p < d_eff) qops_put<IL>(Ls, wmask, nn, p, kh, G, v, qhi, qlo, qlate);
   }
 }
 
@@ -1884,6 +1913,7 @@ __device__ __forceinline__ void qops_givens_rotate(const DecodeArgs& a, const He
 
 // B operands from q' already rotated into the group frames (qops_givens_rotate):
 // q''_p = q'[perm[p]] * softmax_scale * log2(e) / sqrt(m); 256 threads, as qops_scatter.
+template <bool IL = false>
 __device__ __forceinline__ void qops_scatter_rotated(const DecodeArgs& a, const HeadLayout* Ls, const float* qc,
                                                      uint32_t wmask, int nn, int tid, uint4* qhi, uint4* qlo,
                                                      uint4* qlate) {
@@ -1895,7 +1925,7 @@ __device__ __forceinline__ void qops_scatter_rotated(const DecodeArgs& a, const 
       const float f = kscale / sqrtf(float(Ls->g_m[Ls->group[p]]));
       const float4 x = *reinterpret_cast<const float4*>(qc + 8 * Ls->perm[p] + 4 * kh);
       const float v[4] = {x.x * f, x.y * f, x.z * f, x.w * f};
-      qops_put(Ls, wmask, nn, p, kh, G, v, qhi, qlo, qlate);
+      qops_put<IL>(Ls, wmask, nn, p, kh, G, v, qhi, qlo, qlate);
     }
   }
 }
@@ -2034,7 +2064,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // that does not depend on the layout descriptor (descriptor, level tables, query, first
   // tile), then the rotation rows.
   constexpr int NP = QShape<D>::NP, QI = QShape<D>::QI;
-  constexpr int PW = (kPairWords + 255) / 256, SW = (kSingleHalves + 255) / 256;
+  constexpr int PW = (kPairWords + 255) / 256, SW = (kSingleHalves + 255) / 256;   // table pieces per thread
   static_assert(BGTQ_LAYOUT_BYTES == 256 * 16, "one 16-byte piece of the layout per thread");
   uint8_t* const pro = lds + kTcRing;             // aliases the ring, first written in the loop
   HeadLayout* const Ls = reinterpret_cast<HeadLayout*>(pro);
@@ -2047,14 +2077,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     // a packed split's first tile depends on neither the length nor the layout: requested first
     if (!win) load_tile(0);
     const uint4 lw = reinterpret_cast<const uint4*>(L)[tid];
-    uint32_t pt[PW];
-    uint16_t st[SW];
+    uint2 pt[PW];
+    uint32_t st[SW];
 #pragma unroll
     for (int i = 0; i < PW; ++i)
-      if (tid + 256 * i < kPairWords) pt[i] = c_pair[tid + 256 * i];
+      if (tid + 256 * i < kPairWords) pt[i] = c_pair_hl[tid + 256 * i];
 #pragma unroll
     for (int i = 0; i < SW; ++i)
-      if (tid + 256 * i < kSingleHalves) st[i] = c_single[tid + 256 * i];
+      if (tid + 256 * i < kSingleHalves) st[i] = c_single_hl[tid + 256 * i];
     float x0[QI], x1[QI];
     double fr = 0.0;
     {
@@ -2063,11 +2093,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
     if (win && count > 0) load_tile(0);
     reinterpret_cast<uint4*>(Ls)[tid] = lw;
-    uint32_t* ptab = reinterpret_cast<uint32_t*>(lds);
+    uint2* ptab = reinterpret_cast<uint2*>(lds);
 #pragma unroll
     for (int i = 0; i < PW; ++i)
       if (tid + 256 * i < kPairWords) ptab[tid + 256 * i] = pt[i];
-    uint16_t* stab = reinterpret_cast<uint16_t*>(lds + 4 * kPairWords);
+    uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 8 * kPairWords);
 #pragma unroll
     for (int i = 0; i < SW; ++i)
       if (tid + 256 * i < kSingleHalves) stab[tid + 256 * i] = st[i];
@@ -2095,8 +2125,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     for (int i = tid; i < nseg; i += 256) {
       const uint32_t seg = i < 4 * nks ? Ls->seg[i] : (1u << 16);
       const uint32_t o = seg & 0xffffu, w = (seg >> 16) & 15u;
-      const uint32_t tbp = 4u * uint32_t(pair_base(int(w)));
-      const uint32_t tbs = 4u * kPairWords + 2u * uint32_t(single_base(int(w)));
+      const uint32_t tbp = 8u * uint32_t(pair_base(int(w)));
+      const uint32_t tbs = 8u * kPairWords + 4u * uint32_t(single_base(int(w)));
       const uint32_t fast = w <= 4 ? ((o & 31u) | ((2u * w) << 8) | (tbp << 16)) : (2u << 8);
       kd[i < 4 * nks ? 4 * kperm_of(wmask, nn, i >> 2) + (i & 3) : i] =
           uint4{4u * (o >> 5), fast, (o & 31u) | (w << 8) | (tbs << 16), 0u};
@@ -2156,7 +2186,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const uint32_t vrow = uint32_t(geo.v_off + n * 8 * bv);
   const uint32_t vw0 = uint32_t(4 * ((8 * j * bv) >> 5)), vsh0 = uint32_t((8 * j * bv) & 31);
   const uint32_t vw1 = uint32_t(4 * (((32 + 8 * j) * bv) >> 5)), vsh1 = uint32_t(((32 + 8 * j) * bv) & 31);
-  const uint32_t vtb = bv <= 5 ? 4u * uint32_t(pair_base(bv)) : 4u * kPairWords + 2u * uint32_t(single_base(bv));
+  const uint32_t vtb = bv <= 5 ? 8u * uint32_t(pair_base(bv)) : 8u * kPairWords + 4u * uint32_t(single_base(bv));
 
   f32x4 acc[MTV];
 #pragma unroll
@@ -2236,8 +2266,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         }
 #pragma unroll
         for (int mi = 0; mi < MTV; ++mi) {
-          const u32x4 raw = decode8(d0[mi], d1[mi], d2[mi], int(vsh), bv, lds, vtb);
-          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, raw), bpv, acc[mi], 0, 0, 0);
+          u32x4 vh, vl;
+          decode8(d0[mi], d1[mi], d2[mi], int(vsh), bv, lds, vtb, vh, vl);
+          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vh), bpv, acc[mi], 0, 0, 0);
+          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vl), bpv, acc[mi], 0, 0, 0);
         }
       }
     }
@@ -2288,11 +2320,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       // ---- logits of tokens 16 wave + n (A rows).  Pass A issues a chunk's window reads and
       // level lookups (k-steps narrower than 5 bits), pass B runs the matrix cores on them;
       // wide k-steps are decoded separately afterwards.
-      auto mfma_kstep = [&](const u32x4& raw, const f16x8& bh, const f16x8& bl, const f16x4& nv) {
-        const f16x8 A = __builtin_bit_cast(f16x8, raw);
+      auto mfma_kstep = [&](const u32x4& raw, const u32x4& rawl, const f16x8& bh, const f16x8& bl, const f16x4& nv) {
+        const f16x8 A = __builtin_bit_cast(f16x8, raw), Al = __builtin_bit_cast(f16x8, rawl);
         f32x4 T = {0.f, 0.f, 0.f, 0.f};
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, T, 0, 0, 0);
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, T, 0, 0, 0);
+        T = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, bh, T, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[r] = fmaf(T[r], float(nv[r]), S[r]);
       };
@@ -2301,7 +2334,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       auto narrow_chunk = [&](auto kc_c, auto kn_c) {
         constexpr int kc = decltype(kc_c)::value, KC = decltype(kn_c)::value;
         {
-          u32x4 raw[KC];
+          u32x4 raw[KC], rawl[KC];
           f16x4 nrm[KC];
           uint32_t wd0[KC], wd1[KC], ctl[KC];
 #pragma unroll
@@ -2317,14 +2350,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             const uint32_t x = __builtin_amdgcn_alignbit(wd1[q], wd0[q], ctl[q]);   // shift = ctl & 31
             const uint32_t w2 = ctl[q] >> 8;                                          // low 5 bits: 2w
             const uint32_t o4 = w2 << 1, o6 = w2 + o4, tb = ctl[q] >> 16;
-            raw[q][0] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, 0u, w2));
-            raw[q][1] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, w2, w2));
-            raw[q][2] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, o4, w2));
-            raw[q][3] = lds_u32(lds, tb + 4 * __builtin_amdgcn_ubfe(x, o6, w2));
+            const uint32_t idx[4] = {__builtin_amdgcn_ubfe(x, 0u, w2), __builtin_amdgcn_ubfe(x, w2, w2),
+                                     __builtin_amdgcn_ubfe(x, o4, w2), __builtin_amdgcn_ubfe(x, o6, w2)};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const uint2 v = *reinterpret_cast<const uint2*>(lds + tb + 8 * idx[e2]);
+              raw[q][e2] = v.x;
+              rawl[q][e2] = v.y;
+            }
           }
 #pragma unroll
           for (int q = 0; q < KC; ++q)
-            if (kc + q < nn) mfma_kstep(raw[q], qh[kc + q], __builtin_bit_cast(f16x8, qlo[(kc + q) * 64 + lane]), nrm[q]);
+            if (kc + q < nn)
+              mfma_kstep(raw[q], rawl[q], qh[kc + q], __builtin_bit_cast(f16x8, qlo[(kc + q) * 64 + lane]), nrm[q]);
         }
       };
       static_assert(kQRegSteps == 8, "chunks 4 + 2 + 2");
@@ -2340,8 +2378,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
           const uint32_t ka = krec + d.x;
           const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
           const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
-          mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16), qh[ks],
-                     __builtin_bit_cast(f16x8, qlo[ks * 64 + lane]), nv);
+          u32x4 ah, al;
+          decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16, ah, al);
+          mfma_kstep(ah, al, qh[ks], __builtin_bit_cast(f16x8, qlo[ks * 64 + lane]), nv);
         }
       }
       for (int ks = kQRegSteps; ks < nks; ++ks) {   // k-steps beyond the register-resident ones
@@ -2350,8 +2389,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         const uint32_t ka = krec + d.x;
         const uint32_t d0 = lds_u32(buf, ka), d1 = lds_u32(buf, ka + 4), d2 = lds_u32(buf, ka + 8);
         const f16x4 nv = *reinterpret_cast<const f16x4*>(buf + knb + ((knsel[ks] >> nsh) & 0xffffu));
-        mfma_kstep(decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16),
-                   __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + lane]),
+        u32x4 ah, al;
+        decode8_any(d0, d1, d2, int(d.z & 31u), w, lds, d.z >> 16, ah, al);
+        mfma_kstep(ah, al, __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + lane]),
                    __builtin_bit_cast(f16x8, qlate[(ks - kQRegSteps) * 128 + 64 + lane]), nv);
       }
 
@@ -2381,6 +2421,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     if (wave == 0 && je == 0) a.part_ml[row] = float2{m_run, lsm[ne] + lsm[8 + ne] + lsm[16 + ne] + lsm[24 + ne]};
   }
 }
+
+#include "decode_stream.h"
 
 // Merge the splits of one query head and undo the value rotation:
 // out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t], from the per-split
@@ -2550,7 +2592,17 @@ auto mfma_kernel(bool narrow, bool bf16, bool step) -> void (*)(DecodeArgs, Appe
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st, const AppendArgs* step = nullptr) {
   const dim3 grid(a.n_split + (step ? 1 : 0), a.n_kv, a.batch);
-  if (a.use_mfma) {
+  if (a.use_stream) {
+    if constexpr (D <= 128) {
+      const bool bf16 = q_dt == BGTQ_BF16;
+      void (*fn)(DecodeArgs, AppendArgs) =
+          step ? (bf16 ? k_decode_stream<D, uint16_t, true> : k_decode_stream<D, float, true>)
+               : (bf16 ? k_decode_stream<D, uint16_t, false> : k_decode_stream<D, float, false>);
+      hipLaunchKernelGGL(fn, grid, dim3(kStreamThreads), 0, st, a, step ? *step : AppendArgs{});
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (a.use_mfma) {
     int lds = tc_lds_bytes(D, a.chunks, a.v_bits);
     if (step && lds < int(kStepAppendLds)) lds = int(kStepAppendLds);
     const bool narrow = a.chunks <= 4 && a.v_bits <= 4, bf16 = q_dt == BGTQ_BF16;
@@ -2633,6 +2685,8 @@ hipError_t upload_tables(const Tables& t) {
   if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_dgain), t.dgain, sizeof(t.dgain));
   if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_pair), t.pair, sizeof(t.pair));
   if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_single), t.single, sizeof(t.single));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_pair_hl), t.pair_hl, sizeof(t.pair_hl));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(c_single_hl), t.single_hl, sizeof(t.single_hl));
   return e;
 }
 
@@ -2781,6 +2835,16 @@ int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma) {
   if (want < 1) want = 1;
   if (want > 1024) want = 1024;
   return int(want);
+}
+
+bool decode_stream_fits(int d, int chunks, int v_bits) { return stream_fits(d, chunks, v_bits); }
+
+int decode_stream_splits(int batch, int n_kv_heads) {
+  // one workgroup per compute unit: 256 over the (sequence, KV head) units, one of each unit's
+  // share left to a decode step's append role
+  const int64_t units = int64_t(batch) * n_kv_heads;
+  const int64_t base = 256 / units;
+  return base > 2 ? int(base - 1) : 1;
 }
 
 size_t decode_qrot_bytes(int batch, int n_kv_heads, int d) {

@@ -17,6 +17,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "bgtq_internal.h"
@@ -143,6 +144,30 @@ Tables build_tables() {
   for (int w = 1; w <= 8; ++w) {
     const int base = (1 << w) - 2;
     for (int c = 0; c < (1 << w); ++c) t.single[base + c] = h16(t.cen[w - 1][c]);
+  }
+  // hi + lo: the remainder cen - hi is exact in fp32 (hi is cen rounded to 11 bits), then rounded
+  // to fp16 once more
+  auto hl = [&](int w, int c) {
+    const float x = t.cen[w - 1][c];
+    const uint16_t hi = h16(x);
+    _Float16 hf;
+    std::memcpy(&hf, &hi, 2);
+    return std::pair<uint16_t, uint16_t>(hi, h16(x - float(hf)));
+  };
+  for (int w = 1; w <= 5; ++w) {
+    const int base = ((1 << (2 * w)) - 4) / 3;
+    for (int idx = 0; idx < (1 << (2 * w)); ++idx) {
+      const auto a = hl(w, idx & ((1 << w) - 1)), b = hl(w, idx >> w);
+      t.pair_hl[base + idx][0] = uint32_t(a.first) | uint32_t(b.first) << 16;
+      t.pair_hl[base + idx][1] = uint32_t(a.second) | uint32_t(b.second) << 16;
+    }
+  }
+  for (int w = 1; w <= 8; ++w) {
+    const int base = (1 << w) - 2;
+    for (int c = 0; c < (1 << w); ++c) {
+      const auto a = hl(w, c);
+      t.single_hl[base + c] = uint32_t(a.first) | uint32_t(a.second) << 16;
+    }
   }
   return t;
 }

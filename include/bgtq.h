@@ -357,16 +357,18 @@ bgtq_status bgtq_codebook(int bits, float* thresholds, float* centroids, double*
 /* Copy the frozen tables to the current device's constant memory (synchronous) and
  * look up the device's allocation-free scratch (bgtq_decode_step_noalloc).  The first
  * call in the process also reads the options' defaults from the environment:
- * BGTQ_DECODE_KERNEL=valu sets BGTQ_OPT_DECODE_KERNEL to 1, BGTQ_STEP_SPIN_LIMIT=n sets
+ * BGTQ_DECODE_KERNEL=valu (tiled) sets BGTQ_OPT_DECODE_KERNEL to 1 (2), BGTQ_STEP_SPIN_LIMIT=n sets
  * BGTQ_OPT_STEP_WAIT_LIMIT to n.  Nothing reads the environment afterwards. */
 bgtq_status bgtq_init(void);
 
 /* Process-wide options, for tests and diagnosis; every later call reads the value set
  * last.  Not meant to change while calls are in flight on other threads.
  *   BGTQ_OPT_DECODE_KERNEL    0 (default): the decode runs on the matrix cores when the
- *                             group size is <= 8, on the vector ALU otherwise; 1: always
- *                             on the vector ALU (then a cache with a window is refused:
- *                             UNSUPPORTED).
+ *                             group size is <= 8 (the streamed pass where it serves the
+ *                             cache geometry, the tiled one otherwise), on the vector ALU
+ *                             otherwise; 1: always on the vector ALU (then a cache with a
+ *                             window is refused: UNSUPPORTED); 2: matrix cores, always
+ *                             the tiled pass.
  *   BGTQ_OPT_STEP_WAIT_LIMIT  bound of a decode step's wait for its own append, in polls
  *                             of a few hundred cycles (default 1 << 22, about 0.2 s;
  *                             0: no wait, so the step reports through cache->status that

@@ -17,10 +17,9 @@ The Lloyd-Max conditions for N = 2^b cells with thresholds t_1 < ... < t_{N-1}
 They are solved here by Newton's method on the thresholds, started from the
 Panter-Dite companding guess t_k = sqrt(3) * Phi^{-1}(k/N).  The tables are
 then made exactly antisymmetric and rounded to fp32: the quantizer compares
-against the fp32 decision levels.  Reconstruction uses the fp32 levels rounded
-once more to fp16 (nearest-even), the precision in which the packed cache is
-decoded (reading: the pages fix no precision for the codebook; fp16 levels
-differ from the fp32 ones by at most 2^-11 relative).  D(b) is the MSE of
+against the fp32 decision levels, and reconstruction uses the fp32 centroids
+(the pages fix no precision for the codebook; levels16 gives the centroids
+rounded once more to fp16, which differ by at most 2^-11 relative).  D(b) is the MSE of
 the b-bit quantizer of N(0, 1); D(0) = 1 (a coordinate coded with zero bits is
 reconstructed as 0).  The allocator uses fl32(D(b)).
 """

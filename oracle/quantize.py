@@ -9,7 +9,7 @@ outside the pages): store the norm n = |x|; rotate with a fixed random
 orthogonal m x m matrix Pi; scale so that the coordinates are close to
 N(0, 1): z = (Pi x / n) * sqrt(m); code every coordinate with the b-bit
 Lloyd-Max quantizer of N(0, 1).  Reconstruction is n * Pi^T (C_b[code] / sqrt(m)),
-with C_b the fp16-rounded reconstruction levels and n the stored fp16 norm.
+with C_b the fp32 Lloyd-Max centroids and n the stored fp16 norm.
 No residual (QJL) stage, no renormalisation.
 
 Structured rotations (the second rotation kind; the pages fix no rotation type): Pi may
@@ -169,8 +169,8 @@ def quantize_values(v, rot_v, bits: int):
 
 
 def _levels(bits: int, levels: str) -> np.ndarray:
-    """Reconstruction levels as fp64 values: "fp16" = the fp32 centroids rounded to fp16 (the
-    reading the packed cache is decoded with), "fp32" = the fp32 centroids themselves."""
+    """Reconstruction levels as fp64 values: "fp32" = the fp32 Lloyd-Max centroids (the
+    reconstruction the method defines), "fp16" = those rounded once more to fp16."""
     if levels == "fp16":
         return codebook.levels16(bits)
     if levels == "fp32":
@@ -178,7 +178,7 @@ def _levels(bits: int, levels: str) -> np.ndarray:
     raise ValueError(f"levels must be 'fp16' or 'fp32', not {levels!r}")
 
 
-def dequantize_keys(codes, norms, lay: Layout, bank, levels: str = "fp16") -> np.ndarray:
+def dequantize_keys(codes, norms, lay: Layout, bank, levels: str = "fp32") -> np.ndarray:
     """fp64 reconstruction [T, d] in original coordinate order; width-0 blocks are 0."""
     codes = np.asarray(codes)
     t_len = codes.shape[0]
@@ -191,7 +191,7 @@ def dequantize_keys(codes, norms, lay: Layout, bank, levels: str = "fp16") -> np
     return out
 
 
-def dequantize_values(codes, norms, rot_v, bits: int, levels: str = "fp16") -> np.ndarray:
+def dequantize_values(codes, norms, rot_v, bits: int, levels: str = "fp32") -> np.ndarray:
     d = np.asarray(codes).shape[-1]
     cen = _levels(bits, levels)
     yhat = cen[np.asarray(codes)] / np.sqrt(d)

@@ -260,7 +260,9 @@ def test_options_round_trip():
         assert bgtq.get_option(bgtq.OPT_DECODE_KERNEL) == 1
         bgtq.set_option(bgtq.OPT_STEP_WAIT_LIMIT, 0)
         assert bgtq.get_option(bgtq.OPT_STEP_WAIT_LIMIT) == 0
-        assert lib.bgtq_set_option(bgtq.OPT_DECODE_KERNEL, 2) == bgtq.ERR_INVALID_ARG
+        bgtq.set_option(bgtq.OPT_DECODE_KERNEL, 2)
+        assert bgtq.get_option(bgtq.OPT_DECODE_KERNEL) == 2
+        assert lib.bgtq_set_option(bgtq.OPT_DECODE_KERNEL, 3) == bgtq.ERR_INVALID_ARG
         assert lib.bgtq_set_option(bgtq.OPT_STEP_WAIT_LIMIT, -1) == bgtq.ERR_INVALID_ARG
         assert lib.bgtq_set_option(7, 0) == bgtq.ERR_INVALID_ARG
         assert lib.bgtq_get_option(7) == -1
@@ -290,3 +292,32 @@ def test_decode_step_noalloc_validation():
     assert call(_desc(k_norms=None)) == bgtq.ERR_INVALID_ARG
     assert lib.bgtq_decode_step_noalloc(ctypes.byref(_quantizer()), None, 16, FAKE, 0, FAKE, FAKE, 0, 256, 128, 1e6,
                                         0.088, FAKE, None, None) == bgtq.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("batch,n_q,n_kv,d,ksum,vb,cap", [
+    (1, 8, 1, 128, 192, 3, 5056),      # one KV head: the streamed pass runs 255 splits
+    (1, 1, 1, 64, 96, 3, 320),
+    (1, 16, 2, 128, 192, 3, 131136),
+    (2, 2, 1, 64, 0, 3, 128),
+    (16, 28, 4, 128, 192, 2, 65600),
+    (1, 32, 8, 128, 128, 2, 32832),
+    (3, 12, 3, 256, 384, 4, 640),
+    (64, 64, 8, 128, 512, 8, 64),
+])
+def test_decode_workspace_covers_every_split_count(batch, n_q, n_kv, d, ksum, vb, cap):
+    """A workspace of exactly bgtq_decode_workspace_bytes passes the host's own check of the
+    partial-result layout for whichever pass serves the cache (the call then stops at the
+    missing GPU, never at the workspace)."""
+    lib = bgtq.lib()
+    need = lib.bgtq_decode_workspace_bytes(batch, n_q, n_kv, d, cap)
+    desc = _desc(batch=batch, n_kv_heads=n_kv, head_dim=d, k_width_sum=ksum, v_bits=vb, capacity=cap)
+    for opt in (0, 1, 2):
+        old = bgtq.get_option(bgtq.OPT_DECODE_KERNEL)
+        bgtq.set_option(bgtq.OPT_DECODE_KERNEL, opt)
+        try:
+            st = lib.bgtq_decode_attention(ctypes.byref(_quantizer(d)), ctypes.byref(desc), n_q, FAKE, 0, None, 1e6,
+                                           0.088, FAKE, None, FAKE, need, None)
+        finally:
+            bgtq.set_option(bgtq.OPT_DECODE_KERNEL, old)
+        assert st != bgtq.ERR_WORKSPACE, lib.bgtq_last_error()
+        assert st in (bgtq.OK, bgtq.ERR_HIP, bgtq.ERR_UNSUPPORTED)
