@@ -65,6 +65,24 @@ __device__ __forceinline__ uint32_t win32(uint32_t d0, uint32_t d1, uint32_t sh)
   return __builtin_amdgcn_alignbit(d1, d0, sh);
 }
 
+// x as an opaque wave-uniform value: the compiler keeps it in a register from here on instead
+// of reading the kernel argument again where it is used (a late re-read of the argument
+// segment costs a memory round trip after the tile loop)
+template <typename T>
+__device__ __forceinline__ T keep_s(T x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+// the same for a global-memory pointer, returned in the global address space (an opaque generic
+// pointer would make its accesses flat ones, which later LDS waits also wait for)
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ gptr<T> keep_g(T* p) {
+  asm volatile("" : "+s"(p));
+  return (gptr<T>)p;
+}
+
 // 16 bytes per lane from global address p to LDS at lds + 16 lane (lds the same for the whole
 // wave) as one direct-to-LDS load.  It is issued from asm so that the compiler's wait insertion
 // does not track it: that pass cannot tell the two staging rings apart and would make every LDS
@@ -171,35 +189,59 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
     }
   }
   const int split = int(blockIdx.x) - (STEP ? 1 : 0), hk = blockIdx.y, s = blockIdx.z;
+  const int group = keep_s(a.group), n_q = keep_s(a.n_q);
+  const gptr<float> partial = keep_g(a.partial);
+  const gptr<uint64_t> part_ml = keep_g(reinterpret_cast<uint64_t*>(a.part_ml));   // (max, sum) pairs
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, j = lane >> 4;
   if (split == 0)       // the merge adds into this (sequence, KV head)'s output rows
-    for (int i = tid; i < a.group * D; i += kStreamThreads) a.out[(int64_t(s) * a.n_q + hk * a.group) * D + i] = 0.0f;
+    for (int i = tid; i < group * D; i += kStreamThreads) a.out[(int64_t(s) * n_q + hk * group) * D + i] = 0.0f;
   // in a decode step the append role adds the new token beside this pass and the merge kernel
   // advances lengths[], so it still holds the old length here
   const int len0 = a.lengths[s];
   const int len = a.step && len0 + 1 <= a.capacity ? len0 + 1 : len0;
-  const int n_ps = a.n_split;
+  const int n_ps = keep_s(a.n_split);
+  // Work units: whole tiles round-robin over the waves of this (sequence, KV head) (wave
+  // index vidx = split + n_ps * wave, W waves), then the remaining tiles cut into halves of 32
+  // tokens, one half per wave in the same order, so that any two waves' work differs by at most
+  // half a tile.  Unit k < base of a wave is tile vidx + W k; unit k >= base is half
+  // (vidx + (k - base) W) % 2 of tile base W + (vidx + (k - base) W) / 2.
   const int tiles = (len + kTile - 1) / kTile;
-  const int count = tiles > split ? (tiles - split + n_ps - 1) / n_ps : 0;     // this split's tiles
-  const int wcount = count > wave ? (count - wave + kStreamWaves - 1) / kStreamWaves : 0;   // this wave's
-  // a decode step: the wave whose tiles include the new token's waits for the append role
-  // before it requests that tile
+  const int W = kStreamWaves * n_ps, vidx = split + n_ps * wave;
+  const int base = tiles / W, rem = tiles - base * W;
+  int wcount = base + (2 * rem > vidx ? (2 * rem - vidx + W - 1) / W : 0);
+  if (wcount > base) {        // the last tile's second half holds no token when the length ends in its first
+    const int u = vidx + (wcount - 1 - base) * W;
+    if ((u & 1) && kTile * (base * W + u / 2) + 32 >= len) --wcount;
+  }
+  auto unit_tile = [&](int k) { return k < base ? vidx + W * k : base * W + (vidx + (k - base) * W) / 2; };
+  auto unit_half = [&](int k) { return k < base ? -1 : (vidx + (k - base) * W) & 1; };
+  // a decode step: the wave whose units include the new token's waits for the append role
+  // before it requests that unit's tile
   int k_new = -1;
   if constexpr (STEP) {
     if (len == len0 + 1) {
-      const int dt = len0 / kTile - split;
-      if (dt >= 0 && dt % n_ps == 0 && (dt / n_ps) % kStreamWaves == wave) k_new = (dt / n_ps) / kStreamWaves;
+      const int tn = len0 / kTile;
+      int own, kk;
+      if (tn < base * W) {
+        own = tn % W;
+        kk = tn / W;
+      } else {
+        const int u = 2 * (tn - base * W) + (len0 % kTile >= 32 ? 1 : 0);
+        own = u % W;
+        kk = base + u / W;
+      }
+      if (own == vidx) k_new = kk;
     }
   }
-  const int bv = a.v_bits, chunks = a.chunks;
+  const int bv = keep_s(a.v_bits), chunks = keep_s(a.chunks);
   const StreamSlot geo = stream_slot(D, chunks, bv);
   const size_t reg = size_t(s) * a.n_kv + hk;
   const int64_t cap_tiles = a.capacity / kTile;
-  const uint8_t* kc = a.k_codes + reg * cap_tiles * chunks * kTile * 16;
-  const uint8_t* knp = reinterpret_cast<const uint8_t*>(a.k_norms + reg * cap_tiles * kMaxGroups * kTile);
-  const uint8_t* vnp = reinterpret_cast<const uint8_t*>(a.v_norms + reg * cap_tiles * kTile);
-  const uint8_t* vc = a.v_codes + reg * cap_tiles * D * 8 * bv;
+  const uint8_t* const kc = keep_s(a.k_codes + reg * cap_tiles * chunks * kTile * 16);
+  const uint8_t* const knp = keep_s(reinterpret_cast<const uint8_t*>(a.k_norms + reg * cap_tiles * kMaxGroups * kTile));
+  const uint8_t* const vnp = keep_s(reinterpret_cast<const uint8_t*>(a.v_norms + reg * cap_tiles * kTile));
+  const uint8_t* const vc = keep_s(a.v_codes + reg * cap_tiles * D * 8 * bv);
   uint8_t* const slot0 = s_ring0 + wave * SLOT;
   uint8_t* const slot1 = s_ring1 + wave * SLOT;
 
@@ -209,8 +251,8 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   // 8 K norm planes; then the value units u (norms for u < 8, codes after), lanes past the last
   // unit off.
   const uint32_t inv_ch = (65536u + uint32_t(chunks) - 1u) / uint32_t(chunks > 0 ? chunks : 1);
-  auto load_tile = [&](int k, uint8_t* slot) {
-    const int tile = split + (wave + kStreamWaves * k) * n_ps;
+  auto load_tile = [&](int k, uint8_t* slot) {     // the whole tile, also for a half unit
+    const int tile = unit_tile(k);
     const uint8_t* kt = kc + size_t(tile) * chunks * kTile * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -294,6 +336,26 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   const int nks = Ls->n_ksteps;
   const uint32_t wmask = wide_ksteps(Ls, nks, lane);
   const int nn = nks - __popc(wmask);               // narrow k-steps
+  // dense rotations: q''_p = (softmax_scale log2(e) / sqrt(m)) sum_c R_m[p - first][c] q'[perm[first + c]]
+  // for storage position p = tid / 4; the four threads of p take a quarter of the row each
+  // (float2 pairs of coordinates), their rows requested before the k-step descriptors are built
+  const bool giv = a.givens != nullptr;
+  constexpr int RQ = D / 8;                          // float2 of a row quarter at most (m <= D)
+  const int rp = tid >> 2, rk = tid & 3, d_eff = Ls->d_eff;
+  float2 rq[RQ];
+  int rm = 2, rfirst = 0, rb0 = 0, rn = 0;
+  if (!giv && rp < d_eff) {
+    const int g = Ls->group[rp];
+    rm = Ls->g_m[g];
+    rfirst = Ls->g_first[g];
+    const int per = (rm / 2 + 3) / 4;
+    rb0 = rk * per;
+    rn = min(per, rm / 2 - rb0);
+    const float2* R2 = reinterpret_cast<const float2*>(a.rot_bank + bank_offset(rm) + size_t(rp - rfirst) * rm) + rb0;
+#pragma unroll
+    for (int i = 0; i < RQ; ++i)
+      if (i < rn) rq[i] = R2[i];
+  }
   // per k-step (kernel order: narrow ones first) and lane group j: x = byte offset of the
   // window's first record dword, y = shift | 2w << 8 | 4w << 16 | 6w << 24, z = byte offset of
   // the width's pair table (w <= 5), w = byte offset of its single table | w << 16 | class << 20 |
@@ -314,10 +376,52 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
         uint4{4u * (o >> 5), (o & 31u) | (2u * w) << 8 | (4u * w) << 16 | (6u * w) << 24, tbp,
               tbs | w << 16 | seg_class(wmax) << 20 | (kg & 7u) << 24 | ((kg >> 8) & 7u) << 28};
   }
-  if (a.givens) qops_givens_rotate(a, Ls, qc, tid, 256);   // every thread: it holds the barriers
-  if (tid < 256) {
-    if (a.givens) qops_scatter_rotated<true>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlo + 64 * kQRegSteps);
-    else qops_scatter<D, true>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlo + 64 * kQRegSteps);
+  if (giv) {
+    qops_givens_rotate(a, Ls, qc, tid, 256);     // every thread: it holds the barriers
+    if (tid < 256) qops_scatter_rotated<true>(a, Ls, qc, wmask, nn, tid, qhi, qlo, qlo + 64 * kQRegSteps);
+  } else if (rp < d_eff) {
+    float acc[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
+    const uint8_t* pm = Ls->perm + rfirst + 2 * rb0;
+#pragma unroll
+    for (int i = 0; i < RQ; ++i) {
+      if (i < rn) {
+        const float4* xa = reinterpret_cast<const float4*>(qc + 8 * pm[2 * i]);
+        const float4* xb = reinterpret_cast<const float4*>(qc + 8 * pm[2 * i + 1]);
+        const float4 a0 = xa[0], a1 = xa[1], c0 = xb[0], c1 = xb[1];
+        const float r0 = rq[i].x, r1 = rq[i].y;
+        acc[0] = fmaf(r0, a0.x, acc[0]); acc[1] = fmaf(r0, a0.y, acc[1]);
+        acc[2] = fmaf(r0, a0.z, acc[2]); acc[3] = fmaf(r0, a0.w, acc[3]);
+        acc[4] = fmaf(r0, a1.x, acc[4]); acc[5] = fmaf(r0, a1.y, acc[5]);
+        acc[6] = fmaf(r0, a1.z, acc[6]); acc[7] = fmaf(r0, a1.w, acc[7]);
+        acc[0] = fmaf(r1, c0.x, acc[0]); acc[1] = fmaf(r1, c0.y, acc[1]);
+        acc[2] = fmaf(r1, c0.z, acc[2]); acc[3] = fmaf(r1, c0.w, acc[3]);
+        acc[4] = fmaf(r1, c1.x, acc[4]); acc[5] = fmaf(r1, c1.y, acc[5]);
+        acc[6] = fmaf(r1, c1.z, acc[6]); acc[7] = fmaf(r1, c1.w, acc[7]);
+      }
+    }
+    // the quarters' sums (pairwise, so the four threads agree), then heads 2 rk, 2 rk + 1 of p
+    // into the B operand slots of p's k-step: fp16 high part and remainder
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      acc[h] += __shfl_xor(acc[h], 1);
+      acc[h] += __shfl_xor(acc[h], 2);
+    }
+    const float f = a.scale * kLog2e / sqrtf(float(rm));
+    const int kx = Ls->kpos[rp], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm_of(wmask, nn, ks0);
+    const int lb = 16 * jj + 8 * int((Ls->seg[4 * ks0 + jj] >> 28) & 1u);
+    uint16_t* q16 = reinterpret_cast<uint16_t*>((e < 4 ? qhi : qlo) + 64 * ks);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int h = 2 * rk + hh;
+      if (h < group) {
+        const float v = (rk == 0 ? acc[hh] : rk == 1 ? acc[2 + hh] : rk == 2 ? acc[4 + hh] : acc[6 + hh]) * f;
+        const uint16_t hi = f32_to_f16_bits(v);
+        q16[(lb + h) * 8 + (e & 3)] = hi;
+        q16[(lb + h) * 8 + 4 + (e & 3)] = f32_to_f16_bits(v - f16_bits_to_f32(hi));
+      }
+    }
   }
   lds_barrier();
 
@@ -339,121 +443,137 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.0f;
-  const bool real_col = n < a.group;
+  const bool real_col = n < group;
+  const gptr<float> logits = keep_g(a.logits);
+  const int64_t capacity = keep_s(a.capacity);
 
   auto ld32 = [](const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); };
 
-  // ---- one tile from its slot: logits (4 row blocks per k-step), online softmax, P V.  Within a
-  // k-step the four row blocks' reads are issued together (the k-step's class is uniform, so the
-  // decode form is chosen once per k-step), and the next k-step's descriptor and B operands are
-  // requested before this one's lookups.
-  auto process_tile = [&](int k, const uint8_t* slot) {
-    const int tile = split + (wave + kStreamWaves * k) * n_ps;
-    const int valid = len - tile * kTile < kTile ? len - tile * kTile : kTile;
-    f32x4 S[4];
+  // ---- one work unit from its slot: logits (the unit's row blocks per k-step), online softmax,
+  // P V.  NRB = 4: a whole tile (row blocks 0..3, value blocks 0, 1); NRB = 2: half h of a tile
+  // (row blocks 2 h, 2 h + 1, value block h).  Within a k-step the row blocks' reads are issued
+  // together (the k-step's class is uniform, so the decode form is chosen once per k-step), and
+  // the next k-step's descriptor and B operands are requested one k-step ahead.
+  auto process_unit = [&](auto nrb_c, int tile, int h, const uint8_t* slot) {
+    constexpr int NRB = decltype(nrb_c)::value;
+    const int valid = len - tile * kTile < kTile ? len - tile * kTile : kTile;   // the tile's tokens
+    const int t0 = NRB == 4 ? 0 : 32 * h;                                     // the unit's first token
+    f32x4 S[NRB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* kw = slot + krow;
-    uint4 dn = s_kd[j];
-    uint4 qan = qhi[lane], qbn = qlo[lane];
-    for (int ks = 0; ks < nks; ++ks) {
-      const uint4 d = dn;
-      const uint4 qa = qan, qb = qbn;
-      if (ks + 1 < nks) {
-        dn = s_kd[4 * (ks + 1) + j];
-        qan = qhi[64 * (ks + 1) + lane];
-        qbn = qlo[64 * (ks + 1) + lane];
-      }
+    for (int q = 0; q < NRB; ++q) S[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kw = slot + krow + uint32_t(t0) * rec;
+    const uint32_t ro[4] = {0u, kr1, kr2, kr3};      // row block q of the unit: + ro[q]
+    // one k-step: descriptor d, B operands qa (k slots 0..3) and qb (4..7)
+    auto kstep = [&](const uint4& d, const uint4& qa, const uint4& qb) {
       const uint32_t cls = (__builtin_amdgcn_readfirstlane(d.w) >> 20) & 3u;   // the same for every lane group
-      const uint8_t* np = slot + knb + 128u * ((d.w >> nsh) & 7u);
-      const uint4 n01 = *reinterpret_cast<const uint4*>(np);          // row blocks 0, 1
-      const uint4 n23 = *reinterpret_cast<const uint4*>(np + 64);     // row blocks 2, 3
+      const uint8_t* np = slot + knb + 128u * ((d.w >> nsh) & 7u) + 2u * uint32_t(t0);
+      uint4 nq[NRB / 2];                                 // K norms of row blocks 2 i, 2 i + 1
+#pragma unroll
+      for (int i = 0; i < NRB / 2; ++i) nq[i] = *reinterpret_cast<const uint4*>(np + 64 * i);
       const uint8_t* kb = kw + d.x;
       const uint32_t w2 = d.y >> 8, o2 = d.y >> 16, o3 = d.y >> 24;   // the field extracts use bits 4:0
-      u32x4 A1[4], A2[4];
+      u32x4 A1[NRB], A2[NRB];
       if (cls == 0u) {
-        uint32_t wa[4], wb[4];
-        wa[0] = ld32(kb); wb[0] = ld32(kb + 4);
-        wa[1] = ld32(kb + kr1); wb[1] = ld32(kb + kr1 + 4);
-        wa[2] = ld32(kb + kr2); wb[2] = ld32(kb + kr2 + 4);
-        wa[3] = ld32(kb + kr3); wb[3] = ld32(kb + kr3 + 4);
+        uint32_t wa[NRB], wb[NRB];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) dec8_pairs(win32(wa[rb], wb[rb], d.y), w2, w2, o2, o3, d.z, s_tab, A1[rb], A2[rb]);
+        for (int q = 0; q < NRB; ++q) {
+          wa[q] = ld32(kb + ro[q]);
+          wb[q] = ld32(kb + ro[q] + 4);
+        }
+#pragma unroll
+        for (int q = 0; q < NRB; ++q) dec8_pairs(win32(wa[q], wb[q], d.y), w2, w2, o2, o3, d.z, s_tab, A1[q], A2[q]);
       } else {
-        uint32_t wa[4], wb[4], wc[4];
-        const uint32_t ro[4] = {0u, kr1, kr2, kr3};
+        uint32_t wa[NRB], wb[NRB], wc[NRB];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          wa[rb] = ld32(kb + ro[rb]);
-          wb[rb] = ld32(kb + ro[rb] + 4);
-          wc[rb] = ld32(kb + ro[rb] + 8);
+        for (int q = 0; q < NRB; ++q) {
+          wa[q] = ld32(kb + ro[q]);
+          wb[q] = ld32(kb + ro[q] + 4);
+          wc[q] = ld32(kb + ro[q] + 8);
         }
         if (cls == 1u) {
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
-            dec8_pairs5(win32(wa[rb], wb[rb], d.y), win32(wb[rb], wc[rb], d.y), w2, w2, o2, o3, d.z, s_tab, A1[rb],
-                        A2[rb]);
+          for (int q = 0; q < NRB; ++q)
+            dec8_pairs5(win32(wa[q], wb[q], d.y), win32(wb[q], wc[q], d.y), w2, w2, o2, o3, d.z, s_tab, A1[q], A2[q]);
         } else {
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
-            dec8_singles(win32(wa[rb], wb[rb], d.y), win32(wb[rb], wc[rb], d.y), (d.w >> 16) & 15u, d.w & 0xffffu,
-                         s_tab, A1[rb], A2[rb]);
+          for (int q = 0; q < NRB; ++q)
+            dec8_singles(win32(wa[q], wb[q], d.y), win32(wb[q], wc[q], d.y), (d.w >> 16) & 15u, d.w & 0xffffu, s_tab,
+                         A1[q], A2[q]);
         }
       }
       const f16x8 B1h = bdup(qa.x, qa.y), B1l = bdup(qa.z, qa.w), B2h = bdup(qb.x, qb.y), B2l = bdup(qb.z, qb.w);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const f16x8 a1 = __builtin_bit_cast(f16x8, A1[rb]), a2 = __builtin_bit_cast(f16x8, A2[rb]);
+      for (int q = 0; q < NRB; ++q) {
+        const f16x8 a1 = __builtin_bit_cast(f16x8, A1[q]), a2 = __builtin_bit_cast(f16x8, A2[q]);
         f32x4 T = {0.f, 0.f, 0.f, 0.f};
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, B1h, T, 0, 0, 0);
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, B2h, T, 0, 0, 0);
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, B1l, T, 0, 0, 0);
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, B2l, T, 0, 0, 0);
-        const uint4& nq = rb < 2 ? n01 : n23;
-        const f16x4 nv = __builtin_bit_cast(f16x4, (rb & 1) ? uint2{nq.z, nq.w} : uint2{nq.x, nq.y});
+        const uint4& nqq = nq[q >> 1];
+        const f16x4 nv = __builtin_bit_cast(f16x4, (q & 1) ? uint2{nqq.z, nqq.w} : uint2{nqq.x, nqq.y});
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[rb][r] = fmaf(T[r], float(nv[r]), S[rb][r]);
+        for (int r = 0; r < 4; ++r) S[q][r] = fmaf(T[r], float(nv[r]), S[q][r]);
+      }
+    };
+    // k-steps in pairs, each pair's operands requested one k-step ahead into two register sets
+    uint4 d0 = s_kd[j], qa0 = qhi[lane], qb0 = qlo[lane];
+    uint4 d1 = d0, qa1 = qa0, qb1 = qb0;
+    for (int ks = 0; ks < nks; ks += 2) {
+      if (ks + 1 < nks) {
+        d1 = s_kd[4 * (ks + 1) + j];
+        qa1 = qhi[64 * (ks + 1) + lane];
+        qb1 = qlo[64 * (ks + 1) + lane];
+      }
+      kstep(d0, qa0, qb0);
+      if (ks + 1 < nks) {
+        if (ks + 2 < nks) {
+          d0 = s_kd[4 * (ks + 2) + j];
+          qa0 = qhi[64 * (ks + 2) + lane];
+          qb0 = qlo[64 * (ks + 2) + lane];
+        }
+        kstep(d1, qa1, qb1);
       }
     }
 
     // online softmax (base 2).  Head c = column c + column c + 8 (row rotation by 8, so both
-    // lanes hold the head's logit); lane (c, j) holds tokens 32 (rb / 2) + 8 j + 4 (rb % 2) + r
-    // of row block rb.
-    float v[4][4];
+    // lanes hold the head's logit); lane (c, j) holds tokens t0 + 32 (q / 2) + 8 j + 4 (q % 2) + r
+    // of the unit's row block q.
+    float v[NRB][4];
     float lm = -INFINITY;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int q = 0; q < NRB; ++q) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float sr = S[rb][r];
+        const float sr = S[q][r];
         const float other = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sr), 0x128, 0xf, 0xf, false));
         float x = sr + other;
-        if (32 * (rb >> 1) + 8 * j + 4 * (rb & 1) + r >= valid) x = -INFINITY;
-        v[rb][r] = x;
+        if (t0 + 32 * (q >> 1) + 8 * j + 4 * (q & 1) + r >= valid) x = -INFINITY;
+        v[q][r] = x;
         lm = fmaxf(lm, x);
       }
     }
-    if (a.logits && real_col) {
-      float* lg = a.logits + (int64_t(s) * a.n_q + hk * a.group + n) * a.capacity + int64_t(tile) * kTile + 8 * j;
+    if (logits && real_col) {
+      const gptr<float> lg = logits + (int64_t(s) * n_q + hk * group + n) * capacity + int64_t(tile) * kTile + 8 * j;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int q = 0; q < NRB; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 32 * (rb >> 1) + 4 * (rb & 1) + r;
-          if (t + 8 * j < valid) lg[t] = v[rb][r] * kLn2;
+          const int t = t0 + 32 * (q >> 1) + 4 * (q & 1) + r;
+          if (t + 8 * j < valid) lg[t] = v[q][r] * kLn2;
         }
     }
     lm = fmaxf(lm, __shfl_xor(lm, 16));
     lm = fmaxf(lm, __shfl_xor(lm, 32));
-    const float m_new = fmaxf(m_run, lm);            // finite: every tile has a valid token
+    const float m_new = fmaxf(m_run, lm);            // finite: every unit has a valid token
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.0f;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int q = 0; q < NRB; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[rb][r] = __builtin_amdgcn_exp2f(v[rb][r] - m_new);
-        psum += v[rb][r];
+        v[q][r] = __builtin_amdgcn_exp2f(v[q][r] - m_new);
+        psum += v[q][r];
       }
     l_part = l_part * alpha + psum;
     m_run = m_new;
@@ -461,16 +581,17 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
     }
-    // P V: block b (tokens 32 b ..), k slot 8 j + e = token 32 b + 8 j + e: row block 2 b
-    // (e < 4) and 2 b + 1 (e >= 4); P n_v in fp16.  The M-tiles' windows and lookups are
-    // issued together.
+    // P V: value block b (tokens 32 b ..), k slot 8 j + e = token 32 b + 8 j + e: the unit's row
+    // block 2 bl (e < 4) and 2 bl + 1 (e >= 4); P n_v in fp16, in the interleaved B form.  The
+    // M-tiles' windows and lookups are issued together.
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int bl = 0; bl < NRB / 2; ++bl) {
+      const int b = NRB == 4 ? bl : h;
       if (32 * b < valid) {
         const f16x8 vn = *reinterpret_cast<const f16x8*>(slot + geo.vn_off + 2 * (32 * b + 8 * j));
         f16x8 P;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) P[e] = (_Float16)(v[2 * b + (e >> 2)][e & 3] * float(vn[e]));
+        for (int e = 0; e < 8; ++e) P[e] = (_Float16)(v[2 * bl + (e >> 2)][e & 3] * float(vn[e]));
         if (valid < kTile) {       // slots past the length: p is 0, their value norm may be any bits
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -556,7 +677,9 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       load_tile(k, slot);
     }
     wait_tile(k);
-    process_tile(k, slot);
+    const int tile = unit_tile(k), h = unit_half(k);
+    if (h < 0) process_unit(std::integral_constant<int, 4>{}, tile, 0, slot);
+    else process_unit(std::integral_constant<int, 2>{}, tile, h, slot);
     if (k + 2 < wcount && !(STEP && k + 2 == k_new)) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");     // every read of the slot done
       load_tile(k + 2, slot);
@@ -583,24 +706,28 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
 #pragma unroll
   for (int w = 0; w < kStreamWaves; ++w) mmax = fmaxf(mmax, mws[8 * w + (ne & 7)]);
   const float sc = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mmax);
-  float* accw = reinterpret_cast<float*>(s_ring0);  // [8 waves][8 heads][D]
-  static_assert(kStreamWaves * 8 * D * 4 <= kStreamWaves * SLOT, "the merge fits ring 0");
+  // [8 waves][8 heads][D + 16]: the padding puts the 8 heads' rows 16 banks apart, so that a
+  // wave's 16-byte writes meet at most two to a bank (rows D floats apart all fell on the same
+  // banks, and the writes cost more than the rest of the merge)
+  constexpr int RS = D + 16;
+  float* accw = reinterpret_cast<float*>(s_ring0);
+  static_assert(kStreamWaves * 8 * RS * 4 <= kStreamWaves * SLOT, "the merge fits ring 0");
   if (ne < 8) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      *reinterpret_cast<float4*>(accw + (8 * wave + ne) * D + 16 * mt + 4 * je) =
+      *reinterpret_cast<float4*>(accw + (8 * wave + ne) * RS + 16 * mt + 4 * je) =
           float4{acc[mt][0] * sc, acc[mt][1] * sc, acc[mt][2] * sc, acc[mt][3] * sc};
   }
   __syncthreads();
-  for (int i = tid; i < a.group * D; i += kStreamThreads) {
+  for (int i = tid; i < group * D; i += kStreamThreads) {
     const int h = i / D, r = i - h * D;
     float x = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kStreamWaves; ++w) x += accw[(8 * w + h) * D + r];
-    const int64_t row = (int64_t(s) * a.n_q + hk * a.group + h) * a.n_split + split;
-    a.partial[row * D + r] = x;
+    for (int w = 0; w < kStreamWaves; ++w) x += accw[(8 * w + h) * RS + r];
+    const int64_t row = (int64_t(s) * n_q + hk * group + h) * n_ps + split;
+    partial[row * D + r] = x;
   }
-  if (tid < a.group) {
+  if (tid < group) {
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kStreamWaves; ++w) mx = fmaxf(mx, mws[8 * w + tid]);
@@ -610,7 +737,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       const float mw = mws[8 * w + tid];
       lsum += mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mx) * lws[8 * w + tid];
     }
-    const int64_t row = (int64_t(s) * a.n_q + hk * a.group + tid) * a.n_split + split;
-    a.part_ml[row] = float2{mx, lsum};
+    const int64_t row = (int64_t(s) * n_q + hk * group + tid) * n_ps + split;
+    part_ml[row] = uint64_t(__float_as_uint(mx)) | uint64_t(__float_as_uint(lsum)) << 32;
   }
 }
