@@ -242,14 +242,17 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   const uint8_t* const knp = keep_s(reinterpret_cast<const uint8_t*>(a.k_norms + reg * cap_tiles * kMaxGroups * kTile));
   const uint8_t* const vnp = keep_s(reinterpret_cast<const uint8_t*>(a.v_norms + reg * cap_tiles * kTile));
   const uint8_t* const vc = keep_s(a.v_codes + reg * cap_tiles * D * 8 * bv);
+  // K norm planes in use: one 128-byte plane per width group, 8 load lanes each (at least one
+  // plane's lanes, so that every tile takes the same number of loads)
+  const int kn_lanes = 8 * max(1, __builtin_amdgcn_readfirstlane(a.layouts[reg].n_groups));
   uint8_t* const slot0 = s_ring0 + wave * SLOT;
   uint8_t* const slot1 = s_ring1 + wave * SLOT;
 
   // ---- a tile into a slot: direct loads, 1 KiB per wave each, lane l's 16 bytes to slot +
   // base + 16 l.  Load i < chunks: K record unit u = 64 i + l (token u / chunks, chunk
   // u % chunks of the chunk-major HBM layout, so the slot holds token-major records); then the
-  // 8 K norm planes; then the value units u (norms for u < 8, codes after), lanes past the last
-  // unit off.
+  // K norm planes of the layout's groups; then the value units u (norms for u < 8, codes after),
+  // lanes past the last unit off.
   const uint32_t inv_ch = (65536u + uint32_t(chunks) - 1u) / uint32_t(chunks > 0 ? chunks : 1);
   auto load_tile = [&](int k, uint8_t* slot) {     // the whole tile, also for a half unit
     const int tile = unit_tile(k);
@@ -261,7 +264,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
         stage16(kt + (c * kTile + t) * 16, slot + 1024 * i);
       }
     }
-    stage16(knp + size_t(tile) * (2 * kMaxGroups * kTile) + 16 * lane, slot + geo.kn_off);
+    if (lane < kn_lanes) stage16(knp + size_t(tile) * (2 * kMaxGroups * kTile) + 16 * lane, slot + geo.kn_off);
 #pragma unroll
     for (int i = 0; i < (D * 4 + 8 + 63) / 64; ++i) {   // up to 4 bits per value code
       if (i < geo.v_loads) {

@@ -2840,9 +2840,16 @@ int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma) {
 bool decode_stream_fits(int d, int chunks, int v_bits) { return stream_fits(d, chunks, v_bits); }
 
 int decode_stream_splits(int batch, int n_kv_heads) {
-  // one workgroup per compute unit: 256 over the (sequence, KV head) units, one of each unit's
-  // share left to a decode step's append role
+  // Few (sequence, KV head) units: one workgroup per compute unit, 256 over the units, one of
+  // each unit's share left to a decode step's append role.  A batch of many units: the
+  // sequences' lengths may differ widely while every unit takes the same number of splits, so
+  // the grid is four times the compute units and the dispatcher hands a freed unit the next
+  // split; a long sequence's splits then no longer set the time of the whole call.
   const int64_t units = int64_t(batch) * n_kv_heads;
+  if (batch > 1 && units >= 16) {
+    const int64_t over = 4 * 256 / units;
+    return over > 2 ? int(over) : 2;
+  }
   const int64_t base = 256 / units;
   return base > 2 ? int(base - 1) : 1;
 }
