@@ -86,11 +86,20 @@ def bytes_per_token_head(widths_row, v_bits, d) -> int:
     return k_code_bits // 8 + 2 * groups + v_bits * d // 8 + 2
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(texts=None) -> str:
+    """sha256 of the decode kernels' sources with comments and blank space removed, so that a
+    comment edit does not invalidate counters taken on the same code."""
+    import re
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    if texts is None:
+        texts = []
+        for p in KERNEL_SOURCES:
+            with open(p) as f:
+                texts.append(f.read())
+    for t in texts:
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(" ".join(t.split()).encode())
     return h.hexdigest()
 
 

@@ -3,32 +3,36 @@
 //
 // RoPE query-key logits over the packed cache, softmax and the value sum (abstract: the
 // logit is a sum of per-block 2-D RoPE terms; the serving path attends over a packed K3V3
-// cache at 128K context).  One workgroup of 8 waves per split; a split takes tiles tbase,
-// tbase + stride, ... of its (sequence, KV head), and wave w of the split takes that list's
-// entries w, w + 8, ...  Every wave works on whole 64-token tiles on its own: it stages a
-// tile's packed bytes through registers into its own LDS slot (the next tile's loads are in
-// flight meanwhile), computes the tile's logits, runs its own online softmax and accumulates
-// P V; no workgroup barrier falls inside the tile loop.  The 8 waves' results are merged once,
-// at the end, into the split's partial result (the format k_decode_combine reads).
+// cache at 128K context).  One workgroup of 8 waves per split.  The W = 8 n_split waves of a
+// (sequence, KV head) take its tiles round-robin (wave v: tiles v, v + W, ...), then the
+// remaining tiles as 32-token halves, one per wave in the same order.  Every wave works on its
+// own units: it stages a unit's tile with direct-to-LDS loads into its own LDS slot (the next
+// unit's loads are in flight meanwhile), computes the logits, runs its own online softmax and
+// accumulates P V; no workgroup barrier falls inside the unit loop.  The 8 waves' results are
+// merged once, at the end, into the split's partial result (the format k_decode_combine reads).
 //
-//   logits  per k-step ks (32 storage positions of at most two width groups) and row block rb
+//   logits  per k-step ks (32 storage positions of at most two width groups) and row block
 //           (16 tokens): lane (n, j) decodes the 8 codes of its token's segment (ks, j) into
-//           fp16 levels hi + lo (pair tables); T = A_hi B_hi + A_hi B_lo + A_lo B_hi on
-//           v_mfma_f32_16x16x32_f16, B the rotated query (columns 0-7: the G heads restricted
-//           to the k-step's first width group, columns 8-15: its second); S += T * n_group.
-//           Row r of row block rb is token 32 (rb / 2) + 8 (r / 4) + 4 (rb % 2) + r % 4 of the
-//           tile, so that lane (c, j) ends up holding tokens 8 j .. 8 j + 7 of each 32-token
-//           block: exactly the k slots of the P V operand below, with no exchange.
-//   values  A = the value levels (hi + lo) of 16 rotated coordinates x 32 tokens, B = P n_v in
-//           fp16 from the softmax registers; acc holds 16 coordinates x 16 columns per M-tile.
+//           fp16 level pairs hi + lo; two MFMA operands per row block hold codes 0..3 and
+//           4..7 with interleaved k slots (hi 0, hi 1, lo 0, lo 1, ...), B repeats the rotated
+//           query's halves to match (columns 0-7: the G heads restricted to the k-step's first
+//           width group, columns 8-15: its second), in high part and remainder; four
+//           v_mfma_f32_16x16x32_f16 give T, then S += T * n_group.  Row r of row block rb is
+//           token 32 (rb / 2) + 8 (r / 4) + 4 (rb % 2) + r % 4 of the tile, so that lane (c, j)
+//           ends up holding tokens 8 j .. 8 j + 7 of each 32-token block: exactly the k slots
+//           of the P V operand below, with no exchange.
+//   values  A = the value levels (hi + lo, interleaved the same way) of 16 rotated coordinates
+//           x 16 tokens per MFMA, B = P n_v in fp16 from the softmax registers; acc holds 16
+//           coordinates x 16 columns per M-tile.
 // The hi + lo split carries the fp32 Lloyd-Max levels to about 2^-22 relative.
 
 constexpr int kStreamWaves = 8;
 constexpr int kStreamThreads = 64 * kStreamWaves;
 
 // One tile's staging slot in LDS (bytes): K records token-major [64][16 chunks], the K norm
-// planes [8][64] fp16, the value norms [64] fp16, the value codes [D][8 b_v] (coordinate-
-// major, as in HBM), 16 bytes of slack for window reads past the end.  A tile arrives with
+// planes [8][64] fp16 (those of the layout's groups filled), the value norms [64] fp16, the
+// value codes [D][8 b_v] (coordinate-major, as in HBM), 16 bytes of slack for window reads past
+// the end.  A tile arrives with
 // `chunks` + 1 + v_loads direct loads of 1 KiB per wave (the last value load partial).
 struct StreamSlot {
   int kn_off, vn_off, vc_off, bytes;
@@ -644,11 +648,11 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
     }
   };
 
-  // ---- the wave's tiles, two slots: tile k in slot k % 2.  Tile m is requested in the prologue
-  // (m < 2), once the wave has read tile m - 2 out of the same slot, or, for the new token's
-  // tile of a decode step, after the wait for the append role.  The waits for a slot's loads are
-  // explicit: with tile k + 1 requested before tile k is processed, tile k is complete once at
-  // most `ni` (tile k + 1's load count) vector memory operations are outstanding.
+  // ---- the wave's units, two slots: unit k in slot k % 2.  Unit m's tile is requested in the
+  // prologue (m < 2), once the wave has read unit m - 2 out of the same slot, or, for the new
+  // token's unit of a decode step, after the wait for the append role.  The waits for a slot's
+  // loads are explicit: with unit k + 1 requested before unit k is processed, unit k is complete
+  // once at most `ni` (unit k + 1's load count) vector memory operations are outstanding.
   const int ni = chunks + 1 + geo.v_loads;
   auto wait_tile = [&](int k) {
     const bool next = k + 1 < wcount && !(STEP && (k + 1 == k_new || k == k_new));

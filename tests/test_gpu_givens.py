@@ -127,7 +127,7 @@ def test_decode_parity(d, h_q, h_kv, t_lens, kdt, window):
 
 
 @pytest.mark.parametrize("d,h_q,pre", [(128, 16, [200, 63]), (256, 4, [70]),
-                                       (128, 16, [131072])])   # full size: 511 splits per KV head
+                                       (128, 16, [131072])])   # full size: 127 split workgroups per KV head
 def test_decode_step_equals_append_then_decode(d, h_q, pre):
     dev = _cuda()
     _say(f"givens step d={d} h_q={h_q} pre={pre}")

@@ -368,8 +368,8 @@ def test_decode_is_deterministic(rot128):
 def test_decode_qwen3b_layer_128k_full_size(rot128):
     """One layer of the Qwen2.5-3B-shaped 128K decode at full size (16 q / 2 kv heads, K3V3), in the
     launch configuration the benchmark times: prefill 131072 tokens, then one decode step
-    (bgtq_decode_step: the append as one workgroup beside 511 splits per KV head, the split that
-    reads the new token's tile waiting for it) on one cache and bgtq_quantize_append +
+    (bgtq_decode_step: the append as one workgroup beside 127 split workgroups per KV head, the
+    wave whose work unit holds the new token waiting for it) on one cache and bgtq_quantize_append +
     bgtq_decode_attention on its twin, bit for bit equal; logits and outputs against the oracle,
     every head."""
     _say("decode qwen3b 128K full size, step and append + decode")
@@ -418,6 +418,34 @@ def test_decode_valu_kernel_vs_oracle(h_q, h_kv, t_lens, rot128, valu_decode):
     wl = synth.Workload("valu", 95, d=128, h_q=h_q, h_kv=h_kv, theta=1e6, layers=1, seq_lens=tuple(t_lens),
                         k_bits=3, v_bits=3, key_dtype="f32", profile="decay_jitter", outlier_blocks=2)
     _decode_vs_oracle(wl, t_lens, qz, bank, rv, append_then_attend=True, step_twin=True)
+
+
+@pytest.fixture
+def tiled_decode():
+    """Forces the tiled matrix-core decode pass (the one that serves caches with a recent-key
+    window and geometries the streamed pass does not) for one test."""
+    old = bgtq.get_option(bgtq.OPT_DECODE_KERNEL)
+    bgtq.set_option(bgtq.OPT_DECODE_KERNEL, 2)
+    yield
+    bgtq.set_option(bgtq.OPT_DECODE_KERNEL, old)
+
+
+@pytest.mark.parametrize("h_q,h_kv,t_lens", [(16, 2, [4097, 130]), (8, 8, [3000]), (4, 1, [1, 63, 64, 65])])
+def test_decode_tiled_kernel_vs_oracle(h_q, h_kv, t_lens, rot128, tiled_decode):
+    """The tiled matrix-core pass against the oracle, with the decode step beside it."""
+    _say(f"decode tiled pass {h_q}/{h_kv} {t_lens}")
+    bank, rv, qz = rot128
+    wl = synth.Workload("tiled", 96, d=128, h_q=h_q, h_kv=h_kv, theta=1e6, layers=1, seq_lens=tuple(t_lens),
+                        k_bits=3, v_bits=3, key_dtype="f32", profile="decay_jitter", outlier_blocks=2)
+    _decode_vs_oracle(wl, t_lens, qz, bank, rv, append_then_attend=True, step_twin=True)
+
+
+def test_decode_tiled_kernel_qwen3b_128k(rot128, tiled_decode):
+    """The tiled matrix-core pass on the 128K Qwen2.5-3B-shaped layer, every head."""
+    _say("decode tiled pass qwen3b 128K")
+    bank, rv, qz = rot128
+    wl = synth.QWEN3B_128K
+    _decode_vs_oracle(wl, [wl.seq_lens[0] + 1], qz, bank, rv, append_then_attend=True, check_logits=True)
 
 
 def test_decode_valu_kernel_qwen3b_128k(rot128, valu_decode):
