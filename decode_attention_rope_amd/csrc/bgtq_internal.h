@@ -52,6 +52,7 @@ struct alignas(16) HeadLayout {
                    20 * kMaxKSteps - 2 * BGTQ_MAX_HEAD_DIM - 4 * kMaxRecordDwords];
 };
 static_assert(sizeof(HeadLayout) == BGTQ_LAYOUT_BYTES, "layout descriptor size");
+static_assert(offsetof(HeadLayout, seg) % 16 == 0, "a k-step's four segments are read as one 16-byte word");
 
 // Frozen quantizer tables (fp32 as the kernels read them; fp64 distortions).
 constexpr int kPairWords = 1364;    // fp16 pair tables of widths 1..5: sum over w of 4^w entries

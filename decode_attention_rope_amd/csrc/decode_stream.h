@@ -340,12 +340,10 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   if (wcount > 0 && k_new != 0) load_tile(0, slot0);
   if (wcount > 1 && k_new != 1) load_tile(1, slot1);
   lds_barrier();
-  const int nks = Ls->n_ksteps;
-  const uint32_t wmask = wide_ksteps(Ls, nks, lane);
-  const int nn = nks - __popc(wmask);               // narrow k-steps
   // dense rotations: q''_p = (softmax_scale log2(e) / sqrt(m)) sum_c R_m[p - first][c] q'[perm[first + c]]
   // for storage position p = tid / 4; the four threads of p take a quarter of the row each
-  // (float2 pairs of coordinates), their rows requested before the k-step descriptors are built
+  // (float2 pairs of coordinates), their rows requested first (the addresses take dependent
+  // reads of the layout), before the k-step descriptors are built
   const bool giv = a.givens != nullptr;
   constexpr int RQ = D / 8;                          // float2 of a row quarter at most (m <= D)
   const int rp = tid >> 2, rk = tid & 3, d_eff = Ls->d_eff;
@@ -363,6 +361,9 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
     for (int i = 0; i < RQ; ++i)
       if (i < rn) rq[i] = R2[i];
   }
+  const int nks = Ls->n_ksteps;
+  const uint32_t wmask = wide_ksteps(Ls, nks, lane);
+  const int nn = nks - __popc(wmask);               // narrow k-steps
   // per k-step (kernel order: narrow ones first) and lane group j: x = byte offset of the
   // window's first record dword, y = shift | 2w << 8 | 4w << 16 | 6w << 24, z = byte offset of
   // the width's pair table (w <= 5), w = byte offset of its single table | w << 16 | class << 20 |

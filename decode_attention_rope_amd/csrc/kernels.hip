@@ -100,8 +100,8 @@ __device__ __forceinline__ int code_of(const float* thr, int bits, float z) {
 }
 
 __device__ __forceinline__ size_t bank_offset(int m) {  // sum of k*k for even k < m
-  const size_t h = size_t(m) / 2 - 1;                   // number of smaller sizes
-  return 4 * (h * (h + 1) * (2 * h + 1) / 6);
+  const uint32_t h = uint32_t(m) / 2u - 1u;             // number of smaller sizes
+  return size_t(4u * (h * (h + 1u) * (2u * h + 1u) / 6u));   // m <= 256: fits 32 bits
 }
 
 // Layers per size the kernels apply; the records' header must not name more.
@@ -1755,8 +1755,9 @@ __device__ __forceinline__ void q_rope(const DecodeArgs& a, int64_t pos, double 
 __device__ __forceinline__ uint32_t wide_ksteps(const HeadLayout* Ls, int nks, int lane) {
   bool wd = false;
   if (lane < nks) {
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) wd = wd || ((Ls->seg[4 * lane + sl] >> 16) & 15u) > 4u;
+    const uint4 sg = reinterpret_cast<const uint4*>(Ls->seg)[lane];   // the k-step's four segments, one read
+    const uint32_t w = max(max((sg.x >> 16) & 15u, (sg.y >> 16) & 15u), max((sg.z >> 16) & 15u, (sg.w >> 16) & 15u));
+    wd = w > 4u;
   }
   return uint32_t(__ballot(wd));
 }
