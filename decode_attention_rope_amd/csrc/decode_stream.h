@@ -198,8 +198,6 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   const gptr<uint64_t> part_ml = keep_g(reinterpret_cast<uint64_t*>(a.part_ml));   // (max, sum) pairs
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, j = lane >> 4;
-  if (split == 0)       // the merge adds into this (sequence, KV head)'s output rows
-    for (int i = tid; i < group * D; i += kStreamThreads) a.out[(int64_t(s) * n_q + hk * group) * D + i] = 0.0f;
   // in a decode step the append role adds the new token beside this pass and the merge kernel
   // advances lengths[], so it still holds the old length here
   const int len0 = a.lengths[s];

@@ -1389,8 +1389,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   extern __shared__ uint32_t smem[];
   const int split = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
-  if (split == 0)       // the merge adds into this (sequence, KV head)'s output rows
-    for (int i = tid; i < a.group * D; i += blockDim.x) a.out[(int64_t(s) * a.n_q + hk * a.group) * D + i] = 0.0f;
   const int len = a.lengths[s];
   const int tiles = (len + kTile - 1) / kTile;
   const int per = (tiles + a.n_split - 1) / a.n_split;
@@ -1949,8 +1947,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int split = int(blockIdx.x) - (STEP ? 1 : 0), hk = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
-  if (split == 0)       // the merge adds into this (sequence, KV head)'s output rows
-    for (int i = tid; i < a.group * D; i += 256) a.out[(int64_t(s) * a.n_q + hk * a.group) * D + i] = 0.0f;
   // in a decode step the append role adds the new token beside this pass and the merge kernel
   // advances lengths[], so it still holds the old length here
   const int len0 = a.lengths[s];
@@ -2427,89 +2423,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 
 // Merge the splits of one query head and undo the value rotation:
 // out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t], from the per-split
-// (m, l) pairs and accumulators; split i is weighted by exp2(m_i - max m).  Every split's
-// accumulator loads are issued before the maximum is known, so they overlap.  Each head runs
-// on two workgroups, each reading half of the split results (what bounds the merge) and adding
-// its part of out, already scaled by the global maximum and sum of all splits, into out, which
-// the split pass zeroed: a sum of two terms, the same in either order.  With dense rotations
-// a workgroup owns half of acc's coordinates (R_v^T acc is a sum over them); with Givens
-// layers, which mix all coordinates, half of the splits (the un-rotation is linear in acc).
+// (m, l) pairs and accumulators; split i is weighted by exp2(m_i - max m).  Workgroup (h, s, q)
+// of 256 threads first merges every coordinate of head h's splits: thread t takes coordinates
+// 4 (t % (D/4)) .. + 3 of the splits t / (D/4) + NG k, in chunks of 8 requested together,
+// rescaling its running sum when a chunk raises its maximum; the NG split groups are then
+// combined through LDS, in group order.  Dense value rotation: the workgroup writes output
+// coordinates 32 q .. 32 q + 31 (its R_v entries are requested before the split loads, so their
+// latency overlaps the merge), as sums over 8 parts of the coordinates, in part order.  Givens
+// layers mix every coordinate: one workgroup per head (q = 0) applies their transposes in
+// reverse order.  Every output element is written once (no accumulation into out).
 template <int D, bool GIV>
-__global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
-  constexpr int NT = 1024, DH = GIV ? D : D / 2, C4 = DH / 4, NG = NT / C4, RS = NT / D, NB = 16;
-  __shared__ float red[2][NT / 64];
-  __shared__ float4 part4[NT];
-  __shared__ float accs[D];
-  __shared__ float outp[NT];
-  const int h = blockIdx.x, s = blockIdx.y, hf = int(blockIdx.z);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a) {
+  constexpr int NT = 256, C4 = D / 4, NG = NT / C4, CH = 8;
+  constexpr int OQ = 32, KP = NT / OQ, KR = D / KP;    // outputs per workgroup, coordinate parts, rows per part
+  static_assert(NT % C4 == 0 && NT >= D && NT >= D / 2, "thread roles of the merge");
+  __shared__ float4 s_acc[NG][C4];
+  __shared__ float2 s_ml[NG];
+  __shared__ float s_x[D];
+  __shared__ float s_part[KP][OQ];
+  __shared__ float s_l;
+  const int h = blockIdx.x, s = blockIdx.y, q = blockIdx.z;
+  const int tid = threadIdx.x;
   const int ns = a.n_split;
   const size_t base = (size_t(s) * a.n_q + h) * ns;
   const float2* ml = a.part_ml + base;
-  const float4* acc4 = reinterpret_cast<const float4*>(a.partial + base * D) + (GIV ? 0 : hf * C4);   // rows D/4 apart
+  const float4* acc4 = reinterpret_cast<const float4*>(a.partial + base * D);
   const int c4 = tid % C4, g = tid / C4;
-  const int lo = GIV && hf ? ns / 2 : 0, hi = GIV && !hf ? ns / 2 : ns;   // this workgroup's splits
-  float4 x[NB];
-  float2 mlv[NB];
+  // dense rotation: R_v[kp KR + k][32 q + t % 32] for this thread's part kp = t / 32
+  const int ro = OQ * q + tid % OQ, kp = tid / OQ;
+  float rv[GIV ? 1 : KR];
+  if constexpr (!GIV) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {            // first NB splits of this thread's class
-    const int i = lo + g + NG * b;
-    if (i < hi) { x[b] = acc4[size_t(i) * (D / 4) + c4]; mlv[b] = ml[i]; }
+    for (int k = 0; k < KR; ++k) rv[k] = a.rot_v[size_t(kp * KR + k) * D + ro];
   }
-  constexpr bool DENSE = !GIV;
-  float mloc = -INFINITY;
-  for (int i = tid; i < ns; i += NT) mloc = fmaxf(mloc, ml[i].x);
-  mloc = wave_max(mloc);
-  if (lane == 0) red[0][wave] = mloc;
-  __syncthreads();
-  float mmax = red[0][0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) mmax = fmaxf(mmax, red[0][w]);
-  float lloc = 0.0f;
-  for (int i = tid; i < ns; i += NT) {
-    const float2 v = ml[i];
-    lloc += (v.x == -INFINITY) ? 0.0f : exp2f(v.x - mmax) * v.y;
-  }
-  lloc = wave_sum(lloc);
-  if (lane == 0) red[1][wave] = lloc;
-  float4 v = {0.f, 0.f, 0.f, 0.f};
-  auto add = [&](const float4& xx, const float2& mm) {
-    const float w = (mm.x == -INFINITY) ? 0.0f : exp2f(mm.x - mmax);
-    v.x = fmaf(w, xx.x, v.x);
-    v.y = fmaf(w, xx.y, v.y);
-    v.z = fmaf(w, xx.z, v.z);
-    v.w = fmaf(w, xx.w, v.w);
-  };
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-    if (lo + g + NG * b < hi) add(x[b], mlv[b]);
-  for (int i = lo + g + NG * NB; i < hi; i += NG) add(acc4[size_t(i) * (D / 4) + c4], ml[i]);
-  // the groups within a wave (lanes C4 apart share a coordinate), by a fixed xor butterfly
-  static_assert(64 % C4 == 0, "coordinate classes must tile a wave");
-#pragma unroll
-  for (int off = C4; off < 64; off <<= 1) {
-    v.x += __shfl_xor(v.x, off);
-    v.y += __shfl_xor(v.y, off);
-    v.z += __shfl_xor(v.z, off);
-    v.w += __shfl_xor(v.w, off);
-  }
-  if (lane < C4) part4[wave * C4 + c4] = v;
-  // dense value rotation: this thread's rows of R_v for the un-rotation below, requested now
-  // so that their latency overlaps the reduction over waves (requested with the split loads
-  // instead, they made the merge slower)
-  constexpr int RC = DH / RS;                        // rows of R_v per thread, within this half
-  const int r_out = tid % D, q_out = tid / D;
-  float rvr[DENSE ? RC : 1];
-  if constexpr (DENSE) {
-#pragma unroll
-    for (int k = 0; k < RC; ++k) rvr[k] = a.rot_v[(hf * DH + q_out * RC + k) * D + r_out];
-  }
-  // structured value rotation: this thread's pair slot records, requested before the
-  // reduction below so that their latency overlaps it
-  // (the transpose runs the layers backwards: the slot walks them from the last one)
+  // structured rotation: pair slot t < D/2, layers from the last one (records fetched ahead)
   GivensSlot gs;
   gs.n = 0;
-  if (!DENSE && tid < D / 2) {
+  if (GIV && tid < D / 2) {
     const uint4 hv = a.givens[D / 2 - 1];
     gs.n = min(int(hv.y), kMaxGivensLayers);
     gs.rec = a.givens + hv.x + (gs.n - 1) * (D / 2) + tid;
@@ -2517,23 +2467,64 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
 #pragma unroll
     for (int l = 0; l < kGivensAhead; ++l) gs.fetch(l);
   }
-  __syncthreads();
-  float ltot = 0.0f;
+  float4 v = {0.f, 0.f, 0.f, 0.f};
+  float mr = -INFINITY, lr = 0.0f;
+  for (int i0 = g; i0 < ns; i0 += NG * CH) {
+    float4 x[CH];
+    float2 mm[CH];
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) ltot += red[1][w];
-  if (tid < C4) {                           // the waves' sums, in wave order
-    float4 t = part4[tid];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) {
-      const float4 y = part4[w * C4 + tid];
-      t.x += y.x; t.y += y.y; t.z += y.z; t.w += y.w;
+    for (int b = 0; b < CH; ++b) {
+      const int i = i0 + NG * b;
+      if (i < ns) {
+        x[b] = acc4[size_t(i) * C4 + c4];
+        mm[b] = ml[i];
+      } else {
+        x[b] = float4{0.f, 0.f, 0.f, 0.f};
+        mm[b] = float2{-INFINITY, 0.f};
+      }
     }
-    accs[4 * tid] = t.x; accs[4 * tid + 1] = t.y; accs[4 * tid + 2] = t.z; accs[4 * tid + 3] = t.w;
+    float mc = mr;
+#pragma unroll
+    for (int b = 0; b < CH; ++b) mc = fmaxf(mc, mm[b].x);
+    if (mc != -INFINITY) {
+      const float sc = exp2f(mr - mc);               // 0 while nothing is summed yet
+      v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+      lr *= sc;
+#pragma unroll
+      for (int b = 0; b < CH; ++b) {
+        const float w = (mm[b].x == -INFINITY) ? 0.0f : exp2f(mm[b].x - mc);
+        v.x = fmaf(w, x[b].x, v.x);
+        v.y = fmaf(w, x[b].y, v.y);
+        v.z = fmaf(w, x[b].z, v.z);
+        v.w = fmaf(w, x[b].w, v.w);
+        lr = fmaf(w, mm[b].y, lr);
+      }
+      mr = mc;
+    }
+  }
+  s_acc[g][c4] = v;
+  if (c4 == 0) s_ml[g] = float2{mr, lr};
+  __syncthreads();
+  if (tid < D) {                                     // coordinate tid over the split groups
+    float mx = -INFINITY;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) mx = fmaxf(mx, s_ml[gg].x);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      const float w = (s_ml[gg].x == -INFINITY) ? 0.0f : exp2f(s_ml[gg].x - mx);
+      o = fmaf(w, reinterpret_cast<const float*>(s_acc[gg])[tid], o);
+      l = fmaf(w, s_ml[gg].y, l);
+    }
+    s_x[tid] = o;
+    if (tid == 0) s_l = l;
   }
   __syncthreads();
-  if constexpr (!DENSE) {
-    // structured rotations: the transpose, layers in reverse order, each pair as
-    // [[c, s], [-s, c]]; thread t < D/2 owns pair slot t (records fetched above)
+  const float ltot = s_l;
+  const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
+  float* const orow = a.out + (int64_t(s) * a.n_q + h) * D;
+  if constexpr (GIV) {
+    // the transpose, layers in reverse order, each pair as [[c, s], [-s, c]]
     const int nl = givens_count(a.givens, D);
 #pragma unroll
     for (int i = 0; i < kMaxGivensLayers; ++i) {   // i-th layer from the last
@@ -2541,37 +2532,31 @@ __global__ __launch_bounds__(1024) void k_decode_combine(DecodeArgs a) {
         if (i < gs.n) {
           const int k = i % kGivensAhead;
           const int ia = int(gs.ab[k] & 0xffffu), ib = int(gs.ab[k] >> 16);
-          const float xa = accs[ia], xb = accs[ib];
-          accs[ia] = fmaf(gs.c[k], xa, gs.s[k] * xb);
-          accs[ib] = fmaf(gs.c[k], xb, -gs.s[k] * xa);
+          const float xa = s_x[ia], xb = s_x[ib];
+          s_x[ia] = fmaf(gs.c[k], xa, gs.s[k] * xb);
+          s_x[ib] = fmaf(gs.c[k], xb, -gs.s[k] * xa);
           if (i + kGivensAhead < kMaxGivensLayers) gs.fetch(i + kGivensAhead);
         }
         __syncthreads();
       }
     }
-    if (tid < D) {
-      const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
-      atomicAdd(a.out + (int64_t(s) * a.n_q + h) * D + tid, accs[tid] * inv);
-    }
+    if (tid < D) orow[tid] = s_x[tid] * inv;
   } else {
-    {
-      float o = 0.0f;
+    float o = 0.0f;
 #pragma unroll
-      for (int k = 0; k < RC; ++k) o = fmaf(rvr[k], accs[q_out * RC + k], o);
-      outp[tid] = o;
-    }
+    for (int k = 0; k < KR; ++k) o = fmaf(rv[k], s_x[kp * KR + k], o);
+    s_part[kp][tid % OQ] = o;
     __syncthreads();
-    if (tid < D) {
-      float o = 0.0f;
+    if (tid < OQ) {
+      float t = s_part[0][tid];
 #pragma unroll
-      for (int qq = 0; qq < RS; ++qq) o += outp[qq * D + tid];
-      const float inv = (ltot > 0.0f) ? 1.0f / (ltot * sqrtf(float(D))) : 0.0f;
-      atomicAdd(a.out + (int64_t(s) * a.n_q + h) * D + tid, o * inv);
+      for (int p = 1; p < KP; ++p) t += s_part[p][tid];
+      orow[OQ * q + tid] = t * inv;
     }
   }
-  if (hf == 0 && a.step && a.step_flag && h % a.group == 0 && tid == 0)   // ready for the next step
+  if (q == 0 && a.step && a.step_flag && h % a.group == 0 && tid == 0)   // ready for the next step
     a.step_flag[int64_t(s) * a.n_kv + h / a.group] = 0;
-  if (hf == 0 && a.step && h == 0 && tid == 0) {     // the decode step's length advance, after every reader
+  if (q == 0 && a.step && h == 0 && tid == 0) {     // the decode step's length advance, after every reader
     const int len0 = a.lengths[s];
     if (len0 + 1 <= a.capacity) a.lengths[s] = len0 + 1;
   }
@@ -2636,8 +2621,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st,
       default: hipLaunchKernelGGL((k_decode_split<D, 16>), grid, block, lds, st, a); break;
     }
   }
-  if (a.givens) hipLaunchKernelGGL((k_decode_combine<D, true>), dim3(a.n_q, a.batch, 2), dim3(1024), 0, st, a);
-  else hipLaunchKernelGGL((k_decode_combine<D, false>), dim3(a.n_q, a.batch, 2), dim3(1024), 0, st, a);
+  if (a.givens) hipLaunchKernelGGL((k_decode_combine<D, true>), dim3(a.n_q, a.batch, 1), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_decode_combine<D, false>), dim3(a.n_q, a.batch, D / 32), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
