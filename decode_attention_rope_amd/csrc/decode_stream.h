@@ -163,6 +163,21 @@ __device__ __forceinline__ void dec8_singles(uint32_t xl, uint32_t xh, uint32_t 
   A2 = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// Lanes l, l ^ 16, l ^ 32 and l ^ 48 combined by 16-lane row exchanges (VALU, no LDS traffic):
+// the first swap pairs rows 0/1 and 2/3, the second the two halves of the wave.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // B operand of the interleaved form from four values' fp16 halves packed as (x0 | x1 << 16,
 // x2 | x3 << 16)
 __device__ __forceinline__ f16x8 bdup(uint32_t x01, uint32_t x23) {
@@ -407,12 +422,12 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
         acc[6] = fmaf(r1, c1.z, acc[6]); acc[7] = fmaf(r1, c1.w, acc[7]);
       }
     }
-    // the quarters' sums (pairwise, so the four threads agree), then heads 2 rk, 2 rk + 1 of p
+    // the quarters' sums (pairwise within the quad, so the four threads agree), then heads 2 rk, 2 rk + 1 of p
     // into the B operand slots of p's k-step: fp16 high part and remainder
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
-      acc[h] += __shfl_xor(acc[h], 1);
-      acc[h] += __shfl_xor(acc[h], 2);
+      acc[h] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc[h]), 0xB1, 0xf, 0xf, false));   // lane ^ 1
+      acc[h] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc[h]), 0x4E, 0xf, 0xf, false));   // lane ^ 2
     }
     const float f = a.scale * kLog2e / sqrtf(float(rm));
     const int kx = Ls->kpos[rp], ks0 = kx >> 5, jj = (kx >> 3) & 3, e = kx & 7, ks = kperm_of(wmask, nn, ks0);
@@ -546,19 +561,27 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
     // lanes hold the head's logit); lane (c, j) holds tokens t0 + 32 (q / 2) + 8 j + 4 (q % 2) + r
     // of the unit's row block q.
     float v[NRB][4];
-    float lm = -INFINITY;
 #pragma unroll
     for (int q = 0; q < NRB; ++q) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float sr = S[q][r];
         const float other = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sr), 0x128, 0xf, 0xf, false));
-        float x = sr + other;
-        if (t0 + 32 * (q >> 1) + 8 * j + 4 * (q & 1) + r >= valid) x = -INFINITY;
-        v[q][r] = x;
-        lm = fmaxf(lm, x);
+        v[q][r] = sr + other;
       }
     }
+    if (valid < t0 + 16 * NRB) {     // the unit passes the sequence's end (its last tile only)
+#pragma unroll
+      for (int q = 0; q < NRB; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t0 + 32 * (q >> 1) + 8 * j + 4 * (q & 1) + r >= valid) v[q][r] = -INFINITY;
+    }
+    float lm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NRB; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lm = fmaxf(lm, v[q][r]);
     if (logits && real_col) {
       const gptr<float> lg = logits + (int64_t(s) * n_q + hk * group + n) * capacity + int64_t(tile) * kTile + 8 * j;
 #pragma unroll
@@ -569,8 +592,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
           if (t + 8 * j < valid) lg[t] = v[q][r] * kLn2;
         }
     }
-    lm = fmaxf(lm, __shfl_xor(lm, 16));
-    lm = fmaxf(lm, __shfl_xor(lm, 32));
+    lm = rows_max(lm);
     const float m_new = fmaxf(m_run, lm);            // finite: every unit has a valid token
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.0f;
@@ -583,10 +605,8 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       }
     l_part = l_part * alpha + psum;
     m_run = m_new;
-    if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-    }
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;   // unconditional: a skip branch cost register copies
     // P V: value block b (tokens 32 b ..), k slot 8 j + e = token 32 b + 8 j + e: the unit's row
     // block 2 bl (e < 4) and 2 bl + 1 (e >= 4); P n_v in fp16, in the interleaved B form.  The
     // M-tiles' windows and lookups are issued together.
@@ -597,7 +617,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
         const f16x8 vn = *reinterpret_cast<const f16x8*>(slot + geo.vn_off + 2 * (32 * b + 8 * j));
         f16x8 P;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) P[e] = (_Float16)(v[2 * bl + (e >> 2)][e & 3] * float(vn[e]));
+        for (int e = 0; e < 8; ++e) P[e] = (_Float16)fmaf(v[2 * bl + (e >> 2)][e & 3], float(vn[e]), 0.0f);   // the product (p, n_v >= 0), one mixed-precision op
         if (valid < kTile) {       // slots past the length: p is 0, their value norm may be any bits
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -699,8 +719,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   asm volatile("" : "+v"(le));
   const int ne = le & 15, je = le >> 4;
   float l = l_part;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = rows_sum(l);
   float* mws = s_ml;                               // [8 waves][8 heads]
   float* lws = s_ml + 8 * kStreamWaves;
   if (je == 0 && ne < 8) {
