@@ -2425,7 +2425,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // out = R_v^T acc / (sqrt(d) * l), acc = sum_t p_t n_v,t C[code_t], from the per-split
 // (m, l) pairs and accumulators; split i is weighted by exp2(m_i - max m).  Workgroup (h, s, q)
 // of 256 threads first merges every coordinate of head h's splits: thread t takes coordinates
-// 4 (t % (D/4)) .. + 3 of the splits t / (D/4) + NG k, in chunks of 8 requested together,
+// 4 (t % (D/4)) .. + 3 of the splits t / (D/4) + NG k, in chunks of 16 requested together,
 // rescaling its running sum when a chunk raises its maximum; the NG split groups are then
 // combined through LDS, in group order.  Dense value rotation: the workgroup writes output
 // coordinates 32 q .. 32 q + 31 (its R_v entries are requested before the split loads, so their
@@ -2434,7 +2434,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // reverse order.  Every output element is written once (no accumulation into out).
 template <int D, bool GIV>
 __global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a) {
-  constexpr int NT = 256, C4 = D / 4, NG = NT / C4, CH = 8;
+  constexpr int NT = 256, C4 = D / 4, NG = NT / C4, CH = 16;   // CH splits per thread requested together
   constexpr int OQ = 32, KP = NT / OQ, KR = D / KP;    // outputs per workgroup, coordinate parts, rows per part
   static_assert(NT % C4 == 0 && NT >= D && NT >= D / 2, "thread roles of the merge");
   __shared__ float4 s_acc[NG][C4];
