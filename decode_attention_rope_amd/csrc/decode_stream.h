@@ -5,7 +5,7 @@
 // logit is a sum of per-block 2-D RoPE terms; the serving path attends over a packed K3V3
 // cache at 128K context).  One workgroup of 8 waves per split.  The W = 8 n_split waves of a
 // (sequence, KV head) take its tiles round-robin (wave v: tiles v, v + W, ...), then the
-// remaining tiles as 32-token halves, one per wave in the same order.  Every wave works on its
+// remaining tiles as quarters (one 16-token row block each), one per wave in the same order.  Every wave works on its
 // own units: it stages a unit's tile with direct-to-LDS loads into its own LDS slot (the next
 // unit's loads are in flight meanwhile), computes the logits, runs its own online softmax and
 // accumulates P V; no workgroup barrier falls inside the unit loop.  The 8 waves' results are
@@ -219,20 +219,23 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   const int len = a.step && len0 + 1 <= a.capacity ? len0 + 1 : len0;
   const int n_ps = keep_s(a.n_split);
   // Work units: whole tiles round-robin over the waves of this (sequence, KV head) (wave
-  // index vidx = split + n_ps * wave, W waves), then the remaining tiles cut into halves of 32
-  // tokens, one half per wave in the same order, so that any two waves' work differs by at most
-  // half a tile.  Unit k < base of a wave is tile vidx + W k; unit k >= base is half
-  // (vidx + (k - base) W) % 2 of tile base W + (vidx + (k - base) W) / 2.
+  // index vidx = split + n_ps * wave, W waves), and the remaining tiles cut into quarters, one
+  // quarter per wave in the same order, so that any two waves' work differs by at most a quarter
+  // of a tile.  Quarter q of a tile is its row block q: tokens 32 (q / 2) + 4 (q % 2) + 8 i + e,
+  // i, e < 4.  A wave takes its nqu quarters first, while every wave of the workgroup is busy (at
+  // the end a lone wave's quarter is latency-bound): unit k < nqu is quarter (vidx + k W) % 4 of
+  // tile base W + (vidx + k W) / 4, unit k >= nqu is tile vidx + W (k - nqu).
   const int tiles = (len + kTile - 1) / kTile;
   const int W = kStreamWaves * n_ps, vidx = split + n_ps * wave;
   const int base = tiles / W, rem = tiles - base * W;
-  int wcount = base + (2 * rem > vidx ? (2 * rem - vidx + W - 1) / W : 0);
-  if (wcount > base) {        // the last tile's second half holds no token when the length ends in its first
-    const int u = vidx + (wcount - 1 - base) * W;
-    if ((u & 1) && kTile * (base * W + u / 2) + 32 >= len) --wcount;
+  int nqu = 4 * rem > vidx ? (4 * rem - vidx + W - 1) / W : 0;
+  if (nqu > 0) {              // a quarter of the last tile whose first token is past the length holds none
+    const int u = vidx + (nqu - 1) * W;
+    if (kTile * (base * W + u / 4) + 32 * ((u & 3) >> 1) + 4 * (u & 1) >= len) --nqu;
   }
-  auto unit_tile = [&](int k) { return k < base ? vidx + W * k : base * W + (vidx + (k - base) * W) / 2; };
-  auto unit_half = [&](int k) { return k < base ? -1 : (vidx + (k - base) * W) & 1; };
+  const int wcount = base + nqu;
+  auto unit_tile = [&](int k) { return k < nqu ? base * W + (vidx + k * W) / 4 : vidx + W * (k - nqu); };
+  auto unit_quarter = [&](int k) { return k < nqu ? (vidx + k * W) & 3 : -1; };
   // a decode step: the wave whose units include the new token's waits for the append role
   // before it requests that unit's tile
   int k_new = -1;
@@ -242,11 +245,12 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       int own, kk;
       if (tn < base * W) {
         own = tn % W;
-        kk = tn / W;
+        kk = nqu + tn / W;                            // (nqu of the owner: used only when own == vidx)
       } else {
-        const int u = 2 * (tn - base * W) + (len0 % kTile >= 32 ? 1 : 0);
+        const int sl = len0 % kTile;                  // its slot: quarter 2 (sl / 32) + (sl / 4) % 2
+        const int u = 4 * (tn - base * W) + 2 * (sl >> 5) + ((sl >> 2) & 1);
         own = u % W;
-        kk = base + u / W;
+        kk = u / W;
       }
       if (own == vidx) k_new = kk;
     }
@@ -271,7 +275,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   // K norm planes of the layout's groups; then the value units u (norms for u < 8, codes after),
   // lanes past the last unit off.
   const uint32_t inv_ch = (65536u + uint32_t(chunks) - 1u) / uint32_t(chunks > 0 ? chunks : 1);
-  auto load_tile = [&](int k, uint8_t* slot) {     // the whole tile, also for a half unit
+  auto load_tile = [&](int k, uint8_t* slot) {     // the whole tile, also for a quarter unit
     const int tile = unit_tile(k);
     const uint8_t* kt = kc + size_t(tile) * chunks * kTile * 16;
 #pragma unroll
@@ -471,26 +475,28 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   auto ld32 = [](const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); };
 
   // ---- one work unit from its slot: logits (the unit's row blocks per k-step), online softmax,
-  // P V.  NRB = 4: a whole tile (row blocks 0..3, value blocks 0, 1); NRB = 2: half h of a tile
-  // (row blocks 2 h, 2 h + 1, value block h).  Within a k-step the row blocks' reads are issued
-  // together (the k-step's class is uniform, so the decode form is chosen once per k-step), and
-  // the next k-step's descriptor and B operands are requested one k-step ahead.
-  auto process_unit = [&](auto nrb_c, int tile, int h, const uint8_t* slot) {
+  // P V.  NRB = 4: a whole tile (row blocks 0..3, value blocks 0, 1); NRB = 1: quarter rb0 of a
+  // tile (row block rb0, half rb0 % 2 of value block rb0 / 2).  Within a k-step the row blocks'
+  // reads are issued together (the k-step's class is uniform, so the decode form is chosen once
+  // per k-step), and the next k-step's descriptor and B operands are requested one k-step ahead.
+  auto process_unit = [&](auto nrb_c, int tile, int rb0, const uint8_t* slot) {
     constexpr int NRB = decltype(nrb_c)::value;
+    static_assert(NRB == 4 || NRB == 1, "whole tiles and quarters");
     const int valid = len - tile * kTile < kTile ? len - tile * kTile : kTile;   // the tile's tokens
-    const int t0 = NRB == 4 ? 0 : 32 * h;                                     // the unit's first token
+    const int tk0 = 32 * (rb0 >> 1) + 4 * (rb0 & 1);   // row 0 of the unit's first row block
+    const int tb0 = 32 * (rb0 >> 1);                   // the unit's first 32-token value block
     f32x4 S[NRB];
 #pragma unroll
     for (int q = 0; q < NRB; ++q) S[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* kw = slot + krow + uint32_t(t0) * rec;
+    const uint8_t* kw = slot + krow + uint32_t(tk0) * rec;
     const uint32_t ro[4] = {0u, kr1, kr2, kr3};      // row block q of the unit: + ro[q]
     // one k-step: descriptor d, B operands qa (k slots 0..3) and qb (4..7)
     auto kstep = [&](const uint4& d, const uint4& qa, const uint4& qb) {
       const uint32_t cls = (__builtin_amdgcn_readfirstlane(d.w) >> 20) & 3u;   // the same for every lane group
-      const uint8_t* np = slot + knb + 128u * ((d.w >> nsh) & 7u) + 2u * uint32_t(t0);
-      uint4 nq[NRB / 2];                                 // K norms of row blocks 2 i, 2 i + 1
+      const uint8_t* np = slot + knb + 128u * __builtin_amdgcn_ubfe(d.w, nsh, 3u) + 2u * uint32_t(tb0);
+      uint4 nq[(NRB + 1) / 2];                           // K norms of row blocks 2 i, 2 i + 1 (of the unit's block)
 #pragma unroll
-      for (int i = 0; i < NRB / 2; ++i) nq[i] = *reinterpret_cast<const uint4*>(np + 64 * i);
+      for (int i = 0; i < (NRB + 1) / 2; ++i) nq[i] = *reinterpret_cast<const uint4*>(np + 64 * i);
       const uint8_t* kb = kw + d.x;
       const uint32_t w2 = d.y >> 8, o2 = d.y >> 16, o3 = d.y >> 24;   // the field extracts use bits 4:0
       u32x4 A1[NRB], A2[NRB];
@@ -532,7 +538,8 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, B1l, T, 0, 0, 0);
         T = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, B2l, T, 0, 0, 0);
         const uint4& nqq = nq[q >> 1];
-        const f16x4 nv = __builtin_bit_cast(f16x4, (q & 1) ? uint2{nqq.z, nqq.w} : uint2{nqq.x, nqq.y});
+        const bool odd = NRB == 1 ? (rb0 & 1) != 0 : (q & 1) != 0;   // the second row block of its pair
+        const f16x4 nv = __builtin_bit_cast(f16x4, odd ? uint2{nqq.z, nqq.w} : uint2{nqq.x, nqq.y});
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[q][r] = fmaf(T[r], float(nv[r]), S[q][r]);
       }
@@ -558,8 +565,8 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
     }
 
     // online softmax (base 2).  Head c = column c + column c + 8 (row rotation by 8, so both
-    // lanes hold the head's logit); lane (c, j) holds tokens t0 + 32 (q / 2) + 8 j + 4 (q % 2) + r
-    // of the unit's row block q.
+    // lanes hold the head's logit); lane (c, j) holds tokens 32 (rb / 2) + 8 j + 4 (rb % 2) + r
+    // of the tile's row block rb = rb0 + q (the unit's q-th).
     float v[NRB][4];
 #pragma unroll
     for (int q = 0; q < NRB; ++q) {
@@ -570,12 +577,12 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
         v[q][r] = sr + other;
       }
     }
-    if (valid < t0 + 16 * NRB) {     // the unit passes the sequence's end (its last tile only)
+    if (valid < tb0 + (NRB == 4 ? 64 : 32)) {     // the unit passes the sequence's end (its last tile only)
 #pragma unroll
       for (int q = 0; q < NRB; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (t0 + 32 * (q >> 1) + 8 * j + 4 * (q & 1) + r >= valid) v[q][r] = -INFINITY;
+          if (32 * ((rb0 + q) >> 1) + 8 * j + 4 * ((rb0 + q) & 1) + r >= valid) v[q][r] = -INFINITY;
     }
     float lm = -INFINITY;
 #pragma unroll
@@ -588,7 +595,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       for (int q = 0; q < NRB; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = t0 + 32 * (q >> 1) + 4 * (q & 1) + r;
+          const int t = 32 * ((rb0 + q) >> 1) + 4 * ((rb0 + q) & 1) + r;
           if (t + 8 * j < valid) lg[t] = v[q][r] * kLn2;
         }
     }
@@ -607,17 +614,23 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
     m_run = m_new;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;   // unconditional: a skip branch cost register copies
-    // P V: value block b (tokens 32 b ..), k slot 8 j + e = token 32 b + 8 j + e: the unit's row
-    // block 2 bl (e < 4) and 2 bl + 1 (e >= 4); P n_v in fp16, in the interleaved B form.  The
-    // M-tiles' windows and lookups are issued together.
+    // P V: value block b (tokens 32 b ..), k slot 8 j + e = token 32 b + 8 j + e: row block
+    // 2 b (e < 4) and 2 b + 1 (e >= 4); P n_v in fp16, in the interleaved B form (a quarter's
+    // other row block enters as zeros).  The M-tiles' windows and lookups are issued together.
 #pragma unroll
-    for (int bl = 0; bl < NRB / 2; ++bl) {
-      const int b = NRB == 4 ? bl : h;
+    for (int bl = 0; bl < (NRB == 4 ? 2 : 1); ++bl) {
+      const int b = NRB == 4 ? bl : (rb0 >> 1);
       if (32 * b < valid) {
         const f16x8 vn = *reinterpret_cast<const f16x8*>(slot + geo.vn_off + 2 * (32 * b + 8 * j));
         f16x8 P;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) P[e] = (_Float16)fmaf(v[2 * bl + (e >> 2)][e & 3], float(vn[e]), 0.0f);   // the product (p, n_v >= 0), one mixed-precision op
+        for (int e = 0; e < 8; ++e) {    // the product (p, n_v >= 0), one mixed-precision op
+          if constexpr (NRB == 4) {
+            P[e] = (_Float16)fmaf(v[2 * bl + (e >> 2)][e & 3], float(vn[e]), 0.0f);
+          } else {
+            P[e] = (e >> 2) == (rb0 & 1) ? (_Float16)fmaf(v[0][e & 3], float(vn[e]), 0.0f) : (_Float16)0.0f;
+          }
+        }
         if (valid < kTile) {       // slots past the length: p is 0, their value norm may be any bits
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -634,10 +647,23 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
             wa[mt] = ld32(vb + mt * vmt);
             wb[mt] = ld32(vb + mt * vmt + 4);
           }
+          if constexpr (NRB == 1) {    // a quarter: only its row block's four codes, pairs 2 h and 2 h + 1
+            const bool hi = (rb0 & 1) != 0;
+            const uint32_t oa = hi ? vctl >> 16 : 0u, ob = hi ? vctl >> 24 : vctl >> 8, w2 = vctl >> 8;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            dec8_pairs(win32(wa[mt], wb[mt], vctl), vctl >> 8, vctl >> 8, vctl >> 16, vctl >> 24, vtb, s_tab, VA1[mt],
-                       VA2[mt]);
+            for (int mt = 0; mt < MT; ++mt) {
+              const uint32_t x = win32(wa[mt], wb[mt], vctl);
+              const uint2 c0 = *reinterpret_cast<const uint2*>(s_tab + vtb + 8 * __builtin_amdgcn_ubfe(x, oa, w2));
+              const uint2 c1 = *reinterpret_cast<const uint2*>(s_tab + vtb + 8 * __builtin_amdgcn_ubfe(x, ob, w2));
+              VA1[mt] = u32x4{c0.x, c0.y, c1.x, c1.y};
+              VA2[mt] = VA1[mt];
+            }
+          } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              dec8_pairs(win32(wa[mt], wb[mt], vctl), vctl >> 8, vctl >> 8, vctl >> 16, vctl >> 24, vtb, s_tab, VA1[mt],
+                         VA2[mt]);
+          }
         } else {
           uint32_t wa[MT], wb[MT], wc[MT];
 #pragma unroll
@@ -658,10 +684,18 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
                            VA2[mt]);
           }
         }
+        if constexpr (NRB == 1) {      // a quarter: the other row block's operand would add zeros
+          const bool hi = (rb0 & 1) != 0;
+          const f16x8 Bq = hi ? B2 : B1;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA1[mt]), B1, acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA2[mt]), B2, acc[mt], 0, 0, 0);
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hi ? VA2[mt] : VA1[mt]), Bq, acc[mt], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA1[mt]), B1, acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA2[mt]), B2, acc[mt], 0, 0, 0);
+          }
         }
       }
     }
@@ -703,9 +737,9 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       load_tile(k, slot);
     }
     wait_tile(k);
-    const int tile = unit_tile(k), h = unit_half(k);
-    if (h < 0) process_unit(std::integral_constant<int, 4>{}, tile, 0, slot);
-    else process_unit(std::integral_constant<int, 2>{}, tile, h, slot);
+    const int tile = unit_tile(k), qr = unit_quarter(k);
+    if (qr < 0) process_unit(std::integral_constant<int, 4>{}, tile, 0, slot);
+    else process_unit(std::integral_constant<int, 1>{}, tile, qr, slot);
     if (k + 2 < wcount && !(STEP && k + 2 == k_new)) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");     // every read of the slot done
       load_tile(k + 2, slot);
