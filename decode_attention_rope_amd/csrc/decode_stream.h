@@ -222,9 +222,10 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   // index vidx = split + n_ps * wave, W waves), and the remaining tiles cut into quarters, one
   // quarter per wave in the same order, so that any two waves' work differs by at most a quarter
   // of a tile.  Quarter q of a tile is its row block q: tokens 32 (q / 2) + 4 (q % 2) + 8 i + e,
-  // i, e < 4.  A wave takes its nqu quarters first, while every wave of the workgroup is busy (at
-  // the end a lone wave's quarter is latency-bound): unit k < nqu is quarter (vidx + k W) % 4 of
-  // tile base W + (vidx + k W) / 4, unit k >= nqu is tile vidx + W (k - nqu).
+  // i, e < 4.  Unit k < base of a wave is tile vidx + W k; unit k >= base is quarter
+  // (vidx + (k - base) W) % 4 of tile base W + (vidx + (k - base) W) / 4.  (The quarters come
+  // last: in a decode step the new token's unit is then a wave's last one, and its wait for the
+  // append is over long before; taken first, that wait stalled the step.)
   const int tiles = (len + kTile - 1) / kTile;
   const int W = kStreamWaves * n_ps, vidx = split + n_ps * wave;
   const int base = tiles / W, rem = tiles - base * W;
@@ -234,8 +235,8 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
     if (kTile * (base * W + u / 4) + 32 * ((u & 3) >> 1) + 4 * (u & 1) >= len) --nqu;
   }
   const int wcount = base + nqu;
-  auto unit_tile = [&](int k) { return k < nqu ? base * W + (vidx + k * W) / 4 : vidx + W * (k - nqu); };
-  auto unit_quarter = [&](int k) { return k < nqu ? (vidx + k * W) & 3 : -1; };
+  auto unit_tile = [&](int k) { return k < base ? vidx + W * k : base * W + (vidx + (k - base) * W) / 4; };
+  auto unit_quarter = [&](int k) { return k < base ? -1 : (vidx + (k - base) * W) & 3; };
   // a decode step: the wave whose units include the new token's waits for the append role
   // before it requests that unit's tile
   int k_new = -1;
@@ -245,12 +246,12 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       int own, kk;
       if (tn < base * W) {
         own = tn % W;
-        kk = nqu + tn / W;                            // (nqu of the owner: used only when own == vidx)
+        kk = tn / W;
       } else {
         const int sl = len0 % kTile;                  // its slot: quarter 2 (sl / 32) + (sl / 4) % 2
         const int u = 4 * (tn - base * W) + 2 * (sl >> 5) + ((sl >> 2) & 1);
         own = u % W;
-        kk = u / W;
+        kk = base + u / W;
       }
       if (own == vidx) k_new = kk;
     }
