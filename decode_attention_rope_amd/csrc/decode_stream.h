@@ -21,10 +21,10 @@
 //           token 32 (rb / 2) + 8 (r / 4) + 4 (rb % 2) + r % 4 of the tile, so that lane (c, j)
 //           ends up holding tokens 8 j .. 8 j + 7 of each 32-token block: exactly the k slots
 //           of the P V operand below, with no exchange.
-//   values  A = the value levels (hi + lo, interleaved the same way) of 16 rotated coordinates
-//           x 16 tokens per MFMA, B = P n_v in fp16 from the softmax registers; acc holds 16
-//           coordinates x 16 columns per M-tile.
-// The hi + lo split carries the fp32 Lloyd-Max levels to about 2^-22 relative.
+//   values  A = the fp16 value levels of 16 rotated coordinates x 8 tokens per lane group (k slot
+//           e = token 32 b + 8 j + e), B = P n_v in fp16 from the softmax registers, one MFMA per
+//           M-tile and 32-token value block; acc holds 16 coordinates x 16 columns per M-tile.
+// For the keys the hi + lo split carries the fp32 Lloyd-Max levels to about 2^-22 relative.
 
 constexpr int kStreamWaves = 8;
 constexpr int kStreamThreads = 64 * kStreamWaves;
@@ -161,6 +161,46 @@ __device__ __forceinline__ void dec8_singles(uint32_t xl, uint32_t xh, uint32_t 
   }
   A1 = u32x4{o[0], o[1], o[2], o[3]};
   A2 = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// Value codes decode to one fp16 term per level (the nearest fp16 of the fp32 centroid): the
+// value sum is a convex combination of reconstructions, and the fp16 rounding of its levels
+// moves the output by about 2^-12 relative, well inside the decode tolerance.  (The logits do
+// need the hi + lo pair: a rounded key level shifts every logit, and sharp softmax rows amplify
+// that.)  An MFMA operand then holds 8 consecutive codes' levels in k-slot order.
+
+// Eight codes of width w <= 4 from the window x (pair k at bits [2 k w, 2 (k + 1) w)), two per
+// b32 read: the high-part pair, the first dword of each 8-byte hi/lo pair entry at byte offset
+// tb.  o1..o3 = 2w, 4w, 6w; w2 = 2w.
+__device__ __forceinline__ u32x4 vdec8_hpairs4(uint32_t x, uint32_t w2, uint32_t o1, uint32_t o2, uint32_t o3,
+                                               uint32_t tb, const uint8_t* lds) {
+  return u32x4{*reinterpret_cast<const uint32_t*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, 0u, w2)),
+               *reinterpret_cast<const uint32_t*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, o1, w2)),
+               *reinterpret_cast<const uint32_t*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, o2, w2)),
+               *reinterpret_cast<const uint32_t*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, o3, w2))};
+}
+// Eight codes of width 5 from the 64-bit window xh:xl (the fourth pair can cross bit 32), two per
+// b32 read of the high-part pairs of the hi/lo pair table at byte offset tb.
+__device__ __forceinline__ u32x4 vdec8_hpairs(uint32_t xl, uint32_t xh, uint32_t w2, uint32_t o1, uint32_t o2,
+                                              uint32_t o3, uint32_t tb, const uint8_t* lds) {
+  const uint32_t x3 = __builtin_amdgcn_alignbit(xh, xl, o3);
+  const uint32_t i0 = __builtin_amdgcn_ubfe(xl, 0u, w2), i1 = __builtin_amdgcn_ubfe(xl, o1, w2);
+  const uint32_t i2 = __builtin_amdgcn_ubfe(xl, o2, w2), i3 = __builtin_amdgcn_ubfe(x3, 0u, w2);
+  return u32x4{*reinterpret_cast<const uint32_t*>(lds + tb + 8 * i0), *reinterpret_cast<const uint32_t*>(lds + tb + 8 * i1),
+               *reinterpret_cast<const uint32_t*>(lds + tb + 8 * i2), *reinterpret_cast<const uint32_t*>(lds + tb + 8 * i3)};
+}
+// Eight codes of any width w from the 64-bit window xh:xl, one per b32 read of the hi | lo single
+// table at byte offset tb; the high parts (low halves) packed in pairs.
+__device__ __forceinline__ u32x4 vdec8_hsingles(uint32_t xl, uint32_t xh, uint32_t w, uint32_t tb, const uint8_t* lds) {
+  const uint64_t x = (uint64_t(xh) << 32) | xl;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t c = uint32_t(x >> (uint32_t(e) * w)) & ((1u << w) - 1u);   // e w + w <= 64
+    v[e] = *reinterpret_cast<const uint32_t*>(lds + tb + 4 * c);
+  }
+  return u32x4{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+               __builtin_amdgcn_perm(v[5], v[4], 0x05040100u), __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
 }
 
 // Lanes l, l ^ 16, l ^ 32 and l ^ 48 combined by 16-lane row exchanges (VALU, no LDS traffic):
@@ -463,7 +503,9 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   const uint32_t vctl = uint32_t((8 * j * bv) & 31) | (2u * bv) << 8 | (4u * bv) << 16 | (6u * bv) << 24;
   const uint32_t vmt = uint32_t(16 * 8 * bv);                        // bytes between M-tiles
   const uint32_t vtb = bv <= 5 ? uint32_t(kSTabPair + 8 * pair_base(bv)) : uint32_t(kSTabSingle + 4 * single_base(bv));
-  const uint32_t vcls = seg_class(uint32_t(bv));
+  // value decode, from the high parts of the key tables: 0 = widths <= 4, pairs from a 32-bit
+  // window; 1 = width 5, pairs from a 64-bit window; 2 = wider, singles
+  const uint32_t vmode = bv <= 4 ? 0u : (bv == 5 ? 1u : 2u);
 
   f32x4 acc[MT];
 #pragma unroll
@@ -637,35 +679,32 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
           for (int e = 0; e < 8; ++e)
             if (32 * b + 8 * j + e >= valid) P[e] = (_Float16)0.0f;
         }
-        const u32x4 pw = __builtin_bit_cast(u32x4, P);
-        const f16x8 B1 = bdup(pw[0], pw[1]), B2 = bdup(pw[2], pw[3]);
         const uint8_t* vb = slot + vwin + uint32_t(4 * b * bv);
-        u32x4 VA1[MT], VA2[MT];
-        if (vcls == 0u) {
+        u32x4 VA[MT];
+        if (vmode == 0u) {             // b_v <= 4: one 32-bit window per 8 codes
           uint32_t wa[MT], wb[MT];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             wa[mt] = ld32(vb + mt * vmt);
             wb[mt] = ld32(vb + mt * vmt + 4);
           }
-          if constexpr (NRB == 1) {    // a quarter: only its row block's four codes, pairs 2 h and 2 h + 1
+          const uint32_t w2 = vctl >> 8, o2 = vctl >> 16, o3 = vctl >> 24;   // 2 b_v, 4 b_v, 6 b_v (bits 4:0)
+          if constexpr (NRB == 1) {    // a quarter: its row block's four codes, repeated in the other half
             const bool hi = (rb0 & 1) != 0;
-            const uint32_t oa = hi ? vctl >> 16 : 0u, ob = hi ? vctl >> 24 : vctl >> 8, w2 = vctl >> 8;
+            const uint32_t oa = hi ? o2 : 0u, ob = hi ? o3 : w2;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
               const uint32_t x = win32(wa[mt], wb[mt], vctl);
-              const uint2 c0 = *reinterpret_cast<const uint2*>(s_tab + vtb + 8 * __builtin_amdgcn_ubfe(x, oa, w2));
-              const uint2 c1 = *reinterpret_cast<const uint2*>(s_tab + vtb + 8 * __builtin_amdgcn_ubfe(x, ob, w2));
-              VA1[mt] = u32x4{c0.x, c0.y, c1.x, c1.y};
-              VA2[mt] = VA1[mt];
+              const uint32_t c0 = *reinterpret_cast<const uint32_t*>(s_tab + vtb + 8 * __builtin_amdgcn_ubfe(x, oa, w2));
+              const uint32_t c1 = *reinterpret_cast<const uint32_t*>(s_tab + vtb + 8 * __builtin_amdgcn_ubfe(x, ob, w2));
+              VA[mt] = u32x4{c0, c1, c0, c1};
             }
           } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              dec8_pairs(win32(wa[mt], wb[mt], vctl), vctl >> 8, vctl >> 8, vctl >> 16, vctl >> 24, vtb, s_tab, VA1[mt],
-                         VA2[mt]);
+              VA[mt] = vdec8_hpairs4(win32(wa[mt], wb[mt], vctl), w2, w2, o2, o3, vtb, s_tab);
           }
-        } else {
+        } else {                       // wider: high parts from the LDS tables
           uint32_t wa[MT], wb[MT], wc[MT];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
@@ -673,31 +712,22 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
             wb[mt] = ld32(vb + mt * vmt + 4);
             wc[mt] = ld32(vb + mt * vmt + 8);
           }
-          if (vcls == 1u) {
+          if (vmode == 1u) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              dec8_pairs5(win32(wa[mt], wb[mt], vctl), win32(wb[mt], wc[mt], vctl), vctl >> 8, vctl >> 8, vctl >> 16,
-                          vctl >> 24, vtb, s_tab, VA1[mt], VA2[mt]);
+              VA[mt] = vdec8_hpairs(win32(wa[mt], wb[mt], vctl), win32(wb[mt], wc[mt], vctl), vctl >> 8, vctl >> 8,
+                                    vctl >> 16, vctl >> 24, vtb, s_tab);
           } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              dec8_singles(win32(wa[mt], wb[mt], vctl), win32(wb[mt], wc[mt], vctl), uint32_t(bv), vtb, s_tab, VA1[mt],
-                           VA2[mt]);
+              VA[mt] = vdec8_hsingles(win32(wa[mt], wb[mt], vctl), win32(wb[mt], wc[mt], vctl), uint32_t(bv), vtb, s_tab);
           }
         }
-        if constexpr (NRB == 1) {      // a quarter: the other row block's operand would add zeros
-          const bool hi = (rb0 & 1) != 0;
-          const f16x8 Bq = hi ? B2 : B1;
+        // P n_v is zero in the k slots of a quarter's other row block and past the length, so
+        // whatever finite levels A holds there add nothing
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hi ? VA2[mt] : VA1[mt]), Bq, acc[mt], 0, 0, 0);
-        } else {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA1[mt]), B1, acc[mt], 0, 0, 0);
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA2[mt]), B2, acc[mt], 0, 0, 0);
-          }
-        }
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, VA[mt]), P, acc[mt], 0, 0, 0);
       }
     }
   };

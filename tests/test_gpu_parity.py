@@ -308,6 +308,25 @@ def test_decode_ragged_lengths(t_lens, rot128):
     _decode_vs_oracle(wl, t_lens, qz, bank, rv)
 
 
+@pytest.mark.parametrize("d,k_bits,v_bits,t_lens", [
+    (64, 2, 1, [300, 65]),      # the streamed pass, value pairs of width 1
+    (128, 2, 4, [300, 65]),     # width 4: pairs from a 32-bit window
+    (128, 1, 5, [300, 65]),     # width 5: pairs from a 64-bit window
+    (64, 2, 6, [300, 65]),      # width 6: one lookup per code
+    (64, 0, 8, [300]),          # width 8 with no key bits (a zero budget)
+    (128, 3, 8, [300, 65]),     # too wide for the streamed pass's staging: the tiled pass
+])
+def test_decode_value_widths(d, k_bits, v_bits, t_lens, rot64, rot128):
+    """Decode at every value width class against the oracle: each way the decode passes turn
+    value codes into levels (pairs from one or two dwords, single codes)."""
+    _say(f"decode d={d} K{k_bits}V{v_bits} {t_lens}")
+    bank, rv, qz = rot64 if d == 64 else rot128
+    wl = synth.Workload("vwidths", 95, d=d, h_q=8, h_kv=2, theta=1e4, layers=1, seq_lens=tuple(t_lens),
+                        k_bits=k_bits, v_bits=v_bits, key_dtype="f32", profile="decay", outlier_blocks=2)
+    # with no key bits every logit is 0, and a normwise logit error is 0 / 0: outputs only
+    _decode_vs_oracle(wl, t_lens, qz, bank, rv, append_then_attend=True, step_twin=True, check_logits=k_bits > 0)
+
+
 def test_decode_interleaved_pairing_and_no_rope(rot64):
     _say("decode interleaved / no rope")
     bank, rv, qz = rot64
