@@ -54,7 +54,9 @@ __host__ __device__ inline StreamSlot stream_slot(int D, int chunks, int bv) {
 __host__ __device__ constexpr int stream_slot_max(int D) { return D == 128 ? 7424 : 5376; }
 constexpr int kSTabPair = 0;                                   // uint2 [kPairWords] hi, lo
 constexpr int kSTabSingle = kSTabPair + 8 * kPairWords;        // uint32 [kSingleHalves] hi | lo << 16
-constexpr int kSTabBytes = (kSTabSingle + 4 * kSingleHalves + 255) & ~255;
+constexpr int kSTabV = kSTabSingle + 4 * kSingleHalves;       // uint32 [84] high-part pairs of widths 1..3
+constexpr int kVPairWords = 84;                                 // 4 + 16 + 64 entries
+constexpr int kSTabBytes = (kSTabV + 4 * kVPairWords + 255) & ~255;
 __host__ __device__ constexpr int stream_pro_bytes(int D) {
   return BGTQ_LAYOUT_BYTES + 32 * D + 2 * 1024 * kQRegSteps;   // layout, q' [D][8], B hi [8][64], B lo [8][64]
 }
@@ -170,14 +172,14 @@ __device__ __forceinline__ void dec8_singles(uint32_t xl, uint32_t xh, uint32_t 
 // that.)  An MFMA operand then holds 8 consecutive codes' levels in k-slot order.
 
 // Eight codes of width w <= 4 from the window x (pair k at bits [2 k w, 2 (k + 1) w)), two per
-// b32 read: the high-part pair, the first dword of each 8-byte hi/lo pair entry at byte offset
-// tb.  o1..o3 = 2w, 4w, 6w; w2 = 2w.
+// b32 read of high-part pairs at byte offset tb, entries 1 << sh bytes apart.  o1..o3 = 2w, 4w,
+// 6w; w2 = 2w.
 __device__ __forceinline__ u32x4 vdec8_hpairs4(uint32_t x, uint32_t w2, uint32_t o1, uint32_t o2, uint32_t o3,
-                                               uint32_t tb, const uint8_t* lds) {
-  return u32x4{*reinterpret_cast<const uint32_t*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, 0u, w2)),
-               *reinterpret_cast<const uint32_t*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, o1, w2)),
-               *reinterpret_cast<const uint32_t*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, o2, w2)),
-               *reinterpret_cast<const uint32_t*>(lds + tb + 8 * __builtin_amdgcn_ubfe(x, o3, w2))};
+                                               uint32_t tb, uint32_t sh, const uint8_t* lds) {
+  return u32x4{*reinterpret_cast<const uint32_t*>(lds + tb + (__builtin_amdgcn_ubfe(x, 0u, w2) << sh)),
+               *reinterpret_cast<const uint32_t*>(lds + tb + (__builtin_amdgcn_ubfe(x, o1, w2) << sh)),
+               *reinterpret_cast<const uint32_t*>(lds + tb + (__builtin_amdgcn_ubfe(x, o2, w2) << sh)),
+               *reinterpret_cast<const uint32_t*>(lds + tb + (__builtin_amdgcn_ubfe(x, o3, w2) << sh))};
 }
 // Eight codes of width 5 from the 64-bit window xh:xl (the fourth pair can cross bit 32), two per
 // b32 read of the high-part pairs of the hi/lo pair table at byte offset tb.
@@ -387,6 +389,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
 #pragma unroll
     for (int i = 0; i < PW; ++i)
       if (tid + kStreamThreads * i < kPairWords) reinterpret_cast<uint2*>(s_tab + kSTabPair)[tid + kStreamThreads * i] = pt[i];
+    if (tid < kVPairWords) reinterpret_cast<uint32_t*>(s_tab + kSTabV)[tid] = pt[0].x;
 #pragma unroll
     for (int i = 0; i < SW; ++i)
       if (tid + kStreamThreads * i < kSingleHalves) reinterpret_cast<uint32_t*>(s_tab + kSTabSingle)[tid + kStreamThreads * i] = st[i];
@@ -502,7 +505,11 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   const uint32_t vwin = uint32_t(geo.vc_off + n * 8 * bv + 4 * ((8 * j * bv) >> 5));
   const uint32_t vctl = uint32_t((8 * j * bv) & 31) | (2u * bv) << 8 | (4u * bv) << 16 | (6u * bv) << 24;
   const uint32_t vmt = uint32_t(16 * 8 * bv);                        // bytes between M-tiles
-  const uint32_t vtb = bv <= 5 ? uint32_t(kSTabPair + 8 * pair_base(bv)) : uint32_t(kSTabSingle + 4 * single_base(bv));
+  // value pair lookups of widths <= 3 read the compact high-part table (4-byte entries, so that
+  // neighbouring entries fall on neighbouring banks); width 4 the high halves of the hi/lo pairs
+  const uint32_t vtb = bv <= 3 ? uint32_t(kSTabV + 4 * pair_base(bv))
+                               : bv <= 5 ? uint32_t(kSTabPair + 8 * pair_base(bv)) : uint32_t(kSTabSingle + 4 * single_base(bv));
+  const uint32_t vsh = bv <= 3 ? 2u : 3u;
   // value decode, from the high parts of the key tables: 0 = widths <= 4, pairs from a 32-bit
   // window; 1 = width 5, pairs from a 64-bit window; 2 = wider, singles
   const uint32_t vmode = bv <= 4 ? 0u : (bv == 5 ? 1u : 2u);
@@ -695,14 +702,14 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
               const uint32_t x = win32(wa[mt], wb[mt], vctl);
-              const uint32_t c0 = *reinterpret_cast<const uint32_t*>(s_tab + vtb + 8 * __builtin_amdgcn_ubfe(x, oa, w2));
-              const uint32_t c1 = *reinterpret_cast<const uint32_t*>(s_tab + vtb + 8 * __builtin_amdgcn_ubfe(x, ob, w2));
+              const uint32_t c0 = *reinterpret_cast<const uint32_t*>(s_tab + vtb + (__builtin_amdgcn_ubfe(x, oa, w2) << vsh));
+              const uint32_t c1 = *reinterpret_cast<const uint32_t*>(s_tab + vtb + (__builtin_amdgcn_ubfe(x, ob, w2) << vsh));
               VA[mt] = u32x4{c0, c1, c0, c1};
             }
           } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              VA[mt] = vdec8_hpairs4(win32(wa[mt], wb[mt], vctl), w2, w2, o2, o3, vtb, s_tab);
+              VA[mt] = vdec8_hpairs4(win32(wa[mt], wb[mt], vctl), w2, w2, o2, o3, vtb, vsh, s_tab);
           }
         } else {                       // wider: high parts from the LDS tables
           uint32_t wa[MT], wb[MT], wc[MT];
