@@ -432,7 +432,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 MFMA operands (levels and query as fp16 hi+lo pairs), fp32 accumulation",
+        "dtype": ("fp16 MFMA operands (key levels and query as fp16 hi+lo pairs, value levels "
+                  + ("as hi+lo pairs" if args.window else "as fp16") + "), fp32 accumulation"),
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": wl.layers, "q_heads": wl.h_q, "kv_heads": wl.h_kv,
                    "head_dim": wl.d, "context": ctx, "batch": batch, "budget": f"K{wl.k_bits}V{wl.v_bits}",
