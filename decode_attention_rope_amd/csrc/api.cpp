@@ -388,6 +388,7 @@ static bgtq_status prepare_decode(const bgtq_quantizer* qz, const bgtq_cache* ca
                  decode_stream_fits(d, record_chunks(cache->k_width_sum), cache->v_bits);
   if (a.use_stream) {
     a.n_split = decode_stream_splits(cache->batch, cache->n_kv_heads);
+    a.stream_whole_tiles = decode_stream_whole_tiles(cache->batch, cache->n_kv_heads) ? 1 : 0;
   } else {
     const int base = decode_splits(cache->batch, cache->n_kv_heads, cache->capacity, a.use_mfma);
     // the matrix-core pass leaves one workgroup of every (sequence, KV head) to a decode step's

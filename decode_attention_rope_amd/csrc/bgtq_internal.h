@@ -87,6 +87,9 @@ int decode_splits(int batch, int n_kv_heads, int64_t capacity, bool mfma);
 // tiles that fit its staging), and its split count per (sequence, KV head)
 bool decode_stream_fits(int d, int chunks, int v_bits);
 int decode_stream_splits(int batch, int n_kv_heads);
+// whether its remaining tiles go out whole (a launch of several rounds of workgroups) rather than
+// as quarter units
+bool decode_stream_whole_tiles(int batch, int n_kv_heads);
 // splits that attend over a window of w tokens (at most two 64-token tiles each)
 inline int window_splits(int w) { return w > 0 ? ((w + kTile - 1) / kTile + 2) / 2 : 0; }
 constexpr int kMaxWindowSplits = (BGTQ_MAX_WINDOW / kTile + 2) / 2;
@@ -165,6 +168,7 @@ struct DecodeArgs {
   int step;           // decode step: one token is appended beside the pass (its append role)
   int use_mfma;
   int use_stream;             // the streamed matrix-core split pass (no window, head dims 64/128)
+  int stream_whole_tiles;     // streamed pass: remaining tiles go out whole (else as quarter units)
   const uint16_t* k_window;   // fp16 recent keys (see AppendArgs)
   int window;                 // 0: no window
   int n_wsplit;               // the first n_wsplit splits attend over the window's tokens

@@ -270,8 +270,13 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   // append is over long before; taken first, that wait stalled the step.)
   const int tiles = (len + kTile - 1) / kTile;
   const int W = kStreamWaves * n_ps, vidx = split + n_ps * wave;
-  const int base = tiles / W, rem = tiles - base * W;
-  int nqu = 4 * rem > vidx ? (4 * rem - vidx + W - 1) / W : 0;
+  const int base0 = tiles / W, rem = tiles - base0 * W;
+  // a launch of several rounds of workgroups (a batch of many units) hands the remaining tiles
+  // out whole, one more to waves vidx < rem: there the total work sets the time, and a quarter
+  // costs more than a quarter of a tile and stages the whole tile
+  const bool whole = keep_s(a.stream_whole_tiles) != 0;
+  const int base = whole && vidx < rem ? base0 + 1 : base0;
+  int nqu = !whole && 4 * rem > vidx ? (4 * rem - vidx + W - 1) / W : 0;
   if (nqu > 0) {              // a quarter of the last tile whose first token is past the length holds none
     const int u = vidx + (nqu - 1) * W;
     if (kTile * (base * W + u / 4) + 32 * ((u & 3) >> 1) + 4 * (u & 1) >= len) --nqu;
@@ -286,14 +291,14 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
     if (len == len0 + 1) {
       const int tn = len0 / kTile;
       int own, kk;
-      if (tn < base * W) {
+      if (whole || tn < base0 * W) {
         own = tn % W;
         kk = tn / W;
       } else {
         const int sl = len0 % kTile;                  // its slot: quarter 2 (sl / 32) + (sl / 4) % 2
-        const int u = 4 * (tn - base * W) + 2 * (sl >> 5) + ((sl >> 2) & 1);
+        const int u = 4 * (tn - base0 * W) + 2 * (sl >> 5) + ((sl >> 2) & 1);
         own = u % W;
-        kk = base + u / W;
+        kk = base0 + u / W;
       }
       if (own == vidx) k_new = kk;
     }

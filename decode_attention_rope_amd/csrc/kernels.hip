@@ -2840,6 +2840,10 @@ int decode_stream_splits(int batch, int n_kv_heads) {
   return base > 2 ? int(base - 1) : 1;
 }
 
+bool decode_stream_whole_tiles(int batch, int n_kv_heads) {
+  return batch > 1 && int64_t(batch) * n_kv_heads >= 16;   // the oversubscribed grid above
+}
+
 size_t decode_qrot_bytes(int batch, int n_kv_heads, int d) {
   return size_t(batch) * n_kv_heads * d * kQPad * 4;
 }
