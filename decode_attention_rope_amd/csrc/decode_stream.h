@@ -792,6 +792,8 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   // ---- merge of the 8 waves: running maxima and sums through LDS, then each wave's
   // accumulator scaled to the common maximum, summed in wave order.  Lane (c, j) holds head
   // c % 8, coordinates 16 mt + 4 j + r.  The lane indices are taken afresh (opaque copies).
+  // The split's partial result is stored at device scope (written through the L2), which leaves
+  // the end of the pass less to write back before the merge kernel reads it (≈1% per call).
   int le = lane;
   asm volatile("" : "+v"(le));
   const int ne = le & 15, je = le >> 4;
@@ -827,7 +829,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
 #pragma unroll
     for (int w = 0; w < kStreamWaves; ++w) x += accw[(8 * w + h) * RS + r];
     const int64_t row = (int64_t(s) * n_q + hk * group + h) * n_ps + split;
-    partial[row * D + r] = x;
+    __hip_atomic_store(&partial[row * D + r], x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // written through: read by the merge kernel
   }
   if (tid < group) {
     float mx = -INFINITY;
@@ -840,6 +842,7 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       lsum += mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mx) * lws[8 * w + tid];
     }
     const int64_t row = (int64_t(s) * n_q + hk * group + tid) * n_ps + split;
-    part_ml[row] = uint64_t(__float_as_uint(mx)) | uint64_t(__float_as_uint(lsum)) << 32;
+    __hip_atomic_store(&part_ml[row], uint64_t(__float_as_uint(mx)) | uint64_t(__float_as_uint(lsum)) << 32,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
