@@ -56,7 +56,9 @@ constexpr int kSTabPair = 0;                                   // uint2 [kPairWo
 constexpr int kSTabSingle = kSTabPair + 8 * kPairWords;        // uint32 [kSingleHalves] hi | lo << 16
 constexpr int kSTabV = kSTabSingle + 4 * kSingleHalves;       // uint32 [84] high-part pairs of widths 1..3
 constexpr int kVPairWords = 84;                                 // 4 + 16 + 64 entries
-constexpr int kSTabBytes = (kSTabV + 4 * kVPairWords + 255) & ~255;
+constexpr int kSTabVQ = kSTabV + 4 * kVPairWords;             // uint2 [272] fp16 levels of 4 codes, widths 1, 2
+constexpr int kVQuadWords = 16 + 256;
+constexpr int kSTabBytes = (kSTabVQ + 8 * kVQuadWords + 255) & ~255;
 __host__ __device__ constexpr int stream_pro_bytes(int D) {
   return BGTQ_LAYOUT_BYTES + 32 * D + 2 * 1024 * kQRegSteps;   // layout, q' [D][8], B hi [8][64], B lo [8][64]
 }
@@ -497,6 +499,15 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
       }
     }
   }
+  // value quads of widths 1 and 2 (entry c0 | c1 << w | c2 << 2w | c3 << 3w: the fp16 levels of
+  // the four codes), built from the single table's high parts
+  if (tid < kVQuadWords) {
+    const int w = tid < 16 ? 1 : 2, i = tid < 16 ? tid : tid - 16, mk = (1 << w) - 1;
+    const uint32_t* sg = reinterpret_cast<const uint32_t*>(s_tab + kSTabSingle) + single_base(w);
+    const uint32_t l0 = sg[i & mk] & 0xffffu, l1 = sg[(i >> w) & mk] & 0xffffu;
+    const uint32_t l2 = sg[(i >> (2 * w)) & mk] & 0xffffu, l3 = sg[(i >> (3 * w)) & mk] & 0xffffu;
+    reinterpret_cast<uint2*>(s_tab + kSTabVQ)[tid] = uint2{l0 | l1 << 16, l2 | l3 << 16};
+  }
   lds_barrier();
 
   // ---- per-lane constants
@@ -518,6 +529,9 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   // value decode, from the high parts of the key tables: 0 = widths <= 4, pairs from a 32-bit
   // window; 1 = width 5, pairs from a 64-bit window; 2 = wider, singles
   const uint32_t vmode = bv <= 4 ? 0u : (bv == 5 ? 1u : 2u);
+  // widths 1 and 2 read four codes per lookup from the quad table
+  const bool vquad = bv <= 2;
+  const uint32_t vqb = uint32_t(kSTabVQ + 8 * (bv == 1 ? 0 : 16));
 
   f32x4 acc[MT];
 #pragma unroll
@@ -701,7 +715,20 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
             wb[mt] = ld32(vb + mt * vmt + 4);
           }
           const uint32_t w2 = vctl >> 8, o2 = vctl >> 16, o3 = vctl >> 24;   // 2 b_v, 4 b_v, 6 b_v (bits 4:0)
-          if constexpr (NRB == 1) {    // a quarter: its row block's four codes, repeated in the other half
+          if (vquad) {                 // quads: codes 0..3 at bit 0, codes 4..7 at bit 4 b_v
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const uint32_t x = win32(wa[mt], wb[mt], vctl);
+              if constexpr (NRB == 1) {   // a quarter: its row block's four codes, repeated in the other half
+                const uint2 c = *reinterpret_cast<const uint2*>(s_tab + vqb + 8 * __builtin_amdgcn_ubfe(x, (rb0 & 1) ? o2 : 0u, o2));
+                VA[mt] = u32x4{c.x, c.y, c.x, c.y};
+              } else {
+                const uint2 c0 = *reinterpret_cast<const uint2*>(s_tab + vqb + 8 * __builtin_amdgcn_ubfe(x, 0u, o2));
+                const uint2 c1 = *reinterpret_cast<const uint2*>(s_tab + vqb + 8 * __builtin_amdgcn_ubfe(x, o2, o2));
+                VA[mt] = u32x4{c0.x, c0.y, c1.x, c1.y};
+              }
+            }
+          } else if constexpr (NRB == 1) {    // a quarter: its row block's four codes, repeated in the other half
             const bool hi = (rb0 & 1) != 0;
             const uint32_t oa = hi ? o2 : 0u, ob = hi ? o3 : w2;
 #pragma unroll
