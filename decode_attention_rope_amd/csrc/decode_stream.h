@@ -52,6 +52,31 @@ __host__ __device__ inline StreamSlot stream_slot(int D, int chunks, int bv) {
 // compiler's waits for one ring's loads leave the other's in flight), decoder tables, k-step
 // descriptors, the prologue's area (layout copy, q', B operands), the merge's exchange.
 __host__ __device__ constexpr int stream_slot_max(int D) { return D == 128 ? 7424 : 5376; }
+
+// Batch launches of several workgroup rounds: the dispatcher starts workgroups in index order,
+// so grid slot z takes the z-th longest sequence (equal lengths in index order).  The longest
+// sequences' workgroups then start first and the last round holds short ones (longest
+// processing time first).  The ranks come from the lengths every workgroup reads alike, so the
+// slots map one to one onto the sequences, and a decode step's append role (workgroup 0 of a
+// slot) still starts before the splits that wait for it.  Batches of more than kLptMaxBatch
+// sequences keep index order.  lds: kLptMaxBatch + 1 ints.
+constexpr int kLptMaxBatch = 64;
+__device__ __forceinline__ int seq_longest_first(const int32_t* lengths, int nb, int* lds) {
+  const int t = threadIdx.x;
+  if (t < nb) lds[t] = lengths[t];
+  __syncthreads();
+  if (t < nb) {
+    const int lt = lds[t];
+    int rank = 0;
+    for (int u = 0; u < nb; ++u) {
+      const int lu = lds[u];
+      rank += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
+    }
+    if (rank == int(blockIdx.z)) lds[kLptMaxBatch] = t;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(lds[kLptMaxBatch]);
+}
 constexpr int kSTabPair = 0;                                   // uint2 [kPairWords] hi, lo
 constexpr int kSTabSingle = kSTabPair + 8 * kPairWords;        // uint32 [kSingleHalves] hi | lo << 16
 constexpr int kSTabV = kSTabSingle + 4 * kSingleHalves;       // uint32 [84] high-part pairs of widths 1..3
@@ -244,14 +269,17 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   __shared__ __align__(16) uint8_t s_pro[stream_pro_bytes(D)];
   __shared__ __align__(16) uint8_t s_ring0[kStreamWaves * SLOT];
   __shared__ __align__(16) uint8_t s_ring1[kStreamWaves * SLOT];
+  const int s = keep_s(a.stream_whole_tiles) != 0 && a.batch <= kLptMaxBatch
+                    ? seq_longest_first(a.lengths, a.batch, reinterpret_cast<int*>(s_ml))
+                    : int(blockIdx.z);
   if constexpr (STEP) {
     if (blockIdx.x == 0) {          // decode step: workgroup 0 of every (sequence, KV head) appends
-      if (aa.givens) step_append_role<false, true>(aa, a.step_flag, blockIdx.z, blockIdx.y, s_ring0);
-      else step_append_role<false, false>(aa, a.step_flag, blockIdx.z, blockIdx.y, s_ring0);
+      if (aa.givens) step_append_role<false, true>(aa, a.step_flag, s, blockIdx.y, s_ring0);
+      else step_append_role<false, false>(aa, a.step_flag, s, blockIdx.y, s_ring0);
       return;
     }
   }
-  const int split = int(blockIdx.x) - (STEP ? 1 : 0), hk = blockIdx.y, s = blockIdx.z;
+  const int split = int(blockIdx.x) - (STEP ? 1 : 0), hk = blockIdx.y;
   const int group = keep_s(a.group), n_q = keep_s(a.n_q);
   const gptr<float> partial = keep_g(a.partial);
   const gptr<uint64_t> part_ml = keep_g(reinterpret_cast<uint64_t*>(a.part_ml));   // (max, sum) pairs

@@ -2829,11 +2829,13 @@ int decode_stream_splits(int batch, int n_kv_heads) {
   // Few (sequence, KV head) units: one workgroup per compute unit, 256 over the units, one of
   // each unit's share left to a decode step's append role.  A batch of many units: the
   // sequences' lengths may differ widely while every unit takes the same number of splits, so
-  // the grid is four times the compute units and the dispatcher hands a freed unit the next
-  // split; a long sequence's splits then no longer set the time of the whole call.
+  // the grid is two rounds of the compute units, the longest sequences' workgroups first (the
+  // pass maps grid slots to sequences by length), and the dispatcher hands a freed compute unit
+  // the next workgroup: the second round's short workgroups fill in behind the long ones.  (Four
+  // rounds pay the pass's fixed cost per workgroup twice as often.)
   const int64_t units = int64_t(batch) * n_kv_heads;
   if (batch > 1 && units >= 16) {
-    const int64_t over = 4 * 256 / units;
+    const int64_t over = 2 * 256 / units;
     return over > 2 ? int(over) : 2;
   }
   const int64_t base = 256 / units;

@@ -308,13 +308,18 @@ def test_decode_ragged_lengths(t_lens, rot128):
     _decode_vs_oracle(wl, t_lens, qz, bank, rv)
 
 
-def test_decode_batch_whole_remainder_tiles(rot128):
-    """A batch of 16 (sequence, KV head) units, so the streamed pass launches several rounds of
-    workgroups and hands remaining tiles out whole: ragged lengths with partial tiles and lengths
-    below and above one round of waves, decode step twin bit for bit, every head against the oracle."""
-    _say("decode batch of 8 x 2 KV heads, whole remainder tiles")
+@pytest.mark.parametrize("t_lens", [
+    [1000, 3, 129, 4096, 64, 65, 2000, 777],      # distinct lengths, not in order
+    [700, 3, 700, 4096, 64, 700, 2000, 64],       # equal lengths: ranked in index order
+    [(37 * i) % 301 + 2 for i in range(66)],      # more sequences than the pass ranks: index order
+], ids=["distinct", "ties", "66seqs"])
+def test_decode_batch_whole_remainder_tiles(rot128, t_lens):
+    """A batch of at least 16 (sequence, KV head) units, so the streamed pass launches several
+    rounds of workgroups, maps grid slots to sequences longest first and hands remaining tiles out
+    whole: ragged lengths with partial tiles and lengths below and above one round of waves,
+    decode step twin bit for bit, every head against the oracle."""
+    _say(f"decode batch of {len(t_lens)} x 2 KV heads, whole remainder tiles")
     bank, rv, qz = rot128
-    t_lens = [1000, 3, 129, 4096, 64, 65, 2000, 777]
     wl = synth.Workload("wholetiles", 96, d=128, h_q=16, h_kv=2, theta=1e6, layers=1, seq_lens=tuple(t_lens),
                         k_bits=3, v_bits=3, key_dtype="f32", profile="decay_jitter", outlier_blocks=2)
     _decode_vs_oracle(wl, t_lens, qz, bank, rv, append_then_attend=True, step_twin=True)
