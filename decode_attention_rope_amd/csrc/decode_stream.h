@@ -59,7 +59,7 @@ __host__ __device__ constexpr int stream_slot_max(int D) { return D == 128 ? 742
 // processing time first).  The ranks come from the lengths every workgroup reads alike, so the
 // slots map one to one onto the sequences, and a decode step's append role (workgroup 0 of a
 // slot) still starts before the splits that wait for it.  Batches of more than kLptMaxBatch
-// sequences keep index order.  lds: kLptMaxBatch + 1 ints.
+// sequences keep index order (the launch picks the instantiation).  lds: kLptMaxBatch + 1 ints.
 constexpr int kLptMaxBatch = 64;
 __device__ __forceinline__ int seq_longest_first(const int32_t* lengths, int nb, int* lds) {
   const int t = threadIdx.x;
@@ -256,7 +256,7 @@ __device__ __forceinline__ f16x8 bdup(uint32_t x01, uint32_t x23) {
 // k-step class: 0 = every segment at most 4 bits wide, 1 = at most 5, 2 = wider
 __device__ __forceinline__ uint32_t seg_class(uint32_t w) { return w <= 4 ? 0u : (w == 5 ? 1u : 2u); }
 
-template <int D, typename QT, bool STEP>
+template <int D, typename QT, bool STEP, bool ORDER>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   constexpr int MT = D / 16;                         // value M-tiles (16 coordinates each)
@@ -269,9 +269,11 @@ void k_decode_stream(DecodeArgs a, AppendArgs aa) {
   __shared__ __align__(16) uint8_t s_pro[stream_pro_bytes(D)];
   __shared__ __align__(16) uint8_t s_ring0[kStreamWaves * SLOT];
   __shared__ __align__(16) uint8_t s_ring1[kStreamWaves * SLOT];
-  const int s = keep_s(a.stream_whole_tiles) != 0 && a.batch <= kLptMaxBatch
-                    ? seq_longest_first(a.lengths, a.batch, reinterpret_cast<int*>(s_ml))
-                    : int(blockIdx.z);
+  // ORDER: a batch launch of several rounds, grid slots taken longest sequence first (a
+  // separate instantiation, so that the one-round pass carries none of it)
+  int s_slot = int(blockIdx.z);
+  if constexpr (ORDER) s_slot = seq_longest_first(a.lengths, a.batch, reinterpret_cast<int*>(s_ml));
+  const int s = s_slot;
   if constexpr (STEP) {
     if (blockIdx.x == 0) {          // decode step: workgroup 0 of every (sequence, KV head) appends
       if (aa.givens) step_append_role<false, true>(aa, a.step_flag, s, blockIdx.y, s_ring0);

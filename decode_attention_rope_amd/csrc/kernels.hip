@@ -2581,9 +2581,13 @@ hipError_t launch_decode_d(const DecodeArgs& a, bgtq_dtype q_dt, hipStream_t st,
   if (a.use_stream) {
     if constexpr (D <= 128) {
       const bool bf16 = q_dt == BGTQ_BF16;
+      // batch launches of several rounds start the longest sequences first
+      const bool order = a.stream_whole_tiles != 0 && a.batch <= kLptMaxBatch;
       void (*fn)(DecodeArgs, AppendArgs) =
-          step ? (bf16 ? k_decode_stream<D, uint16_t, true> : k_decode_stream<D, float, true>)
-               : (bf16 ? k_decode_stream<D, uint16_t, false> : k_decode_stream<D, float, false>);
+          order ? (step ? (bf16 ? k_decode_stream<D, uint16_t, true, true> : k_decode_stream<D, float, true, true>)
+                        : (bf16 ? k_decode_stream<D, uint16_t, false, true> : k_decode_stream<D, float, false, true>))
+                : (step ? (bf16 ? k_decode_stream<D, uint16_t, true, false> : k_decode_stream<D, float, true, false>)
+                        : (bf16 ? k_decode_stream<D, uint16_t, false, false> : k_decode_stream<D, float, false, false>));
       hipLaunchKernelGGL(fn, grid, dim3(kStreamThreads), 0, st, a, step ? *step : AppendArgs{});
     } else {
       return hipErrorInvalidValue;
